@@ -1,0 +1,218 @@
+/*
+ * lca.h -- C ABI of the MI355X (gfx950) CSA/HCA hot-path library (liblca.so).
+ *
+ * The library implements DeepSeek-V4's hybrid compressed attention for decode
+ * and chunked prefill:
+ *   - compression of raw KV tokens by softmax-gated pooling with a learned
+ *     positional bias, every m tokens into one entry (m = 4 for CSA, m' = 128
+ *     for HCA);
+ *   - the lightning indexer (ReLU-scored multi-head dot products on FP4) and
+ *     top-k selection of compressed entries per query;
+ *   - shared-KV (MQA) attention over the selected entries (CSA) or over all
+ *     entries (HCA), plus a sliding window of recent raw tokens and a per-head
+ *     attention sink.
+ * Sources: "DeepSeek-V4 發佈說明：為 AI Agents 提供高效的 1M-Token 上下文"
+ * (agentlenshq.com), sections 壓縮稀疏注意力 (CSA), 重度壓縮注意力 (HCA) and
+ * 架構實現; "DeepSeek V4: Towards Highly Efficient Million-Token Context
+ * Intelligence" (chenshi221.pages.dev wiki), section 关键技术方法 (架构创新,
+ * 基础设施).
+ *
+ * Conventions (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, at least
+ *     16-byte aligned.  The library never allocates device memory and never
+ *     synchronises; scratch space comes from a caller-provided workspace whose
+ *     size the *_ws() queries return.
+ *   - Every compute call is enqueued asynchronously on `stream` (a hipStream_t;
+ *     NULL is the default stream) and keeps no state between calls.  Calls are
+ *     thread-safe; calls that share a workspace must not overlap.
+ *   - Layouts are row-major and dense; D (or d_I) is the innermost dimension.
+ *     "[B][R][D]" means sequence b's row r starts at element (b*R + r)*D.
+ *   - Storage types (lca_dtype):
+ *       LCA_F32      float
+ *       LCA_BF16     bfloat16 (uint16 bit patterns)
+ *       LCA_FP8E4M3  OCP E4M3 bytes + one fp32 scale per 64 consecutive
+ *                    elements of a row (decoded value = e4m3(code) * scale)
+ *       LCA_MXFP4    OCP MX E2M1 nibbles, two per byte (element 2i in the low
+ *                    nibble) + one E8M0 scale byte per 32 elements (decoded
+ *                    value = e2m1(code) * 2^(byte - 127))
+ *   - Host-side validation runs before anything is enqueued.  On any error the
+ *     call returns a non-zero lca_status, enqueues nothing, and
+ *     lca_last_error() returns a message (thread-local).  No exception crosses
+ *     the ABI.  Loading the library and validating arguments need no GPU.
+ *   - Values held in device index arrays (lengths, offsets, selected indices)
+ *     cannot be checked on the host; the caller guarantees the ranges stated
+ *     for each call.  Kernels clamp what they can (out-of-range selected
+ *     indices are skipped) and never read outside the stated buffers when the
+ *     ranges hold.
+ *   - Inputs must be finite (no NaN/Inf, no FP8 NaN codes, no E8M0 0xFF).
+ */
+#ifndef LCA_H
+#define LCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lca_status {
+  LCA_OK = 0,
+  LCA_EINVAL = 1,      /* null pointer, bad size or stride, misalignment, k out of range */
+  LCA_ENOTSUP = 2,     /* unsupported dtype or shape combination */
+  LCA_EHIP = 3,        /* a HIP runtime or launch error (message kept) */
+  LCA_EWORKSPACE = 4   /* workspace pointer null or smaller than the *_ws() query */
+} lca_status;
+
+typedef enum lca_dtype {
+  LCA_F32 = 0,
+  LCA_BF16 = 1,
+  LCA_FP8E4M3 = 2,
+  LCA_MXFP4 = 3
+} lca_dtype;
+
+#define LCA_ABI_VERSION 1
+
+/* Version of this ABI (LCA_ABI_VERSION). */
+int32_t lca_abi_version(void);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* lca_last_error(void);
+
+/*
+ * lca_csa_compress / lca_hca_compress -- softmax-gated pooling with positional
+ * bias.  [release notes (agentlenshq.com), 壓縮稀疏注意力 (CSA): 4x along the
+ * sequence; 重度壓縮注意力 (HCA): 128x.  wiki (chenshi221), 架构创新: every m
+ * tokens become one entry.]
+ *
+ * For sequence b and block i < nblk[b], with tokens t = x_tok0[b] + i*m + u
+ * (u = 0..m-1):
+ *     a_u = gate[b][t] + pos_bias[u]
+ *     w_u = exp(a_u - max a) / sum_u' exp(a_u' - max a)
+ *     c   = sum_u w_u * x[b][t]            (accumulated in fp32)
+ * c is written to row dst_row0[b] + i of sequence b in `dst`, encoded as
+ * dst_dt (FP8: per-64 scale s = amax/448, codes RNE-saturated; MXFP4: per-32
+ * shared exponent floor(log2 amax) - 2, E2M1 RNE-saturated; BF16: RNE).
+ *   x        [B][x_rows][D]   x_dt in {F32, BF16}
+ *   gate     [B][x_rows]      fp32, one logit per raw token
+ *   pos_bias [m]              fp32
+ *   x_tok0, nblk [B] int32; dst_row0 [B] int64 (device arrays).  Caller
+ *            guarantees 0 <= nblk[b] <= nblk_max, x_tok0[b] >= 0,
+ *            x_tok0[b] + nblk[b]*m <= x_rows, 0 <= dst_row0[b],
+ *            dst_row0[b] + nblk[b] <= dst_rows.
+ *   dst      [B][dst_rows][D] (MXFP4: [B][dst_rows][D/2] bytes)
+ *   dst_scale FP8: float [B][dst_rows][D/64]; MXFP4: uint8 [B][dst_rows][D/32];
+ *            must be NULL for F32/BF16.
+ *   pooled   optional fp32 [B][nblk_max][D]: c before encoding (row i of
+ *            sequence b), rows i >= nblk[b] untouched.
+ * Supported: D in {64, 128}; csa_compress 1 <= m <= 64; hca_compress
+ * 1 <= m <= 1024.  m = 1 with zero gate and bias is an exact copy (used to
+ * encode raw values into a cache format).
+ */
+lca_status lca_csa_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const float* gate,
+                            const float* pos_bias, int32_t m, const int32_t* x_tok0,
+                            const int32_t* nblk, const int64_t* dst_row0, int32_t B,
+                            int32_t nblk_max, int32_t D, void* dst, lca_dtype dst_dt,
+                            void* dst_scale, int64_t dst_rows, float* pooled, void* stream);
+
+lca_status lca_hca_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const float* gate,
+                            const float* pos_bias, int32_t m, const int32_t* x_tok0,
+                            const int32_t* nblk, const int64_t* dst_row0, int32_t B,
+                            int32_t nblk_max, int32_t D, void* dst, lca_dtype dst_dt,
+                            void* dst_scale, int64_t dst_rows, float* pooled, void* stream);
+
+/*
+ * lca_lightning_index_topk -- lightning-indexer scores and top-k selection.
+ * [release notes (agentlenshq.com), 壓縮稀疏注意力 (CSA): FP4, ReLU-scored
+ * multi-head dot products pick the top-k compressed blocks per query; wiki
+ * (chenshi221), 基础设施: MXFP4 on the indexer QK path.]
+ *
+ * Query row r = b*Tq + t scores entries j < n_elig[r] of sequence b:
+ *     s_j = sum_{h<H_I} w[r][h] * max(0, sum_{i<d_I} qi[r][h][i] * ki[b][j][i])
+ * with every per-head dot product and the head sum evaluated exactly as the
+ * float64 sum left to right over i and then over h of the decoded values
+ * (products formed, then added).  The selection orders entries by (s_j
+ * descending, j ascending) and keeps the first min(k, n_elig[r]).
+ *   qi     [B][Tq][H_I][d_I]   qi_dt in {F32, MXFP4}; qi_scale: E8M0
+ *          [B][Tq][H_I][d_I/32] for MXFP4, NULL otherwise
+ *   w      [B][Tq][H_I] fp32 head weights
+ *   ki     [B][N_cap][d_I]     ki_dt == qi_dt; ki_scale E8M0 [B][N_cap][d_I/32]
+ *   n_elig [B][Tq] int32 (device), caller guarantees 0 <= n_elig <= N_cap
+ *   idx_out   [B][Tq][k] int32: the selected j in ascending order, -1 padded
+ *   score_out optional [B][Tq][k] double: s_j of each idx_out entry (0 for -1)
+ *   ws / ws_bytes: workspace of at least lca_index_topk_ws(...) bytes
+ * Supported: 1 <= k <= 2048; MXFP4: H_I <= 16, d_I in {64, 128}; F32:
+ * H_I <= 64, d_I in {32, 64, 128}; N_cap < 2^31.
+ * Results are deterministic and independent of B and of the other rows.
+ */
+lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8_t* qi_scale,
+                                    const float* w, const void* ki, lca_dtype ki_dt,
+                                    const uint8_t* ki_scale, const int32_t* n_elig, int32_t B,
+                                    int32_t Tq, int32_t H_I, int32_t d_I, int64_t N_cap,
+                                    int32_t k, int32_t* idx_out, double* score_out, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+size_t lca_index_topk_ws(int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int64_t N_cap,
+                         int32_t k);
+
+/*
+ * lca_sparse_mqa_attend -- CSA attention of each query over its selected
+ * compressed entries, a window of raw tokens and a per-head sink.
+ * [wiki (chenshi221), 架构创新: top-k sparse selection + MQA, sliding-window
+ * branch and attention sink; release notes, 壓縮稀疏注意力 (CSA): the window
+ * holds recent uncompressed tokens.]
+ *
+ * For query row r = b*Tq + t and head h (one vector per entry/token serves as
+ * key and value, shared by all heads):
+ *     l_j = scale * <q[r][h], kv[b][j]>     for j in idx[r] (entries != -1)
+ *     l_u = scale * <q[r][h], win[b][u]>    for u in [win_begin[r], win_begin[r] + win_len[r])
+ *     M   = max(sink[h], all l);  Z = exp(sink[h] - M) + sum exp(l - M)
+ *     out[r][h] = (sum_j exp(l_j - M) kv[b][j] + sum_u exp(l_u - M) win[b][u]) / Z
+ *     lse[r][h] = M + log Z
+ * The sink logit is not multiplied by `scale` and has a zero value vector.
+ *   q      [B][Tq][Hq][D]  q_dt in {F32, BF16}
+ *   kv     [B][N_cap][D]   kv_dt in {F32, BF16, FP8E4M3}; kv_scale fp32
+ *          [B][N_cap][D/64] for FP8, NULL otherwise
+ *   idx    [B][Tq][k] int32 (device); entries < 0 or >= N_cap are skipped
+ *   win    [B][W_buf][D]   win_dt in {F32, BF16}; win_begin/win_len [B][Tq]
+ *          int32 (device), caller guarantees 0 <= win_begin,
+ *          0 <= win_len, win_begin + win_len <= W_buf
+ *   sink   [Hq] fp32
+ *   out    [B][Tq][Hq][D]  out_dt in {F32, BF16}; lse optional fp32 [B][Tq][Hq]
+ * Supported: D = 128; Hq in {16, 32, 64}; 0 <= k <= 2048.  F32 inputs are
+ * computed in fp32; BF16/FP8 inputs use bf16 matrix cores with fp32
+ * accumulation and softmax.
+ */
+lca_status lca_sparse_mqa_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,
+                                 const float* kv_scale, int64_t N_cap, const int32_t* idx,
+                                 int32_t k, const void* win, lca_dtype win_dt, int64_t W_buf,
+                                 const int32_t* win_begin, const int32_t* win_len,
+                                 const float* sink, float scale, int32_t B, int32_t Tq,
+                                 int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * lca_hca_attend -- HCA attention: as lca_sparse_mqa_attend, but over every
+ * eligible entry j < n_elig[r] of sequence b instead of a selected list.
+ * [release notes (agentlenshq.com), 重度壓縮注意力 (HCA): the 128x compressed
+ * sequence is short, so it is attended densely, plus a sliding window.]
+ *   n_elig [B][Tq] int32 (device), caller guarantees 0 <= n_elig <= N_cap.
+ * Supported: as lca_sparse_mqa_attend.
+ */
+lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,
+                          const float* kv_scale, int64_t N_cap, const int32_t* n_elig,
+                          const void* win, lca_dtype win_dt, int64_t W_buf,
+                          const int32_t* win_begin, const int32_t* win_len, const float* sink,
+                          float scale, int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out,
+                          lca_dtype out_dt, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for the attention calls.  n_kv_max is k for
+ * lca_sparse_mqa_attend and N_cap for lca_hca_attend; W_buf the window buffer
+ * rows. */
+size_t lca_attend_ws(int32_t B, int32_t Tq, int32_t Hq, int32_t D, int64_t n_kv_max,
+                     int64_t W_buf);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCA_H */

@@ -1,0 +1,178 @@
+"""Python binding of liblca.so, the MI355X (gfx950) CSA/HCA hot-path library.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch tensors on the GPU (PyTorch provides device memory and the
+current stream); each wrapper passes their data pointers to the C ABI declared
+in include/lca.h and raises LcaError when the library reports an error.  If
+the built library is missing, importing works but every call raises.
+
+Storage types: F32 (torch.float32), BF16 (torch.bfloat16), FP8E4M3 (uint8 codes
++ float32 scale per 64 elements), MXFP4 (uint8, two E2M1 codes per byte +
+uint8 E8M0 scale per 32 elements).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblca.so")
+
+F32, BF16, FP8E4M3, MXFP4 = 0, 1, 2, 3
+STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA_EWORKSPACE"}
+
+EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress",
+           "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
+           "lca_hca_attend", "lca_attend_ws"]
+
+
+class LcaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load liblca.so (no GPU needed) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise LcaError(3, f"liblca.so not built at {path}; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    L.lca_abi_version.restype = i32
+    L.lca_abi_version.argtypes = []
+    L.lca_last_error.restype = ctypes.c_char_p
+    L.lca_last_error.argtypes = []
+    comp = [vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp, i64, vp, vp]
+    for name in ("lca_csa_compress", "lca_hca_compress"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = comp
+    L.lca_lightning_index_topk.restype = i32
+    L.lca_lightning_index_topk.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i64,
+                                           i32, vp, vp, vp, sz, vp]
+    L.lca_index_topk_ws.restype = sz
+    L.lca_index_topk_ws.argtypes = [i32, i32, i32, i32, i64, i32]
+    L.lca_sparse_mqa_attend.restype = i32
+    L.lca_sparse_mqa_attend.argtypes = [vp, i32, vp, i32, vp, i64, vp, i32, vp, i32, i64, vp, vp, vp,
+                                        f32, i32, i32, i32, i32, vp, i32, vp, vp, sz, vp]
+    L.lca_hca_attend.restype = i32
+    L.lca_hca_attend.argtypes = [vp, i32, vp, i32, vp, i64, vp, vp, i32, i64, vp, vp, vp, f32, i32,
+                                 i32, i32, i32, vp, i32, vp, vp, sz, vp]
+    L.lca_attend_ws.restype = sz
+    L.lca_attend_ws.argtypes = [i32, i32, i32, i32, i64, i64]
+    _lib = L
+    return L
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise LcaError(status, load().lca_last_error().decode())
+
+
+def dtype_of(t, scale=None) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.uint8:
+        if scale is None:
+            raise ValueError("uint8 storage needs its scale tensor")
+        return FP8E4M3 if scale.dtype == torch.float32 else MXFP4
+    raise ValueError(f"unsupported tensor dtype {t.dtype}")
+
+
+def abi_version() -> int:
+    return load().lca_abi_version()
+
+
+# ---------------------------------------------------------------------------
+def _compress(fn, x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max, dst, dst_dt,
+              dst_scale=None, pooled=None, stream=None):
+    B, x_rows, D = x.shape
+    _check(fn(_p(x), dtype_of(x), x_rows, _p(gate), _p(pos_bias), int(m), _p(x_tok0), _p(nblk),
+              _p(dst_row0), B, int(nblk_max), D, _p(dst), int(dst_dt), _p(dst_scale),
+              dst.shape[1], _p(pooled), _stream(stream)))
+
+
+def csa_compress(x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max, dst, dst_dt,
+                 dst_scale=None, pooled=None, stream=None):
+    """Pool blocks of m raw tokens into cache rows (see lca_csa_compress).
+    x [B, x_rows, D] f32/bf16; gate [B, x_rows] f32; pos_bias [m] f32;
+    x_tok0/nblk int32 [B], dst_row0 int64 [B] on the device; dst [B, rows, D or D/2]."""
+    _compress(load().lca_csa_compress, x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max,
+              dst, dst_dt, dst_scale, pooled, stream)
+
+
+def hca_compress(x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max, dst, dst_dt,
+                 dst_scale=None, pooled=None, stream=None):
+    """As csa_compress, for m' up to 1024 (see lca_hca_compress)."""
+    _compress(load().lca_hca_compress, x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max,
+              dst, dst_dt, dst_scale, pooled, stream)
+
+
+# ---------------------------------------------------------------------------
+def index_topk_ws(B, Tq, H_I, d_I, N_cap, k) -> int:
+    return load().lca_index_topk_ws(B, Tq, H_I, d_I, N_cap, k)
+
+
+def lightning_index_topk(qi, qi_scale, w, ki, ki_scale, n_elig, k, idx_out, ws, score_out=None,
+                         H_I=None, d_I=None, stream=None):
+    """qi [B, Tq, H_I, d_I] f32, or uint8 [B, Tq, H_I, d_I/2] + qi_scale E8M0;
+    w [B, Tq, H_I] f32; ki [B, N_cap, d_I] f32 or uint8 [B, N_cap, d_I/2] + ki_scale;
+    n_elig int32 [B, Tq]; idx_out int32 [B, Tq, k]; ws uint8 workspace."""
+    B, Tq = qi.shape[0], qi.shape[1]
+    H = qi.shape[2] if H_I is None else H_I
+    dt = F32 if qi_scale is None else MXFP4
+    d = (qi.shape[3] if dt == F32 else qi.shape[3] * 2) if d_I is None else d_I
+    N_cap = ki.shape[1]
+    _check(load().lca_lightning_index_topk(
+        _p(qi), dt, _p(qi_scale), _p(w), _p(ki), dt, _p(ki_scale), _p(n_elig), B, Tq, H, d, N_cap,
+        int(k), _p(idx_out), _p(score_out), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+def attend_ws(B, Tq, Hq, D, n_kv_max, W_buf) -> int:
+    return load().lca_attend_ws(B, Tq, Hq, D, n_kv_max, W_buf)
+
+
+def sparse_mqa_attend(q, kv, kv_scale, idx, win, win_begin, win_len, sink, scale, out, lse=None,
+                      ws=None, stream=None):
+    """q [B,Tq,Hq,D] f32/bf16; kv [B,N_cap,D] f32/bf16/uint8(+kv_scale f32 [B,N_cap,D/64]);
+    idx int32 [B,Tq,k]; win [B,W_buf,D]; win_begin/win_len int32 [B,Tq]; sink f32 [Hq];
+    out [B,Tq,Hq,D] f32/bf16; lse optional f32 [B,Tq,Hq]."""
+    B, Tq, Hq, D = q.shape
+    k = idx.shape[-1]
+    _check(load().lca_sparse_mqa_attend(
+        _p(q), dtype_of(q), _p(kv), dtype_of(kv, kv_scale), _p(kv_scale), kv.shape[1], _p(idx), k,
+        _p(win), dtype_of(win), win.shape[1], _p(win_begin), _p(win_len), _p(sink), float(scale),
+        B, Tq, Hq, D, _p(out), dtype_of(out), _p(lse), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hca_attend(q, kv, kv_scale, n_elig, win, win_begin, win_len, sink, scale, out, lse=None,
+               ws=None, stream=None):
+    """As sparse_mqa_attend, attending densely over entries j < n_elig [B,Tq]."""
+    B, Tq, Hq, D = q.shape
+    _check(load().lca_hca_attend(
+        _p(q), dtype_of(q), _p(kv), dtype_of(kv, kv_scale), _p(kv_scale), kv.shape[1], _p(n_elig),
+        _p(win), dtype_of(win), win.shape[1], _p(win_begin), _p(win_len), _p(sink), float(scale),
+        B, Tq, Hq, D, _p(out), dtype_of(out), _p(lse), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))

@@ -1,0 +1,213 @@
+// abi.cpp -- the extern "C" entry points declared in include/lca.h: argument
+// validation (before anything is enqueued), workspace checks, launch
+// configuration and error reporting.  No HIP call is made before validation
+// succeeds, so loading the library and validating arguments need no GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/lca.h"
+#include "lca_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lca_status fail(lca_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lca_status ok() {
+  g_err[0] = '\0';
+  return LCA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQ(cond, st, ...) \
+  do {                      \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define PTR(p) REQ((p) != nullptr && aligned16(p), LCA_EINVAL, "%s must be a non-null 16-byte aligned pointer", #p)
+
+lca_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LCA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+lca_status compress_common(const char* name, int mmax, const void* x, lca_dtype x_dt, int64_t x_rows,
+                           const float* gate, const float* pos_bias, int32_t m, const int32_t* x_tok0,
+                           const int32_t* nblk, const int64_t* dst_row0, int32_t B, int32_t nblk_max,
+                           int32_t D, void* dst, lca_dtype dst_dt, void* dst_scale, int64_t dst_rows,
+                           float* pooled, void* stream) {
+  REQ(B >= 0 && nblk_max >= 0, LCA_EINVAL, "%s: B and nblk_max must be >= 0", name);
+  REQ(m >= 1 && m <= mmax, LCA_ENOTSUP, "%s: m=%d outside [1, %d]", name, m, mmax);
+  REQ(D == 64 || D == 128, LCA_ENOTSUP, "%s: D=%d (supported: 64, 128)", name, D);
+  REQ(x_dt == LCA_F32 || x_dt == LCA_BF16, LCA_ENOTSUP, "%s: x_dt must be F32 or BF16", name);
+  REQ(dst_dt >= LCA_F32 && dst_dt <= LCA_MXFP4, LCA_ENOTSUP, "%s: unknown dst_dt %d", name, (int)dst_dt);
+  REQ(x_rows >= 0 && dst_rows >= 0, LCA_EINVAL, "%s: x_rows and dst_rows must be >= 0", name);
+  REQ(B <= 65535, LCA_ENOTSUP, "%s: B=%d exceeds 65535", name, B);
+  REQ((int64_t)nblk_max * m <= x_rows, LCA_EINVAL, "%s: nblk_max*m=%lld exceeds x_rows=%lld", name,
+      (long long)nblk_max * m, (long long)x_rows);
+  REQ(nblk_max <= dst_rows, LCA_EINVAL, "%s: nblk_max=%d exceeds dst_rows=%lld", name, nblk_max,
+      (long long)dst_rows);
+  if (B == 0 || nblk_max == 0) return ok();
+  PTR(x); PTR(gate); PTR(pos_bias); PTR(x_tok0); PTR(nblk); PTR(dst_row0); PTR(dst);
+  if (dst_dt == LCA_FP8E4M3 || dst_dt == LCA_MXFP4) {
+    PTR(dst_scale);
+  } else {
+    REQ(dst_scale == nullptr, LCA_EINVAL, "%s: dst_scale must be NULL for F32/BF16 output", name);
+  }
+  if (pooled) REQ(aligned16(pooled), LCA_EINVAL, "%s: pooled must be 16-byte aligned", name);
+  lca::CompressArgs a{x, (int)x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0,
+                      B, nblk_max, D, dst, (int)dst_dt, dst_scale, dst_rows, pooled};
+  return hip_status(lca::launch_compress(a, (hipStream_t)stream), name);
+}
+
+lca_status attend_common(const char* name, int sparse, const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,
+                         const float* kv_scale, int64_t N_cap, const int32_t* idx, int32_t k,
+                         const int32_t* n_elig, const void* win, lca_dtype win_dt, int64_t W_buf,
+                         const int32_t* win_begin, const int32_t* win_len, const float* sink, float scale,
+                         int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  REQ(B >= 0 && Tq >= 0, LCA_EINVAL, "%s: B and Tq must be >= 0", name);
+  REQ(D == 128, LCA_ENOTSUP, "%s: D=%d (supported: 128)", name, D);
+  REQ(Hq == 16 || Hq == 32 || Hq == 64, LCA_ENOTSUP, "%s: Hq=%d (supported: 16, 32, 64)", name, Hq);
+  REQ(q_dt == LCA_F32 || q_dt == LCA_BF16, LCA_ENOTSUP, "%s: q_dt must be F32 or BF16", name);
+  REQ(kv_dt == LCA_F32 || kv_dt == LCA_BF16 || kv_dt == LCA_FP8E4M3, LCA_ENOTSUP,
+      "%s: kv_dt must be F32, BF16 or FP8E4M3", name);
+  REQ(win_dt == LCA_F32 || win_dt == LCA_BF16, LCA_ENOTSUP, "%s: win_dt must be F32 or BF16", name);
+  REQ(out_dt == LCA_F32 || out_dt == LCA_BF16, LCA_ENOTSUP, "%s: out_dt must be F32 or BF16", name);
+  REQ(N_cap >= 0 && N_cap < (1ll << 31), LCA_EINVAL, "%s: N_cap out of range", name);
+  REQ(W_buf >= 0 && W_buf < (1ll << 31), LCA_EINVAL, "%s: W_buf out of range", name);
+  REQ(scale == scale, LCA_EINVAL, "%s: scale is NaN", name);
+  REQ(Tq <= 65535 * 1024 && (int64_t)B * Tq < (1ll << 31), LCA_ENOTSUP, "%s: too many query rows", name);
+  if (sparse) REQ(k >= 0 && k <= 2048, LCA_EINVAL, "%s: k=%d outside [0, 2048]", name, k);
+  if ((int64_t)B * Tq == 0) return ok();
+  PTR(q); PTR(win); PTR(win_begin); PTR(win_len); PTR(sink); PTR(out);
+  if (N_cap > 0) PTR(kv);
+  if (kv_dt == LCA_FP8E4M3 && N_cap > 0) PTR(kv_scale);
+  if (kv_dt != LCA_FP8E4M3) REQ(kv_scale == nullptr, LCA_EINVAL, "%s: kv_scale must be NULL unless FP8", name);
+  if (lse) REQ(aligned16(lse), LCA_EINVAL, "%s: lse must be 16-byte aligned", name);
+  const size_t need = lca::attend_ws_bytes(B, Tq, Hq, D, sparse ? k : N_cap, W_buf);
+  if (need > 0) {
+    REQ(ws != nullptr && aligned16(ws), LCA_EWORKSPACE, "%s: workspace of %zu bytes required", name, need);
+    REQ(ws_bytes >= need, LCA_EWORKSPACE, "%s: workspace too small (%zu < %zu)", name, ws_bytes, need);
+  }
+  lca::AttendArgs a{};
+  a.q = q; a.q_dt = (int)q_dt; a.kv = kv; a.kv_dt = (int)kv_dt; a.kv_scale = kv_scale; a.N_cap = N_cap;
+  a.sparse = sparse; a.idx = idx; a.k = k; a.n_elig = n_elig; a.win = win; a.win_dt = (int)win_dt; a.W_buf = W_buf;
+  a.win_begin = win_begin; a.win_len = win_len; a.sink = sink; a.scale = scale;
+  a.B = B; a.Tq = Tq; a.Hq = Hq; a.D = D; a.out = out; a.out_dt = (int)out_dt; a.lse = lse;
+  a.ws = ws; a.ws_bytes = ws_bytes;
+  return hip_status(lca::launch_attend(a, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lca_abi_version(void) { return LCA_ABI_VERSION; }
+
+const char* lca_last_error(void) { return g_err; }
+
+lca_status lca_csa_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const float* gate,
+                            const float* pos_bias, int32_t m, const int32_t* x_tok0, const int32_t* nblk,
+                            const int64_t* dst_row0, int32_t B, int32_t nblk_max, int32_t D, void* dst,
+                            lca_dtype dst_dt, void* dst_scale, int64_t dst_rows, float* pooled, void* stream) {
+  return compress_common("lca_csa_compress", 64, x, x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0, B,
+                         nblk_max, D, dst, dst_dt, dst_scale, dst_rows, pooled, stream);
+}
+
+lca_status lca_hca_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const float* gate,
+                            const float* pos_bias, int32_t m, const int32_t* x_tok0, const int32_t* nblk,
+                            const int64_t* dst_row0, int32_t B, int32_t nblk_max, int32_t D, void* dst,
+                            lca_dtype dst_dt, void* dst_scale, int64_t dst_rows, float* pooled, void* stream) {
+  return compress_common("lca_hca_compress", 1024, x, x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0,
+                         B, nblk_max, D, dst, dst_dt, dst_scale, dst_rows, pooled, stream);
+}
+
+size_t lca_index_topk_ws(int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int64_t N_cap, int32_t k) {
+  if (B <= 0 || Tq <= 0 || N_cap < 0) return 0;
+  return lca::index_ws_bytes(B, Tq, H_I, d_I, N_cap, k, lca::DT_MXFP4 /* same layout for both types */);
+}
+
+lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8_t* qi_scale, const float* w,
+                                    const void* ki, lca_dtype ki_dt, const uint8_t* ki_scale,
+                                    const int32_t* n_elig, int32_t B, int32_t Tq, int32_t H_I, int32_t d_I,
+                                    int64_t N_cap, int32_t k, int32_t* idx_out, double* score_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  const char* name = "lca_lightning_index_topk";
+  REQ(B >= 0 && Tq >= 0, LCA_EINVAL, "%s: B and Tq must be >= 0", name);
+  REQ(k >= 1 && k <= 2048, LCA_EINVAL, "%s: k=%d outside [1, 2048]", name, k);
+  REQ(N_cap >= 0 && N_cap < (1ll << 31), LCA_EINVAL, "%s: N_cap out of range", name);
+  REQ(qi_dt == ki_dt, LCA_ENOTSUP, "%s: qi_dt and ki_dt must match", name);
+  if (qi_dt == LCA_MXFP4) {
+    REQ(H_I >= 1 && H_I <= 16, LCA_ENOTSUP, "%s: MXFP4 needs 1 <= H_I <= 16 (got %d)", name, H_I);
+    REQ(d_I == 64 || d_I == 128, LCA_ENOTSUP, "%s: MXFP4 needs d_I in {64, 128} (got %d)", name, d_I);
+  } else if (qi_dt == LCA_F32) {
+    REQ(H_I >= 1 && H_I <= 64, LCA_ENOTSUP, "%s: F32 needs 1 <= H_I <= 64 (got %d)", name, H_I);
+    REQ(d_I == 32 || d_I == 64 || d_I == 128, LCA_ENOTSUP, "%s: F32 needs d_I in {32, 64, 128}", name);
+  } else {
+    return fail(LCA_ENOTSUP, "%s: qi_dt must be F32 or MXFP4", name);
+  }
+  {
+    const int qpm = (qi_dt == LCA_MXFP4 && H_I <= 8) ? 2 : 1;
+    REQ((int64_t)B * ((Tq + qpm - 1) / qpm) <= 65535, LCA_ENOTSUP, "%s: too many query rows", name);
+  }
+  if ((int64_t)B * Tq == 0) return ok();
+  PTR(qi); PTR(w); PTR(n_elig); PTR(idx_out);
+  if (N_cap > 0) PTR(ki);
+  if (qi_dt == LCA_MXFP4) {
+    PTR(qi_scale);
+    if (N_cap > 0) PTR(ki_scale);
+  } else {
+    REQ(qi_scale == nullptr && ki_scale == nullptr, LCA_EINVAL, "%s: scales must be NULL for F32", name);
+  }
+  if (score_out) REQ(aligned16(score_out), LCA_EINVAL, "%s: score_out must be 16-byte aligned", name);
+  const size_t need = lca_index_topk_ws(B, Tq, H_I, d_I, N_cap, k);
+  REQ(ws != nullptr && aligned16(ws), LCA_EWORKSPACE, "%s: workspace of %zu bytes required", name, need);
+  REQ(ws_bytes >= need, LCA_EWORKSPACE, "%s: workspace too small (%zu < %zu)", name, ws_bytes, need);
+  lca::IndexArgs a{};
+  a.qi = qi; a.dt = (int)qi_dt; a.qi_scale = qi_scale; a.w = w; a.ki = ki; a.ki_scale = ki_scale;
+  a.n_elig = n_elig; a.B = B; a.Tq = Tq; a.H = H_I; a.d = d_I; a.N_cap = N_cap; a.k = k;
+  a.idx_out = idx_out; a.score_out = score_out; a.ws = ws; a.ws_bytes = ws_bytes;
+  return hip_status(lca::launch_index(a, (hipStream_t)stream), name);
+}
+
+size_t lca_attend_ws(int32_t B, int32_t Tq, int32_t Hq, int32_t D, int64_t n_kv_max, int64_t W_buf) {
+  if (B <= 0 || Tq <= 0) return 0;
+  return lca::attend_ws_bytes(B, Tq, Hq, D, n_kv_max, W_buf);
+}
+
+lca_status lca_sparse_mqa_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,
+                                 const float* kv_scale, int64_t N_cap, const int32_t* idx, int32_t k,
+                                 const void* win, lca_dtype win_dt, int64_t W_buf, const int32_t* win_begin,
+                                 const int32_t* win_len, const float* sink, float scale, int32_t B, int32_t Tq,
+                                 int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  const char* name = "lca_sparse_mqa_attend";
+  if ((int64_t)B * Tq > 0 && k > 0) PTR(idx);
+  REQ(k >= 0 && k <= 2048, LCA_EINVAL, "%s: k=%d outside [0, 2048]", name, k);
+  return attend_common(name, 1, q, q_dt, kv, kv_dt, kv_scale, N_cap, idx, k, nullptr, win, win_dt,
+                       W_buf, win_begin, win_len, sink, scale, B, Tq, Hq, D, out, out_dt, lse, ws, ws_bytes,
+                       stream);
+}
+
+lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt, const float* kv_scale,
+                          int64_t N_cap, const int32_t* n_elig, const void* win, lca_dtype win_dt, int64_t W_buf,
+                          const int32_t* win_begin, const int32_t* win_len, const float* sink, float scale,
+                          int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if ((int64_t)B * Tq > 0) PTR(n_elig);
+  return attend_common("lca_hca_attend", 0, q, q_dt, kv, kv_dt, kv_scale, N_cap, nullptr, 0, n_elig, win, win_dt,
+                       W_buf, win_begin, win_len, sink, scale, B, Tq, Hq, D, out, out_dt, lse, ws, ws_bytes,
+                       stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// lca_device.h -- device-side helpers shared by the gfx950 kernels:
+// storage codecs (FP8 E4M3 with per-64 scale, MXFP4 E2M1/E8M0, bf16), the
+// order-preserving map from float64 scores to uint64 keys, and wave-level
+// reductions.  gfx950 only (64-lane wavefronts).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lca_internal.h"
+
+namespace lca {
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Round-to-nearest-even of a finite fp32 value onto bfloat16.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- FP8 -----
+// OCP E4M3 (bias 7, max 448, S.1111.111 = NaN), exact decode.  gfx950's
+// hardware conversion decodes OCP E4M3 (checked by the codec tests).
+__device__ __forceinline__ float2 fp8x2_to_f32(uint32_t packed16) {
+  auto v = __builtin_amdgcn_cvt_pk_f32_fp8(packed16, false);
+  return make_float2(v[0], v[1]);
+}
+
+// Round-to-nearest-even onto E4M3 with saturation at +-448, from a finite
+// fp32 value.  Works on the binary exponent and the 3 kept mantissa bits.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  float a = fabsf(y);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {               // below 2^-6: subnormal grid 2^-9
+    code = (uint32_t)rintf(a * 512.0f);     // 0..8 (8 is the smallest normal)
+  } else {
+    int e = ilogbf(a);                      // -6..8
+    float mant = ldexpf(a, -e);             // [1, 2), exact
+    uint32_t r = (uint32_t)rintf((mant - 1.0f) * 8.0f);   // 0..8, RNE
+    if (r == 8u) { r = 0u; e += 1; }
+    code = ((uint32_t)(e + 7) << 3) | r;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return code | sign;
+}
+
+// ---------------------------------------------------------------- MXFP4 ---
+// Shared exponent of a 32-element block: floor(log2 amax) - 2 clamped to the
+// E8M0 range; amax == 0 gives -127.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (amax == 0.0f) return -127;
+  int e = ilogbf(amax) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Round-to-nearest-even onto E2M1 magnitudes {0,.5,1,1.5,2,3,4,6}, saturating,
+// keeping the sign bit of the input.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
+  float a = fabsf(y);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t m = c & 7u;
+  float v = (m < 2u) ? 0.5f * (float)m : (float)(1u << ((m >> 1) - 1u)) * (1.0f + 0.5f * (float)(m & 1u));
+  return (c & 8u) ? -v : v;
+}
+
+// ------------------------------------------------------- score keys -------
+// Order-preserving map from a float64 score to uint64 (larger key = larger
+// score).  -0.0 is folded onto +0.0 so equal scores get equal keys.  Key 0 is
+// below every real score and marks "no entry".
+__device__ __forceinline__ uint64_t score_key(double s) {
+  s = s + 0.0;
+  uint64_t b = (uint64_t)__double_as_longlong(s);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double key_score(uint64_t k) {
+  uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+
+// --------------------------------------------------------- wave utils -----
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, o, WAVE);
+  hi = __shfl_xor(hi, o, WAVE);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t t = shfl_xor_u64(v, o);
+    v = t > v ? t : v;
+  }
+  return v;
+}
+
+// Number of set lanes strictly below this lane in a 64-bit ballot.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  const int lane = threadIdx.x & 63;
+  return __popcll(mask & ((1ull << lane) - 1ull));
+}
+
+}  // namespace lca

@@ -1,0 +1,50 @@
+// lca_internal.h -- declarations shared by the C-ABI layer (abi.cpp) and the
+// kernel translation units.  Not part of the public interface.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lca {
+
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3 };
+
+struct CompressArgs {
+  const void* x; int x_dt; int64_t x_rows;
+  const float* gate; const float* bias; int m;
+  const int32_t* x_tok0; const int32_t* nblk; const int64_t* dst_row0;
+  int B; int nblk_max; int D;
+  void* dst; int dst_dt; void* dst_scale; int64_t dst_rows;
+  float* pooled;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+struct IndexArgs {
+  const void* qi; int dt; const uint8_t* qi_scale;
+  const float* w;
+  const void* ki; const uint8_t* ki_scale;
+  const int32_t* n_elig;
+  int B, Tq, H, d; int64_t N_cap; int k;
+  int32_t* idx_out; double* score_out;
+  void* ws; size_t ws_bytes;
+};
+size_t index_ws_bytes(int B, int Tq, int H, int d, int64_t N_cap, int k, int dt);
+hipError_t launch_index(const IndexArgs& a, hipStream_t s);
+
+struct AttendArgs {
+  const void* q; int q_dt;
+  const void* kv; int kv_dt; const float* kv_scale; int64_t N_cap;
+  int sparse;                         // 1: CSA list idx[r][0..k), 0: HCA entries 0..n_elig[r)
+  const int32_t* idx; int k;
+  const int32_t* n_elig;
+  const void* win; int win_dt; int64_t W_buf;
+  const int32_t* win_begin; const int32_t* win_len;
+  const float* sink; float scale;
+  int B, Tq, Hq, D;
+  void* out; int out_dt; float* lse;
+  void* ws; size_t ws_bytes;
+};
+size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W_buf);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+}  // namespace lca
