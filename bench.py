@@ -1,0 +1,295 @@
+"""Benchmark: CSA+HCA layer-pair decode at 1M-token context on one MI355X.
+
+Workload (synthetic, seeded): 4 sequences with lengths uniform in
+[0.9 * 2^20, 2^20] tokens.  CSA layer: 262144-row FP8 E4M3 entry cache
+(per-64 fp32 scales) + MXFP4 indexer keys (8 heads x 128), top-1024, window 128,
+64 query heads sharing one KV head (D = 128).  HCA layer: 8192-row FP8 entry
+cache, dense, window 128.  All values N(0,1) before quantisation; caches are
+generated on the GPU and encoded by the library's own compression kernel (m = 1
+is an exact copy).  Several copies of the caches rotate between steps so each
+step reads cold HBM (the copies exceed the 256 MB last-level cache).
+
+One step = the whole hot path for one new token per sequence:
+  csa_compress  newest 4-token block -> FP8 entry   (from the raw window)
+  csa_compress  newest 4-token block -> MXFP4 indexer key
+  hca_compress  newest 128-token block -> FP8 entry
+  lightning_index_topk  (MXFP4 scoring + exact top-1024)
+  sparse_mqa_attend     (1024 selected entries + 128 window tokens + sink)
+  hca_attend            (all <= 8192 entries + 128 window tokens + sink)
+Compression runs every step here (a real decoder runs it every 4 / 128 steps).
+
+Prints one JSON line (metric, value = decode tokens/s, roofline of the
+dominant kernel measured with HIP events over the timed region, CPU baseline
+of the float64 oracle on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    return ap.parse_args()
+
+
+class Workload:
+    """Device buffers of the layer-pair decode workload."""
+
+    def __init__(self, copies: int, seed: int = 1004):
+        import torch
+        import long_context_attention_13_amd as lca
+        import synth
+
+        self.lca = lca
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        c = synth.layer_pair_1m(draw_caches=False, seed=seed)
+        self.cfg = c
+        B, D, d_I, H_I, Hq, W = c["B"], c["D"], c["d_I"], c["H_I"], c["Hq"], c["W"]
+        self.B, self.Hq, self.D, self.H_I, self.d_I, self.k = B, Hq, D, H_I, d_I, c["k"]
+        N, N2 = c["N_cap"], c["N2_cap"]
+        self.N, self.N2 = N, N2
+        L = c["L"]
+        self.L = L
+        self.tau = c["tau"]
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+
+        # caches, generated N(0,1) on the GPU and encoded with the library (m = 1)
+        self.ent, self.ent_sc, self.key, self.key_sc, self.hca, self.hca_sc = [], [], [], [], [], []
+        zeros_B = torch.zeros(B, dtype=torch.int32, device=dev)
+        zeros_B64 = torch.zeros(B, dtype=torch.int64, device=dev)
+        bias1 = torch.zeros(1, dtype=torch.float32, device=dev)
+
+        def encode(rows, dim, dt):
+            x = torch.randn(B, rows, dim, generator=g, device=dev, dtype=torch.float32)
+            gate = torch.zeros(B, rows, dtype=torch.float32, device=dev)
+            if dt == lca.FP8E4M3:
+                dst = torch.empty(B, rows, dim, dtype=torch.uint8, device=dev)
+                sc = torch.empty(B, rows, dim // 64, dtype=torch.float32, device=dev)
+            else:
+                dst = torch.empty(B, rows, dim // 2, dtype=torch.uint8, device=dev)
+                sc = torch.empty(B, rows, dim // 32, dtype=torch.uint8, device=dev)
+            nblk = torch.full((B,), rows, dtype=torch.int32, device=dev)
+            lca.csa_compress(x, gate, bias1, 1, zeros_B, nblk, zeros_B64, rows, dst, dt, sc)
+            del x, gate
+            return dst, sc
+
+        for _ in range(copies):
+            e, es = encode(N, D, lca.FP8E4M3)
+            k_, ks = encode(N, d_I, lca.MXFP4)
+            h, hs = encode(N2, D, lca.FP8E4M3)
+            self.ent.append(e); self.ent_sc.append(es); self.key.append(k_); self.key_sc.append(ks)
+            self.hca.append(h); self.hca_sc.append(hs)
+        torch.cuda.synchronize()
+
+        # queries and the indexer query (MXFP4, encoded by the library)
+        qi32 = t(c["qi"].reshape(B, H_I, d_I))
+        self.qi = torch.empty(B, 1, H_I, d_I // 2, dtype=torch.uint8, device=dev)
+        self.qi_sc = torch.empty(B, 1, H_I, d_I // 32, dtype=torch.uint8, device=dev)
+        lca.csa_compress(qi32, torch.zeros(B, H_I, device=dev), bias1, 1, zeros_B,
+                         torch.full((B,), H_I, dtype=torch.int32, device=dev), zeros_B64, H_I,
+                         self.qi.view(B, H_I, d_I // 2), lca.MXFP4, self.qi_sc.view(B, H_I, d_I // 32))
+        self.w = t(c["w"])
+        self.q_csa = bf(c["q_csa"])
+        self.q_hca = bf(c["q_hca"])
+        self.sink_csa = t(c["sink_csa"])
+        self.sink_hca = t(c["sink_hca"])
+        # raw buffers: CSA window (128 tokens), indexer raw keys (128), HCA buffer (256 tokens:
+        # the previous 128 + the window) so the newest complete 128-block is always inside
+        self.win_csa = bf(c["win_csa"])
+        self.win_keys = bf(c["win_keys"])
+        hbuf = np.concatenate([c["win_hca"][:, ::-1], c["win_hca"]], axis=1)   # 256 tokens
+        self.win_hca = bf(hbuf)
+        self.gate_csa = t(c["gate_csa"])
+        self.gate_i = t(c["gate_i"])
+        self.gate_hca = t(np.concatenate([c["gate_hca"], c["gate_hca"]], axis=1))
+        self.bias_csa = t(c["bias_csa"])
+        self.bias_i = t(c["bias_i"])
+        self.bias_hca = t(c["bias_hca"])
+        # per-sequence positions
+        n_csa = (L // 4).astype(np.int32)
+        n_hca = (L // 128).astype(np.int32)
+        self.n_csa = t(n_csa.reshape(B, 1))
+        self.n_hca = t(n_hca.reshape(B, 1))
+        self.csa_tok0 = t((124 - L % 4).astype(np.int32))
+        self.csa_row0 = t((n_csa - 1).astype(np.int64))
+        self.hca_tok0 = t((128 - L % 128).astype(np.int32))
+        self.hca_row0 = t((n_hca - 1).astype(np.int64))
+        self.one = torch.ones(B, dtype=torch.int32, device=dev)
+        self.wb_csa = torch.zeros(B, 1, dtype=torch.int32, device=dev)
+        self.wl = torch.full((B, 1), W, dtype=torch.int32, device=dev)
+        self.wb_hca = torch.full((B, 1), 128, dtype=torch.int32, device=dev)
+        # outputs and workspaces
+        self.idx = torch.empty(B, 1, self.k, dtype=torch.int32, device=dev)
+        self.out_csa = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
+        self.out_hca = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
+        self.ws_idx = torch.empty(lca.index_topk_ws(B, 1, H_I, d_I, N, self.k), dtype=torch.uint8, device=dev)
+        self.ws_csa = torch.empty(max(lca.attend_ws(B, 1, Hq, D, self.k, 128), 16), dtype=torch.uint8, device=dev)
+        self.ws_hca = torch.empty(max(lca.attend_ws(B, 1, Hq, D, N2, 256), 16), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    # -- the hot path ------------------------------------------------------
+    def compress(self, c):
+        lca = self.lca
+        lca.csa_compress(self.win_csa, self.gate_csa, self.bias_csa, 4, self.csa_tok0, self.one, self.csa_row0, 1,
+                         self.ent[c], lca.FP8E4M3, self.ent_sc[c])
+        lca.csa_compress(self.win_keys, self.gate_i, self.bias_i, 4, self.csa_tok0, self.one, self.csa_row0, 1,
+                         self.key[c], lca.MXFP4, self.key_sc[c])
+        lca.hca_compress(self.win_hca, self.gate_hca, self.bias_hca, 128, self.hca_tok0, self.one, self.hca_row0, 1,
+                         self.hca[c], lca.FP8E4M3, self.hca_sc[c])
+
+    def index(self, c):
+        self.lca.lightning_index_topk(self.qi, self.qi_sc, self.w, self.key[c], self.key_sc[c], self.n_csa, self.k,
+                                      self.idx, self.ws_idx)
+
+    def attend(self, c):
+        lca = self.lca
+        lca.sparse_mqa_attend(self.q_csa, self.ent[c], self.ent_sc[c], self.idx, self.win_csa, self.wb_csa, self.wl,
+                              self.sink_csa, self.tau, self.out_csa, ws=self.ws_csa)
+        lca.hca_attend(self.q_hca, self.hca[c], self.hca_sc[c], self.n_hca, self.win_hca, self.wb_hca, self.wl,
+                       self.sink_hca, self.tau, self.out_hca, ws=self.ws_hca)
+
+    def step(self, c):
+        self.compress(c)
+        self.index(c)
+        self.attend(c)
+
+    # -- algorithmic bytes -------------------------------------------------
+    def index_bytes(self) -> float:
+        """Bytes the indexer must move once: every eligible MXFP4 key row (64 B codes
+        + 4 B E8M0), the query rows, head weights and the selected indices."""
+        n = self.L // 4
+        return float(n.sum() * (self.d_I // 2 + self.d_I // 32)
+                     + self.B * (self.H_I * (self.d_I // 2 + self.d_I // 32) + self.H_I * 4 + self.k * 4))
+
+    def step_bytes(self) -> float:
+        B, D, Hq, k = self.B, self.D, self.Hq, self.k
+        ent = D + 8                                    # FP8 row + two fp32 scales
+        qo = 2 * Hq * D * 2                            # bf16 q in, bf16 out
+        csa = B * (k * ent + 128 * D * 2 + qo)
+        hca = float((self.L // 128).sum() * ent + B * (128 * D * 2 + qo))
+        comp = B * (4 * D * 2 * 2 + 128 * D * 2 + 3 * ent)  # raw blocks read, rows written
+        return self.index_bytes() + csa + hca + comp
+
+
+def cpu_baseline(wl, steps):
+    """The float64 oracle on one full layer-pair step, on the host cores."""
+    import torch
+    import oracle
+    c = 0
+    B, H_I, d_I = wl.B, wl.H_I, wl.d_I
+    host = lambda t: t.cpu().numpy()
+    ent, ent_sc = host(wl.ent[c]), host(wl.ent_sc[c])
+    key, key_sc = host(wl.key[c]), host(wl.key_sc[c])
+    hca, hca_sc = host(wl.hca[c]), host(wl.hca_sc[c])
+    qi = oracle.decode(host(wl.qi), oracle.MXFP4, host(wl.qi_sc))
+    w = host(wl.w)
+    q_csa = oracle.decode(host(wl.q_csa.view(torch.int16)).view(np.uint16), oracle.BF16)
+    q_hca = oracle.decode(host(wl.q_hca.view(torch.int16)).view(np.uint16), oracle.BF16)
+    win_c = host(wl.win_csa.view(torch.int16)).view(np.uint16)
+    win_h = host(wl.win_hca.view(torch.int16)).view(np.uint16)
+    n_csa, n_hca = host(wl.n_csa), host(wl.n_hca)
+    wb0 = np.zeros((B, 1), np.int32)
+    wl_ = np.full((B, 1), 128, np.int32)
+    wb1 = np.full((B, 1), 128, np.int32)
+    sink_c, sink_h = host(wl.sink_csa), host(wl.sink_hca)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        idx, _ = oracle.index_topk(qi, w, key, oracle.MXFP4, key_sc, n_csa, wl.k)
+        oracle.attend(q_csa, ent, oracle.FP8E4M3, ent_sc, idx, None, win_c, oracle.BF16, wb0, wl_, sink_c, wl.tau)
+        oracle.attend(q_hca, hca, oracle.FP8E4M3, hca_sc, None, n_hca, win_h, oracle.BF16, wb1, wl_, sink_h, wl.tau)
+    dt = time.perf_counter() - t0
+    return {"value": round(B * steps / dt, 3), "unit": "decode tokens/s", "cores": min(oracle.num_threads(), B),
+            "kind": "oracle",
+            "sample": f"{steps} full layer-pair decode steps (4 sequences; indexer + top-k + both attentions, "
+                      f"compression excluded); the oracle parallelises over the 4 query rows"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
+              f"note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    wl = Workload(args.copies)
+    stream = torch.cuda.current_stream()
+    C = args.copies
+    for s in range(args.warmup):
+        wl.step(s % C)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, plus events around the indexer call of each step
+    ev_idx = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        c = s % C
+        wl.compress(c)
+        ev_idx[s][0].record(stream)
+        wl.index(c)
+        ev_idx[s][1].record(stream)
+        wl.attend(c)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    idx_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_idx]))
+    idx_bytes = wl.index_bytes()
+    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    step_gbs = wl.step_bytes() / (ms_step * 1e-3) / 1e9
+    value = wl.B * args.steps / (total_ms * 1e-3)
+
+    res = {
+        "metric": "CSA+HCA decode tokens/s at 1M ctx; % peak HBM BW; indexer MFMA util",
+        "value": round(value, 1),
+        "unit": "decode tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+mxfp4 storage; bf16/fp32 compute",
+        "data": "synthetic N(0,1), seeded",
+        "config": {"workload": "layer_pair_1m: CSA+HCA layer-pair decode, batch 4, context ~U[0.9,1.0]*2^20, "
+                               "CSA 262144 FP8 entries + MXFP4 indexer (8x128) top-1024, HCA 8192 FP8 entries, "
+                               "window 128, 64 query heads, head_dim 128",
+                   "global_batch": wl.B, "seq_len": int(wl.L.max()), "parallelism": "single GPU"},
+        "step_hbm_gbs": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "lightning_index_topk (index_chunk_kernel + index_select_kernel)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(idx_ms * 1e3, 2), "algorithmic_bytes": int(idx_bytes)},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

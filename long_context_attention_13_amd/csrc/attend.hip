@@ -19,25 +19,29 @@
 namespace lca {
 
 constexpr int ATT_THREADS = 256;
-constexpr int ATT_SPLIT = 256;     // list items per split
 constexpr int ATT_TE = 32;         // items per LDS tile (VALU path)
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Number of splits per row; a single split when there are enough rows to fill
-// the GPU on their own.
-static int att_splits(int64_t R, int64_t n_kv_max, int64_t W_buf) {
-  if (R >= 256) return 1;
+// Split plan: one split per row when there are enough rows to fill the GPU on
+// their own; otherwise the list is cut into splits of 256 items (128 when that
+// still leaves fewer than 256 workgroups).
+struct Plan { int S; int items; };
+
+static Plan att_plan(int64_t R, int64_t n_kv_max, int64_t W_buf) {
   const int64_t L = n_kv_max + W_buf;
-  const int64_t s = (L + ATT_SPLIT - 1) / ATT_SPLIT;
-  return (int)(s < 1 ? 1 : s);
+  if (R >= 256 || L <= 128) return Plan{1, (int)(L < 1 ? 1 : L)};
+  int items = 256;
+  if (R * ((L + 255) / 256) < 256) items = 128;
+  const int64_t s = (L + items - 1) / items;
+  return Plan{(int)(s < 1 ? 1 : s), items};
 }
 
 size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W_buf) {
   const int64_t R = (int64_t)B * Tq;
-  const int S = att_splits(R, n_kv_max, W_buf);
-  if (S == 1) return 0;
-  return align256(sizeof(float) * R * S * Hq * 2) + align256(sizeof(float) * R * S * Hq * D);
+  const Plan P = att_plan(R, n_kv_max, W_buf);
+  if (P.S == 1) return 0;
+  return align256(sizeof(float) * R * P.S * Hq * 2) + align256(sizeof(float) * R * P.S * Hq * D);
 }
 
 // Item p of row r's list: returns the source pointer class and row, or -1.
@@ -90,7 +94,8 @@ __device__ __forceinline__ void store_out(const AttendArgs& A, int64_t i, float 
 // fp32 VALU kernel (any storage types; used for F32 inputs).
 // ------------------------------------------------------------------------
 template <int QDT, int KVDT, int WDT, int HQ>
-__global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, int S, float* part_ml, float* part_o) {
+__global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, int S, int split_items, float* part_ml,
+                                                                   float* part_o) {
   constexpr int D = 128;
   constexpr int TPH = ATT_THREADS / HQ;      // threads per head
   constexpr int DPT = D / TPH;               // output dims per thread
@@ -99,8 +104,8 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   const int tid = threadIdx.x;
   const int nkv = A.sparse ? A.k : A.n_elig[r];
   const int L = nkv + A.win_len[r];
-  const int p0 = split * ATT_SPLIT;
-  const int p1 = min(L, p0 + (S == 1 ? L : ATT_SPLIT));
+  const int p0 = split * split_items;
+  const int p1 = S == 1 ? L : min(L, p0 + split_items);
 
   __shared__ float qs[HQ][D];
   __shared__ float kvs[ATT_TE][D + 1];
@@ -185,6 +190,194 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
 }
 
 // ------------------------------------------------------------------------
+// bf16 matrix-core kernel: bf16 queries, bf16 or FP8 items, bf16 window.
+//
+// Each wavefront owns 16 heads; the workgroup's waves share one LDS copy of
+// each 64-item tile.  Per tile:
+//   S^T = K Q^T      16x16x32 bf16 MFMA, items x heads (K from LDS, Q^T in
+//                    registers).  FP8 items are staged as their exact bf16
+//                    codes; the two per-64 scales multiply the fp32 partial
+//                    dot products of dims 0-63 and 64-127.
+//   online softmax   per head = per lane column; the max over a tile's items
+//                    is one in-lane max plus two cross-lane steps.
+//   O^T += V^T P^T   16x16x32 bf16 MFMA, dims x heads.  The B operand is the
+//                    softmax numerator straight from the S^T accumulator
+//                    layout (items taken in a permuted order that the V^T
+//                    reads follow), with the FP8 scales folded in.
+// The next tile's items are fetched into registers while the current one is
+// computed.
+// ------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int MT_TE = 64;                 // items per tile
+constexpr int MT_KROW = 136;              // bf16 per K row in LDS (128 + pad)
+constexpr int MT_VROW = 72;               // bf16 per V^T row in LDS (64 + pad)
+
+template <int KVDT, int HQ>
+__global__ __launch_bounds__(HQ * 4) void attend_mfma_kernel(AttendArgs A, int S, int split_items, float* part_ml,
+                                                             float* part_o) {
+  constexpr int NT = HQ * 4;              // threads (HQ/16 waves)
+  const int split = blockIdx.x, r = blockIdx.y;
+  const int b = r / A.Tq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int nkv = A.sparse ? A.k : A.n_elig[r];
+  const int L = nkv + A.win_len[r];
+  const int p0 = split * split_items;
+  const int p1 = S == 1 ? L : min(L, p0 + split_items);
+
+  __shared__ __align__(16) __bf16 Kl[MT_TE * MT_KROW];
+  __shared__ __align__(16) __bf16 Vt[128 * MT_VROW];
+  __shared__ float sclo[MT_TE], schi[MT_TE];
+  __shared__ int okl[MT_TE];
+
+  // Q^T operand: this lane's head = wave*16 + col, dims 32*ks + 8*g .. +7
+  const int head = wave * 16 + col;
+  bf16x8 qv[4];
+  {
+    const uint16_t* qrow = (const uint16_t*)A.q + ((int64_t)r * HQ + head) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int4 v = *(const int4*)(qrow + 32 * ks + 8 * g);
+      qv[ks] = *(const bf16x8*)&v;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = p0; t0 < p1; t0 += MT_TE) {
+    // ---- stage the tile: item rows -> Kl (bf16 codes), V^T, scales, valid flags
+    __syncthreads();
+    for (int lin = tid; lin < MT_TE * 16; lin += NT) {
+      const int e = lin >> 4, dc = lin & 15;          // item, 8-dim chunk
+      const int p = t0 + e;
+      int4 v = make_int4(0, 0, 0, 0);
+      int kind = -1;
+      float slo = 1.f, shi = 1.f;
+      if (p < p1) {
+        const ListItem it = list_item(A, b, r, p, nkv);
+        kind = it.kind;
+        if (kind == 0) {
+          if (KVDT == DT_FP8) {
+            const uint2 c8 = *(const uint2*)((const uint8_t*)A.kv + it.row * 128 + dc * 8);
+            const float2 f0 = fp8x2_to_f32(c8.x & 0xFFFF), f1 = fp8x2_to_f32(c8.x >> 16);
+            const float2 f2 = fp8x2_to_f32(c8.y & 0xFFFF), f3 = fp8x2_to_f32(c8.y >> 16);
+            v.x = (int)__builtin_amdgcn_perm(__float_as_uint(f0.y), __float_as_uint(f0.x), 0x07060302u);
+            v.y = (int)__builtin_amdgcn_perm(__float_as_uint(f1.y), __float_as_uint(f1.x), 0x07060302u);
+            v.z = (int)__builtin_amdgcn_perm(__float_as_uint(f2.y), __float_as_uint(f2.x), 0x07060302u);
+            v.w = (int)__builtin_amdgcn_perm(__float_as_uint(f3.y), __float_as_uint(f3.x), 0x07060302u);
+            if (dc == 0) { slo = A.kv_scale[it.row * 2]; shi = A.kv_scale[it.row * 2 + 1]; }
+          } else {
+            v = *(const int4*)((const uint16_t*)A.kv + it.row * 128 + dc * 8);
+          }
+        } else if (kind == 1) {
+          v = *(const int4*)((const uint16_t*)A.win + it.row * 128 + dc * 8);
+        }
+      }
+      *(int4*)&Kl[e * MT_KROW + dc * 8] = v;
+      const uint16_t* hv = (const uint16_t*)&v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ((uint16_t*)Vt)[(dc * 8 + i) * MT_VROW + e] = hv[i];
+      if (dc == 0) { sclo[e] = slo; schi[e] = shi; okl[e] = kind >= 0; }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for 4 subtiles of 16 items
+    float sv[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      f32x4 clo = {0.f, 0.f, 0.f, 0.f}, chi = {0.f, 0.f, 0.f, 0.f};
+      const __bf16* krow = &Kl[(st * 16 + col) * MT_KROW + 8 * g];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kv = *(const bf16x8*)(krow + 32 * ks);
+        if (ks < 2) clo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[ks], clo, 0, 0, 0);
+        else chi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[ks], chi, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = st * 16 + 4 * g + i;
+        const float sdot = clo[i] * sclo[e] + chi[i] * schi[e];
+        sv[st][i] = okl[e] ? sdot * A.scale : -INFINITY;
+      }
+    }
+    // ---- online softmax for head `head`
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sv[st][i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+    float pv[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = (sv[st][i] == -INFINITY) ? 0.f : __expf(sv[st][i] - m_new);
+        pv[st][i] = pe;
+        lsum += pe;
+      }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+
+    // ---- O^T += V^T P^T, two K-steps of 32 items
+#pragma unroll
+    for (int kap = 0; kap < 2; ++kap) {
+      bf16x8 plo, phi;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int st = 2 * kap + (jj >> 2), i = jj & 3;
+        const int e = st * 16 + 4 * g + i;
+        plo[jj] = (__bf16)(pv[st][i] * sclo[e]);
+        phi[jj] = (__bf16)(pv[st][i] * schi[e]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const int dim = mt * 16 + col;
+        const __bf16* vrow = &Vt[dim * MT_VROW + 32 * kap + 4 * g];
+        const uint2 a0 = *(const uint2*)vrow;
+        const uint2 a1 = *(const uint2*)(vrow + 16);
+        const uint4 av = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        const bf16x8 va = *(const bf16x8*)&av;
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, mt < 4 ? plo : phi, acc[mt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- finish: the per-head sum over the 4 lanes that share the head
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (S == 1) {
+    const float sk = A.sink[head];
+    const float M = fmaxf(m_run, sk);
+    const float em = (m_run == -INFINITY) ? 0.f : __expf(m_run - M);
+    const float Z = __expf(sk - M) + l_run * em;
+    const float f = em / Z;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_out(A, ((int64_t)r * HQ + head) * 128 + mt * 16 + 4 * g + i, acc[mt][i] * f);
+    if (A.lse && g == 0) A.lse[(int64_t)r * HQ + head] = M + __logf(Z);
+  } else {
+    const int64_t base = ((int64_t)r * S + split) * HQ + head;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      *(float4*)&part_o[base * 128 + mt * 16 + 4 * g] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+    if (g == 0) { part_ml[base * 2] = m_run; part_ml[base * 2 + 1] = l_run; }
+  }
+}
+
+// ------------------------------------------------------------------------
 // merge: combine the split partials of one row in split order with the sink
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, const float* part_ml,
@@ -211,44 +404,58 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, 
 // host side
 // ------------------------------------------------------------------------
 template <int QDT, int KVDT, int WDT>
-static hipError_t launch_h(const AttendArgs& a, hipStream_t s, int S, float* ml, float* po) {
-  dim3 grid(S, (unsigned)(a.B * a.Tq));
+static hipError_t launch_h(const AttendArgs& a, hipStream_t s, Plan P, float* ml, float* po) {
+  dim3 grid(P.S, (unsigned)(a.B * a.Tq));
   switch (a.Hq) {
-    case 16: hipLaunchKernelGGL((attend_valu_kernel<QDT, KVDT, WDT, 16>), grid, dim3(ATT_THREADS), 0, s, a, S, ml, po); break;
-    case 32: hipLaunchKernelGGL((attend_valu_kernel<QDT, KVDT, WDT, 32>), grid, dim3(ATT_THREADS), 0, s, a, S, ml, po); break;
-    default: hipLaunchKernelGGL((attend_valu_kernel<QDT, KVDT, WDT, 64>), grid, dim3(ATT_THREADS), 0, s, a, S, ml, po); break;
+    case 16: hipLaunchKernelGGL((attend_valu_kernel<QDT, KVDT, WDT, 16>), grid, dim3(ATT_THREADS), 0, s, a, P.S, P.items, ml, po); break;
+    case 32: hipLaunchKernelGGL((attend_valu_kernel<QDT, KVDT, WDT, 32>), grid, dim3(ATT_THREADS), 0, s, a, P.S, P.items, ml, po); break;
+    default: hipLaunchKernelGGL((attend_valu_kernel<QDT, KVDT, WDT, 64>), grid, dim3(ATT_THREADS), 0, s, a, P.S, P.items, ml, po); break;
   }
   return hipGetLastError();
 }
 
 template <int QDT, int KVDT>
-static hipError_t launch_w(const AttendArgs& a, hipStream_t s, int S, float* ml, float* po) {
-  return a.win_dt == DT_F32 ? launch_h<QDT, KVDT, DT_F32>(a, s, S, ml, po) : launch_h<QDT, KVDT, DT_BF16>(a, s, S, ml, po);
+static hipError_t launch_w(const AttendArgs& a, hipStream_t s, Plan P, float* ml, float* po) {
+  return a.win_dt == DT_F32 ? launch_h<QDT, KVDT, DT_F32>(a, s, P, ml, po) : launch_h<QDT, KVDT, DT_BF16>(a, s, P, ml, po);
 }
 
 template <int QDT>
-static hipError_t launch_kv(const AttendArgs& a, hipStream_t s, int S, float* ml, float* po) {
+static hipError_t launch_kv(const AttendArgs& a, hipStream_t s, Plan P, float* ml, float* po) {
   switch (a.kv_dt) {
-    case DT_F32: return launch_w<QDT, DT_F32>(a, s, S, ml, po);
-    case DT_BF16: return launch_w<QDT, DT_BF16>(a, s, S, ml, po);
-    default: return launch_w<QDT, DT_FP8>(a, s, S, ml, po);
+    case DT_F32: return launch_w<QDT, DT_F32>(a, s, P, ml, po);
+    case DT_BF16: return launch_w<QDT, DT_BF16>(a, s, P, ml, po);
+    default: return launch_w<QDT, DT_FP8>(a, s, P, ml, po);
   }
+}
+
+template <int KVDT>
+static hipError_t launch_mfma(const AttendArgs& a, hipStream_t s, Plan P, float* ml, float* po) {
+  dim3 grid(P.S, (unsigned)(a.B * a.Tq));
+  switch (a.Hq) {
+    case 16: hipLaunchKernelGGL((attend_mfma_kernel<KVDT, 16>), grid, dim3(64), 0, s, a, P.S, P.items, ml, po); break;
+    case 32: hipLaunchKernelGGL((attend_mfma_kernel<KVDT, 32>), grid, dim3(128), 0, s, a, P.S, P.items, ml, po); break;
+    default: hipLaunchKernelGGL((attend_mfma_kernel<KVDT, 64>), grid, dim3(256), 0, s, a, P.S, P.items, ml, po); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   const int64_t R = (int64_t)a.B * a.Tq;
   if (R == 0) return hipSuccess;
   const int64_t nkv = a.sparse ? a.k : a.N_cap;
-  const int S = att_splits(R, nkv, a.W_buf);
+  const Plan P = att_plan(R, nkv, a.W_buf);
   float* ml = nullptr;
   float* po = nullptr;
-  if (S > 1) {
+  if (P.S > 1) {
     ml = (float*)a.ws;
-    po = (float*)((char*)a.ws + align256(sizeof(float) * R * S * a.Hq * 2));
+    po = (float*)((char*)a.ws + align256(sizeof(float) * R * P.S * a.Hq * 2));
   }
-  hipError_t e = a.q_dt == DT_F32 ? launch_kv<DT_F32>(a, s, S, ml, po) : launch_kv<DT_BF16>(a, s, S, ml, po);
-  if (e != hipSuccess || S == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, S, ml, po);
+  hipError_t e;
+  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8);
+  if (mfma) e = a.kv_dt == DT_FP8 ? launch_mfma<DT_FP8>(a, s, P, ml, po) : launch_mfma<DT_BF16>(a, s, P, ml, po);
+  else e = a.q_dt == DT_F32 ? launch_kv<DT_F32>(a, s, P, ml, po) : launch_kv<DT_BF16>(a, s, P, ml, po);
+  if (e != hipSuccess || P.S == 1) return e;
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, P.S, ml, po);
   return hipGetLastError();
 }
 
