@@ -157,8 +157,8 @@ lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8
     return fail(LCA_ENOTSUP, "%s: qi_dt must be F32 or MXFP4", name);
   }
   {
-    const int qpm = (qi_dt == LCA_MXFP4 && H_I <= 8) ? 2 : 1;
-    REQ((int64_t)B * ((Tq + qpm - 1) / qpm) <= 65535, LCA_ENOTSUP, "%s: too many query rows", name);
+    const int nq = (qi_dt == LCA_MXFP4 && H_I <= 8 && Tq > 1) ? 2 : 1;   // query rows per wavefront
+    REQ((int64_t)B * ((Tq + nq - 1) / nq) <= 65535, LCA_ENOTSUP, "%s: too many query rows", name);
   }
   if ((int64_t)B * Tq == 0) return ok();
   PTR(qi); PTR(w); PTR(n_elig); PTR(idx_out);

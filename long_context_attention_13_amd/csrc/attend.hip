@@ -31,10 +31,11 @@ struct Plan { int S; int items; };
 static Plan att_plan(int64_t R, int64_t n_kv_max, int64_t W_buf) {
   const int64_t L = n_kv_max + W_buf;
   if (R >= 256 || L <= 128) return Plan{1, (int)(L < 1 ? 1 : L)};
-  int items = 256;
+  int64_t items = 256;
   if (R * ((L + 255) / 256) < 256) items = 128;
+  if ((L + items - 1) / items > 1024) items = ((L + 1023) / 1024 + 63) / 64 * 64;   // merge holds <= 1024 splits
   const int64_t s = (L + items - 1) / items;
-  return Plan{(int)(s < 1 ? 1 : s), items};
+  return Plan{(int)(s < 1 ? 1 : s), (int)items};
 }
 
 size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W_buf) {
@@ -214,10 +215,110 @@ constexpr int MT_TE = 64;                 // items per tile
 constexpr int MT_KROW = 136;              // bf16 per K row in LDS (128 + pad)
 constexpr int MT_VROW = 72;               // bf16 per V^T row in LDS (64 + pad)
 
+// Rows of one tile fetched into registers: each thread owns CPT (item, 16-dim
+// chunk) tasks.  Entry and window loads are both issued unconditionally (from
+// clamped, valid addresses) and the right one is picked when the tile is
+// written to LDS, so every load of a tile is in flight at once.
+template <int KVDT, int CPT>
+struct MtRegs {
+  int4 ent[CPT][KVDT == DT_FP8 ? 1 : 2];
+  int4 win[CPT][2];
+  float2 sc[CPT];
+  int kind[CPT];          // 0 entry, 1 window token, -1 nothing
+};
+
+template <int KVDT, int NT, int CPT>
+__device__ __forceinline__ void mt_fetch(const AttendArgs& A, int b, int r, int nkv, int e_lo, const int* idxl, int t0,
+                                         int p1, MtRegs<KVDT, CPT>& R) {
+  const int tid = threadIdx.x;
+  const int64_t wbase = (int64_t)b * A.W_buf + A.win_begin[r];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int lin = c * NT + tid;
+    const int e = lin >> 3, ch = lin & 7;
+    const int p = t0 + e;
+    int kind = -1;
+    int64_t j = 0;
+    if (p < p1) {
+      if (p < nkv) {
+        j = A.sparse ? (int64_t)idxl[p - e_lo] : (int64_t)p;
+        kind = (j >= 0 && j < A.N_cap) ? 0 : -1;
+      } else {
+        kind = 1;
+      }
+    }
+    R.kind[c] = kind;
+    const int64_t erow = (int64_t)b * A.N_cap + (kind == 0 ? j : 0);
+    if (KVDT == DT_FP8) {
+      R.ent[c][0] = *(const int4*)((const uint8_t*)A.kv + erow * 128 + ch * 16);
+      R.sc[c] = *(const float2*)(A.kv_scale + erow * 2);
+    } else {
+      R.ent[c][0] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16);
+      R.ent[c][1] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16 + 8);
+    }
+    if (A.W_buf > 0) {
+      const int64_t wrow = wbase + (kind == 1 ? p - nkv : 0);
+      R.win[c][0] = *(const int4*)((const uint16_t*)A.win + wrow * 128 + ch * 16);
+      R.win[c][1] = *(const int4*)((const uint16_t*)A.win + wrow * 128 + ch * 16 + 8);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2_from_fp8x2(uint32_t two_codes) {
+  const float2 f = fp8x2_to_f32(two_codes);
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+
+template <int KVDT, int NT, int CPT>
+__device__ __forceinline__ void mt_store(const MtRegs<KVDT, CPT>& R, __bf16* Kl, __bf16* Vt, float* sclo, float* schi,
+                                         int* okl) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int lin = c * NT + tid;
+    const int e = lin >> 3, ch = lin & 7;
+    const int kind = R.kind[c];
+    int4 v0 = make_int4(0, 0, 0, 0), v1 = make_int4(0, 0, 0, 0);
+    float slo = 1.f, shi = 1.f;
+    if (kind == 0) {
+      if (KVDT == DT_FP8) {
+        const int4 q = R.ent[c][0];
+        v0.x = (int)pack_bf16x2_from_fp8x2((uint32_t)q.x & 0xFFFFu);
+        v0.y = (int)pack_bf16x2_from_fp8x2((uint32_t)q.x >> 16);
+        v0.z = (int)pack_bf16x2_from_fp8x2((uint32_t)q.y & 0xFFFFu);
+        v0.w = (int)pack_bf16x2_from_fp8x2((uint32_t)q.y >> 16);
+        v1.x = (int)pack_bf16x2_from_fp8x2((uint32_t)q.z & 0xFFFFu);
+        v1.y = (int)pack_bf16x2_from_fp8x2((uint32_t)q.z >> 16);
+        v1.z = (int)pack_bf16x2_from_fp8x2((uint32_t)q.w & 0xFFFFu);
+        v1.w = (int)pack_bf16x2_from_fp8x2((uint32_t)q.w >> 16);
+        slo = R.sc[c].x;
+        shi = R.sc[c].y;
+      } else {
+        v0 = R.ent[c][0];
+        v1 = R.ent[c][KVDT == DT_FP8 ? 0 : 1];
+      }
+    } else if (kind == 1) {
+      v0 = R.win[c][0];
+      v1 = R.win[c][1];
+    }
+    *(int4*)&Kl[e * MT_KROW + ch * 16] = v0;
+    *(int4*)&Kl[e * MT_KROW + ch * 16 + 8] = v1;
+    const uint16_t* h0 = (const uint16_t*)&v0;
+    const uint16_t* h1 = (const uint16_t*)&v1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ((uint16_t*)Vt)[(ch * 16 + i) * MT_VROW + e] = h0[i];
+      ((uint16_t*)Vt)[(ch * 16 + 8 + i) * MT_VROW + e] = h1[i];
+    }
+    if (ch == 0) { sclo[e] = slo; schi[e] = shi; okl[e] = kind >= 0; }
+  }
+}
+
 template <int KVDT, int HQ>
 __global__ __launch_bounds__(HQ * 4) void attend_mfma_kernel(AttendArgs A, int S, int split_items, float* part_ml,
                                                              float* part_o) {
   constexpr int NT = HQ * 4;              // threads (HQ/16 waves)
+  constexpr int CPT = MT_TE * 8 / NT;     // (item, 16-dim chunk) tasks per thread and tile
   const int split = blockIdx.x, r = blockIdx.y;
   const int b = r / A.Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -231,6 +332,12 @@ __global__ __launch_bounds__(HQ * 4) void attend_mfma_kernel(AttendArgs A, int S
   __shared__ __align__(16) __bf16 Vt[128 * MT_VROW];
   __shared__ float sclo[MT_TE], schi[MT_TE];
   __shared__ int okl[MT_TE];
+  __shared__ int idxl[2048];
+
+  // the selected indices of this split's entry range, staged once
+  const int e_lo = p0, e_hi = min(p1, nkv);
+  if (A.sparse)
+    for (int i = tid; i < e_hi - e_lo; i += NT) idxl[i] = A.idx[(int64_t)r * A.k + e_lo + i];
 
   // Q^T operand: this lane's head = wave*16 + col, dims 32*ks + 8*g .. +7
   const int head = wave * 16 + col;
@@ -247,43 +354,15 @@ __global__ __launch_bounds__(HQ * 4) void attend_mfma_kernel(AttendArgs A, int S
   f32x4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
 
+  MtRegs<KVDT, CPT> R;
+  if (p0 < p1) mt_fetch<KVDT, NT, CPT>(A, b, r, nkv, e_lo, idxl, p0, p1, R);
   for (int t0 = p0; t0 < p1; t0 += MT_TE) {
-    // ---- stage the tile: item rows -> Kl (bf16 codes), V^T, scales, valid flags
     __syncthreads();
-    for (int lin = tid; lin < MT_TE * 16; lin += NT) {
-      const int e = lin >> 4, dc = lin & 15;          // item, 8-dim chunk
-      const int p = t0 + e;
-      int4 v = make_int4(0, 0, 0, 0);
-      int kind = -1;
-      float slo = 1.f, shi = 1.f;
-      if (p < p1) {
-        const ListItem it = list_item(A, b, r, p, nkv);
-        kind = it.kind;
-        if (kind == 0) {
-          if (KVDT == DT_FP8) {
-            const uint2 c8 = *(const uint2*)((const uint8_t*)A.kv + it.row * 128 + dc * 8);
-            const float2 f0 = fp8x2_to_f32(c8.x & 0xFFFF), f1 = fp8x2_to_f32(c8.x >> 16);
-            const float2 f2 = fp8x2_to_f32(c8.y & 0xFFFF), f3 = fp8x2_to_f32(c8.y >> 16);
-            v.x = (int)__builtin_amdgcn_perm(__float_as_uint(f0.y), __float_as_uint(f0.x), 0x07060302u);
-            v.y = (int)__builtin_amdgcn_perm(__float_as_uint(f1.y), __float_as_uint(f1.x), 0x07060302u);
-            v.z = (int)__builtin_amdgcn_perm(__float_as_uint(f2.y), __float_as_uint(f2.x), 0x07060302u);
-            v.w = (int)__builtin_amdgcn_perm(__float_as_uint(f3.y), __float_as_uint(f3.x), 0x07060302u);
-            if (dc == 0) { slo = A.kv_scale[it.row * 2]; shi = A.kv_scale[it.row * 2 + 1]; }
-          } else {
-            v = *(const int4*)((const uint16_t*)A.kv + it.row * 128 + dc * 8);
-          }
-        } else if (kind == 1) {
-          v = *(const int4*)((const uint16_t*)A.win + it.row * 128 + dc * 8);
-        }
-      }
-      *(int4*)&Kl[e * MT_KROW + dc * 8] = v;
-      const uint16_t* hv = (const uint16_t*)&v;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ((uint16_t*)Vt)[(dc * 8 + i) * MT_VROW + e] = hv[i];
-      if (dc == 0) { sclo[e] = slo; schi[e] = shi; okl[e] = kind >= 0; }
-    }
+    mt_store<KVDT, NT, CPT>(R, Kl, Vt, sclo, schi, okl);
     __syncthreads();
+    if (t0 + MT_TE < p1) mt_fetch<KVDT, NT, CPT>(A, b, r, nkv, e_lo, idxl, t0 + MT_TE, p1, R);
 
     // ---- S^T = K Q^T for 4 subtiles of 16 items
     float sv[4][4];
@@ -382,22 +461,44 @@ __global__ __launch_bounds__(HQ * 4) void attend_mfma_kernel(AttendArgs A, int S
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, const float* part_ml,
                                                            const float* part_o) {
+  // one workgroup per (row, head); thread d owns output dim d
   const int r = blockIdx.x / A.Hq, h = blockIdx.x % A.Hq;
   const int d = threadIdx.x;
+  __shared__ float wsp[1024];
+  __shared__ float red[2][2];
   const float sk = A.sink[h];
-  float M = sk;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[(((int64_t)r * S + s) * A.Hq + h) * 2]);
-  float Z = expf(sk - M), o = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const int64_t base = ((int64_t)r * S + s) * A.Hq + h;
-    const float m = part_ml[base * 2];
-    if (m == -INFINITY) continue;
-    const float e = expf(m - M);
-    Z += part_ml[base * 2 + 1] * e;
-    o = fmaf(part_o[base * A.D + d], e, o);
+  const int64_t base0 = (int64_t)r * S * A.Hq + h;          // partial (r, s, h) = base0 + s*Hq
+  float mx = -INFINITY;
+  for (int s = d; s < S; s += 128) mx = fmaxf(mx, part_ml[(base0 + (int64_t)s * A.Hq) * 2]);
+  mx = wave_max(mx);
+  if ((d & 63) == 0) red[0][d >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(sk, fmaxf(red[0][0], red[0][1]));
+  float z = 0.f;
+  for (int s = d; s < S; s += 128) {
+    const float m = part_ml[(base0 + (int64_t)s * A.Hq) * 2];
+    const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
+    wsp[s] = e;
+    z += part_ml[(base0 + (int64_t)s * A.Hq) * 2 + 1] * e;
   }
+  z = wave_sum(z);
+  if ((d & 63) == 0) red[1][d >> 6] = z;
+  __syncthreads();
+  const float Z = __expf(sk - M) + red[1][0] + red[1][1];
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    const float* p = part_o + (base0 + (int64_t)s * A.Hq) * A.D + d;
+    const int64_t st = (int64_t)A.Hq * A.D;
+    o0 = fmaf(p[0], wsp[s], o0);
+    o1 = fmaf(p[st], wsp[s + 1], o1);
+    o2 = fmaf(p[2 * st], wsp[s + 2], o2);
+    o3 = fmaf(p[3 * st], wsp[s + 3], o3);
+  }
+  for (; s < S; ++s) o0 = fmaf(part_o[(base0 + (int64_t)s * A.Hq) * A.D + d], wsp[s], o0);
+  const float o = (o0 + o1) + (o2 + o3);
   store_out(A, ((int64_t)r * A.Hq + h) * A.D + d, o / Z);
-  if (A.lse && d == 0) A.lse[(int64_t)r * A.Hq + h] = M + logf(Z);
+  if (A.lse && d == 0) A.lse[(int64_t)r * A.Hq + h] = M + __logf(Z);
 }
 
 // ------------------------------------------------------------------------

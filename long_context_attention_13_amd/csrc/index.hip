@@ -40,12 +40,15 @@ namespace lca {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int CAP = 128;           // candidate slots per chunk
 constexpr int NDIRECT = 8192;      // rows with n_elig <= NDIRECT skip the chunk kernel
-constexpr int SEL_THREADS = 1024;  // select kernel workgroup
+constexpr int SEL_THREADS = 1024;  // select kernel workgroup (16 wavefronts)
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
-constexpr int RMAX = 16;           // candidate slots per select thread
+constexpr int CMAX = 8192;         // candidates per row held in LDS by the select kernel
+constexpr int LB = 4;              // candidate loads per thread and batch
+constexpr int MAXCH = 1024;        // chunks per row the candidate path handles
 constexpr int KROW = 20;           // LDS floats per key in the transpose buffer (16 + pad)
 constexpr int BITMAP_BITS = 1 << 18;
 
@@ -122,23 +125,35 @@ __device__ __forceinline__ void mx_load_query(const IndexArgs& A, const Rows& rw
 struct MxTiles {
   int4 code[4];
   int sc[4];
+  uint32_t valid;   // bit t: this lane's tile-t operand is a real key block
+  uint32_t kscale;  // the scale bytes of key j0 + lane (for the exactness envelope)
 };
 
-// Load the B operands of 4 MFMA tiles = 64 keys [j0, j0+64).
+// Load the B operands of 4 MFMA tiles = 64 keys [j0, j0+64).  The loads are
+// unconditional (addresses clamped into the sequence's valid rows) so that
+// they all stay in flight; lanes outside the valid range are zeroed where the
+// operands are consumed.
 __device__ __forceinline__ void mx_load_round(const IndexArgs& A, int b, int j0, int jlim, MxTiles& T) {
   const int lane = threadIdx.x & 63;
   const int kb = lane >> 4;
   const bool kbok = kb * 32 < A.d;
+  const int kbc = kbok ? kb : 0;
+  T.valid = 0;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = j0 + t * 16 + (lane & 15);
-    T.code[t] = make_int4(0, 0, 0, 0);
-    T.sc[t] = 127;
-    if (j < jlim && kbok) {
-      const int64_t row = (int64_t)b * A.N_cap + j;
-      T.code[t] = *(const int4*)((const uint8_t*)A.ki + row * (A.d / 2) + kb * 16);
-      T.sc[t] = A.ki_scale[row * (A.d / 32) + kb];
-    }
+    const int jc = j < jlim ? j : jlim - 1;
+    const int64_t row = (int64_t)b * A.N_cap + jc;
+    const v4i v = __builtin_nontemporal_load((const v4i*)((const uint8_t*)A.ki + row * (A.d / 2) + kbc * 16));
+    T.code[t] = make_int4(v[0], v[1], v[2], v[3]);
+    T.sc[t] = A.ki_scale[row * (A.d / 32) + kbc];
+    T.valid |= (uint32_t)(j < jlim && kbok) << t;
+  }
+  {
+    const int j = j0 + lane;
+    const int64_t row = (int64_t)b * A.N_cap + (j < jlim ? j : jlim - 1);
+    const uint8_t* ks = A.ki_scale + row * (A.d / 32);
+    T.kscale = A.d == 128 ? *(const uint32_t*)ks : (uint32_t)*(const uint16_t*)ks;
   }
 }
 
@@ -150,7 +165,7 @@ __device__ __forceinline__ double mx_value(const uint8_t* codes, const uint8_t* 
 
 // Exact float64 dot product of query head (row qr, head h) and key row krow,
 // left to right over the elements.
-__device__ double mx_dot_exact(const IndexArgs& A, int64_t qrow, int64_t krow) {
+__device__ __forceinline__ double mx_dot_exact(const IndexArgs& A, int64_t qrow, int64_t krow) {
   const uint8_t* qc = (const uint8_t*)A.qi + qrow * (A.d / 2);
   const uint8_t* qs = A.qi_scale + qrow * (A.d / 32);
   const uint8_t* kc = (const uint8_t*)A.ki + krow * (A.d / 2);
@@ -169,55 +184,69 @@ __device__ __forceinline__ double combine_step(double s, double dot, float w) {
   return s + t;
 }
 
-// Score one round of 64 keys for the wave's rows.  Lane L ends with the keys
-// of entry j0+L for row 0 and row 1 (0 when not eligible).
+// Score one round of 64 keys for the wave's NQ rows.  Lane L ends with the
+// keys of entry j0+L (0 when not eligible).
 // wbuf: this wave's LDS transpose buffer (64*KROW floats); wl: LDS weights
-// [2][16] for the two rows.
-template <int HP>
+// [2][16].
+__device__ __forceinline__ bool mx_exact(const MxQuery& Q, int kmin, int kmax) {
+  return (Q.dq + kmax - kmin <= 9) && (Q.qmin + kmin >= 130) && (Q.qmax + kmax <= 368);
+}
+
+template <int HP, int NQ>
 __device__ __forceinline__ void mx_score_round(const IndexArgs& A, const Rows& rw, const MxQuery& Q,
                                                const MxTiles& T, int j0, float* wbuf, const float* wl,
-                                               uint64_t& key0, uint64_t& key1) {
+                                               uint64_t* key, bool& inexact) {
   const int lane = threadIdx.x & 63;
   v8i av = {Q.a[0], Q.a[1], Q.a[2], Q.a[3], 0, 0, 0, 0};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    v8i bv = {T.code[t].x, T.code[t].y, T.code[t].z, T.code[t].w, 0, 0, 0, 0};
+    const bool ok = (T.valid >> t) & 1u;
+    v8i bv = {ok ? T.code[t].x : 0, ok ? T.code[t].y : 0, ok ? T.code[t].z : 0, ok ? T.code[t].w : 0, 0, 0, 0, 0};
+    const int scb = ok ? T.sc[t] : 127;
     v4f c = {0.f, 0.f, 0.f, 0.f};
-    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, Q.sa, 0, T.sc[t]);
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, Q.sa, 0, scb);
     float* dst = wbuf + (t * 16 + (lane & 15)) * KROW + 4 * (lane >> 4);
     *(float4*)dst = make_float4(c[0], c[1], c[2], c[3]);
   }
-  __builtin_amdgcn_wave_barrier();
+  // exponent envelope of this lane's key j0+lane from its own scale bytes
+  const uint32_t sw = T.kscale;
+  int kmin = (int)(sw & 0xFFu), kmax = kmin;
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    if (i * 32 < A.d) {
+      const int v = (int)((sw >> (8 * i)) & 0xFFu);
+      kmin = min(kmin, v);
+      kmax = max(kmax, v);
+    }
+  }
+  const bool exact = mx_exact(Q, kmin, kmax);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int j = j0 + lane;
   const float* mine = wbuf + lane * KROW;
-  key0 = key1 = 0;
-  // exactness envelope of this key
-  bool exact = true;
-  if (j < max(rw.n[0], rw.n[1])) {
-    const uint8_t* ks = A.ki_scale + ((int64_t)rw.b * A.N_cap + j) * (A.d / 32);
-    int kmin = 1000, kmax = -1000;
-    for (int i = 0; i < A.d / 32; ++i) { const int s = ks[i]; kmin = min(kmin, s); kmax = max(kmax, s); }
-    exact = (Q.dq + kmax - kmin <= 9) && (Q.qmin + kmin >= 130) && (Q.qmax + kmax <= 368);
-  }
+  inexact = false;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (rw.r[q] < 0 || j >= rw.n[q]) continue;
-    double s = 0.0;
-    if (exact) {
+  for (int q = 0; q < NQ; ++q) {
+    double sc = 0.0;
 #pragma unroll
-      for (int h = 0; h < HP; ++h)
-        if (h < A.H) s = combine_step(s, (double)mine[q * HP + h], wl[q * 16 + h]);
-    } else {
-      for (int h = 0; h < A.H; ++h)
-        s = combine_step(s, mx_dot_exact(A, (int64_t)rw.r[q] * A.H + h, (int64_t)rw.b * A.N_cap + j),
-                         wl[q * 16 + h]);
-    }
-    const uint64_t kk = score_key(s);
-    if (q == 0) key0 = kk; else key1 = kk;
+    for (int h = 0; h < HP; ++h)
+      if (h < A.H) sc = combine_step(sc, (double)mine[q * HP + h], wl[q * 16 + h]);
+    const bool elig = rw.r[q] >= 0 && j < rw.n[q];
+    key[q] = elig ? score_key(sc) : 0ull;
+    inexact |= elig && !exact;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Exact float64 score of entry j for row q of the wave (keys outside the
+// exact-MFMA envelope).
+__device__ __forceinline__ uint64_t mx_score_exact(const IndexArgs& A, int qrow, int b, int j, const float* wlq) {
+  double sc = 0.0;
+  for (int h = 0; h < A.H; ++h)
+    sc = combine_step(sc, mx_dot_exact(A, (int64_t)qrow * A.H + h, (int64_t)b * A.N_cap + j), wlq[h]);
+  return score_key(sc);
 }
 
 // F32 indexer: lane L scores entry j0+L for row 0 (F32 groups hold one row).
@@ -260,23 +289,47 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
 }
 
 // ------------------------------------------------------------------------
-// Chunk kernel
+// Chunk kernel.  A workgroup of 4 wavefronts owns one chunk of CH = 64*KPL
+// consecutive entries for NQ query rows; each wavefront scores KPL/4 rounds
+// of 64 entries (all its key tiles loaded up front), keeps its keys in
+// registers, and contributes its 64 lane maxima (sorted) to the chunk
+// threshold: the r-th largest of the chunk's 256 lane maxima, found by
+// merging the four sorted lists with bitonic half-cleaners.
 // ------------------------------------------------------------------------
-template <int DT, int KPL, int HP>
-__global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, int NCH, int groups_per_b,
-                                                          int qpm) {
+constexpr int WBUF = 64 * KROW;           // floats per wave: dot-product transpose buffer
+
+// Descending bitonic clean of a bitonic sequence held one value per lane.
+__device__ __forceinline__ uint64_t wave_bitonic_clean_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, j);
+    const bool lower = (lane & j) == 0;
+    v = lower ? (o > v ? o : v) : (o < v ? o : v);
+  }
+  return v;
+}
+
+template <int DT, int KPL, int HP, int NQ>
+__global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, int NCH, int groups_per_b) {
   constexpr int CH = 64 * KPL;
+  constexpr int RPW = KPL / 4;            // rounds per wavefront
+  static_assert(KPL % 4 == 0, "four wavefronts share a chunk");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + wave;
+  const int c = blockIdx.x;
   const int g = blockIdx.y;
-  __shared__ float tbuf[4][64 * KROW];
-  __shared__ float wl_s[4][32];
+  __shared__ __align__(16) float tbuf[4][WBUF];
+  __shared__ float wl[32];
+  __shared__ uint64_t lists[NQ][4][64];
+  __shared__ int wcnt[NQ][4];
+  __shared__ uint64_t wmex[NQ][4];
+  __shared__ uint64_t thr_s[NQ];
 
   Rows rw;
   rw.b = g / groups_per_b;
-  const int t0 = (g % groups_per_b) * qpm;
+  const int t0 = (g % groups_per_b) * NQ;
   rw.r[0] = rw.b * A.Tq + t0;
-  rw.r[1] = (qpm == 2 && t0 + 1 < A.Tq) ? rw.r[0] + 1 : -1;
+  rw.r[1] = (NQ == 2 && t0 + 1 < A.Tq) ? rw.r[0] + 1 : -1;
   rw.n[0] = A.n_elig[rw.r[0]];
   rw.n[1] = rw.r[1] >= 0 ? A.n_elig[rw.r[1]] : 0;
   // rows with few entries are done by the select kernel alone
@@ -284,79 +337,129 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
   if (rw.n[1] <= NDIRECT) rw.n[1] = 0;
   const int jlim = max(rw.n[0], rw.n[1]);
   const int jbeg = c * CH;
-  if (jbeg >= jlim || c >= NCH) return;
+  if (jbeg >= jlim) return;                 // uniform over the workgroup
+  const int jl = min(jlim, jbeg + CH);
+  const int jw = jbeg + wave * RPW * 64;    // this wavefront's first entry
 
-  float* wl = wl_s[wave];
-  if (lane < 32) {
-    const int q = lane >> 4, h = lane & 15;
-    wl[lane] = (rw.r[q] >= 0 && h < A.H) ? A.w[(int64_t)rw.r[q] * A.H + h] : 0.f;
+  if (threadIdx.x < 32) {
+    const int q = threadIdx.x >> 4, h = threadIdx.x & 15;
+    wl[threadIdx.x] = (q < NQ && rw.r[q] >= 0 && h < A.H) ? A.w[(int64_t)rw.r[q] * A.H + h] : 0.f;
   }
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
 
-  uint64_t k0[KPL], k1[KPL];
+  uint64_t kq[NQ][RPW];
   if (DT == DT_MXFP4) {
     MxQuery Q;
     mx_load_query<HP>(A, rw, Q);
-    MxTiles cur, nxt;
-    mx_load_round(A, rw.b, jbeg, jlim, cur);
+    MxTiles T[RPW];
 #pragma unroll
-    for (int rr = 0; rr < KPL; ++rr) {
-      if (rr + 1 < KPL) mx_load_round(A, rw.b, jbeg + (rr + 1) * 64, jlim, nxt);
-      mx_score_round<HP>(A, rw, Q, cur, jbeg + rr * 64, tbuf[wave], wl, k0[rr], k1[rr]);
-      if (rr + 1 < KPL) cur = nxt;
+    for (int rr = 0; rr < RPW; ++rr) mx_load_round(A, rw.b, min(jw + rr * 64, jl), jl, T[rr]);
+    uint32_t fix = 0;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      uint64_t kk[NQ];
+      bool ix;
+      mx_score_round<HP, NQ>(A, rw, Q, T[rr], jw + rr * 64, tbuf[wave], wl, kk, ix);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) kq[q][rr] = kk[q];
+      fix |= __ballot(ix) ? 1u << rr : 0u;
+    }
+    if (fix) {
+      // rare: keys outside the exact-MFMA envelope, re-scored in float64
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        if (!((fix >> rr) & 1u)) continue;
+        const int j = jw + rr * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if (kq[q][rr] == 0) continue;
+          const uint8_t* ks = A.ki_scale + ((int64_t)rw.b * A.N_cap + j) * (A.d / 32);
+          int kmin = 1000, kmax = -1000;
+          for (int i = 0; i < A.d / 32; ++i) { kmin = min(kmin, (int)ks[i]); kmax = max(kmax, (int)ks[i]); }
+          if (!mx_exact(Q, kmin, kmax)) kq[q][rr] = mx_score_exact(A, rw.r[q], rw.b, j, wl + q * 16);
+        }
+      }
     }
   } else {
     const float* qrow = (const float*)A.qi + (int64_t)rw.r[0] * A.H * A.d;
 #pragma unroll
-    for (int rr = 0; rr < KPL; ++rr) {
-      f32_score_round(A, rw, jbeg + rr * 64, qrow, wl, k0[rr]);
-      k1[rr] = 0;
-    }
+    for (int rr = 0; rr < RPW; ++rr) f32_score_round(A, rw, jw + rr * 64, qrow, wl, kq[0][rr]);
   }
 
-  // per row: threshold from the lane maxima, emit, record the best excluded key
+  // chunk threshold per row from the 256 lane maxima
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (rw.r[q] < 0 || rw.n[q] == 0 || jbeg >= rw.n[q]) continue;
-    const uint64_t* kq = q == 0 ? k0 : k1;
+  for (int q = 0; q < NQ; ++q) {
     uint64_t lmax = 0;
 #pragma unroll
-    for (int rr = 0; rr < KPL; ++rr) lmax = kq[rr] > lmax ? kq[rr] : lmax;
-    const uint64_t sorted = wave_sort_desc(lmax);
-    const float lam = (float)A.k * (float)CH / (float)rw.n[q];
-    int rsel = (int)ceilf(lam + 6.0f * sqrtf(lam) + 8.0f);
-    rsel = rsel > 64 ? 64 : rsel;
-    const uint32_t tlo = __shfl((uint32_t)sorted, rsel - 1, WAVE);
-    const uint32_t thi = __shfl((uint32_t)(sorted >> 32), rsel - 1, WAVE);
-    uint64_t thr = ((uint64_t)thi << 32) | tlo;
-    if (thr == 0) thr = 1;     // key 0 marks "no entry"; never emit those
-    int total = 0;
-    uint64_t exmax = 0;
+    for (int rr = 0; rr < RPW; ++rr) lmax = kq[q][rr] > lmax ? kq[q][rr] : lmax;
+    lists[q][wave][lane] = wave_sort_desc(lmax);
+  }
+  __syncthreads();
+  if (wave == 0) {
 #pragma unroll
-    for (int rr = 0; rr < KPL; ++rr) {
-      const bool f = kq[rr] >= thr;
-      total += __popcll(__ballot(f));
-      if (!f && kq[rr] > exmax) exmax = kq[rr];
+    for (int q = 0; q < NQ; ++q) {
+      uint64_t cur = lists[q][0][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const uint64_t o = lists[q][w][63 - lane];
+        cur = wave_bitonic_clean_desc(cur > o ? cur : o);
+      }
+      const int n = rw.n[q];
+      const float lam = n > 0 ? (float)A.k * (float)CH / (float)n : 0.f;
+      int rsel = (int)ceilf(lam + 6.0f * sqrtf(lam) + 8.0f);
+      rsel = rsel > 64 ? 64 : (rsel < 1 ? 1 : rsel);
+      const uint32_t tlo = __shfl((uint32_t)cur, rsel - 1, WAVE);
+      const uint32_t thi = __shfl((uint32_t)(cur >> 32), rsel - 1, WAVE);
+      uint64_t thr = ((uint64_t)thi << 32) | tlo;
+      if (lane == 0) thr_s[q] = thr == 0 ? 1 : thr;   // key 0 marks "no entry"; never emit those
     }
-    exmax = wave_max_u64(exmax);
+  }
+  __syncthreads();
+  // counts and the best excluded key per wavefront
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const uint64_t thr = thr_s[q];
+    int cnt = 0;
+    uint64_t ex = 0;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const bool f = kq[q][rr] >= thr;
+      cnt += __popcll(__ballot(f));
+      if (!f && kq[q][rr] > ex) ex = kq[q][rr];
+    }
+    ex = wave_max_u64(ex);
+    if (lane == 0) { wcnt[q][wave] = cnt; wmex[q][wave] = ex; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (rw.r[q] < 0 || rw.n[q] == 0 || jbeg >= rw.n[q]) continue;
     const int64_t slot = (int64_t)rw.r[q] * NCH + c;
+    const int total = wcnt[q][0] + wcnt[q][1] + wcnt[q][2] + wcnt[q][3];
     if (total > CAP) {
-      if (lane == 0) { W.cnt[slot] = -1; W.mex[slot] = ~0ull; }
+      if (threadIdx.x == 0) { W.cnt[slot] = -1; W.mex[slot] = ~0ull; }
       continue;
     }
+    const uint64_t thr = thr_s[q];
     int base = 0;
+    for (int w = 0; w < wave; ++w) base += wcnt[q][w];
 #pragma unroll
-    for (int rr = 0; rr < KPL; ++rr) {
-      const bool f = kq[rr] >= thr;
+    for (int rr = 0; rr < RPW; ++rr) {
+      const bool f = kq[q][rr] >= thr;
       const uint64_t bal = __ballot(f);
       if (f) {
         const int pos = base + lanes_below(bal);
-        W.ckey[slot * CAP + pos] = kq[rr];
-        W.cidx[slot * CAP + pos] = jbeg + rr * 64 + lane;
+        W.ckey[slot * CAP + pos] = kq[q][rr];
+        W.cidx[slot * CAP + pos] = jw + rr * 64 + lane;
       }
       base += __popcll(bal);
     }
-    if (lane == 0) { W.cnt[slot] = total; W.mex[slot] = exmax; }
+    if (threadIdx.x == 0) {
+      uint64_t m = wmex[q][0];
+      for (int w = 1; w < 4; ++w) m = wmex[q][w] > m ? wmex[q][w] : m;
+      W.cnt[slot] = total;
+      W.mex[slot] = m;
+    }
   }
 }
 
@@ -366,38 +469,34 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
 struct SelShared {
   uint32_t hist[2048];
   uint32_t scan[SEL_WAVES];
-  uint64_t red64[SEL_WAVES];
-  int32_t off[SEL_THREADS + 1];
+  uint64_t red64[2][SEL_WAVES];
+  int32_t off[MAXCH + 1];
   uint32_t bitmap[BITMAP_BITS / 32];
+  uint64_t rkey[64];           // items of the threshold bin, resolved exactly
+  int32_t rj[64];
+  int nres;
   int bcast[8];
   uint64_t bcast64[4];
 };
 
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, SelShared& S) {
-  v = wave_max_u64(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) S.red64[wave] = v;
-  __syncthreads();
-  uint64_t m = 0;
-  for (int i = 0; i < SEL_WAVES; ++i) m = S.red64[i] > m ? S.red64[i] : m;
-  return m;
-}
-
-__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, SelShared& S) {
-  // min over valid keys; callers pass ~0 for invalid
+// Block-wide max and min of one u64 per thread (min over values != ~0).
+__device__ __forceinline__ void block_minmax_u64(uint64_t& mx, uint64_t& mn, SelShared& S) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t t = shfl_xor_u64(v, o);
-    v = t < v ? t : v;
+    const uint64_t a = shfl_xor_u64(mx, o), c = shfl_xor_u64(mn, o);
+    mx = a > mx ? a : mx;
+    mn = c < mn ? c : mn;
   }
   const int wave = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) S.red64[wave] = v;
+  if ((threadIdx.x & 63) == 0) { S.red64[0][wave] = mx; S.red64[1][wave] = mn; }
   __syncthreads();
-  uint64_t m = ~0ull;
-  for (int i = 0; i < SEL_WAVES; ++i) m = S.red64[i] < m ? S.red64[i] : m;
-  return m;
+  mx = 0; mn = ~0ull;
+#pragma unroll
+  for (int i = 0; i < SEL_WAVES; ++i) {
+    mx = S.red64[0][i] > mx ? S.red64[0][i] : mx;
+    mn = S.red64[1][i] < mn ? S.red64[1][i] : mn;
+  }
 }
 
 // Exclusive block scan of one int per thread; returns the exclusive prefix,
@@ -414,6 +513,7 @@ __device__ __forceinline__ int block_scan(int v, int* tot, SelShared& S) {
   if (lane == 63) S.scan[wave] = (uint32_t)incl;
   __syncthreads();
   int before = 0, all = 0;
+#pragma unroll
   for (int i = 0; i < SEL_WAVES; ++i) {
     const int s = (int)S.scan[i];
     if (i < wave) before += s;
@@ -429,6 +529,7 @@ __device__ __forceinline__ int block_scan(int v, int* tot, SelShared& S) {
 // [2] count in digit.
 template <class Src>
 __device__ void radix_digit(Src& src, uint64_t prefix, uint64_t mask, int shift, int nb, int rem, SelShared& S) {
+  constexpr int BPT = 2048 / SEL_THREADS;       // bins per thread
   const int nbins = 1 << nb;
   for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
   __syncthreads();
@@ -436,18 +537,19 @@ __device__ void radix_digit(Src& src, uint64_t prefix, uint64_t mask, int shift,
     if (key != 0 && (key & mask) == prefix) atomicAdd(&S.hist[(key >> shift) & (uint64_t)(nbins - 1)], 1u);
   });
   __syncthreads();
-  // suffix sums: thread t owns bins 2t, 2t+1 (counted from the top)
-  const int t = threadIdx.x;
-  const int bhi = nbins - 1 - 2 * t, blo = bhi - 1;
-  const int c_hi = (bhi >= 0) ? (int)S.hist[bhi] : 0;
-  const int c_lo = (blo >= 0) ? (int)S.hist[blo] : 0;
+  // thread t owns bins top-BPT*t .. top-BPT*t-BPT+1 (counted from the top bin)
+  const int top = nbins - 1 - BPT * (int)threadIdx.x;
+  int cnt[BPT], mine = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) { cnt[i] = (top - i >= 0) ? (int)S.hist[top - i] : 0; mine += cnt[i]; }
   int tot;
-  const int above = block_scan(c_hi + c_lo, &tot, S);   // count in bins above bhi
-  if (bhi >= 0 && above < rem && above + c_hi >= rem) {
-    S.bcast[0] = bhi; S.bcast[1] = above; S.bcast[2] = c_hi;
-  }
-  if (blo >= 0 && above + c_hi < rem && above + c_hi + c_lo >= rem) {
-    S.bcast[0] = blo; S.bcast[1] = above + c_hi; S.bcast[2] = c_lo;
+  int above = block_scan(mine, &tot, S);        // count in bins above this thread's bins
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    if (top - i >= 0 && above < rem && above + cnt[i] >= rem) {
+      S.bcast[0] = top - i; S.bcast[1] = above; S.bcast[2] = cnt[i];
+    }
+    above += cnt[i];
   }
   __syncthreads();
 }
@@ -455,6 +557,7 @@ __device__ void radix_digit(Src& src, uint64_t prefix, uint64_t mask, int shift,
 // Smallest-j selection among ties (key == T): find the rem-th smallest j.
 template <class Src>
 __device__ int tie_select_j(Src& src, uint64_t T, int rem, SelShared& S) {
+  constexpr int BPT = 2048 / SEL_THREADS;
   uint32_t prefix = 0, mask = 0;
   int shift = 31;
   while (shift > 0) {
@@ -467,14 +570,17 @@ __device__ int tie_select_j(Src& src, uint64_t T, int rem, SelShared& S) {
       if (key == T && ((uint32_t)j & mask) == prefix) atomicAdd(&S.hist[((uint32_t)j >> shift) & (nbins - 1)], 1u);
     });
     __syncthreads();
-    const int t = threadIdx.x;
-    const int b0 = 2 * t, b1 = b0 + 1;
-    const int c0 = b0 < (int)nbins ? (int)S.hist[b0] : 0;
-    const int c1 = b1 < (int)nbins ? (int)S.hist[b1] : 0;
+    const int b0 = BPT * (int)threadIdx.x;
+    int cnt[BPT], mine = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) { cnt[i] = (b0 + i < (int)nbins) ? (int)S.hist[b0 + i] : 0; mine += cnt[i]; }
     int tot;
-    const int below = block_scan(c0 + c1, &tot, S);
-    if (b0 < (int)nbins && below < rem && below + c0 >= rem) { S.bcast[0] = b0; S.bcast[1] = below; }
-    if (b1 < (int)nbins && below + c0 < rem && below + c0 + c1 >= rem) { S.bcast[0] = b1; S.bcast[1] = below + c0; }
+    int below = block_scan(mine, &tot, S);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (b0 + i < (int)nbins && below < rem && below + cnt[i] >= rem) { S.bcast[0] = b0 + i; S.bcast[1] = below; }
+      below += cnt[i];
+    }
     __syncthreads();
     const int dsel = S.bcast[0];
     rem -= S.bcast[1];
@@ -499,6 +605,35 @@ __device__ __forceinline__ bool selected(const Thr& th, uint64_t key, int j) {
   return key > th.T || (key == th.T && j <= th.Tj);
 }
 
+// Exact rank resolution inside one radix bin of at most 64 items: the items
+// (key & mask) == prefix are gathered in LDS and the rem-th of them in the
+// order (key desc, j asc) is found by counting, per item, the items before it.
+template <class Src>
+__device__ void resolve_bin(Src& src, uint64_t prefix, uint64_t mask, int rem, SelShared& S) {
+  if (threadIdx.x == 0) S.nres = 0;
+  __syncthreads();
+  src.for_each([&](uint64_t key, int j) {
+    if (key != 0 && (key & mask) == prefix) {
+      const int p = atomicAdd(&S.nres, 1);
+      if (p < 64) { S.rkey[p] = key; S.rj[p] = j; }
+    }
+  });
+  __syncthreads();
+  const int n = S.nres;
+  if (threadIdx.x < 64) {
+    const int i = threadIdx.x;
+    int rank = 0;
+    const uint64_t ki = i < n ? S.rkey[i] : 0;
+    const int ji = i < n ? S.rj[i] : 0;
+    for (int m = 0; m < n; ++m) {
+      const uint64_t km = S.rkey[m];
+      rank += (km > ki) || (km == ki && S.rj[m] < ji);
+    }
+    if (i < n && rank == rem - 1) { S.bcast64[0] = ki; S.bcast[3] = ji; }
+  }
+  __syncthreads();
+}
+
 // Exact selection threshold for the kk largest (by key desc, j asc) items.
 template <class Src>
 __device__ Thr find_threshold(Src& src, int kk, SelShared& S) {
@@ -507,8 +642,7 @@ __device__ Thr find_threshold(Src& src, int kk, SelShared& S) {
   src.for_each([&](uint64_t key, int j) {
     if (key != 0) { mx = key > mx ? key : mx; mn = key < mn ? key : mn; }
   });
-  mx = block_max_u64(mx, S);
-  mn = block_min_u64(mn, S);
+  block_minmax_u64(mx, mn, S);
   th.Tj = 0x7FFFFFFF;
   if (mx == 0) { th.T = ~0ull; th.low = 0; return th; }   // nothing eligible
   if (mx == mn) {
@@ -530,6 +664,15 @@ __device__ Thr find_threshold(Src& src, int kk, SelShared& S) {
       prefix |= (uint64_t)dsel << shift;
       mask |= (uint64_t)((1u << nb) - 1u) << shift;
       if (indig == rem) { early = shift > 0; break; }
+      if (indig <= 64 && shift > 0) {
+        // few items left in the bin: rank them exactly (ties by index)
+        resolve_bin(src, prefix, mask, rem, S);
+        th.T = S.bcast64[0];
+        th.Tj = S.bcast[3];
+        th.low = 0;
+        __syncthreads();
+        return th;
+      }
     }
     th.T = prefix;
     th.low = early ? shift : 0;
@@ -598,12 +741,13 @@ __device__ void emit_sorted(Src& src, const Thr& th, int n, int k, int32_t* out,
 }
 
 // Source over candidates held in registers.
-struct RegSrc {
-  uint64_t key[RMAX];
-  int j[RMAX];
+// Source over candidates held in LDS.
+struct LdsSrc {
+  const uint64_t* key;
+  const int32_t* j;
+  int n;
   template <class F> __device__ __forceinline__ void for_each(F&& f) {
-#pragma unroll
-    for (int s = 0; s < RMAX; ++s) f(key[s], j[s]);
+    for (int i = threadIdx.x; i < n; i += SEL_THREADS) f(key[i], j[i]);
   }
 };
 
@@ -613,18 +757,20 @@ struct StreamSrc {
   const IndexArgs* A;
   Rows rw;
   MxQuery Q;
-  float* tbuf;     // per-wave transpose buffers [SEL_WAVES][64*KROW]
+  float* tbuf;     // per-wave buffers [SEL_WAVES][WBUF]
   const float* wl; // [32] weights (row 0)
   const float* ql; // F32 query in LDS
   template <class F> __device__ void for_each(F&& f) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = rw.n[0];
     for (int j0 = wave * 64; j0 < n; j0 += SEL_THREADS) {
-      uint64_t k0, k1;
+      uint64_t k0;
       if (DT == DT_MXFP4) {
         MxTiles T;
+        bool ix;
         mx_load_round(*A, rw.b, j0, n, T);
-        mx_score_round<HP>(*A, rw, Q, T, j0, tbuf + wave * 64 * KROW, wl, k0, k1);
+        mx_score_round<HP, 1>(*A, rw, Q, T, j0, tbuf + wave * WBUF, wl, &k0, ix);
+        if (ix) k0 = mx_score_exact(*A, rw.r[0], rw.b, j0 + lane, wl);
       } else {
         f32_score_round(*A, rw, j0, ql, wl, k0);
       }
@@ -633,13 +779,44 @@ struct StreamSrc {
   }
 };
 
+// Exact selection of one row from scratch, re-scoring every eligible entry in
+// each pass (rows with few entries, and rows whose candidates failed the
+// certification).  Kept out of line: it is the rare or the small case.
+template <int DT, int HP>
+__device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n, int kk, int32_t* out, double* sout,
+                                             SelShared& S, float* tbuf, const float* wl, const float* ql,
+                                             bool all_selected) {
+  StreamSrc<DT, HP> src;
+  src.A = &A;
+  src.rw.b = r / A.Tq;
+  src.rw.r[0] = r; src.rw.r[1] = -1;
+  src.rw.n[0] = n; src.rw.n[1] = 0;
+  if (DT == DT_MXFP4) mx_load_query<HP>(A, src.rw, src.Q);
+  src.tbuf = tbuf;
+  src.wl = wl;
+  src.ql = ql;
+  if (all_selected) {
+    // every eligible entry is selected: only the scores are needed
+    for (int i = n + threadIdx.x; i < A.k; i += SEL_THREADS) sout[i] = 0.0;
+    src.for_each([&](uint64_t key, int j) { if (j < n) sout[j] = key_score(key); });
+    return;
+  }
+  const Thr th = find_threshold(src, kk, S);
+  emit_sorted(src, th, n, A.k, out, sout, S);
+}
+
 template <int DT, int HP>
 __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, IdxWs W, int NCH, int CH) {
   extern __shared__ __align__(16) char smem[];
   SelShared& S = *(SelShared*)smem;
-  float* tbuf = (float*)(smem + sizeof(SelShared));               // [SEL_WAVES][64*KROW]
-  float* wl = tbuf + SEL_WAVES * 64 * KROW;                        // [32]
-  float* ql = wl + 32;                                             // F32 query [H*d]
+  // the candidate arrays (candidate path) and the scoring buffers (streamed
+  // path) share one region
+  char* region = smem + sizeof(SelShared);
+  uint64_t* ckey_l = (uint64_t*)region;                            // [CMAX]
+  int32_t* cidx_l = (int32_t*)(region + sizeof(uint64_t) * CMAX);  // [CMAX]
+  float* tbuf = (float*)region;                                    // [SEL_WAVES][WBUF]
+  float* wl = (float*)(region + 12 * CMAX);                        // [32]
+  const float* ql = (const float*)A.qi + (int64_t)blockIdx.x * A.H * A.d;   // F32 query row (global)
 
   const int r = blockIdx.x;
   const int n = A.n_elig[r];
@@ -648,68 +825,87 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
   double* sout = A.score_out ? A.score_out + (int64_t)r * A.k : nullptr;
 
   if (threadIdx.x < 32) wl[threadIdx.x] = (threadIdx.x < (unsigned)A.H) ? A.w[(int64_t)r * A.H + threadIdx.x] : 0.f;
-  if (DT == DT_F32)
-    for (int i = threadIdx.x; i < A.H * A.d; i += SEL_THREADS) ql[i] = ((const float*)A.qi)[(int64_t)r * A.H * A.d + i];
   __syncthreads();
 
-  bool done = false;
   if (n <= A.k) {
-    // every eligible entry is selected; scores only if asked for
+    // every eligible entry is selected
     for (int i = threadIdx.x; i < A.k; i += SEL_THREADS) out[i] = i < n ? i : -1;
-    if (sout) {
-      StreamSrc<DT, HP> src;
-      src.A = &A;
-      src.rw.b = r / A.Tq;
-      src.rw.r[0] = r; src.rw.r[1] = -1;
-      src.rw.n[0] = n; src.rw.n[1] = 0;
-      if (DT == DT_MXFP4) mx_load_query<HP>(A, src.rw, src.Q);
-      src.tbuf = tbuf; src.wl = wl; src.ql = ql;
-      for (int i = n + threadIdx.x; i < A.k; i += SEL_THREADS) sout[i] = 0.0;
-      src.for_each([&](uint64_t key, int j) { if (j < n) sout[j] = key_score(key); });
-    }
-    done = true;
-  } else if (n > NDIRECT) {
+    if (sout) select_streamed<DT, HP>(A, r, n, kk, out, sout, S, tbuf, wl, ql, true);
+    return;
+  }
+  bool done = false;
+  const int nch = (n + CH - 1) / CH;
+  if (n > NDIRECT && nch <= MAXCH) {
     // ---------------- candidate path ----------------
-    const int nch = (n + CH - 1) / CH;
-    int bad = 0;
-    // prefix offsets of the chunk counts
-    int total = 0;
-    for (int c0 = 0; c0 < nch; c0 += SEL_THREADS) {
-      const int c = c0 + threadIdx.x;
-      int v = 0;
-      if (c < nch) {
-        v = W.cnt[(int64_t)r * NCH + c];
-        if (v < 0) { bad = 1; v = 0; }
-      }
+    constexpr int CPTH = MAXCH / SEL_THREADS;        // chunks per thread
+    int cv[CPTH];
+    uint64_t mv[CPTH];
+#pragma unroll
+    for (int i = 0; i < CPTH; ++i) {                 // independent loads, all in flight
+      const int c = i * SEL_THREADS + threadIdx.x;
+      const int cc = c < nch ? c : 0;
+      cv[i] = W.cnt[(int64_t)r * NCH + cc];
+      mv[i] = W.mex[(int64_t)r * NCH + cc];
+    }
+    int bad = 0, carry = 0;
+#pragma unroll
+    for (int i = 0; i < CPTH; ++i) {
+      const int c = i * SEL_THREADS + threadIdx.x;
+      int v = c < nch ? cv[i] : 0;
+      if (v < 0) { bad = 1; v = 0; }
       int tot;
       const int ex = block_scan(v, &tot, S);
-      if (nch <= SEL_THREADS) S.off[threadIdx.x] = ex;
-      total += tot;
+      if (c < nch) S.off[c] = carry + ex;
+      carry += tot;
     }
-    if (nch <= SEL_THREADS && threadIdx.x == 0) S.off[nch] = total;
+    const int total = carry;
+    if (threadIdx.x == 0) S.off[nch] = total;
     bad = __syncthreads_or(bad);
-    if (!bad && nch <= SEL_THREADS && total <= RMAX * SEL_THREADS && total >= kk) {
-      RegSrc src;
+    if (!bad && total <= CMAX && total >= kk) {
+      // copy the candidates into LDS: batches of LB per thread, the next
+      // batch's loads issued before the current batch is stored
+      auto addr = [&](int i) -> int64_t {
+        int lo = 0, hi = nch;                    // chunk c with off[c] <= i < off[c+1]
+        while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (S.off[mid] <= i) lo = mid; else hi = mid; }
+        return ((int64_t)r * NCH + lo) * CAP + (i - S.off[lo]);
+      };
+      uint64_t bk[2][LB];
+      int32_t bj[2][LB];
+      const int nb = (total + SEL_THREADS * LB - 1) / (SEL_THREADS * LB);
 #pragma unroll
-      for (int s = 0; s < RMAX; ++s) {
-        const int i = s * SEL_THREADS + threadIdx.x;
-        src.key[s] = 0;
-        src.j[s] = 0x7FFFFFFF;
-        if (i < total) {
-          int lo = 0, hi = nch;      // find chunk c with off[c] <= i < off[c+1]
-          while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (S.off[mid] <= i) lo = mid; else hi = mid; }
-          const int64_t slot = (int64_t)r * NCH + lo;
-          const int p = i - S.off[lo];
-          src.key[s] = W.ckey[slot * CAP + p];
-          src.j[s] = W.cidx[slot * CAP + p];
+      for (int u = 0; u < LB; ++u) {
+        const int i = u * SEL_THREADS + threadIdx.x;
+        const int64_t a = i < total ? addr(i) : 0;
+        bk[0][u] = W.ckey[a];
+        bj[0][u] = W.cidx[a];
+      }
+      for (int bt = 0; bt < nb; ++bt) {
+        const int cur = bt & 1;
+        if (bt + 1 < nb) {
+#pragma unroll
+          for (int u = 0; u < LB; ++u) {
+            const int i = ((bt + 1) * LB + u) * SEL_THREADS + threadIdx.x;
+            const int64_t a = i < total ? addr(i) : 0;
+            bk[cur ^ 1][u] = W.ckey[a];
+            bj[cur ^ 1][u] = W.cidx[a];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          const int i = (bt * LB + u) * SEL_THREADS + threadIdx.x;
+          if (i < total) { ckey_l[i] = bk[cur][u]; cidx_l[i] = bj[cur][u]; }
         }
       }
+      __syncthreads();
+      LdsSrc src{ckey_l, cidx_l, total};
       const Thr th = find_threshold(src, kk, S);
       // certification: no excluded entry may reach the threshold
       int unsafe = 0;
-      for (int c = threadIdx.x; c < nch; c += SEL_THREADS) {
-        const uint64_t m = W.mex[(int64_t)r * NCH + c];
-        if (m != 0) {
+#pragma unroll
+      for (int i = 0; i < CPTH; ++i) {
+        const int c = i * SEL_THREADS + threadIdx.x;
+        const uint64_t m = mv[i];
+        if (c < nch && m != 0) {
           if (th.low > 0) unsafe |= (m >> th.low) >= (th.T >> th.low);
           else unsafe |= m >= th.T;
         }
@@ -721,56 +917,46 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
       }
     }
   }
-  if (!done) {
-    // ---------------- exact streamed path ----------------
-    StreamSrc<DT, HP> src;
-    src.A = &A;
-    src.rw.b = r / A.Tq;
-    src.rw.r[0] = r; src.rw.r[1] = -1;
-    src.rw.n[0] = n; src.rw.n[1] = 0;
-    if (DT == DT_MXFP4) mx_load_query<HP>(A, src.rw, src.Q);
-    src.tbuf = tbuf;
-    src.wl = wl;
-    src.ql = ql;
-    const Thr th = find_threshold(src, kk, S);
-    emit_sorted(src, th, n, A.k, out, sout, S);
-  }
+  if (!done) select_streamed<DT, HP>(A, r, n, kk, out, sout, S, tbuf, wl, ql, false);
 }
 
 // ------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------
-static int choose_kpl(const IndexArgs& a, int qpm) {
-  const int64_t groups = (int64_t)a.B * ((a.Tq + qpm - 1) / qpm);
+// Rows per wavefront: two query rows share the MFMA A operand when the heads
+// fit in 8 rows and there is more than one query per sequence.
+static int nq_of(int dt, int H, int Tq) { return (dt == DT_MXFP4 && H <= 8 && Tq > 1) ? 2 : 1; }
+
+static int choose_kpl(const IndexArgs& a, int nq) {
+  const int64_t groups = (int64_t)a.B * ((a.Tq + nq - 1) / nq);
   const int64_t waves16 = groups * ((a.N_cap + 1023) / 1024);
   return waves16 >= 1024 ? 16 : 4;
 }
 
-static int qpm_of(int dt, int H) { return (dt == DT_MXFP4 && H <= 8) ? 2 : 1; }
-
 size_t index_ws_bytes(int B, int Tq, int H, int d, int64_t N_cap, int k, int dt) {
   IndexArgs a{};
   a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.N_cap = N_cap; a.k = k;
-  const int kpl = choose_kpl(a, qpm_of(dt, H));
+  const int kpl = choose_kpl(a, nq_of(dt, H, Tq));
   const int64_t NCH = (N_cap + 64 * kpl - 1) / (64 * kpl);
   return carve_bytes((int64_t)B * Tq, NCH > 0 ? NCH : 1);
 }
 
 static size_t select_smem(int dt, int H, int d) {
-  size_t s = sizeof(SelShared) + sizeof(float) * (SEL_WAVES * 64 * KROW + 32);
-  if (dt == DT_F32) s += sizeof(float) * H * d;
-  return s;
+  size_t region = 12 * (size_t)CMAX;                                   // candidate keys + indices
+  const size_t stream = sizeof(float) * SEL_WAVES * WBUF;              // scoring buffers (aliased)
+  if (stream > region) region = stream;
+  return sizeof(SelShared) + region + sizeof(float) * 32;
 }
 
-template <int DT, int KPL, int HP>
-static hipError_t launch_t(const IndexArgs& a, hipStream_t s, int qpm) {
+template <int DT, int KPL, int HP, int NQ>
+static hipError_t launch_t(const IndexArgs& a, hipStream_t s) {
   const int CH = 64 * KPL;
   const int64_t NCH = (a.N_cap + CH - 1) / CH;
   IdxWs W = carve(a.ws, (int64_t)a.B * a.Tq, NCH > 0 ? NCH : 1);
-  const int gpb = (a.Tq + qpm - 1) / qpm;
+  const int gpb = (a.Tq + NQ - 1) / NQ;
   if (a.N_cap > NDIRECT) {
-    dim3 grid((unsigned)((NCH + 3) / 4), (unsigned)(a.B * gpb));
-    hipLaunchKernelGGL((index_chunk_kernel<DT, KPL, HP>), grid, dim3(256), 0, s, a, W, (int)NCH, gpb, qpm);
+    dim3 grid((unsigned)NCH, (unsigned)(a.B * gpb));
+    hipLaunchKernelGGL((index_chunk_kernel<DT, KPL, HP, NQ>), grid, dim3(256), 0, s, a, W, (int)NCH, gpb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -780,15 +966,19 @@ static hipError_t launch_t(const IndexArgs& a, hipStream_t s, int qpm) {
   return hipGetLastError();
 }
 
+template <int DT, int HP, int NQ>
+static hipError_t launch_k(const IndexArgs& a, hipStream_t s) {
+  return choose_kpl(a, NQ) == 16 ? launch_t<DT, 16, HP, NQ>(a, s) : launch_t<DT, 4, HP, NQ>(a, s);
+}
+
 hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
   if ((int64_t)a.B * a.Tq == 0) return hipSuccess;
-  const int qpm = qpm_of(a.dt, a.H);
-  const int kpl = choose_kpl(a, qpm);
+  const int nq = nq_of(a.dt, a.H, a.Tq);
   if (a.dt == DT_MXFP4) {
-    if (a.H <= 8) return kpl == 16 ? launch_t<DT_MXFP4, 16, 8>(a, s, qpm) : launch_t<DT_MXFP4, 4, 8>(a, s, qpm);
-    return kpl == 16 ? launch_t<DT_MXFP4, 16, 16>(a, s, qpm) : launch_t<DT_MXFP4, 4, 16>(a, s, qpm);
+    if (a.H <= 8) return nq == 2 ? launch_k<DT_MXFP4, 8, 2>(a, s) : launch_k<DT_MXFP4, 8, 1>(a, s);
+    return launch_k<DT_MXFP4, 16, 1>(a, s);
   }
-  return kpl == 16 ? launch_t<DT_F32, 16, 16>(a, s, 1) : launch_t<DT_F32, 4, 16>(a, s, 1);
+  return launch_k<DT_F32, 16, 1>(a, s);
 }
 
 }  // namespace lca
