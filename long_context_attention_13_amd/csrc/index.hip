@@ -47,15 +47,17 @@ constexpr int NDIRECT = 8192;      // rows with n_elig <= NDIRECT skip the chunk
 constexpr int SEL_THREADS = 1024;  // select kernel workgroup (16 wavefronts)
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
 constexpr int CMAX = 8192;         // candidates per row held in LDS by the select kernel
-constexpr int LB = 4;              // candidate loads per thread and batch
+constexpr int LB = CMAX / 1024;    // candidate loads per thread and batch (one batch at 1024 threads)
 constexpr int MAXCH = 1024;        // chunks per row the candidate path handles
 constexpr int KROW = 20;           // LDS floats per key in the transpose buffer (16 + pad)
 constexpr int BITMAP_BITS = 1 << 18;
 
 struct IdxWs {
-  int32_t* cnt;   // [R][NCH]
-  uint64_t* mex;  // [R][NCH]
-  uint64_t* ckey; // [R][NCH][CAP]
+  int32_t* cnt;   // [R][NCH] candidates emitted by each chunk (-1: overflow)
+  uint64_t* mex;  // [R][NCH] largest key a chunk did not emit (0: none)
+  uint64_t* cmax; // [R][NCH] largest key of a chunk
+  uint64_t* cthr; // [R][NCH] emission threshold of a chunk (every candidate >= it)
+  uint64_t* ckey; // [R][NCH][CAP] candidates, ascending index within a chunk
   int32_t* cidx;  // [R][NCH][CAP]
 };
 
@@ -66,13 +68,15 @@ static IdxWs carve(void* ws, int64_t R, int64_t NCH) {
   char* p = (char*)ws;
   w.cnt = (int32_t*)p; p += align256(sizeof(int32_t) * R * NCH);
   w.mex = (uint64_t*)p; p += align256(sizeof(uint64_t) * R * NCH);
+  w.cmax = (uint64_t*)p; p += align256(sizeof(uint64_t) * R * NCH);
+  w.cthr = (uint64_t*)p; p += align256(sizeof(uint64_t) * R * NCH);
   w.ckey = (uint64_t*)p; p += align256(sizeof(uint64_t) * R * NCH * CAP);
   w.cidx = (int32_t*)p;
   return w;
 }
 
 static size_t carve_bytes(int64_t R, int64_t NCH) {
-  return align256(sizeof(int32_t) * R * NCH) + align256(sizeof(uint64_t) * R * NCH) +
+  return align256(sizeof(int32_t) * R * NCH) + 3 * align256(sizeof(uint64_t) * R * NCH) +
          align256(sizeof(uint64_t) * R * NCH * CAP) + align256(sizeof(int32_t) * R * NCH * CAP);
 }
 
@@ -96,12 +100,13 @@ __device__ __forceinline__ void mx_load_query(const IndexArgs& A, const Rows& rw
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, kb = lane >> 4;
   const int q = row / HP, h = row % HP;
-  const bool valid = (q < 2) && rw.r[q] >= 0 && h < A.H && kb * 32 < A.d;
+  const int rq = q == 0 ? rw.r[0] : rw.r[1];     // (no dynamic indexing: keeps rw in registers)
+  const bool valid = (q < 2) && rq >= 0 && h < A.H && kb * 32 < A.d;
   Q.a[0] = Q.a[1] = Q.a[2] = Q.a[3] = 0;
   Q.sa = 127;
   int smin = 1000, smax = -1000;
   if (valid) {
-    const int64_t qrow = (int64_t)rw.r[q] * A.H + h;
+    const int64_t qrow = (int64_t)rq * A.H + h;
     const int4 v = *(const int4*)((const uint8_t*)A.qi + qrow * (A.d / 2) + kb * 16);
     Q.a[0] = v.x; Q.a[1] = v.y; Q.a[2] = v.z; Q.a[3] = v.w;
     Q.sa = A.qi_scale[qrow * (A.d / 32) + kb];
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
   __shared__ uint64_t lists[NQ][4][64];
   __shared__ int wcnt[NQ][4];
   __shared__ uint64_t wmex[NQ][4];
-  __shared__ uint64_t thr_s[NQ];
+  __shared__ uint64_t thr_s[NQ], top_s[NQ];
 
   Rows rw;
   rw.b = g / groups_per_b;
@@ -351,15 +356,17 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
   if (DT == DT_MXFP4) {
     MxQuery Q;
     mx_load_query<HP>(A, rw, Q);
-    MxTiles T[RPW];
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) mx_load_round(A, rw.b, min(jw + rr * 64, jl), jl, T[rr]);
+    // two-stage pipeline: the next round's tiles load while this one is scored
+    MxTiles cur, nxt;
+    mx_load_round(A, rw.b, min(jw, jl), jl, cur);
     uint32_t fix = 0;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       uint64_t kk[NQ];
       bool ix;
-      mx_score_round<HP, NQ>(A, rw, Q, T[rr], jw + rr * 64, tbuf[wave], wl, kk, ix);
+      if (rr + 1 < RPW) mx_load_round(A, rw.b, min(jw + (rr + 1) * 64, jl), jl, nxt);
+      mx_score_round<HP, NQ>(A, rw, Q, cur, jw + rr * 64, tbuf[wave], wl, kk, ix);
+      if (rr + 1 < RPW) cur = nxt;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) kq[q][rr] = kk[q];
       fix |= __ballot(ix) ? 1u << rr : 0u;
@@ -408,10 +415,10 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
       const float lam = n > 0 ? (float)A.k * (float)CH / (float)n : 0.f;
       int rsel = (int)ceilf(lam + 6.0f * sqrtf(lam) + 8.0f);
       rsel = rsel > 64 ? 64 : (rsel < 1 ? 1 : rsel);
-      const uint32_t tlo = __shfl((uint32_t)cur, rsel - 1, WAVE);
-      const uint32_t thi = __shfl((uint32_t)(cur >> 32), rsel - 1, WAVE);
-      uint64_t thr = ((uint64_t)thi << 32) | tlo;
-      if (lane == 0) thr_s[q] = thr == 0 ? 1 : thr;   // key 0 marks "no entry"; never emit those
+      const uint64_t thr = ((uint64_t)readlane_u32((uint32_t)(cur >> 32), rsel - 1) << 32) |
+                           readlane_u32((uint32_t)cur, rsel - 1);
+      const uint64_t top = ((uint64_t)readlane_u32((uint32_t)(cur >> 32), 0) << 32) | readlane_u32((uint32_t)cur, 0);
+      if (lane == 0) { thr_s[q] = thr == 0 ? 1 : thr; top_s[q] = top; }   // key 0 marks "no entry"
     }
   }
   __syncthreads();
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
       cnt += __popcll(__ballot(f));
       if (!f && kq[q][rr] > ex) ex = kq[q][rr];
     }
-    ex = wave_max_u64(ex);
+    ex = wave_max_u64_dpp(ex);
     if (lane == 0) { wcnt[q][wave] = cnt; wmex[q][wave] = ex; }
   }
   __syncthreads();
@@ -459,6 +466,8 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
       for (int w = 1; w < 4; ++w) m = wmex[q][w] > m ? wmex[q][w] : m;
       W.cnt[slot] = total;
       W.mex[slot] = m;
+      W.cmax[slot] = top_s[q];
+      W.cthr[slot] = thr;
     }
   }
 }
@@ -481,12 +490,8 @@ struct SelShared {
 
 // Block-wide max and min of one u64 per thread (min over values != ~0).
 __device__ __forceinline__ void block_minmax_u64(uint64_t& mx, uint64_t& mn, SelShared& S) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t a = shfl_xor_u64(mx, o), c = shfl_xor_u64(mn, o);
-    mx = a > mx ? a : mx;
-    mn = c < mn ? c : mn;
-  }
+  mx = wave_max_u64_dpp(mx);
+  mn = wave_min_u64_dpp(mn);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) { S.red64[0][wave] = mx; S.red64[1][wave] = mn; }
@@ -503,12 +508,7 @@ __device__ __forceinline__ void block_minmax_u64(uint64_t& mx, uint64_t& mn, Sel
 // total in *tot.
 __device__ __forceinline__ int block_scan(int v, int* tot, SelShared& S) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, WAVE);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_incl_scan_dpp(v);
   __syncthreads();
   if (lane == 63) S.scan[wave] = (uint32_t)incl;
   __syncthreads();
@@ -805,6 +805,50 @@ __device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n
   emit_sorted(src, th, n, A.k, out, sout, S);
 }
 
+// Emission for candidates stored in ascending index order: a block scan over
+// the selection flags of contiguous slices keeps that order, so no sorting is
+// needed.  Items equal to the threshold key are taken in array (= index)
+// order until `ties` of them are in.
+__device__ void emit_in_order(const uint64_t* key, const int32_t* jj, int total, const Thr& th, int ties, int k,
+                              int32_t* out, double* sout, SelShared& S) {
+  const int per = (total + SEL_THREADS - 1) / SEL_THREADS;
+  const int i0 = threadIdx.x * per, i1 = min(total, i0 + per);
+  int nt = 0;
+  for (int i = i0; i < i1; ++i) nt += (th.low == 0 && key[i] == th.T);
+  int tt;
+  int tie_before = block_scan(nt, &tt, S);
+  int nsel = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t kv = key[i];
+    bool f;
+    if (th.low > 0) f = kv != 0 && (kv >> th.low) >= (th.T >> th.low);
+    else if (kv == th.T) { f = tie_before < ties; ++tie_before; }
+    else f = kv > th.T;
+    nsel += f;
+  }
+  int tot;
+  int pos = block_scan(nsel, &tot, S);
+  tie_before -= nt;   // rewind for the write pass
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t kv = key[i];
+    bool f;
+    if (th.low > 0) f = kv != 0 && (kv >> th.low) >= (th.T >> th.low);
+    else if (kv == th.T) { f = tie_before < ties; ++tie_before; }
+    else f = kv > th.T;
+    if (f) {
+      if (pos < k) {
+        out[pos] = jj[i];
+        if (sout) sout[pos] = key_score(kv);
+      }
+      ++pos;
+    }
+  }
+  for (int i = tot + threadIdx.x; i < k; i += SEL_THREADS) {
+    out[i] = -1;
+    if (sout) sout[i] = 0.0;
+  }
+}
+
 template <int DT, int HP>
 __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, IdxWs W, int NCH, int CH) {
   extern __shared__ __align__(16) char smem[];
@@ -819,6 +863,21 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
   const float* ql = (const float*)A.qi + (int64_t)blockIdx.x * A.H * A.d;   // F32 query row (global)
 
   const int r = blockIdx.x;
+  // everything that does not depend on n_elig is requested at once: the row
+  // length, head weights and the per-chunk summaries
+  constexpr int CPTH = MAXCH / SEL_THREADS;          // chunks per thread
+  int cv[CPTH];
+  uint64_t mv[CPTH], xv[CPTH], tv[CPTH];
+  const bool cand_ok = NCH <= MAXCH;
+#pragma unroll
+  for (int i = 0; i < CPTH; ++i) {
+    const int c = i * SEL_THREADS + threadIdx.x;
+    const int64_t cc = (int64_t)r * NCH + ((cand_ok && c < NCH) ? c : 0);
+    cv[i] = W.cnt[cc];
+    mv[i] = W.mex[cc];
+    xv[i] = W.cmax[cc];
+    tv[i] = W.cthr[cc];
+  }
   const int n = A.n_elig[r];
   const int kk = n < A.k ? n : A.k;
   int32_t* out = A.idx_out + (int64_t)r * A.k;
@@ -835,24 +894,17 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
   }
   bool done = false;
   const int nch = (n + CH - 1) / CH;
-  if (n > NDIRECT && nch <= MAXCH) {
+  if (n > NDIRECT && nch <= MAXCH && cand_ok) {
     // ---------------- candidate path ----------------
-    constexpr int CPTH = MAXCH / SEL_THREADS;        // chunks per thread
-    int cv[CPTH];
-    uint64_t mv[CPTH];
-#pragma unroll
-    for (int i = 0; i < CPTH; ++i) {                 // independent loads, all in flight
-      const int c = i * SEL_THREADS + threadIdx.x;
-      const int cc = c < nch ? c : 0;
-      cv[i] = W.cnt[(int64_t)r * NCH + cc];
-      mv[i] = W.mex[(int64_t)r * NCH + cc];
-    }
+    // chunk offsets, and the key range [gmin, gmax] of all candidates
     int bad = 0, carry = 0;
+    uint64_t gmax = 0, gmin = ~0ull;
 #pragma unroll
     for (int i = 0; i < CPTH; ++i) {
       const int c = i * SEL_THREADS + threadIdx.x;
       int v = c < nch ? cv[i] : 0;
       if (v < 0) { bad = 1; v = 0; }
+      if (v > 0) { gmax = xv[i] > gmax ? xv[i] : gmax; gmin = tv[i] < gmin ? tv[i] : gmin; }
       int tot;
       const int ex = block_scan(v, &tot, S);
       if (c < nch) S.off[c] = carry + ex;
@@ -860,45 +912,103 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
     }
     const int total = carry;
     if (threadIdx.x == 0) S.off[nch] = total;
+    block_minmax_u64(gmax, gmin, S);
     bad = __syncthreads_or(bad);
-    if (!bad && total <= CMAX && total >= kk) {
-      // copy the candidates into LDS: batches of LB per thread, the next
-      // batch's loads issued before the current batch is stored
+    if (!bad && total <= CMAX && total >= kk && gmax >= gmin) {
+      // first radix digit: the 11 bits below the common prefix of the range
+      const int hb = gmax == gmin ? -1 : 63 - __clzll(gmax ^ gmin);
+      int shift = hb + 1 > 11 ? hb + 1 - 11 : 0;
+      const int nb = hb + 1 - shift;
+      uint64_t mask = (hb + 1 >= 64) ? 0 : ~((1ull << (hb + 1)) - 1ull);
+      uint64_t prefix = gmax & mask;
+      for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
+      __syncthreads();
+      // copy the candidates into LDS (one batch of loads in flight) and
+      // histogram the first digit on the way
       auto addr = [&](int i) -> int64_t {
         int lo = 0, hi = nch;                    // chunk c with off[c] <= i < off[c+1]
         while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (S.off[mid] <= i) lo = mid; else hi = mid; }
         return ((int64_t)r * NCH + lo) * CAP + (i - S.off[lo]);
       };
-      uint64_t bk[2][LB];
-      int32_t bj[2][LB];
-      const int nb = (total + SEL_THREADS * LB - 1) / (SEL_THREADS * LB);
+      uint64_t bk[LB];
+      int32_t bj[LB];
 #pragma unroll
       for (int u = 0; u < LB; ++u) {
         const int i = u * SEL_THREADS + threadIdx.x;
         const int64_t a = i < total ? addr(i) : 0;
-        bk[0][u] = W.ckey[a];
-        bj[0][u] = W.cidx[a];
+        bk[u] = W.ckey[a];
+        bj[u] = W.cidx[a];
       }
-      for (int bt = 0; bt < nb; ++bt) {
-        const int cur = bt & 1;
-        if (bt + 1 < nb) {
 #pragma unroll
-          for (int u = 0; u < LB; ++u) {
-            const int i = ((bt + 1) * LB + u) * SEL_THREADS + threadIdx.x;
-            const int64_t a = i < total ? addr(i) : 0;
-            bk[cur ^ 1][u] = W.ckey[a];
-            bj[cur ^ 1][u] = W.cidx[a];
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < LB; ++u) {
-          const int i = (bt * LB + u) * SEL_THREADS + threadIdx.x;
-          if (i < total) { ckey_l[i] = bk[cur][u]; cidx_l[i] = bj[cur][u]; }
+      for (int u = 0; u < LB; ++u) {
+        const int i = u * SEL_THREADS + threadIdx.x;
+        if (i < total) {
+          ckey_l[i] = bk[u];
+          cidx_l[i] = bj[u];
+          if (nb > 0) atomicAdd(&S.hist[(bk[u] >> shift) & ((1ull << nb) - 1ull)], 1u);
         }
       }
       __syncthreads();
       LdsSrc src{ckey_l, cidx_l, total};
-      const Thr th = find_threshold(src, kk, S);
+      Thr th;
+      th.Tj = 0x7FFFFFFF;
+      int rem = kk, ties = 0;
+      bool have = false;
+      if (nb == 0) {
+        // every candidate has the same key
+        th.T = gmax; th.low = 0; ties = rem; have = true;
+      } else {
+        // digit holding the rem-th largest (bins counted from the top)
+        constexpr int BPT = 2048 / SEL_THREADS;
+        const int nbins = 1 << nb;
+        const int top = nbins - 1 - BPT * (int)threadIdx.x;
+        int cnt[BPT], mine = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) { cnt[i] = (top - i >= 0) ? (int)S.hist[top - i] : 0; mine += cnt[i]; }
+        int tot;
+        int above = block_scan(mine, &tot, S);
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+          if (top - i >= 0 && above < rem && above + cnt[i] >= rem) { S.bcast[0] = top - i; S.bcast[1] = above; S.bcast[2] = cnt[i]; }
+          above += cnt[i];
+        }
+        __syncthreads();
+        int dsel = S.bcast[0], indig = S.bcast[2];
+        rem -= S.bcast[1];
+        prefix |= (uint64_t)dsel << shift;
+        mask |= (uint64_t)((1u << nb) - 1u) << shift;
+        __syncthreads();
+        // narrow down until the threshold is exact
+        while (!have) {
+          if (indig == rem) {                     // the whole bin is in
+            th.T = prefix; th.low = shift; ties = rem; have = true;
+            if (shift == 0) th.low = 0;
+          } else if (shift == 0) {                // a full key with more ties than needed
+            th.T = prefix; th.low = 0; ties = rem; have = true;
+          } else if (indig <= 64) {               // few items: rank them exactly
+            resolve_bin(src, prefix, mask, rem, S);
+            th.T = S.bcast64[0]; th.low = 0;
+            // items equal to T before it (in index order) are the ties taken
+            const int tj = S.bcast[3];
+            int nt = 0;
+            src.for_each([&](uint64_t key, int j) { nt += (key == th.T && j <= tj); });
+            int tt;
+            block_scan(nt, &tt, S);
+            ties = tt;
+            have = true;
+          } else {
+            const int nb2 = shift >= 11 ? 11 : shift;
+            shift -= nb2;
+            radix_digit(src, prefix, mask, shift, nb2, rem, S);
+            dsel = S.bcast[0]; indig = S.bcast[2];
+            const int above2 = S.bcast[1];
+            __syncthreads();
+            rem -= above2;
+            prefix |= (uint64_t)dsel << shift;
+            mask |= (uint64_t)((1u << nb2) - 1u) << shift;
+          }
+        }
+      }
       // certification: no excluded entry may reach the threshold
       int unsafe = 0;
 #pragma unroll
@@ -912,7 +1022,7 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
       }
       unsafe = __syncthreads_or(unsafe);
       if (!unsafe) {
-        emit_sorted(src, th, n, A.k, out, sout, S);
+        emit_in_order(ckey_l, cidx_l, total, th, ties, A.k, out, sout, S);
         done = true;
       }
     }

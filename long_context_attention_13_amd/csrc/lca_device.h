@@ -134,6 +134,84 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// ------------------------------------------------ DPP wavefront primitives
+// Row (16-lane) steps use DPP permutes, which run at VALU latency; the four
+// row results are then combined through v_readlane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_QP_1032 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int DPP_QP_2301 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// max over the wavefront, returned to every lane (uniform)
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  auto step = [](uint64_t x, uint32_t lo, uint32_t hi) {
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    return y > x ? y : x;
+  };
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_QP_1032>(lo, lo), dpp_u32<DPP_QP_1032>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_QP_2301>(lo, lo), dpp_u32<DPP_QP_2301>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_ROW_HALF_MIRROR>(lo, lo), dpp_u32<DPP_ROW_HALF_MIRROR>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_ROW_MIRROR>(lo, lo), dpp_u32<DPP_ROW_MIRROR>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t y = ((uint64_t)readlane_u32(hi, 16 * r + 15) << 32) | readlane_u32(lo, 16 * r + 15);
+    m = y > m ? y : m;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t v) {
+  auto step = [](uint64_t x, uint32_t lo, uint32_t hi) {
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    return y < x ? y : x;
+  };
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_QP_1032>(lo, lo), dpp_u32<DPP_QP_1032>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_QP_2301>(lo, lo), dpp_u32<DPP_QP_2301>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_ROW_HALF_MIRROR>(lo, lo), dpp_u32<DPP_ROW_HALF_MIRROR>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  v = step(v, dpp_u32<DPP_ROW_MIRROR>(lo, lo), dpp_u32<DPP_ROW_MIRROR>(hi, hi));
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  uint64_t m = ~0ull;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t y = ((uint64_t)readlane_u32(hi, 16 * r + 15) << 32) | readlane_u32(lo, 16 * r + 15);
+    m = y < m ? y : m;
+  }
+  return m;
+}
+
+// inclusive prefix sum over the wavefront (lane order)
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = (uint32_t)v;
+  x += dpp_u32<DPP_ROW_SHR1>(0u, x);
+  x += dpp_u32<DPP_ROW_SHR2>(0u, x);
+  x += dpp_u32<DPP_ROW_SHR4>(0u, x);
+  x += dpp_u32<DPP_ROW_SHR8>(0u, x);
+  const uint32_t r0 = readlane_u32(x, 15), r1 = readlane_u32(x, 31), r2 = readlane_u32(x, 47);
+  const int row = lane >> 4;
+  x += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+  return (int)x;
+}
+
 // Number of set lanes strictly below this lane in a 64-bit ballot.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   const int lane = threadIdx.x & 63;
