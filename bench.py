@@ -37,6 +37,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "layer_pair_1m_decode_index_traffic.json")
+
+
+def recorded_traffic():
+    """HBM bytes per indexer launch from the committed FETCH_SIZE/WRITE_SIZE
+    counter runs, or None when the kernel sources differ from the ones the
+    counters were taken on."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in rec["kernel_sources"]:
+        h.update(open(os.path.join(ROOT, "long_context_attention_13_amd", f), "rb").read())
+    return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def parse():
@@ -47,6 +63,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB 3 times (a known-size kernel "
+                         "that scales the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -233,6 +252,15 @@ def main():
               f"note, not a measured path.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"calibration copy: {n} bytes read and {n} bytes written per launch", flush=True)
+        del src, dst
     wl = Workload(args.copies)
     stream = torch.cuda.current_stream()
     C = args.copies
@@ -283,7 +311,7 @@ def main():
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"kernel": "lightning_index_topk (index_chunk_kernel + index_select_kernel)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "avg_launch_us": round(idx_ms * 1e3, 2), "algorithmic_bytes": int(idx_bytes)},
     }
     if not args.no_cpu:
