@@ -37,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MXFP4_PEAK_TFLOPS = 10100.0     # dense fp4 matrix peak
+BF16_PEAK_TFLOPS = 2500.0       # dense bf16 matrix peak
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "layer_pair_1m_decode_index_traffic.json")
 
 
@@ -63,6 +65,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 3 times (a known-size kernel "
                          "that scales the HBM byte counters of a profiler run)")
@@ -212,6 +216,155 @@ class Workload:
         return self.index_bytes() + csa + hca + comp
 
 
+class PrefillWorkload:
+    """Chunked prefill: 8192 new bf16 tokens after a 262144-token cached context
+    (one sequence).  Cached entries (65536 bf16 CSA entries, 65536 MXFP4
+    indexer keys, 2048 bf16 HCA entries) and the 127 raw tokens before the
+    chunk are drawn N(0,1) on the GPU; the chunk's raw tokens, gates, indexer
+    raw keys, indexer queries (MXFP4), head weights U(0,1) and queries are
+    drawn the same way.  One pass = compress the chunk's 2048 CSA blocks (entries
+    and indexer keys) and 64 HCA blocks, causal indexer top-1024 for all 8192
+    queries, sparse MQA over the selections + window 128 + sink, and the HCA
+    dense branch."""
+
+    def __init__(self, seed: int = 1005, ctx: int = 262144, T: int = 8192):
+        import torch
+        import long_context_attention_13_amd as lca
+        self.lca = lca
+        dev = torch.device("cuda:0")
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        H_I, d_I, D, Hq, W, k = 8, 128, 128, 64, 128, 1024
+        self.T, self.ctx, self.k, self.H_I, self.d_I, self.Hq, self.D = T, ctx, k, H_I, d_I, Hq, D
+        N, N2 = (ctx + T) // 4, (ctx + T) // 128
+        N0, N20 = ctx // 4, ctx // 128
+        self.N, self.N2 = N, N2
+        rn = lambda *sh: torch.randn(*sh, generator=g, device=dev, dtype=torch.float32)
+        z32 = lambda n: torch.zeros(n, dtype=torch.int32, device=dev)
+        z64 = lambda n: torch.zeros(n, dtype=torch.int64, device=dev)
+        full32 = lambda n, v: torch.full((n,), v, dtype=torch.int32, device=dev)
+        one0 = torch.zeros(1, dtype=torch.float32, device=dev)
+        # caches (rows below the context length drawn directly)
+        self.ent = torch.empty(1, N, D, dtype=torch.bfloat16, device=dev)
+        self.ent[:, :N0] = rn(1, N0, D).to(torch.bfloat16)
+        self.hca = torch.empty(1, N2, D, dtype=torch.bfloat16, device=dev)
+        self.hca[:, :N20] = rn(1, N20, D).to(torch.bfloat16)
+        self.key = torch.empty(1, N, d_I // 2, dtype=torch.uint8, device=dev)
+        self.key_sc = torch.empty(1, N, d_I // 32, dtype=torch.uint8, device=dev)
+        kraw = rn(1, N0, d_I)
+        lca.csa_compress(kraw, torch.zeros(1, N0, device=dev), one0, 1, z32(1), full32(1, N0), z64(1), N0,
+                         self.key, lca.MXFP4, self.key_sc)
+        del kraw
+        # the chunk
+        self.win = torch.cat([rn(1, W - 1, D), rn(1, T, D)], dim=1).to(torch.bfloat16)   # raw tokens
+        self.gate, self.gate_i, self.gate2 = rn(1, T + W - 1), rn(1, T + W - 1), rn(1, T + W - 1)
+        self.bias = (rn(4) * 0.1).contiguous()
+        self.bias_i = (rn(4) * 0.1).contiguous()
+        self.bias2 = (rn(128) * 0.1).contiguous()
+        self.xi = rn(1, T + W - 1, d_I).to(torch.bfloat16)
+        qi32 = rn(T * H_I, d_I)
+        self.qi = torch.empty(1, T, H_I, d_I // 2, dtype=torch.uint8, device=dev)
+        self.qi_sc = torch.empty(1, T, H_I, d_I // 32, dtype=torch.uint8, device=dev)
+        lca.csa_compress(qi32[None], torch.zeros(1, T * H_I, device=dev), one0, 1, z32(1), full32(1, T * H_I),
+                         z64(1), T * H_I, self.qi.view(1, T * H_I, d_I // 2), lca.MXFP4,
+                         self.qi_sc.view(1, T * H_I, d_I // 32))
+        del qi32
+        self.w = torch.rand(1, T, H_I, generator=g, device=dev, dtype=torch.float32)
+        self.q = rn(1, T, Hq, D).to(torch.bfloat16)
+        self.sink_csa, self.sink_hca = rn(Hq), rn(Hq)
+        self.tau = 1.0 / math.sqrt(128.0)
+        p = ctx + torch.arange(T, device=dev, dtype=torch.int32)
+        self.n_csa = ((p + 1) // 4).view(1, T).to(torch.int32).contiguous()
+        self.n_hca = ((p + 1) // 128).view(1, T).to(torch.int32).contiguous()
+        self.wb = torch.arange(T, device=dev, dtype=torch.int32).view(1, T).contiguous()
+        self.wl = torch.full((1, T), W, dtype=torch.int32, device=dev)
+        self.tok0 = full32(1, W - 1)
+        self.nb4, self.nb128 = full32(1, T // 4), full32(1, T // 128)
+        self.row4 = torch.full((1,), N0, dtype=torch.int64, device=dev)
+        self.row128 = torch.full((1,), N20, dtype=torch.int64, device=dev)
+        self.idx = torch.empty(1, T, k, dtype=torch.int32, device=dev)
+        self.out_csa = torch.empty(1, T, Hq, D, dtype=torch.bfloat16, device=dev)
+        self.out_hca = torch.empty(1, T, Hq, D, dtype=torch.bfloat16, device=dev)
+        self.ws_idx = torch.empty(lca.index_topk_ws(1, T, H_I, d_I, N, k), dtype=torch.uint8, device=dev)
+        self.ws_csa = torch.empty(max(lca.attend_ws(1, T, Hq, D, k, T + W - 1), 16), dtype=torch.uint8, device=dev)
+        self.ws_hca = torch.empty(max(lca.attend_ws(1, T, Hq, D, N2, T + W - 1), 16), dtype=torch.uint8,
+                                  device=dev)
+        torch.cuda.synchronize()
+
+    def compress(self):
+        lca = self.lca
+        lca.csa_compress(self.win, self.gate, self.bias, 4, self.tok0, self.nb4, self.row4, self.T // 4,
+                         self.ent, lca.BF16)
+        lca.csa_compress(self.xi, self.gate_i, self.bias_i, 4, self.tok0, self.nb4, self.row4, self.T // 4,
+                         self.key, lca.MXFP4, self.key_sc)
+        lca.hca_compress(self.win, self.gate2, self.bias2, 128, self.tok0, self.nb128, self.row128, self.T // 128,
+                         self.hca, lca.BF16)
+
+    def index(self):
+        self.lca.lightning_index_topk(self.qi, self.qi_sc, self.w, self.key, self.key_sc, self.n_csa, self.k,
+                                      self.idx, self.ws_idx)
+
+    def attend(self):
+        lca = self.lca
+        lca.sparse_mqa_attend(self.q, self.ent, None, self.idx, self.win, self.wb, self.wl, self.sink_csa,
+                              self.tau, self.out_csa, ws=self.ws_csa)
+        lca.hca_attend(self.q, self.hca, None, self.n_hca, self.win, self.wb, self.wl, self.sink_hca, self.tau,
+                       self.out_hca, ws=self.ws_hca)
+
+    def index_flops(self) -> float:
+        """MXFP4 multiply-adds of the indexer (2 flops each): every eligible
+        (query, entry) pair, H_I heads of d_I."""
+        n = ((self.ctx + np.arange(self.T) + 1) // 4).sum()
+        return float(n) * self.H_I * self.d_I * 2
+
+    def attend_flops(self) -> float:
+        """bf16 flops of both attentions: QK and PV over each query's items."""
+        p = self.ctx + np.arange(self.T)
+        items_csa = np.minimum(self.k, (p + 1) // 4) + 128
+        items_hca = (p + 1) // 128 + 128
+        return float((items_csa + items_hca).sum()) * self.Hq * self.D * 4
+
+
+def run_prefill(steps: int, warmup: int):
+    import torch
+    pw = PrefillWorkload()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        pw.compress(); pw.index(); pw.attend()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record(stream)
+        pw.compress()
+        ev[s][1].record(stream)
+        pw.index()
+        ev[s][2].record(stream)
+        pw.attend()
+        ev[s][3].record(stream)
+    torch.cuda.synchronize()
+    tot = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    t_idx = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    t_att = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    t_cmp = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    fl_i, fl_a = pw.index_flops(), pw.attend_flops()
+    res = {"workload": "prefill_chunk: 8192 new bf16 tokens after a 262144-token context, CSA top-1024 "
+                       "(MXFP4 indexer 8x128) + HCA dense, window 128, 64 query heads",
+           "prefill_tokens_per_s": round(pw.T / (tot * 1e-3), 1), "ms_per_chunk": round(tot, 4),
+           "ms_compress": round(t_cmp, 4), "ms_index": round(t_idx, 4), "ms_attend": round(t_att, 4),
+           "indexer_mfma": {"bound": "mfma", "achieved": round(fl_i / (t_idx * 1e-3) / 1e12, 2),
+                            "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(fl_i / (t_idx * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4),
+                            "algorithmic_tflop": round(fl_i / 1e12, 4)},
+           "attend_mfma": {"bound": "mfma", "achieved": round(fl_a / (t_att * 1e-3) / 1e12, 2),
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(fl_a / (t_att * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                           "algorithmic_tflop": round(fl_a / 1e12, 4)},
+           "steps": steps}
+    del pw
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, steps):
     """The float64 oracle on one full layer-pair step, on the host cores."""
     import torch
@@ -316,6 +469,10 @@ def main():
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
+    if not args.no_prefill:
+        del wl
+        torch.cuda.empty_cache()
+        res["prefill"] = run_prefill(args.prefill_steps, 2)
     print(json.dumps(res))
 
 
