@@ -26,12 +26,15 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
-SOURCES = ["compress.hip", "index.hip", "attend.hip", "abi.cpp"]
+SOURCES = ["compress.hip", "index.hip", "index_prefill.hip", "attend.hip", "abi.cpp"]
+# per-source flags: keep MFMA results in ordinary VGPRs (the score kernel's
+# epilogue reads every result; accumulation-register copies would double it)
+EXTRA = {"index_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l
                      and "not a recognized feature" not in l)

@@ -34,23 +34,9 @@
 //                 re-scoring every entry in streamed passes.  Rows with few
 //                 entries are always done that way.  Output in ascending index
 //                 order through an LDS bitmap.
-#include "lca_device.h"
+#include "index_common.h"
 
 namespace lca {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-constexpr int CAP = 128;           // candidate slots per chunk
-constexpr int NDIRECT = 8192;      // rows with n_elig <= NDIRECT skip the chunk kernel
-constexpr int SEL_THREADS = 1024;  // select kernel workgroup (16 wavefronts)
-constexpr int SEL_WAVES = SEL_THREADS / WAVE;
-constexpr int CMAX = 8192;         // candidates per row held in LDS by the select kernel
-constexpr int LB = CMAX / 1024;    // candidate loads per thread and batch (one batch at 1024 threads)
-constexpr int MAXCH = 1024;        // chunks per row the candidate path handles
-constexpr int KROW = 20;           // LDS floats per key in the transpose buffer (16 + pad)
-constexpr int BITMAP_BITS = 1 << 18;
 
 struct IdxWs {
   int32_t* cnt;   // [R][NCH] candidates emitted by each chunk (-1: overflow)
@@ -60,8 +46,6 @@ struct IdxWs {
   uint64_t* ckey; // [R][NCH][CAP] candidates, ascending index within a chunk
   int32_t* cidx;  // [R][NCH][CAP]
 };
-
-static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static IdxWs carve(void* ws, int64_t R, int64_t NCH) {
   IdxWs w;
@@ -78,241 +62,6 @@ static IdxWs carve(void* ws, int64_t R, int64_t NCH) {
 static size_t carve_bytes(int64_t R, int64_t NCH) {
   return align256(sizeof(int32_t) * R * NCH) + 3 * align256(sizeof(uint64_t) * R * NCH) +
          align256(sizeof(uint64_t) * R * NCH * CAP) + align256(sizeof(int32_t) * R * NCH * CAP);
-}
-
-// ------------------------------------------------------------------------
-// Query state of one wavefront (up to two query rows of one sequence).
-// ------------------------------------------------------------------------
-struct Rows {
-  int b;            // sequence
-  int r[2];         // query rows (r[1] < 0: absent)
-  int n[2];         // n_elig per row (0 for absent rows)
-};
-
-struct MxQuery {
-  int a[4];         // this lane's 16 bytes of the A operand
-  int sa;           // this lane's E8M0 byte
-  int dq, qmin, qmax;
-};
-
-template <int HP>
-__device__ __forceinline__ void mx_load_query(const IndexArgs& A, const Rows& rw, MxQuery& Q) {
-  const int lane = threadIdx.x & 63;
-  const int row = lane & 15, kb = lane >> 4;
-  const int q = row / HP, h = row % HP;
-  const int rq = q == 0 ? rw.r[0] : rw.r[1];     // (no dynamic indexing: keeps rw in registers)
-  const bool valid = (q < 2) && rq >= 0 && h < A.H && kb * 32 < A.d;
-  Q.a[0] = Q.a[1] = Q.a[2] = Q.a[3] = 0;
-  Q.sa = 127;
-  int smin = 1000, smax = -1000;
-  if (valid) {
-    const int64_t qrow = (int64_t)rq * A.H + h;
-    const int4 v = *(const int4*)((const uint8_t*)A.qi + qrow * (A.d / 2) + kb * 16);
-    Q.a[0] = v.x; Q.a[1] = v.y; Q.a[2] = v.z; Q.a[3] = v.w;
-    Q.sa = A.qi_scale[qrow * (A.d / 32) + kb];
-    smin = smax = Q.sa;
-  }
-  // per (query, head): spread of the block exponents over the 4 lanes of a row
-  int rmin = smin, rmax = smax;
-  rmin = min(rmin, __shfl_xor(rmin, 16, WAVE)); rmax = max(rmax, __shfl_xor(rmax, 16, WAVE));
-  rmin = min(rmin, __shfl_xor(rmin, 32, WAVE)); rmax = max(rmax, __shfl_xor(rmax, 32, WAVE));
-  int dq = valid ? rmax - rmin : 0;
-  int gmin = smin, gmax = smax;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    dq = max(dq, __shfl_xor(dq, o, WAVE));
-    gmin = min(gmin, __shfl_xor(gmin, o, WAVE));
-    gmax = max(gmax, __shfl_xor(gmax, o, WAVE));
-  }
-  Q.dq = dq; Q.qmin = gmin; Q.qmax = gmax;
-}
-
-struct MxTiles {
-  int4 code[4];
-  int sc[4];
-  uint32_t valid;   // bit t: this lane's tile-t operand is a real key block
-  uint32_t kscale;  // the scale bytes of key j0 + lane (for the exactness envelope)
-};
-
-// Load the B operands of 4 MFMA tiles = 64 keys [j0, j0+64).  The loads are
-// unconditional (addresses clamped into the sequence's valid rows) so that
-// they all stay in flight; lanes outside the valid range are zeroed where the
-// operands are consumed.
-__device__ __forceinline__ void mx_load_round(const IndexArgs& A, int b, int j0, int jlim, MxTiles& T) {
-  const int lane = threadIdx.x & 63;
-  const int kb = lane >> 4;
-  const bool kbok = kb * 32 < A.d;
-  const int kbc = kbok ? kb : 0;
-  T.valid = 0;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int j = j0 + t * 16 + (lane & 15);
-    const int jc = j < jlim ? j : jlim - 1;
-    const int64_t row = (int64_t)b * A.N_cap + jc;
-    const v4i v = __builtin_nontemporal_load((const v4i*)((const uint8_t*)A.ki + row * (A.d / 2) + kbc * 16));
-    T.code[t] = make_int4(v[0], v[1], v[2], v[3]);
-    T.sc[t] = A.ki_scale[row * (A.d / 32) + kbc];
-    T.valid |= (uint32_t)(j < jlim && kbok) << t;
-  }
-  {
-    const int j = j0 + lane;
-    const int64_t row = (int64_t)b * A.N_cap + (j < jlim ? j : jlim - 1);
-    const uint8_t* ks = A.ki_scale + row * (A.d / 32);
-    T.kscale = A.d == 128 ? *(const uint32_t*)ks : (uint32_t)*(const uint16_t*)ks;
-  }
-}
-
-__device__ __forceinline__ double mx_value(const uint8_t* codes, const uint8_t* scales, int i) {
-  const uint32_t byte = codes[i >> 1];
-  const uint32_t c = (i & 1) ? (byte >> 4) : (byte & 15u);
-  return ldexp((double)e2m1_to_f32(c), (int)scales[i >> 5] - 127);
-}
-
-// Exact float64 dot product of query head (row qr, head h) and key row krow,
-// left to right over the elements.
-__device__ __forceinline__ double mx_dot_exact(const IndexArgs& A, int64_t qrow, int64_t krow) {
-  const uint8_t* qc = (const uint8_t*)A.qi + qrow * (A.d / 2);
-  const uint8_t* qs = A.qi_scale + qrow * (A.d / 32);
-  const uint8_t* kc = (const uint8_t*)A.ki + krow * (A.d / 2);
-  const uint8_t* ks = A.ki_scale + krow * (A.d / 32);
-  double dot = 0.0;
-  for (int i = 0; i < A.d; ++i) dot = fma(mx_value(qc, qs, i), mx_value(kc, ks, i), dot);
-  return dot;
-}
-
-// One step of the float64 head combine s = sum_h w_h * max(0, dot_h), taken in
-// head order: multiply, then add (no contraction).
-__device__ __forceinline__ double combine_step(double s, double dot, float w) {
-#pragma clang fp contract(off)
-  const double r = dot > 0.0 ? dot : 0.0;
-  const double t = (double)w * r;
-  return s + t;
-}
-
-// Score one round of 64 keys for the wave's NQ rows.  Lane L ends with the
-// keys of entry j0+L (0 when not eligible).
-// wbuf: this wave's LDS transpose buffer (64*KROW floats); wl: LDS weights
-// [2][16].
-__device__ __forceinline__ bool mx_exact(const MxQuery& Q, int kmin, int kmax) {
-  return (Q.dq + kmax - kmin <= 9) && (Q.qmin + kmin >= 130) && (Q.qmax + kmax <= 368);
-}
-
-template <int HP, int NQ>
-__device__ __forceinline__ void mx_score_round(const IndexArgs& A, const Rows& rw, const MxQuery& Q,
-                                               const MxTiles& T, int j0, float* wbuf, const float* wl,
-                                               uint64_t* key, bool& inexact) {
-  const int lane = threadIdx.x & 63;
-  v8i av = {Q.a[0], Q.a[1], Q.a[2], Q.a[3], 0, 0, 0, 0};
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const bool ok = (T.valid >> t) & 1u;
-    v8i bv = {ok ? T.code[t].x : 0, ok ? T.code[t].y : 0, ok ? T.code[t].z : 0, ok ? T.code[t].w : 0, 0, 0, 0, 0};
-    const int scb = ok ? T.sc[t] : 127;
-    v4f c = {0.f, 0.f, 0.f, 0.f};
-    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, Q.sa, 0, scb);
-    float* dst = wbuf + (t * 16 + (lane & 15)) * KROW + 4 * (lane >> 4);
-    *(float4*)dst = make_float4(c[0], c[1], c[2], c[3]);
-  }
-  // exponent envelope of this lane's key j0+lane from its own scale bytes
-  const uint32_t sw = T.kscale;
-  int kmin = (int)(sw & 0xFFu), kmax = kmin;
-#pragma unroll
-  for (int i = 1; i < 4; ++i) {
-    if (i * 32 < A.d) {
-      const int v = (int)((sw >> (8 * i)) & 0xFFu);
-      kmin = min(kmin, v);
-      kmax = max(kmax, v);
-    }
-  }
-  const bool exact = mx_exact(Q, kmin, kmax);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int j = j0 + lane;
-  const float* mine = wbuf + lane * KROW;
-  inexact = false;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    double sc = 0.0;
-#pragma unroll
-    for (int h = 0; h < HP; ++h)
-      if (h < A.H) sc = combine_step(sc, (double)mine[q * HP + h], wl[q * 16 + h]);
-    const bool elig = rw.r[q] >= 0 && j < rw.n[q];
-    key[q] = elig ? score_key(sc) : 0ull;
-    inexact |= elig && !exact;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Exact float64 score of entry j for row q of the wave (keys outside the
-// exact-MFMA envelope).
-__device__ __forceinline__ uint64_t mx_score_exact(const IndexArgs& A, int qrow, int b, int j, const float* wlq) {
-  double sc = 0.0;
-  for (int h = 0; h < A.H; ++h)
-    sc = combine_step(sc, mx_dot_exact(A, (int64_t)qrow * A.H + h, (int64_t)b * A.N_cap + j), wlq[h]);
-  return score_key(sc);
-}
-
-// F32 indexer: lane L scores entry j0+L for row 0 (F32 groups hold one row).
-// qrow: the query row [H][d] (LDS or global; every lane reads the same
-// addresses).
-__device__ __forceinline__ void f32_score_round(const IndexArgs& A, const Rows& rw, int j0, const float* qrow,
-                                                const float* wl, uint64_t& key0) {
-  const int lane = threadIdx.x & 63;
-  const int j = j0 + lane;
-  key0 = 0;
-  if (j >= rw.n[0]) return;
-  const float* kr = (const float*)A.ki + ((int64_t)rw.b * A.N_cap + j) * A.d;
-  double s = 0.0;
-  for (int h = 0; h < A.H; ++h) {
-    double dot = 0.0;
-    for (int i = 0; i < A.d; ++i) dot = fma((double)qrow[h * A.d + i], (double)kr[i], dot);
-    s = combine_step(s, dot, wl[h]);
-  }
-  key0 = score_key(s);
-}
-
-// ------------------------------------------------------------------------
-// Wavefront bitonic sort of one u64 per lane, descending across lanes.
-// ------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t o = shfl_xor_u64(v, j);
-      const bool up = ((lane & k) == 0);         // this k-block sorts descending
-      const bool lower = ((lane & j) == 0);
-      // descending block: lower lane keeps the max
-      const bool keep_max = (up == lower);
-      v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
-    }
-  }
-  return v;
-}
-
-// ------------------------------------------------------------------------
-// Chunk kernel.  A workgroup of 4 wavefronts owns one chunk of CH = 64*KPL
-// consecutive entries for NQ query rows; each wavefront scores KPL/4 rounds
-// of 64 entries (all its key tiles loaded up front), keeps its keys in
-// registers, and contributes its 64 lane maxima (sorted) to the chunk
-// threshold: the r-th largest of the chunk's 256 lane maxima, found by
-// merging the four sorted lists with bitonic half-cleaners.
-// ------------------------------------------------------------------------
-constexpr int WBUF = 64 * KROW;           // floats per wave: dot-product transpose buffer
-
-// Descending bitonic clean of a bitonic sequence held one value per lane.
-__device__ __forceinline__ uint64_t wave_bitonic_clean_desc(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) {
-    const uint64_t o = shfl_xor_u64(v, j);
-    const bool lower = (lane & j) == 0;
-    v = lower ? (o > v ? o : v) : (o < v ? o : v);
-  }
-  return v;
 }
 
 template <int DT, int KPL, int HP, int NQ>
@@ -469,383 +218,6 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
       W.cmax[slot] = top_s[q];
       W.cthr[slot] = thr;
     }
-  }
-}
-
-// ------------------------------------------------------------------------
-// Select kernel helpers (block of SEL_THREADS threads)
-// ------------------------------------------------------------------------
-struct SelShared {
-  uint32_t hist[2048];
-  uint32_t scan[SEL_WAVES];
-  uint64_t red64[2][SEL_WAVES];
-  int32_t off[MAXCH + 1];
-  uint32_t bitmap[BITMAP_BITS / 32];
-  uint64_t rkey[64];           // items of the threshold bin, resolved exactly
-  int32_t rj[64];
-  int nres;
-  int bcast[8];
-  uint64_t bcast64[4];
-};
-
-// Block-wide max and min of one u64 per thread (min over values != ~0).
-__device__ __forceinline__ void block_minmax_u64(uint64_t& mx, uint64_t& mn, SelShared& S) {
-  mx = wave_max_u64_dpp(mx);
-  mn = wave_min_u64_dpp(mn);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) { S.red64[0][wave] = mx; S.red64[1][wave] = mn; }
-  __syncthreads();
-  mx = 0; mn = ~0ull;
-#pragma unroll
-  for (int i = 0; i < SEL_WAVES; ++i) {
-    mx = S.red64[0][i] > mx ? S.red64[0][i] : mx;
-    mn = S.red64[1][i] < mn ? S.red64[1][i] : mn;
-  }
-}
-
-// Exclusive block scan of one int per thread; returns the exclusive prefix,
-// total in *tot.
-__device__ __forceinline__ int block_scan(int v, int* tot, SelShared& S) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_incl_scan_dpp(v);
-  __syncthreads();
-  if (lane == 63) S.scan[wave] = (uint32_t)incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < SEL_WAVES; ++i) {
-    const int s = (int)S.scan[i];
-    if (i < wave) before += s;
-    all += s;
-  }
-  *tot = all;
-  return before + incl - v;
-}
-
-// One radix digit step: among keys with (key & mask) == prefix, find the digit
-// (nb bits at `shift`) holding the rem-th largest.  `src` is a functor
-// for_each(fn(key, j)).  Returns via S.bcast: [0] digit, [1] count above,
-// [2] count in digit.
-template <class Src>
-__device__ void radix_digit(Src& src, uint64_t prefix, uint64_t mask, int shift, int nb, int rem, SelShared& S) {
-  constexpr int BPT = 2048 / SEL_THREADS;       // bins per thread
-  const int nbins = 1 << nb;
-  for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
-  __syncthreads();
-  src.for_each([&](uint64_t key, int j) {
-    if (key != 0 && (key & mask) == prefix) atomicAdd(&S.hist[(key >> shift) & (uint64_t)(nbins - 1)], 1u);
-  });
-  __syncthreads();
-  // thread t owns bins top-BPT*t .. top-BPT*t-BPT+1 (counted from the top bin)
-  const int top = nbins - 1 - BPT * (int)threadIdx.x;
-  int cnt[BPT], mine = 0;
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) { cnt[i] = (top - i >= 0) ? (int)S.hist[top - i] : 0; mine += cnt[i]; }
-  int tot;
-  int above = block_scan(mine, &tot, S);        // count in bins above this thread's bins
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    if (top - i >= 0 && above < rem && above + cnt[i] >= rem) {
-      S.bcast[0] = top - i; S.bcast[1] = above; S.bcast[2] = cnt[i];
-    }
-    above += cnt[i];
-  }
-  __syncthreads();
-}
-
-// Smallest-j selection among ties (key == T): find the rem-th smallest j.
-template <class Src>
-__device__ int tie_select_j(Src& src, uint64_t T, int rem, SelShared& S) {
-  constexpr int BPT = 2048 / SEL_THREADS;
-  uint32_t prefix = 0, mask = 0;
-  int shift = 31;
-  while (shift > 0) {
-    const int nb = shift >= 11 ? 11 : shift;
-    shift -= nb;
-    const uint32_t nbins = 1u << nb;
-    for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
-    __syncthreads();
-    src.for_each([&](uint64_t key, int j) {
-      if (key == T && ((uint32_t)j & mask) == prefix) atomicAdd(&S.hist[((uint32_t)j >> shift) & (nbins - 1)], 1u);
-    });
-    __syncthreads();
-    const int b0 = BPT * (int)threadIdx.x;
-    int cnt[BPT], mine = 0;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) { cnt[i] = (b0 + i < (int)nbins) ? (int)S.hist[b0 + i] : 0; mine += cnt[i]; }
-    int tot;
-    int below = block_scan(mine, &tot, S);
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      if (b0 + i < (int)nbins && below < rem && below + cnt[i] >= rem) { S.bcast[0] = b0 + i; S.bcast[1] = below; }
-      below += cnt[i];
-    }
-    __syncthreads();
-    const int dsel = S.bcast[0];
-    rem -= S.bcast[1];
-    prefix |= (uint32_t)dsel << shift;
-    mask |= (nbins - 1) << shift;
-    __syncthreads();
-  }
-  return (int)prefix;
-}
-
-// Threshold of a selection: items with key > T, or key == T and j <= Tj when
-// low == 0; with low > 0, items with (key >> low) >= (T >> low).
-struct Thr {
-  uint64_t T;
-  int low;
-  int Tj;          // INT_MAX when all ties are taken
-};
-
-__device__ __forceinline__ bool selected(const Thr& th, uint64_t key, int j) {
-  if (key == 0) return false;
-  if (th.low > 0) return (key >> th.low) >= (th.T >> th.low);
-  return key > th.T || (key == th.T && j <= th.Tj);
-}
-
-// Exact rank resolution inside one radix bin of at most 64 items: the items
-// (key & mask) == prefix are gathered in LDS and the rem-th of them in the
-// order (key desc, j asc) is found by counting, per item, the items before it.
-template <class Src>
-__device__ void resolve_bin(Src& src, uint64_t prefix, uint64_t mask, int rem, SelShared& S) {
-  if (threadIdx.x == 0) S.nres = 0;
-  __syncthreads();
-  src.for_each([&](uint64_t key, int j) {
-    if (key != 0 && (key & mask) == prefix) {
-      const int p = atomicAdd(&S.nres, 1);
-      if (p < 64) { S.rkey[p] = key; S.rj[p] = j; }
-    }
-  });
-  __syncthreads();
-  const int n = S.nres;
-  if (threadIdx.x < 64) {
-    const int i = threadIdx.x;
-    int rank = 0;
-    const uint64_t ki = i < n ? S.rkey[i] : 0;
-    const int ji = i < n ? S.rj[i] : 0;
-    for (int m = 0; m < n; ++m) {
-      const uint64_t km = S.rkey[m];
-      rank += (km > ki) || (km == ki && S.rj[m] < ji);
-    }
-    if (i < n && rank == rem - 1) { S.bcast64[0] = ki; S.bcast[3] = ji; }
-  }
-  __syncthreads();
-}
-
-// Exact selection threshold for the kk largest (by key desc, j asc) items.
-template <class Src>
-__device__ Thr find_threshold(Src& src, int kk, SelShared& S) {
-  Thr th;
-  uint64_t mx = 0, mn = ~0ull;
-  src.for_each([&](uint64_t key, int j) {
-    if (key != 0) { mx = key > mx ? key : mx; mn = key < mn ? key : mn; }
-  });
-  block_minmax_u64(mx, mn, S);
-  th.Tj = 0x7FFFFFFF;
-  if (mx == 0) { th.T = ~0ull; th.low = 0; return th; }   // nothing eligible
-  if (mx == mn) {
-    th.T = mx; th.low = 0;
-  } else {
-    const int hb = 63 - __clzll(mx ^ mn);
-    int shift = hb + 1;
-    uint64_t mask = (shift >= 64) ? 0 : ~((1ull << shift) - 1ull);
-    uint64_t prefix = mx & mask;
-    int rem = kk;
-    bool early = false;
-    while (shift > 0) {
-      const int nb = shift >= 11 ? 11 : shift;
-      shift -= nb;
-      radix_digit(src, prefix, mask, shift, nb, rem, S);
-      const int dsel = S.bcast[0], above = S.bcast[1], indig = S.bcast[2];
-      __syncthreads();
-      rem -= above;
-      prefix |= (uint64_t)dsel << shift;
-      mask |= (uint64_t)((1u << nb) - 1u) << shift;
-      if (indig == rem) { early = shift > 0; break; }
-      if (indig <= 64 && shift > 0) {
-        // few items left in the bin: rank them exactly (ties by index)
-        resolve_bin(src, prefix, mask, rem, S);
-        th.T = S.bcast64[0];
-        th.Tj = S.bcast[3];
-        th.low = 0;
-        __syncthreads();
-        return th;
-      }
-    }
-    th.T = prefix;
-    th.low = early ? shift : 0;
-    if (!early) {
-      // count of items equal to T
-      int cnt = 0;
-      src.for_each([&](uint64_t key, int j) { cnt += (key == prefix); });
-      int tot;
-      block_scan(cnt, &tot, S);
-      __syncthreads();
-      if (tot > rem) th.Tj = tie_select_j(src, prefix, rem, S);
-    }
-  }
-  return th;
-}
-
-// Write the selected indices in ascending order (LDS bitmap over segments of
-// the index range), padded with -1, and optionally their scores.
-template <class Src>
-__device__ void emit_sorted(Src& src, const Thr& th, int n, int k, int32_t* out, double* sout, SelShared& S) {
-  constexpr int WPT = BITMAP_BITS / 32 / SEL_THREADS;   // bitmap words per thread
-  int written = 0;
-  for (int seg0 = 0; seg0 < n; seg0 += BITMAP_BITS) {
-    for (int i = threadIdx.x; i < BITMAP_BITS / 32; i += SEL_THREADS) S.bitmap[i] = 0;
-    __syncthreads();
-    src.for_each([&](uint64_t key, int j) {
-      if (j >= seg0 && j < seg0 + BITMAP_BITS && selected(th, key, j))
-        atomicOr(&S.bitmap[(j - seg0) >> 5], 1u << ((j - seg0) & 31));
-    });
-    __syncthreads();
-    int cnt = 0;
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) cnt += __popc(S.bitmap[threadIdx.x * WPT + w]);
-    int tot;
-    int pos = written + block_scan(cnt, &tot, S);
-    S.off[threadIdx.x] = pos;
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) {
-      uint32_t bits = S.bitmap[threadIdx.x * WPT + w];
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < k) out[pos] = seg0 + (threadIdx.x * WPT + w) * 32 + bit;
-        ++pos;
-      }
-    }
-    __syncthreads();
-    if (sout) {
-      src.for_each([&](uint64_t key, int j) {
-        if (j >= seg0 && j < seg0 + BITMAP_BITS && selected(th, key, j)) {
-          const int word = (j - seg0) >> 5, owner = word / WPT;
-          int p = S.off[owner];
-          for (int w = owner * WPT; w < word; ++w) p += __popc(S.bitmap[w]);
-          p += __popc(S.bitmap[word] & ((1u << ((j - seg0) & 31)) - 1u));
-          if (p < k) sout[p] = key_score(key);
-        }
-      });
-      __syncthreads();
-    }
-    written += tot;
-  }
-  for (int i = written + threadIdx.x; i < k; i += SEL_THREADS) {
-    out[i] = -1;
-    if (sout) sout[i] = 0.0;
-  }
-}
-
-// Source over candidates held in registers.
-// Source over candidates held in LDS.
-struct LdsSrc {
-  const uint64_t* key;
-  const int32_t* j;
-  int n;
-  template <class F> __device__ __forceinline__ void for_each(F&& f) {
-    for (int i = threadIdx.x; i < n; i += SEL_THREADS) f(key[i], j[i]);
-  }
-};
-
-// Source that re-scores every eligible entry of the row on each pass.
-template <int DT, int HP>
-struct StreamSrc {
-  const IndexArgs* A;
-  Rows rw;
-  MxQuery Q;
-  float* tbuf;     // per-wave buffers [SEL_WAVES][WBUF]
-  const float* wl; // [32] weights (row 0)
-  const float* ql; // F32 query in LDS
-  template <class F> __device__ void for_each(F&& f) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n = rw.n[0];
-    for (int j0 = wave * 64; j0 < n; j0 += SEL_THREADS) {
-      uint64_t k0;
-      if (DT == DT_MXFP4) {
-        MxTiles T;
-        bool ix;
-        mx_load_round(*A, rw.b, j0, n, T);
-        mx_score_round<HP, 1>(*A, rw, Q, T, j0, tbuf + wave * WBUF, wl, &k0, ix);
-        if (ix) k0 = mx_score_exact(*A, rw.r[0], rw.b, j0 + lane, wl);
-      } else {
-        f32_score_round(*A, rw, j0, ql, wl, k0);
-      }
-      f(k0, j0 + lane);
-    }
-  }
-};
-
-// Exact selection of one row from scratch, re-scoring every eligible entry in
-// each pass (rows with few entries, and rows whose candidates failed the
-// certification).  Kept out of line: it is the rare or the small case.
-template <int DT, int HP>
-__device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n, int kk, int32_t* out, double* sout,
-                                             SelShared& S, float* tbuf, const float* wl, const float* ql,
-                                             bool all_selected) {
-  StreamSrc<DT, HP> src;
-  src.A = &A;
-  src.rw.b = r / A.Tq;
-  src.rw.r[0] = r; src.rw.r[1] = -1;
-  src.rw.n[0] = n; src.rw.n[1] = 0;
-  if (DT == DT_MXFP4) mx_load_query<HP>(A, src.rw, src.Q);
-  src.tbuf = tbuf;
-  src.wl = wl;
-  src.ql = ql;
-  if (all_selected) {
-    // every eligible entry is selected: only the scores are needed
-    for (int i = n + threadIdx.x; i < A.k; i += SEL_THREADS) sout[i] = 0.0;
-    src.for_each([&](uint64_t key, int j) { if (j < n) sout[j] = key_score(key); });
-    return;
-  }
-  const Thr th = find_threshold(src, kk, S);
-  emit_sorted(src, th, n, A.k, out, sout, S);
-}
-
-// Emission for candidates stored in ascending index order: a block scan over
-// the selection flags of contiguous slices keeps that order, so no sorting is
-// needed.  Items equal to the threshold key are taken in array (= index)
-// order until `ties` of them are in.
-__device__ void emit_in_order(const uint64_t* key, const int32_t* jj, int total, const Thr& th, int ties, int k,
-                              int32_t* out, double* sout, SelShared& S) {
-  const int per = (total + SEL_THREADS - 1) / SEL_THREADS;
-  const int i0 = threadIdx.x * per, i1 = min(total, i0 + per);
-  int nt = 0;
-  for (int i = i0; i < i1; ++i) nt += (th.low == 0 && key[i] == th.T);
-  int tt;
-  int tie_before = block_scan(nt, &tt, S);
-  int nsel = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint64_t kv = key[i];
-    bool f;
-    if (th.low > 0) f = kv != 0 && (kv >> th.low) >= (th.T >> th.low);
-    else if (kv == th.T) { f = tie_before < ties; ++tie_before; }
-    else f = kv > th.T;
-    nsel += f;
-  }
-  int tot;
-  int pos = block_scan(nsel, &tot, S);
-  tie_before -= nt;   // rewind for the write pass
-  for (int i = i0; i < i1; ++i) {
-    const uint64_t kv = key[i];
-    bool f;
-    if (th.low > 0) f = kv != 0 && (kv >> th.low) >= (th.T >> th.low);
-    else if (kv == th.T) { f = tie_before < ties; ++tie_before; }
-    else f = kv > th.T;
-    if (f) {
-      if (pos < k) {
-        out[pos] = jj[i];
-        if (sout) sout[pos] = key_score(kv);
-      }
-      ++pos;
-    }
-  }
-  for (int i = tot + threadIdx.x; i < k; i += SEL_THREADS) {
-    out[i] = -1;
-    if (sout) sout[i] = 0.0;
   }
 }
 
@@ -1045,17 +417,11 @@ static int choose_kpl(const IndexArgs& a, int nq) {
 
 size_t index_ws_bytes(int B, int Tq, int H, int d, int64_t N_cap, int k, int dt) {
   IndexArgs a{};
-  a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.N_cap = N_cap; a.k = k;
+  a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.N_cap = N_cap; a.k = k; a.dt = dt;
+  if (index_prefill_applies(a)) return index_prefill_ws_bytes(B, Tq);
   const int kpl = choose_kpl(a, nq_of(dt, H, Tq));
   const int64_t NCH = (N_cap + 64 * kpl - 1) / (64 * kpl);
   return carve_bytes((int64_t)B * Tq, NCH > 0 ? NCH : 1);
-}
-
-static size_t select_smem(int dt, int H, int d) {
-  size_t region = 12 * (size_t)CMAX;                                   // candidate keys + indices
-  const size_t stream = sizeof(float) * SEL_WAVES * WBUF;              // scoring buffers (aliased)
-  if (stream > region) region = stream;
-  return sizeof(SelShared) + region + sizeof(float) * 32;
 }
 
 template <int DT, int KPL, int HP, int NQ>
@@ -1083,6 +449,7 @@ static hipError_t launch_k(const IndexArgs& a, hipStream_t s) {
 
 hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
   if ((int64_t)a.B * a.Tq == 0) return hipSuccess;
+  if (index_prefill_applies(a)) return launch_index_prefill(a, s);
   const int nq = nq_of(a.dt, a.H, a.Tq);
   if (a.dt == DT_MXFP4) {
     if (a.H <= 8) return nq == 2 ? launch_k<DT_MXFP4, 8, 2>(a, s) : launch_k<DT_MXFP4, 8, 1>(a, s);
