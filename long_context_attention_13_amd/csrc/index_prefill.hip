@@ -46,11 +46,12 @@ constexpr int PF_NKC = 16;            // key ranges per row
 constexpr int PF_LCAP = 96;           // candidates per (row, key range, lane group)
 constexpr int PF_SMAX = 2560;         // sampled keys per row at most
 constexpr int PF_RANK = 64;           // threshold = PF_RANK-th largest sampled score
-constexpr int PF_CAND = 3072;         // candidates per row the select pass holds
+constexpr int PF_CAND = 3840;         // candidates per row the select pass holds
 constexpr int PF_CPL = PF_CAND / 64;  // ... per lane
 constexpr int PF_BAND = 64;           // band entries re-scored exactly
 constexpr int PF_NMAX = 32 * PF_SMAX; // largest key cache the prefill path takes
 constexpr int PF_FALLBACK_GRID = 128;
+constexpr int PF_SWAVES = 8;         // wavefronts of the sample workgroup (16 rows)
 
 struct PfWs {
   float* thr;       // [R] candidate threshold (fp32 score)
@@ -177,10 +178,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // in LDS; then each wave finds the thresholds of 4 rows.
 // ------------------------------------------------------------------------
 template <int HP>
-__global__ __launch_bounds__(256) void pf_sample_kernel(IndexArgs A, PfWs W, int sigma, int srow) {
+__global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, PfWs W, int sigma, int srow) {
   extern __shared__ __align__(16) char smem[];
   uint16_t* sc = (uint16_t*)smem;                                  // [16][srow]
-  uint32_t* hist = (uint32_t*)(smem + 16 * srow * 2);              // [4][256]
+  uint32_t* hist = (uint32_t*)(smem + 16 * srow * 2);              // [PF_SWAVES][256]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
@@ -199,35 +200,45 @@ __global__ __launch_bounds__(256) void pf_sample_kernel(IndexArgs A, PfWs W, int
   for (int o = 32; o > 0; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, WAVE));
   const int S = nmax > 0 ? (nmax + sigma - 1) / sigma : 0;         // samples j = s * sigma < nmax
   const int ntile = (S + 15) / 16;
-  for (int tt = wave; tt < ntile; tt += 4) {
+  // A operand of sample tile tt (16 sampled keys): lane = key c, K-block g
+  auto ld = [&](int tt, v4i& av, int& ka) {
     const int sa = min(tt * 16 + c, S - 1);
     const int64_t krow = (int64_t)b * A.N_cap + (int64_t)sa * sigma;
-    const v4i av = *(const v4i*)((const uint8_t*)A.ki + krow * 64 + g * 16);
-    const v8i a8 = {av[0], av[1], av[2], av[3], 0, 0, 0, 0};
-    const int ka = A.ki_scale[krow * 4 + g];
+    av = *(const v4i*)((const uint8_t*)A.ki + krow * 64 + g * 16);
+    ka = A.ki_scale[krow * 4 + g];
+  };
+  v4i avc = {0, 0, 0, 0}, avn = {0, 0, 0, 0};
+  int kac = 127, kan = 127;
+  if (wave < ntile) ld(wave, avc, kac);
+#pragma unroll 1
+  for (int tt = wave; tt < ntile; tt += PF_SWAVES) {
+    if (tt + PF_SWAVES < ntile) ld(tt + PF_SWAVES, avn, kan);
+    const v8i a8 = {avc[0], avc[1], avc[2], avc[3], 0, 0, 0, 0};
     v4f acc[HP];
 #pragma unroll
     for (int h = 0; h < HP; ++h) {
       const v4f z = {0.f, 0.f, 0.f, 0.f};
-      acc[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, P.bq[h], z, 4, 4, 0, ka, 0, P.sb[h]);
+      acc[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, P.bq[h], z, 4, 4, 0, kac, 0, P.sb[h]);
     }
-    float s[4];
-    pf_combine<HP>(acc, P, s);
+    float sv[4];
+    pf_combine<HP>(acc, P, sv);
     uint32_t u[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int si = tt * 16 + 4 * g + i;
       const bool el = si < S && si * sigma < nq && !wneg;
-      u[i] = el ? (__float_as_uint(s[i]) >> 16) : 0u;
+      u[i] = el ? (__float_as_uint(sv[i]) >> 16) : 0u;
     }
     *(uint2*)(sc + c * srow + tt * 16 + 4 * g) = make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16));
+    avc = avn;
+    kac = kan;
   }
   __syncthreads();
 
   uint32_t* hw = hist + wave * 256;
 #pragma unroll 1
-  for (int qq = 0; qq < 4; ++qq) {
-    const int cq = wave * 4 + qq;
+  for (int qq = 0; qq < 16 / PF_SWAVES; ++qq) {
+    const int cq = wave * (16 / PF_SWAVES) + qq;
     const int tq = t0 + cq;
     if (tq >= A.Tq) break;
     const int64_t rq = (int64_t)b * A.Tq + tq;
@@ -311,8 +322,14 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
     atomicMax(&s_q[2], dq);
   }
   const int nlim = min(nq, j1);
-  uint64_t* list = W.cand + (((r * PF_NKC + kc) * 4 + g) * PF_LCAP);
-  int cnt = 0;
+  int nlim_min = rv ? nlim : 1 << 30;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nlim_min = min(nlim_min, __shfl_xor(nlim_min, o, WAVE));
+  // candidate lists of the wave's 16 rows: uniform base + 32-bit lane offset
+  const int64_t r0 = (int64_t)b * A.Tq + blockIdx.x * PF_QROWS + wave * 16;
+  char* wlist = (char*)(W.cand + (r0 * PF_NKC + kc) * 4 * PF_LCAP);
+  const uint32_t lane_off = (uint32_t)(((c * PF_NKC) * 4 + g) * PF_LCAP) * 8u;
+  uint32_t cnt = 0;
 
   const int nst = (j1 - j0 + PF_STAGE - 1) / PF_STAGE;
   const uint8_t* kbase = (const uint8_t*)A.ki + (int64_t)b * A.N_cap * 64;
@@ -363,10 +380,13 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
       if (bad) s_bad = 1;
     }
     const int ntl = (nk + 15) / 16;
-    auto mfma_tile = [&](int tt, v4f (&acc)[HP]) {
+    // A operand of tile tt from LDS: lane = key c of the tile, K-block g
+    auto frag = [&](int tt, v8i& a8, int& ka) {
       const v4i av = *(const v4i*)(base + ((tt * 4 + g) * 16 + c) * 16);
-      const v8i a8 = {av[0], av[1], av[2], av[3], 0, 0, 0, 0};
-      const int ka = (int)(uint8_t)base[PF_CODE_B + (tt * 16 + c) * 4 + g];
+      a8 = (v8i){av[0], av[1], av[2], av[3], 0, 0, 0, 0};
+      ka = (int)(uint8_t)base[PF_CODE_B + (tt * 16 + c) * 4 + g];
+    };
+    auto mfma = [&](const v8i& a8, int ka, v4f (&acc)[HP]) {
 #pragma unroll
       for (int h = 0; h < HP; ++h) {
         const v4f z = {0.f, 0.f, 0.f, 0.f};
@@ -376,29 +396,37 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
     auto epilogue = [&](const v4f (&acc)[HP], int tt) {
       float sc[4];
       pf_combine<HP>(acc, P, sc);
-      const int jt = sj + tt * 16 + 4 * g;
+      const int jt = sj + tt * 16;
+      const bool full = jt + 16 <= nlim_min;        // uniform: every key of the tile is eligible for every row
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (sc[i] >= thr && jt + i < nlim) {
+        const uint32_t j = (uint32_t)(jt + 4 * g + i);
+        if (sc[i] >= thr && (full || (int)j < nlim)) {
           // an overflowing list sends the row to the fallback: clamping the slot is enough
-          list[min(cnt, PF_LCAP - 1)] = ((uint64_t)__float_as_uint(sc[i]) << 32) | (uint32_t)(jt + i);
+          *(uint64_t*)(wlist + lane_off + min(cnt, (uint32_t)PF_LCAP - 1u) * 8u) =
+              ((uint64_t)__float_as_uint(sc[i]) << 32) | j;
           ++cnt;
         }
       }
     };
-    // two accumulator sets: the next tile's MFMAs run while this tile's
-    // combine and filter run on the vector ALU
+    // software pipeline: the next tile's fragment is read from LDS and its
+    // MFMAs issued before this tile's combine and filter run on the vector ALU
+    v8i fa, fb;
+    int ka, kb2;
     v4f accA[HP], accB[HP];
-    mfma_tile(0, accA);
+    frag(0, fa, ka);
+    if (ntl > 1) frag(1, fb, kb2);
+    mfma(fa, ka, accA);
 #pragma unroll 1
     for (int tt = 0; tt < ntl; tt += 2) {
-      const bool two = tt + 1 < ntl;
-      if (two) mfma_tile(tt + 1, accB);
+      if (tt + 1 < ntl) mfma(fb, kb2, accB);
+      if (tt + 2 < ntl) frag(tt + 2, fa, ka);
       __builtin_amdgcn_sched_barrier(0);
       epilogue(accA, tt);
       __builtin_amdgcn_sched_barrier(0);
-      if (two) {
-        if (tt + 2 < ntl) mfma_tile(tt + 2, accA);
+      if (tt + 1 < ntl) {
+        if (tt + 2 < ntl) mfma(fa, ka, accA);
+        if (tt + 3 < ntl) frag(tt + 3, fb, kb2);
         __builtin_amdgcn_sched_barrier(0);
         epilogue(accB, tt + 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -407,7 +435,7 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
   }
   __syncthreads();
   if (rv) {
-    W.cnt[(r * PF_NKC + kc) * 4 + g] = cnt;
+    W.cnt[(r * PF_NKC + kc) * 4 + g] = (int)min(cnt, (uint32_t)PF_LCAP + 1u);
     if (s_bad && g == 0) atomicOr(&W.flags[r], 2);
   }
 }
@@ -416,13 +444,15 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
 // Select pass: one wavefront per row.
 // ------------------------------------------------------------------------
 struct PfSelShared {
-  uint32_t cs[PF_CAND];     // candidate scores (fp32 bits); later the bitmap
+  uint32_t cs[PF_CAND];     // candidate scores (fp32 bits); then the MFMA transpose
+                            // buffer, then the bitmap (the scores live in registers)
   int32_t cj[PF_CAND];      // candidate indices; later the output list
   uint32_t hist[256];
-  float wbuf[WBUF];
   float wl[32];
   int32_t bj[PF_BAND];
 };
+static_assert(sizeof(float) * WBUF <= sizeof(uint32_t) * PF_CAND, "transpose buffer fits the score array");
+static_assert(PF_NMAX / 32 <= PF_CAND, "bitmap fits the score array");
 
 template <int HP>
 __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int KC) {
@@ -453,38 +483,26 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
   const int total = __shfl(incl, 63, WAVE);
   if (total > PF_CAND || total < kk) { enqueue(); return; }
   const int loff = incl - cl;
-  // gather the lists into LDS, 16 lists of loads in flight at a time
-  const uint64_t* lists = W.cand + r * PF_NKC * 4 * PF_LCAP;
+  // gather the lists into LDS with direct global->LDS dword loads: the high
+  // halves (scores) into cs, the low halves (indices) into cj, every list at
+  // its flat offset; all loads are in flight at once
+  const uint32_t* lw = (const uint32_t*)(W.cand + r * PF_NKC * 4 * PF_LCAP);
 #pragma unroll 1
-  for (int L0 = 0; L0 < nl; L0 += 16) {
-    uint64_t v[16][2];
+  for (int Lx = 0; Lx < nl; ++Lx) {
+    const int cn = __builtin_amdgcn_readlane(cl, Lx);
+    const int o = __builtin_amdgcn_readlane(loff, Lx);
+    const uint32_t* src = lw + (int64_t)Lx * PF_LCAP * 2;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int Lx = L0 + u;
-      const int cn = __shfl(cl, Lx < 64 ? Lx : 0, WAVE);
-      const bool ok = Lx < nl;
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const int e = lane + 64 * e2;
-        v[u][e2] = (ok && e < cn) ? lists[(int64_t)Lx * PF_LCAP + e] : 0ull;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int Lx = L0 + u;
-      const int cn = __shfl(cl, Lx < 64 ? Lx : 0, WAVE);
-      const int o = __shfl(loff, Lx < 64 ? Lx : 0, WAVE);
-      const bool ok = Lx < nl;
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const int e = lane + 64 * e2;
-        if (ok && e < cn) {
-          L.cs[o + e] = (uint32_t)(v[u][e2] >> 32);
-          L.cj[o + e] = (int32_t)(uint32_t)v[u][e2];
-        }
+    for (int e2 = 0; e2 < 2; ++e2) {
+      if (e2 * 64 >= cn) break;
+      const int e = lane + 64 * e2;
+      if (e < cn) {
+        __builtin_amdgcn_global_load_lds((const void*)(src + 2 * e), (void*)(L.cj + o + 64 * e2), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src + 2 * e + 1), (void*)(L.cs + o + 64 * e2), 4, 0, 0);
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
   wave_lds_sync();
   uint32_t sv[PF_CPL];
 #pragma unroll
@@ -492,11 +510,24 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
     const int i = lane + 64 * m;
     sv[m] = i < total ? L.cs[i] : 0u;
   }
-  // exact radix select (8-bit digits) of the kk-th largest s32
-  uint32_t prefix = 0, mask = 0;
+  // exact radix select (8-bit digits) of the kk-th largest s32, from the first
+  // byte where the largest and smallest candidate differ
+  uint32_t vmax = 0, vmin = ~0u;
+#pragma unroll
+  for (int m = 0; m < PF_CPL; ++m) {
+    if (lane + 64 * m < total) { vmax = max(vmax, sv[m]); vmin = min(vmin, sv[m]); }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, o, WAVE));
+    vmin = min(vmin, (uint32_t)__shfl_xor((int)vmin, o, WAVE));
+  }
+  const int top = vmax == vmin ? 0 : (31 - __clz(vmax ^ vmin)) / 8 * 8;
+  uint32_t mask = top == 24 ? 0u : ~((1u << (top + 8)) - 1u);
+  uint32_t prefix = vmax & mask;
   int rem = kk;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = top; shift >= 0; shift -= 8) {
     for (int i = lane; i < 256; i += 64) L.hist[i] = 0;
     wave_lds_sync();
 #pragma unroll
@@ -552,7 +583,7 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
     MxTiles T;
     bool ix;
     mx_load_gather(A, rw.b, jm, nband, T);
-    mx_score_round<HP, 1>(A, rw, Q, T, 0, L.wbuf, L.wl, &key, ix);
+    mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, L.wl, &key, ix);
     if (ix) key = mx_score_exact(A, (int)r, rw.b, jm, L.wl);
     if (lane >= nband) key = 0;
   }
@@ -610,7 +641,7 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
       bool ix;
       uint64_t k2;
       mx_load_gather(A, rw.b, je, cntr, T);
-      mx_score_round<HP, 1>(A, rw, Q, T, 0, L.wbuf, L.wl, &k2, ix);
+      mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, L.wl, &k2, ix);
       if (ix) k2 = mx_score_exact(A, (int)r, rw.b, je, L.wl);
       if (lane < cntr) sout[i0 + lane] = key_score(k2);
     }
@@ -652,8 +683,8 @@ static hipError_t launch_pf(const IndexArgs& a, hipStream_t s) {
   const int smax = (int)((a.N_cap + sigma - 1) / sigma);
   const int srow = (smax + 63) / 64 * 64;
   const int KC = pf_key_range(a);
-  const size_t smem0 = (size_t)16 * srow * 2 + 4 * 256 * 4;
-  hipLaunchKernelGGL((pf_sample_kernel<HP>), dim3((unsigned)((a.Tq + 15) / 16), (unsigned)a.B), dim3(256), smem0, s,
+  const size_t smem0 = (size_t)16 * srow * 2 + PF_SWAVES * 256 * 4;
+  hipLaunchKernelGGL((pf_sample_kernel<HP>), dim3((unsigned)((a.Tq + 15) / 16), (unsigned)a.B), dim3(PF_SWAVES * 64), smem0, s,
                      a, W, sigma, srow);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
