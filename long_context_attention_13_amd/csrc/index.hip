@@ -296,28 +296,38 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
       for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
       __syncthreads();
       // copy the candidates into LDS (one batch of loads in flight) and
-      // histogram the first digit on the way
-      auto addr = [&](int i) -> int64_t {
-        int lo = 0, hi = nch;                    // chunk c with off[c] <= i < off[c+1]
-        while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (S.off[mid] <= i) lo = mid; else hi = mid; }
-        return ((int64_t)r * NCH + lo) * CAP + (i - S.off[lo]);
-      };
-      uint64_t bk[LB];
-      int32_t bj[LB];
-#pragma unroll
-      for (int u = 0; u < LB; ++u) {
-        const int i = u * SEL_THREADS + threadIdx.x;
-        const int64_t a = i < total ? addr(i) : 0;
-        bk[u] = W.ckey[a];
-        bj[u] = W.cidx[a];
+      // histogram the first digit on the way; a chunk map (candidate slot ->
+      // chunk, written one chunk per wavefront into the bitmap area, which the
+      // candidate path does not use) gives each slot its source address
+      uint16_t* cmap = (uint16_t*)S.bitmap;
+      {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll 1
+        for (int c = wave; c < nch; c += SEL_WAVES) {
+          const int o = S.off[c], cnt = S.off[c + 1] - o;
+          for (int e = lane; e < cnt; e += 64) cmap[o + e] = (uint16_t)c;
+        }
       }
+      __syncthreads();
+      {
+        uint64_t bk[LB];
+        int32_t bj[LB];
 #pragma unroll
-      for (int u = 0; u < LB; ++u) {
-        const int i = u * SEL_THREADS + threadIdx.x;
-        if (i < total) {
-          ckey_l[i] = bk[u];
-          cidx_l[i] = bj[u];
-          if (nb > 0) atomicAdd(&S.hist[(bk[u] >> shift) & ((1ull << nb) - 1ull)], 1u);
+        for (int u = 0; u < LB; ++u) {
+          const int i = u * SEL_THREADS + threadIdx.x;
+          const int c = i < total ? cmap[i] : 0;
+          const int64_t a = i < total ? ((int64_t)r * NCH + c) * CAP + (i - S.off[c]) : 0;
+          bk[u] = W.ckey[a];
+          bj[u] = W.cidx[a];
+        }
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          const int i = u * SEL_THREADS + threadIdx.x;
+          if (i < total) {
+            ckey_l[i] = bk[u];
+            cidx_l[i] = bj[u];
+            if (nb > 0) atomicAdd(&S.hist[(bk[u] >> shift) & ((1ull << nb) - 1ull)], 1u);
+          }
         }
       }
       __syncthreads();
@@ -359,14 +369,8 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
             th.T = prefix; th.low = 0; ties = rem; have = true;
           } else if (indig <= 64) {               // few items: rank them exactly
             resolve_bin(src, prefix, mask, rem, S);
-            th.T = S.bcast64[0]; th.low = 0;
-            // items equal to T before it (in index order) are the ties taken
-            const int tj = S.bcast[3];
-            int nt = 0;
-            src.for_each([&](uint64_t key, int j) { nt += (key == th.T && j <= tj); });
-            int tt;
-            block_scan(nt, &tt, S);
-            ties = tt;
+            // exact: the rem-th item of the bin is (T, Tj); ties up to Tj are in
+            th.T = S.bcast64[0]; th.low = 0; th.Tj = S.bcast[3];
             have = true;
           } else {
             const int nb2 = shift >= 11 ? 11 : shift;

@@ -16,7 +16,7 @@ constexpr int NDIRECT = 8192;      // rows with n_elig <= NDIRECT skip the chunk
 constexpr int SEL_THREADS = 1024;  // select kernel workgroup (16 wavefronts)
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
 constexpr int CMAX = 8192;         // candidates per row held in LDS by the select kernel
-constexpr int LB = CMAX / 1024;    // candidate loads per thread and batch (one batch at 1024 threads)
+constexpr int LB = CMAX / SEL_THREADS;   // candidate loads per thread (one batch)
 constexpr int MAXCH = 1024;        // chunks per row the candidate path handles
 constexpr int KROW = 20;           // LDS floats per key in the transpose buffer (16 + pad)
 constexpr int BITMAP_BITS = 1 << 18;
@@ -430,15 +430,17 @@ __device__ void resolve_bin(Src& src, uint64_t prefix, uint64_t mask, int rem, S
     }
   });
   __syncthreads();
-  const int n = S.nres;
+  const int n = min(S.nres, 64);
   if (threadIdx.x < 64) {
     const int i = threadIdx.x;
     int rank = 0;
     const uint64_t ki = i < n ? S.rkey[i] : 0;
     const int ji = i < n ? S.rj[i] : 0;
+    const uint32_t klo = (uint32_t)ki, khi = (uint32_t)(ki >> 32);
     for (int m = 0; m < n; ++m) {
-      const uint64_t km = S.rkey[m];
-      rank += (km > ki) || (km == ki && S.rj[m] < ji);
+      const uint64_t km = ((uint64_t)readlane_u32(khi, m) << 32) | readlane_u32(klo, m);
+      const int jm = (int)readlane_u32((uint32_t)ji, m);
+      rank += (km > ki) || (km == ki && jm < ji);
     }
     if (i < n && rank == rem - 1) { S.bcast64[0] = ki; S.bcast[3] = ji; }
   }
@@ -624,6 +626,28 @@ __device__ void emit_in_order(const uint64_t* key, const int32_t* jj, int total,
                               int32_t* out, double* sout, SelShared& S) {
   const int per = (total + SEL_THREADS - 1) / SEL_THREADS;
   const int i0 = threadIdx.x * per, i1 = min(total, i0 + per);
+  if (th.low == 0 && th.Tj != 0x7FFFFFFF) {
+    // exact threshold (T, Tj): key > T, or key == T and j <= Tj
+    int nsel = 0;
+    for (int i = i0; i < i1; ++i) nsel += key[i] > th.T || (key[i] == th.T && jj[i] <= th.Tj);
+    int tot;
+    int pos = block_scan(nsel, &tot, S);
+    for (int i = i0; i < i1; ++i) {
+      const uint64_t kv = key[i];
+      if (kv > th.T || (kv == th.T && jj[i] <= th.Tj)) {
+        if (pos < k) {
+          out[pos] = jj[i];
+          if (sout) sout[pos] = key_score(kv);
+        }
+        ++pos;
+      }
+    }
+    for (int i = tot + threadIdx.x; i < k; i += SEL_THREADS) {
+      out[i] = -1;
+      if (sout) sout[i] = 0.0;
+    }
+    return;
+  }
   int nt = 0;
   for (int i = i0; i < i1; ++i) nt += (th.low == 0 && key[i] == th.T);
   int tt;
