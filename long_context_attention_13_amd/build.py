@@ -29,7 +29,7 @@ FLAGS = [
 SOURCES = ["compress.hip", "index.hip", "index_prefill.hip", "attend.hip", "abi.cpp"]
 # per-source flags: keep MFMA results in ordinary VGPRs (the score kernel's
 # epilogue reads every result; accumulation-register copies would double it)
-EXTRA = {"index_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"index_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -128,3 +128,26 @@ def test_empty_lists_give_sink_only():
                        np.zeros((B, 1), np.int32), sink, 0.1, lca.F32)
     assert np.all(o == 0)
     np.testing.assert_allclose(l, np.broadcast_to(sink, l.shape), rtol=1e-6)
+
+
+@pytest.mark.parametrize("Hq,kv_dt", [(64, lca.FP8E4M3), (16, lca.BF16)])
+def test_dense_row_groups(Hq, kv_dt):
+    """Dense prefill rows processed in groups that share staged tiles: a
+    ragged last group, rows of two sequences, n_elig from 0 up, windows that
+    start short (sequence start), an empty window and windows in any order."""
+    B, Tq, N_cap, W = 2, 301, 700, 128
+    W_buf = W - 1 + Tq
+    g, q, kv, kv_sc, win, sink = make(71 + Hq, B, Tq, Hq, N_cap, W_buf, kv_dt, lca.BF16)
+    wb = np.stack([np.arange(Tq), np.maximum(np.arange(Tq) - 40, 0)]).astype(np.int32) + W - 1
+    wb[1] = np.minimum(wb[1], W_buf - W)
+    wl = np.full((B, Tq), W, np.int32)
+    wl[1, :40] = np.arange(40)                  # the second sequence starts inside the chunk
+    wl[0, 7] = 0                                # an empty window
+    wb[0] -= W - 1
+    wb[0, 100:104] = wb[0, 100:104][::-1]       # a group with windows out of order
+    n = np.stack([np.minimum(np.arange(Tq) // 2, N_cap), np.minimum(300 + np.arange(Tq), N_cap)]).astype(np.int32)
+    n[0, :5] = 0
+    o, l, ro, rl = run(False, q, lca.BF16, kv, kv_dt, kv_sc, n, win, lca.BF16, wb, wl, sink, 1 / math.sqrt(128),
+                       lca.BF16)
+    assert_rows_close(o, ro, 2e-2, "out")
+    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
