@@ -260,15 +260,19 @@ __device__ __forceinline__ void mt_fetch(const AttendArgs& A, int b, int64_t wba
         }
       }
       R.kind[c][u] = kind;
-      const int64_t erow = (int64_t)b * A.N_cap + (kind == 0 ? j : 0);
-      if (KVDT == DT_FP8) {
-        R.ent[c][u][0] = *(const int4*)((const uint8_t*)A.kv + erow * 128 + ch * 16);
-        R.sc[c][u] = *(const float2*)(A.kv_scale + erow * 2);
-      } else {
-        R.ent[c][u][0] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16);
-        R.ent[c][u][1] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16 + 8);
+      // which sources the tile touches is uniform over the workgroup, so
+      // these branches do not split the loads
+      if (t0 < nkv) {
+        const int64_t erow = (int64_t)b * A.N_cap + (kind == 0 ? j : 0);
+        if (KVDT == DT_FP8) {
+          R.ent[c][u][0] = *(const int4*)((const uint8_t*)A.kv + erow * 128 + ch * 16);
+          R.sc[c][u] = *(const float2*)(A.kv_scale + erow * 2);
+        } else {
+          R.ent[c][u][0] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16);
+          R.ent[c][u][1] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16 + 8);
+        }
       }
-      if (A.W_buf > 0) {
+      if (t0 + MT_TE > nkv && A.W_buf > 0) {
         const int64_t wrow = wbase + (kind == 1 ? p - nkv : 0);
         R.win[c][u][0] = *(const int4*)((const uint16_t*)A.win + wrow * 128 + ch * 16);
         R.win[c][u][1] = *(const int4*)((const uint16_t*)A.win + wrow * 128 + ch * 16 + 8);
@@ -345,7 +349,7 @@ __device__ __forceinline__ void mt_store(const MtRegs<KVDT, CPT>& R, __bf16* Kl,
 }
 
 template <int KVDT, int HQ, int QB>
-__global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB <= 256 ? 2 : 1) void attend_mfma_kernel(AttendArgs A, int S, int split_items, float* part_ml,
+__global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void attend_mfma_kernel(AttendArgs A, int S, int split_items, float* part_ml,
                                                                   float* part_o) {
   // QB query rows of one sequence share each staged tile (dense lists only):
   // the workgroup's list is entries 0 .. max n_elig - 1 followed by the union
@@ -488,8 +492,12 @@ __global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB <= 256 ? 2 : 1) void atten
         lsum += pe;
       }
     l_run = l_run * alpha + lsum;
+    // rescale only when some lane's running max moved (usually only the
+    // first tiles)
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    }
 
     // ---- O^T += V^T P^T, two K-steps of 32 items
 #pragma unroll
