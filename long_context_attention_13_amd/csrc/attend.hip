@@ -26,8 +26,9 @@ constexpr int ATT_TE = 32;         // items per LDS tile (VALU path)
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Split plan: one split per row when there are enough rows to fill the GPU on
-// their own; otherwise the list is cut into splits of 256 items (128 when that
-// still leaves fewer than 256 workgroups).
+// their own; otherwise the list is cut into splits of 64 items (one tile)
+// while that stays within one workgroup per compute unit, else 128 or 256
+// (the split size depends only on the shape, never on the data).
 struct Plan { int S; int items; };
 
 static Plan att_plan(int64_t R, int64_t n_kv_max, int64_t W_buf) {
@@ -35,6 +36,7 @@ static Plan att_plan(int64_t R, int64_t n_kv_max, int64_t W_buf) {
   if (R >= 256 || L <= 128) return Plan{1, (int)(L < 1 ? 1 : L)};
   int64_t items = 256;
   if (R * ((L + 255) / 256) < 256) items = 128;
+  if (R * ((L + 63) / 64) <= 256) items = 64;
   if ((L + items - 1) / items > 1024) items = ((L + 1023) / 1024 + 63) / 64 * 64;   // merge holds <= 1024 splits
   const int64_t s = (L + items - 1) / items;
   return Plan{(int)(s < 1 ? 1 : s), (int)items};
@@ -554,42 +556,64 @@ __global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void atten
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, const float* part_ml,
                                                            const float* part_o) {
-  // one workgroup per (row, head); thread d owns output dim d
+  // one workgroup per (row, head); thread d owns output dim d.  Every load
+  // (the split maxima and sums, and the first MG_PRE splits' outputs) is
+  // issued before any of them is used.
+  constexpr int MG_PRE = 64;
   const int r = blockIdx.x / A.Hq, h = blockIdx.x % A.Hq;
   const int d = threadIdx.x;
   __shared__ float wsp[1024];
   __shared__ float red[2][2];
   const float sk = A.sink[h] * LOG2E;                       // partial maxima are base-2 logits
   const int64_t base0 = (int64_t)r * S * A.Hq + h;          // partial (r, s, h) = base0 + s*Hq
+  const int64_t ost = (int64_t)A.Hq * A.D;
+  const float* po = part_o + base0 * A.D + d;
+  float ov[MG_PRE];
+#pragma unroll
+  for (int i = 0; i < MG_PRE; ++i) ov[i] = i < S ? po[i * ost] : 0.f;
+  float mv[8], lv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = d + 128 * i;
+    mv[i] = s < S ? part_ml[(base0 + (int64_t)s * A.Hq) * 2] : -INFINITY;
+    lv[i] = s < S ? part_ml[(base0 + (int64_t)s * A.Hq) * 2 + 1] : 0.f;
+  }
   float mx = -INFINITY;
-  for (int s = d; s < S; s += 128) mx = fmaxf(mx, part_ml[(base0 + (int64_t)s * A.Hq) * 2]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, mv[i]);
   mx = wave_max(mx);
   if ((d & 63) == 0) red[0][d >> 6] = mx;
   __syncthreads();
   const float M = fmaxf(sk, fmaxf(red[0][0], red[0][1]));
   float z = 0.f;
-  for (int s = d; s < S; s += 128) {
-    const float m = part_ml[(base0 + (int64_t)s * A.Hq) * 2];
-    const float e = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    wsp[s] = e;
-    z += part_ml[(base0 + (int64_t)s * A.Hq) * 2 + 1] * e;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = d + 128 * i;
+    if (s < S) {
+      const float e = (mv[i] == -INFINITY) ? 0.f : exp2f(mv[i] - M);
+      wsp[s] = e;
+      z += lv[i] * e;
+    }
   }
   z = wave_sum(z);
   if ((d & 63) == 0) red[1][d >> 6] = z;
   __syncthreads();
   const float Z = exp2f(sk - M) + red[1][0] + red[1][1];
-  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    const float* p = part_o + (base0 + (int64_t)s * A.Hq) * A.D + d;
-    const int64_t st = (int64_t)A.Hq * A.D;
-    o0 = fmaf(p[0], wsp[s], o0);
-    o1 = fmaf(p[st], wsp[s + 1], o1);
-    o2 = fmaf(p[2 * st], wsp[s + 2], o2);
-    o3 = fmaf(p[3 * st], wsp[s + 3], o3);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < MG_PRE; i += 2) {
+    if (i < S) o0 = fmaf(ov[i], wsp[i], o0);
+    if (i + 1 < S) o1 = fmaf(ov[i + 1], wsp[i + 1], o1);
   }
-  for (; s < S; ++s) o0 = fmaf(part_o[(base0 + (int64_t)s * A.Hq) * A.D + d], wsp[s], o0);
-  const float o = (o0 + o1) + (o2 + o3);
+  for (int s0 = MG_PRE; s0 < S; s0 += 32) {
+    float ot[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ot[i] = s0 + i < S ? po[(s0 + i) * ost] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (s0 + i < S) o0 = fmaf(ot[i], wsp[s0 + i], o0);
+  }
+  const float o = o0 + o1;
   store_out(A, ((int64_t)r * A.Hq + h) * A.D + d, o / Z);
   if (A.lse && d == 0) A.lse[(int64_t)r * A.Hq + h] = (M + log2f(Z)) * LN2;
 }

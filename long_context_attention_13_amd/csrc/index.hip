@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
       }
       const int n = rw.n[q];
       const float lam = n > 0 ? (float)A.k * (float)CH / (float)n : 0.f;
-      int rsel = (int)ceilf(lam + 6.0f * sqrtf(lam) + 8.0f);
+      int rsel = (int)ceilf(lam + 5.0f * sqrtf(lam) + 6.0f);
       rsel = rsel > 64 ? 64 : (rsel < 1 ? 1 : rsel);
       const uint64_t thr = ((uint64_t)readlane_u32((uint32_t)(cur >> 32), rsel - 1) << 32) |
                            readlane_u32((uint32_t)cur, rsel - 1);
