@@ -414,9 +414,16 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
 static int nq_of(int dt, int H, int Tq) { return (dt == DT_MXFP4 && H <= 8 && Tq > 1) ? 2 : 1; }
 
 static int choose_kpl(const IndexArgs& a, int nq) {
+  // the largest chunk (fewer candidates for the select kernel) that still
+  // gives at least 2048 wavefronts and keeps the expected top-k count of a
+  // full-length chunk (lambda) low enough for the per-chunk rank to stay <= 64
   const int64_t groups = (int64_t)a.B * ((a.Tq + nq - 1) / nq);
-  const int64_t waves16 = groups * ((a.N_cap + 1023) / 1024);
-  return waves16 >= 1024 ? 16 : 4;
+  for (int kpl : {32, 16}) {
+    const int64_t ch = 64 * kpl;
+    const double lam = (double)a.k * (double)ch / (double)(a.N_cap > 0 ? a.N_cap : 1);
+    if (groups * ((a.N_cap + ch - 1) / ch) * 4 >= 2048 && lam <= 24.0) return kpl;
+  }
+  return 4;
 }
 
 size_t index_ws_bytes(int B, int Tq, int H, int d, int64_t N_cap, int k, int dt) {
@@ -448,7 +455,11 @@ static hipError_t launch_t(const IndexArgs& a, hipStream_t s) {
 
 template <int DT, int HP, int NQ>
 static hipError_t launch_k(const IndexArgs& a, hipStream_t s) {
-  return choose_kpl(a, NQ) == 16 ? launch_t<DT, 16, HP, NQ>(a, s) : launch_t<DT, 4, HP, NQ>(a, s);
+  switch (choose_kpl(a, NQ)) {
+    case 32: return launch_t<DT, 32, HP, NQ>(a, s);
+    case 16: return launch_t<DT, 16, HP, NQ>(a, s);
+    default: return launch_t<DT, 4, HP, NQ>(a, s);
+  }
 }
 
 hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
