@@ -6,9 +6,10 @@
 //  重度壓縮注意力 (HCA): the same at 128x; 架構實現: most KV entries in FP8, the
 //  indexer in FP4.]
 //
-// One workgroup pools one block of m raw tokens: D threads (one per channel),
-// the m gate weights are formed once in LDS, each thread accumulates its
-// channel over the m tokens in fp32 (coalesced row reads), and the encoder
+// One workgroup pools one block of m raw tokens: the m gate weights are
+// formed once in LDS, token rows are read in 16-byte pieces by token groups
+// of threads and accumulated in fp32, the group partials are summed in LDS,
+// and the encoder
 // runs on the pooled row while it is still in registers: a wavefront is
 // exactly one 64-channel FP8 scale group, a half wavefront one 32-channel MX
 // block.  The kernel is HBM-bound (every raw token read once).
@@ -16,34 +17,55 @@
 
 namespace lca {
 
+// 128 threads per block.  For the pooling sum, thread t reads 16-byte pieces
+// (8 bf16 or 4 fp32 channels) of the tokens of its token group: chunk
+// t % NCK of a row, tokens t / NCK, t / NCK + G, ...; all of a thread's token
+// loads of a batch are issued before the gate softmax.  The G group partials
+// are then added in LDS in group order, and thread d < D encodes channel d.
+constexpr int PE_THREADS = 128;
+
 template <int XDT, int ODT, int D>
-__global__ __launch_bounds__(D) void pool_encode_kernel(CompressArgs a) {
+__global__ __launch_bounds__(PE_THREADS) void pool_encode_kernel(CompressArgs a) {
+  constexpr int CPL = XDT == DT_F32 ? 4 : 8;    // channels per 16-byte piece
+  constexpr int NCK = D / CPL;                  // pieces per token row
+  constexpr int G = PE_THREADS / NCK;           // token groups
+  constexpr int TB = 16;                        // token loads in flight per thread and batch
   const int b = blockIdx.y;
   const int i = blockIdx.x;
-  if (i >= a.nblk[b]) return;
+  const int nblk = a.nblk[b];
+  const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * a.m;
+  if (i >= nblk) return;
   const int tid = threadIdx.x;
+  const int ck = tid % NCK, grp = tid / NCK;
   const int m = a.m;
-  const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * m;
 
   __shared__ float wgt[1024];
-  __shared__ float red[2][D / WAVE];
+  __shared__ float red[2][PE_THREADS / WAVE];
+  __shared__ __align__(16) float part[G][D];
 
-  // gate logits + positional bias, block max
-  const float* g = a.gate + (int64_t)b * a.x_rows + tok0;
+  const char* xrow = (const char*)a.x + (((int64_t)b * a.x_rows + tok0) * D + ck * CPL) * (XDT == DT_F32 ? 4 : 2);
+  const int64_t rstride = (int64_t)D * (XDT == DT_F32 ? 4 : 2);
+  int4 xv[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    const int u = grp + t * G;
+    xv[t] = u < m ? *(const int4*)(xrow + u * rstride) : make_int4(0, 0, 0, 0);
+  }
+
+  // gate logits + positional bias, block max and sum
+  const float* gp = a.gate + (int64_t)b * a.x_rows + tok0;
   float mx = -INFINITY;
-  for (int u = tid; u < m; u += D) {
-    float v = g[u] + a.bias[u];
+  for (int u = tid; u < m; u += PE_THREADS) {
+    const float v = gp[u] + a.bias[u];
     wgt[u] = v;
     mx = fmaxf(mx, v);
   }
   mx = wave_max(mx);
   if ((tid & 63) == 0) red[0][tid >> 6] = mx;
   __syncthreads();
-  mx = red[0][0];
-#pragma unroll
-  for (int w = 1; w < D / WAVE; ++w) mx = fmaxf(mx, red[0][w]);
+  mx = fmaxf(red[0][0], red[0][1]);
   float z = 0.0f;
-  for (int u = tid; u < m; u += D) {
+  for (int u = tid; u < m; u += PE_THREADS) {
     const float e = expf(wgt[u] - mx);
     wgt[u] = e;
     z += e;
@@ -51,25 +73,59 @@ __global__ __launch_bounds__(D) void pool_encode_kernel(CompressArgs a) {
   z = wave_sum(z);
   if ((tid & 63) == 0) red[1][tid >> 6] = z;
   __syncthreads();
-  z = red[1][0];
-#pragma unroll
-  for (int w = 1; w < D / WAVE; ++w) z += red[1][w];
+  z = red[1][0] + red[1][1];
   const float inv_z = 1.0f / z;
 
-  // pooled channel tid
-  float c = 0.0f;
-  if (XDT == DT_F32) {
-    const float* x = (const float*)a.x + ((int64_t)b * a.x_rows + tok0) * D + tid;
-    for (int u = 0; u < m; ++u) c = fmaf(wgt[u] * inv_z, x[(int64_t)u * D], c);
-  } else {
-    const uint16_t* x = (const uint16_t*)a.x + ((int64_t)b * a.x_rows + tok0) * D + tid;
-    for (int u = 0; u < m; ++u) c = fmaf(wgt[u] * inv_z, bf16_to_f32(x[(int64_t)u * D]), c);
+  // this group's share of CPL channels, its tokens in increasing order
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  auto add = [&](const int4& v, float w) {
+    if (XDT == DT_F32) {
+      acc[0] = fmaf(w, __int_as_float(v.x), acc[0]);
+      acc[1] = fmaf(w, __int_as_float(v.y), acc[1]);
+      acc[2] = fmaf(w, __int_as_float(v.z), acc[2]);
+      acc[3] = fmaf(w, __int_as_float(v.w), acc[3]);
+    } else {
+      const uint32_t q[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = fmaf(w, __uint_as_float(q[k] << 16), acc[2 * k]);
+        acc[2 * k + 1] = fmaf(w, __uint_as_float(q[k] & 0xFFFF0000u), acc[2 * k + 1]);
+      }
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    const int u = grp + t * G;
+    if (u < m) add(xv[t], wgt[u] * inv_z);
+  }
+  for (int t0 = TB; grp + t0 * G < m; t0 += TB) {
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int u = grp + (t0 + t) * G;
+      xv[t] = u < m ? *(const int4*)(xrow + u * rstride) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int u = grp + (t0 + t) * G;
+      if (u < m) add(xv[t], wgt[u] * inv_z);
+    }
   }
   if (m == 1) {
     // exact copy (weight is 1): keep the input bits
-    if (XDT == DT_F32) c = ((const float*)a.x)[((int64_t)b * a.x_rows + tok0) * D + tid];
-    else c = bf16_to_f32(((const uint16_t*)a.x)[((int64_t)b * a.x_rows + tok0) * D + tid]);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    add(xv[0], 1.0f);
   }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) part[grp][ck * CPL + c] = acc[c];
+  __syncthreads();
+  if (tid >= D) return;
+  float c = 0.f;
+#pragma unroll
+  for (int q = 0; q < G; ++q) c += part[q][tid];
+  if (m == 1) c = part[0][tid];
 
   const int64_t row = (int64_t)b * a.dst_rows + a.dst_row0[b] + i;
   if (a.pooled) a.pooled[((int64_t)b * a.nblk_max + i) * D + tid] = c;
@@ -102,8 +158,8 @@ __global__ __launch_bounds__(D) void pool_encode_kernel(CompressArgs a) {
 template <int XDT, int ODT>
 static hipError_t launch_d(const CompressArgs& a, hipStream_t s) {
   dim3 grid(a.nblk_max, a.B);
-  if (a.D == 64) hipLaunchKernelGGL((pool_encode_kernel<XDT, ODT, 64>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((pool_encode_kernel<XDT, ODT, 128>), grid, dim3(128), 0, s, a);
+  if (a.D == 64) hipLaunchKernelGGL((pool_encode_kernel<XDT, ODT, 64>), grid, dim3(PE_THREADS), 0, s, a);
+  else hipLaunchKernelGGL((pool_encode_kernel<XDT, ODT, 128>), grid, dim3(PE_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
