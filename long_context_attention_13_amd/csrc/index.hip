@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
   constexpr int CH = 64 * KPL;
   constexpr int RPW = KPL / 4;            // rounds per wavefront
   static_assert(KPL % 4 == 0, "four wavefronts share a chunk");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = blockIdx.x;
   const int g = blockIdx.y;
   __shared__ __align__(16) float tbuf[4][WBUF];
@@ -105,16 +105,19 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
   if (DT == DT_MXFP4) {
     MxQuery Q;
     mx_load_query<HP>(A, rw, Q);
+    MxW<HP, NQ> Wt;
+    mx_load_weights<HP, NQ>(wl, Wt);
     // two-stage pipeline: the next round's tiles load while this one is scored
+    const MxRows R = mx_rows(A, rw.b, min(jw, jl - 1));
     MxTiles cur, nxt;
-    mx_load_round(A, rw.b, min(jw, jl), jl, cur);
+    mx_load_round(A, R, min(jw, jl), jl, cur);
     uint32_t fix = 0;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       uint64_t kk[NQ];
       bool ix;
-      if (rr + 1 < RPW) mx_load_round(A, rw.b, min(jw + (rr + 1) * 64, jl), jl, nxt);
-      mx_score_round<HP, NQ>(A, rw, Q, cur, jw + rr * 64, tbuf[wave], wl, kk, ix);
+      if (rr + 1 < RPW) mx_load_round(A, R, min(jw + (rr + 1) * 64, jl), jl, nxt);
+      mx_score_round<HP, NQ>(A, rw, Q, cur, jw + rr * 64, tbuf[wave], Wt, kk, ix);
       if (rr + 1 < RPW) cur = nxt;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) kq[q][rr] = kk[q];

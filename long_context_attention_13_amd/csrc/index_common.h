@@ -73,61 +73,105 @@ __device__ __forceinline__ void mx_load_query(const IndexArgs& A, const Rows& rw
 struct MxTiles {
   int4 code[4];
   int sc[4];
-  uint32_t valid;   // bit t: this lane's tile-t operand is a real key block
   uint32_t kscale;  // the scale bytes of key j0 + lane (for the exactness envelope)
 };
 
-// Load the B operands of 4 MFMA tiles = 64 keys [j0, j0+64).  The loads are
-// unconditional (addresses clamped into the sequence's valid rows) so that
-// they all stay in flight; lanes outside the valid range are zeroed where the
-// operands are consumed.
-__device__ __forceinline__ void mx_load_round(const IndexArgs& A, int b, int j0, int jlim, MxTiles& T) {
+// Head weights of a wavefront's NQ rows in registers, as float64, zero for
+// heads >= H (wl: LDS weights [2][16], zero-filled beyond H).
+template <int HP, int NQ>
+struct MxW {
+  double w[NQ][HP];
+};
+template <int HP, int NQ>
+__device__ __forceinline__ void mx_load_weights(const float* wl, MxW<HP, NQ>& W) {
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int h = 0; h < HP; ++h) W.w[q][h] = (double)wl[q * 16 + h];
+}
+
+// The scale bytes of a key row as one word (d_I in {64, 128}: 2 or 4 bytes).
+__device__ __forceinline__ uint32_t mx_scale_word(const uint8_t* ks, int d) {
+  return d == 128 ? *(const uint32_t*)ks : (uint32_t)*(const uint16_t*)ks;
+}
+
+// A value that is uniform over the wavefront, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Uniform addresses of a wavefront's key rows: row `base` of sequence b (b and
+// base uniform over the wavefront) and the byte strides of the code and scale
+// rows.  Rows up to 2^18 past `base` are addressed with 24-bit offset
+// products.
+struct MxRows {
+  const uint8_t* code;
+  const uint8_t* scale;
+  int base;
+  uint32_t cb, sb;
+};
+__device__ __forceinline__ MxRows mx_rows(const IndexArgs& A, int b, int base) {
+  MxRows R;
+  const int64_t row = (int64_t)b * A.N_cap + base;
+  R.code = (const uint8_t*)A.ki + uniform_i64(row * (A.d / 2));
+  R.scale = A.ki_scale + uniform_i64(row * (A.d / 32));
+  R.base = base;
+  R.cb = (uint32_t)A.d / 2;
+  R.sb = (uint32_t)A.d / 32;
+  return R;
+}
+
+// Load the B operands of 4 MFMA tiles = 64 keys [j0, j0+64), rows relative to
+// R (R.base <= min(j0, jlim-1), j0 - R.base < 2^18).  The loads are
+// unconditional (rows clamped into [0, jlim)) so that they all stay in flight;
+// a lane past jlim scores a copy of the last row, which the caller's
+// eligibility test discards.  K blocks past d_I load block 0 (the query
+// operand is zero there, so they add nothing).
+__device__ __forceinline__ void mx_load_round(const IndexArgs& A, const MxRows& R, int j0, int jlim, MxTiles& T) {
   const int lane = threadIdx.x & 63;
   const int kb = lane >> 4;
-  const bool kbok = kb * 32 < A.d;
-  const int kbc = kbok ? kb : 0;
-  T.valid = 0;
+  const uint32_t kbc = kb * 32 < A.d ? kb : 0;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int j = j0 + t * 16 + (lane & 15);
-    const int jc = j < jlim ? j : jlim - 1;
-    const int64_t row = (int64_t)b * A.N_cap + jc;
-    const v4i v = __builtin_nontemporal_load((const v4i*)((const uint8_t*)A.ki + row * (A.d / 2) + kbc * 16));
+    const uint32_t jo = (uint32_t)(min(j0 + t * 16 + (lane & 15), jlim - 1) - R.base);
+    const v4i v = __builtin_nontemporal_load((const v4i*)(R.code + (__umul24(jo, R.cb) + kbc * 16u)));
     T.code[t] = make_int4(v[0], v[1], v[2], v[3]);
-    T.sc[t] = A.ki_scale[row * (A.d / 32) + kbc];
-    T.valid |= (uint32_t)(j < jlim && kbok) << t;
+    T.sc[t] = R.scale[__umul24(jo, R.sb) + kbc];
   }
-  {
-    const int j = j0 + lane;
-    const int64_t row = (int64_t)b * A.N_cap + (j < jlim ? j : jlim - 1);
-    const uint8_t* ks = A.ki_scale + row * (A.d / 32);
-    T.kscale = A.d == 128 ? *(const uint32_t*)ks : (uint32_t)*(const uint16_t*)ks;
-  }
+  const uint32_t jo = (uint32_t)(min(j0 + lane, jlim - 1) - R.base);
+  T.kscale = mx_scale_word(R.scale + __umul24(jo, R.sb), A.d);
+}
+
+// The same for a round anywhere in the sequence.
+__device__ __forceinline__ void mx_load_round(const IndexArgs& A, int b, int j0, int jlim, MxTiles& T) {
+  mx_load_round(A, mx_rows(A, b, min(j0, jlim - 1)), j0, jlim, T);
 }
 
 // Load the B operands of 4 MFMA tiles for an arbitrary list of entries: lane
 // e < cnt names entry jmine; tile t covers the entries of lanes t*16..t*16+15.
-// Loads stay unconditional (absent entries read row 0 and are masked).
+// Loads stay unconditional (absent entries read row 0; the caller's
+// eligibility test discards them).
 __device__ __forceinline__ void mx_load_gather(const IndexArgs& A, int b, int jmine, int cnt, MxTiles& T) {
   const int lane = threadIdx.x & 63;
   const int kb = lane >> 4;
-  const bool kbok = kb * 32 < A.d;
-  const int kbc = kbok ? kb : 0;
-  T.valid = 0;
+  const uint32_t kbc = kb * 32 < A.d ? kb : 0;
+  const int64_t row0 = (int64_t)b * A.N_cap;
+  const uint8_t* cbase = (const uint8_t*)A.ki + row0 * (A.d / 2);
+  const uint8_t* sbase = A.ki_scale + row0 * (A.d / 32);
+  const uint64_t cb = (uint32_t)A.d / 2, sb = (uint32_t)A.d / 32;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int src = t * 16 + (lane & 15);
     const int js = __shfl(jmine, src, WAVE);
-    const bool ok = src < cnt;
-    const int64_t row = (int64_t)b * A.N_cap + (ok ? js : 0);
-    const v4i v = *(const v4i*)((const uint8_t*)A.ki + row * (A.d / 2) + kbc * 16);
+    const uint64_t jo = (uint32_t)(src < cnt ? js : 0);
+    const v4i v = *(const v4i*)(cbase + jo * cb + kbc * 16u);
     T.code[t] = make_int4(v[0], v[1], v[2], v[3]);
-    T.sc[t] = A.ki_scale[row * (A.d / 32) + kbc];
-    T.valid |= (uint32_t)(ok && kbok) << t;
+    T.sc[t] = sbase[jo * sb + kbc];
   }
-  const int64_t row = (int64_t)b * A.N_cap + (lane < cnt ? jmine : 0);
-  const uint8_t* ks = A.ki_scale + row * (A.d / 32);
-  T.kscale = A.d == 128 ? *(const uint32_t*)ks : (uint32_t)*(const uint16_t*)ks;
+  const uint64_t jo = (uint32_t)(lane < cnt ? jmine : 0);
+  T.kscale = mx_scale_word(sbase + jo * sb, A.d);
 }
 
 __device__ __forceinline__ double mx_value(const uint8_t* codes, const uint8_t* scales, int i) {
@@ -165,46 +209,57 @@ __device__ __forceinline__ bool mx_exact(const MxQuery& Q, int kmin, int kmax) {
   return (Q.dq + kmax - kmin <= 9) && (Q.qmin + kmin >= 130) && (Q.qmax + kmax <= 368);
 }
 
+// Score one round of 64 keys for the wave's NQ rows.  Lane L ends with the
+// key of entry j0+L (0 when not eligible).  The float64 head combine is taken
+// in head order; each step is one fma, which equals multiply-then-add here
+// because the product of two floats is exact in float64.  Heads >= H carry a
+// zero weight and a zero dot and leave the sum unchanged (it is never -0).
+// wbuf: this wave's LDS transpose buffer (64*KROW floats).
 template <int HP, int NQ>
 __device__ __forceinline__ void mx_score_round(const IndexArgs& A, const Rows& rw, const MxQuery& Q,
-                                               const MxTiles& T, int j0, float* wbuf, const float* wl,
+                                               const MxTiles& T, int j0, float* wbuf, const MxW<HP, NQ>& W,
                                                uint64_t* key, bool& inexact) {
   const int lane = threadIdx.x & 63;
-  v8i av = {Q.a[0], Q.a[1], Q.a[2], Q.a[3], 0, 0, 0, 0};
+  const v8i av = {Q.a[0], Q.a[1], Q.a[2], Q.a[3], 0, 0, 0, 0};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const bool ok = (T.valid >> t) & 1u;
-    v8i bv = {ok ? T.code[t].x : 0, ok ? T.code[t].y : 0, ok ? T.code[t].z : 0, ok ? T.code[t].w : 0, 0, 0, 0, 0};
-    const int scb = ok ? T.sc[t] : 127;
+    const v8i bv = {T.code[t].x, T.code[t].y, T.code[t].z, T.code[t].w, 0, 0, 0, 0};
     v4f c = {0.f, 0.f, 0.f, 0.f};
-    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, Q.sa, 0, scb);
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, Q.sa, 0, T.sc[t]);
     float* dst = wbuf + (t * 16 + (lane & 15)) * KROW + 4 * (lane >> 4);
     *(float4*)dst = make_float4(c[0], c[1], c[2], c[3]);
   }
   // exponent envelope of this lane's key j0+lane from its own scale bytes
-  const uint32_t sw = T.kscale;
+  uint32_t sw = T.kscale;
+  if (A.d != 128) sw = (sw & 0xFFFFu) | ((sw & 0xFFu) * 0x01010000u);   // d_I = 64: repeat block 0
   int kmin = (int)(sw & 0xFFu), kmax = kmin;
 #pragma unroll
   for (int i = 1; i < 4; ++i) {
-    if (i * 32 < A.d) {
-      const int v = (int)((sw >> (8 * i)) & 0xFFu);
-      kmin = min(kmin, v);
-      kmax = max(kmax, v);
-    }
+    const int v = (int)((sw >> (8 * i)) & 0xFFu);
+    kmin = min(kmin, v);
+    kmax = max(kmax, v);
   }
   const bool exact = mx_exact(Q, kmin, kmax);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int j = j0 + lane;
-  const float* mine = wbuf + lane * KROW;
+  const float4* mine = (const float4*)(wbuf + lane * KROW);
+  float dv[NQ * HP];
+#pragma unroll
+  for (int i = 0; i < NQ * HP / 4; ++i) {
+    const float4 v = mine[i];
+    dv[4 * i] = v.x; dv[4 * i + 1] = v.y; dv[4 * i + 2] = v.z; dv[4 * i + 3] = v.w;
+  }
   inexact = false;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     double sc = 0.0;
 #pragma unroll
-    for (int h = 0; h < HP; ++h)
-      if (h < A.H) sc = combine_step(sc, (double)mine[q * HP + h], wl[q * 16 + h]);
+    for (int h = 0; h < HP; ++h) {
+      const float r = __int_as_float(max(__float_as_int(dv[q * HP + h]), 0));   // ReLU (-0 -> +0)
+      sc = fma(W.w[q][h], (double)r, sc);
+    }
     const bool elig = rw.r[q] >= 0 && j < rw.n[q];
     key[q] = elig ? score_key(sc) : 0ull;
     inexact |= elig && !exact;
@@ -576,13 +631,15 @@ struct StreamSrc {
   template <class F> __device__ void for_each(F&& f) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = rw.n[0];
+    MxW<HP, 1> W;
+    if (DT == DT_MXFP4) mx_load_weights<HP, 1>(wl, W);
     for (int j0 = wave * 64; j0 < n; j0 += SEL_THREADS) {
       uint64_t k0;
       if (DT == DT_MXFP4) {
         MxTiles T;
         bool ix;
         mx_load_round(*A, rw.b, j0, n, T);
-        mx_score_round<HP, 1>(*A, rw, Q, T, j0, tbuf + wave * WBUF, wl, &k0, ix);
+        mx_score_round<HP, 1>(*A, rw, Q, T, j0, tbuf + wave * WBUF, W, &k0, ix);
         if (ix) k0 = mx_score_exact(*A, rw.r[0], rw.b, j0 + lane, wl);
       } else {
         f32_score_round(*A, rw, j0, ql, wl, k0);

@@ -582,8 +582,10 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
   {
     MxTiles T;
     bool ix;
+    MxW<HP, 1> W;
+    mx_load_weights<HP, 1>(L.wl, W);
     mx_load_gather(A, rw.b, jm, nband, T);
-    mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, L.wl, &key, ix);
+    mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, W, &key, ix);
     if (ix) key = mx_score_exact(A, (int)r, rw.b, jm, L.wl);
     if (lane >= nband) key = 0;
   }
@@ -640,8 +642,10 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
       MxTiles T;
       bool ix;
       uint64_t k2;
+      MxW<HP, 1> W;
+      mx_load_weights<HP, 1>(L.wl, W);
       mx_load_gather(A, rw.b, je, cntr, T);
-      mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, L.wl, &k2, ix);
+      mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, W, &k2, ix);
       if (ix) k2 = mx_score_exact(A, (int)r, rw.b, je, L.wl);
       if (lane < cntr) sout[i0 + lane] = key_score(k2);
     }
