@@ -84,33 +84,45 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
   const int t0 = (g % groups_per_b) * NQ;
   rw.r[0] = rw.b * A.Tq + t0;
   rw.r[1] = (NQ == 2 && t0 + 1 < A.Tq) ? rw.r[0] + 1 : -1;
+  // everything that does not depend on the row lengths is requested before
+  // they arrive, in a fixed order: row lengths, head weights, the query
+  // operand, then the first round of key tiles (rows up to N_cap exist, and
+  // entries past a row's length are discarded by the eligibility test)
   rw.n[0] = A.n_elig[rw.r[0]];
-  rw.n[1] = rw.r[1] >= 0 ? A.n_elig[rw.r[1]] : 0;
+  rw.n[1] = A.n_elig[rw.r[1] >= 0 ? rw.r[1] : rw.r[0]];
+  const int wq = (threadIdx.x >> 4) & 1, wh = threadIdx.x & 15;
+  const int wrow = (wq < NQ && rw.r[wq] >= 0) ? rw.r[wq] : rw.r[0];
+  const float wv = A.w[(int64_t)wrow * A.H + (wh < A.H ? wh : 0)];
+  MxQueryRaw QR{};
+  if (DT == DT_MXFP4) QR = mx_query_issue<HP>(A, rw);
+  const int jbeg = c * CH;                  // < N_cap: the grid covers N_cap
+  const int jl = min((int)A.N_cap, jbeg + CH);
+  const int jw = jbeg + wave * RPW * 64;    // this wavefront's first entry
+  MxRows R{};
+  MxTiles cur, nxt;
+  if (DT == DT_MXFP4) {
+    R = mx_rows(A, rw.b, min(jw, jl - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    mx_load_round(A, R, min(jw, jl), jl, cur);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (rw.r[1] < 0) rw.n[1] = 0;
   // rows with few entries are done by the select kernel alone
   if (rw.n[0] <= NDIRECT) rw.n[0] = 0;
   if (rw.n[1] <= NDIRECT) rw.n[1] = 0;
   const int jlim = max(rw.n[0], rw.n[1]);
-  const int jbeg = c * CH;
   if (jbeg >= jlim) return;                 // uniform over the workgroup
-  const int jl = min(jlim, jbeg + CH);
-  const int jw = jbeg + wave * RPW * 64;    // this wavefront's first entry
 
-  if (threadIdx.x < 32) {
-    const int q = threadIdx.x >> 4, h = threadIdx.x & 15;
-    wl[threadIdx.x] = (q < NQ && rw.r[q] >= 0 && h < A.H) ? A.w[(int64_t)rw.r[q] * A.H + h] : 0.f;
-  }
+  if (threadIdx.x < 32) wl[threadIdx.x] = (wq < NQ && rw.r[wq] >= 0 && wh < A.H) ? wv : 0.f;
   __syncthreads();
 
   uint64_t kq[NQ][RPW];
   if (DT == DT_MXFP4) {
     MxQuery Q;
-    mx_load_query<HP>(A, rw, Q);
+    mx_query_finish(QR, Q);
     MxW<HP, NQ> Wt;
     mx_load_weights<HP, NQ>(wl, Wt);
     // two-stage pipeline: the next round's tiles load while this one is scored
-    const MxRows R = mx_rows(A, rw.b, min(jw, jl - 1));
-    MxTiles cur, nxt;
-    mx_load_round(A, R, min(jw, jl), jl, cur);
     uint32_t fix = 0;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
@@ -238,29 +250,71 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
   const float* ql = (const float*)A.qi + (int64_t)blockIdx.x * A.H * A.d;   // F32 query row (global)
 
   const int r = blockIdx.x;
-  // everything that does not depend on n_elig is requested at once: the row
-  // length, head weights and the per-chunk summaries
+  // the row length and head weights first (waits for them then do not wait
+  // for the larger requests behind), then the per-chunk summaries
+  const int n = A.n_elig[r];
+  const float wv = (threadIdx.x < (unsigned)A.H) ? A.w[(int64_t)r * A.H + threadIdx.x] : 0.f;
   constexpr int CPTH = MAXCH / SEL_THREADS;          // chunks per thread
   int cv[CPTH];
   uint64_t mv[CPTH], xv[CPTH], tv[CPTH];
   const bool cand_ok = NCH <= MAXCH;
+  const int64_t rc0 = (int64_t)r * NCH;                 // this row's first chunk slot
 #pragma unroll
   for (int i = 0; i < CPTH; ++i) {
     const int c = i * SEL_THREADS + threadIdx.x;
-    const int64_t cc = (int64_t)r * NCH + ((cand_ok && c < NCH) ? c : 0);
-    cv[i] = W.cnt[cc];
-    mv[i] = W.mex[cc];
-    xv[i] = W.cmax[cc];
-    tv[i] = W.cthr[cc];
+    const int cc = (cand_ok && c < NCH) ? c : 0;
+    cv[i] = W.cnt[rc0 + cc];
+    mv[i] = W.mex[rc0 + cc];
+    xv[i] = W.cmax[rc0 + cc];
+    tv[i] = W.cthr[rc0 + cc];
   }
-  const int n = A.n_elig[r];
+  // and, speculatively, the first SPEC slots of every chunk (SPEC: a power of
+  // two with NCH * SPEC <= CMAX, at least 8), copied by DMA straight into the
+  // candidate arrays at position c * SPEC + slot; chunks with more candidates
+  // are gathered again once the counts are known
+  int spec_sh = 3;
+  while (spec_sh < 7 && (NCH << (spec_sh + 1)) <= CMAX) ++spec_sh;
+  const int spec = 1 << spec_sh;
+  {
+    // a fixed number of copies per wavefront (all CMAX slots; slots past
+    // NCH*SPEC repeat the last real one and are never read), so that waits
+    // on the earlier requests stay exact
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nst = cand_ok ? NCH << spec_sh : 4;          // staged slots
+    const uint64_t* krow = W.ckey + (cand_ok ? rc0 * CAP : 0);
+    const int32_t* jrow = W.cidx + (cand_ok ? rc0 * CAP : 0);
+    // keys: 128 per instruction (2 per lane); indices: 256 (4 per lane)
+#pragma unroll
+    for (int t = 0; t < CMAX / 128 / SEL_WAVES; ++t) {
+      const int q = wave + t * SEL_WAVES;
+      const int i = min(q * 128 + 2 * lane, nst - 2);
+      const uint32_t a = (uint32_t)(i >> spec_sh) * CAP + (i & (spec - 1));
+      __builtin_amdgcn_global_load_lds((const void*)(krow + a), (void*)(ckey_l + q * 128), 16, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < CMAX / 256 / SEL_WAVES; ++t) {
+      const int q = wave + t * SEL_WAVES;
+      const int i = min(q * 256 + 4 * lane, nst - 4);
+      const uint32_t a = (uint32_t)(i >> spec_sh) * CAP + (i & (spec - 1));
+      __builtin_amdgcn_global_load_lds((const void*)(jrow + a), (void*)(cidx_l + q * 256), 16, 0, 0);
+    }
+  }
+  for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
+  if (threadIdx.x == 0) { S.bcast[6] = 0; S.bcast[7] = 0; }
   const int kk = n < A.k ? n : A.k;
   int32_t* out = A.idx_out + (int64_t)r * A.k;
   double* sout = A.score_out ? A.score_out + (int64_t)r * A.k : nullptr;
 
-  if (threadIdx.x < 32) wl[threadIdx.x] = (threadIdx.x < (unsigned)A.H) ? A.w[(int64_t)r * A.H + threadIdx.x] : 0.f;
-  __syncthreads();
-
+  const int nch = (n + CH - 1) / CH;
+  const bool cand_path = n > A.k && n > NDIRECT && nch <= MAXCH && cand_ok;
+  if (!cand_path) {
+    // the slot copies must land before the region is reused; the weights
+    // are only needed by the re-scoring paths
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x < 32) wl[threadIdx.x] = wv;
+    __syncthreads();
+  }
   if (n <= A.k) {
     // every eligible entry is selected
     for (int i = threadIdx.x; i < A.k; i += SEL_THREADS) out[i] = i < n ? i : -1;
@@ -268,108 +322,147 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
     return;
   }
   bool done = false;
-  const int nch = (n + CH - 1) / CH;
-  if (n > NDIRECT && nch <= MAXCH && cand_ok) {
+  if (cand_path) {
     // ---------------- candidate path ----------------
-    // chunk offsets, and the key range [gmin, gmax] of all candidates
-    int bad = 0, carry = 0;
-    uint64_t gmax = 0, gmin = ~0ull;
-#pragma unroll
-    for (int i = 0; i < CPTH; ++i) {
-      const int c = i * SEL_THREADS + threadIdx.x;
-      int v = c < nch ? cv[i] : 0;
-      if (v < 0) { bad = 1; v = 0; }
-      if (v > 0) { gmax = xv[i] > gmax ? xv[i] : gmax; gmin = tv[i] < gmin ? tv[i] : gmin; }
-      int tot;
-      const int ex = block_scan(v, &tot, S);
-      if (c < nch) S.off[c] = carry + ex;
-      carry += tot;
+    // chunk offsets, the key range [gmin, gmax] of all candidates and the
+    // flags (a chunk over its slots: bit 0; a chunk over the speculative
+    // slots: bit 1), in one exchange of per-wavefront partials
+    static_assert(CPTH == 1, "one chunk per thread");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c0 = threadIdx.x;
+    int v = c0 < nch ? cv[0] : 0;
+    const bool bad_c = v < 0;
+    if (bad_c) v = 0;
+    const uint64_t bal_bad = __ballot(bad_c), bal_over = __ballot(v > spec);
+    const int incl = wave_incl_scan_dpp(v);
+    const uint64_t wmx = wave_max_u64_dpp(v > 0 ? xv[0] : 0ull);
+    const uint64_t wmn = wave_min_u64_dpp(v > 0 ? tv[0] : ~0ull);
+    if (lane == 63) S.scan[wave] = (uint32_t)incl;
+    if (lane == 0) {
+      S.red64[0][wave] = wmx;
+      S.red64[1][wave] = wmn;
+      if (bal_bad | bal_over) atomicOr(&S.bcast[7], (bal_bad ? 1 : 0) | (bal_over ? 2 : 0));
     }
-    const int total = carry;
-    if (threadIdx.x == 0) S.off[nch] = total;
-    block_minmax_u64(gmax, gmin, S);
-    bad = __syncthreads_or(bad);
-    if (!bad && total <= CMAX && total >= kk && gmax >= gmin) {
+    __syncthreads();
+    if (wave == 0) {
+      // one wavefront combines the per-wavefront partials
+      const int t = lane < SEL_WAVES ? (int)S.scan[lane] : 0;
+      const int ti = wave_incl_scan_dpp(t);
+      const uint64_t gx = wave_max_u64_dpp(lane < SEL_WAVES ? S.red64[0][lane] : 0ull);
+      const uint64_t gn = wave_min_u64_dpp(lane < SEL_WAVES ? S.red64[1][lane] : ~0ull);
+      if (lane < SEL_WAVES) S.woff[lane] = ti - t;
+      if (lane == SEL_WAVES - 1) { S.bcast[4] = ti; S.bcast64[1] = gx; S.bcast64[2] = gn; }
+    }
+    __syncthreads();
+    const int total = S.bcast[4];
+    const uint64_t gmax = S.bcast64[1], gmin = S.bcast64[2];
+    const int flags = S.bcast[7];
+    if (c0 < nch) S.off[c0] = (int)S.woff[wave] + incl - v;
+    if (c0 == 0) S.off[nch] = total;
+    __builtin_amdgcn_s_waitcnt(0);            // this wavefront's slot copies have landed
+    __syncthreads();
+    if (!(flags & 1) && total <= CMAX && total >= kk && gmax >= gmin) {
+      // Every thread holds up to LB candidates in registers: item i =
+      // u*SEL_THREADS + tid in candidate order (ascending entry index).
+      uint64_t bk[LB];
+      int32_t bj[LB];
+      uint32_t vm = 0;
+      if (!(flags & 2)) {
+        // staged layout (slot c*SPEC + e of chunk c): valid when e < count
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          const int i = u * SEL_THREADS + threadIdx.x;
+          const int c = i >> spec_sh, e = i & (spec - 1);
+          const int cc = c < nch ? c : 0;
+          const bool ok = c < nch && e < S.off[cc + 1] - S.off[cc];
+          bk[u] = ckey_l[i];
+          bj[u] = cidx_l[i];
+          vm |= (uint32_t)ok << u;
+        }
+      } else {
+        // some chunk has more than SPEC candidates: gather all of them in
+        // dense order; a chunk map (candidate slot -> chunk, written one
+        // chunk per wavefront into the bitmap area) gives each its address
+        uint16_t* cmap = (uint16_t*)S.bitmap;
+#pragma unroll 1
+        for (int c = wave; c < nch; c += SEL_WAVES) {
+          const int o = S.off[c], cnt = S.off[c + 1] - o;
+          for (int e = lane; e < cnt; e += 64) cmap[o + e] = (uint16_t)c;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          const int i = u * SEL_THREADS + threadIdx.x;
+          const int c = i < total ? cmap[i] : 0;
+          const int64_t a = (rc0 + c) * CAP + (i < total ? i - S.off[c] : 0);
+          bk[u] = W.ckey[a];
+          bj[u] = W.cidx[a];
+          vm |= (uint32_t)(i < total) << u;
+        }
+      }
+      RegSrc src{bk, bj, vm};
       // first radix digit: the 11 bits below the common prefix of the range
       const int hb = gmax == gmin ? -1 : 63 - __clzll(gmax ^ gmin);
       int shift = hb + 1 > 11 ? hb + 1 - 11 : 0;
       const int nb = hb + 1 - shift;
       uint64_t mask = (hb + 1 >= 64) ? 0 : ~((1ull << (hb + 1)) - 1ull);
       uint64_t prefix = gmax & mask;
-      for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
+      if (nb > 0) src.for_each([&](uint64_t kv, int) { atomicAdd(&S.hist[(kv >> shift) & ((1ull << nb) - 1ull)], 1u); });
       __syncthreads();
-      // copy the candidates into LDS (one batch of loads in flight) and
-      // histogram the first digit on the way; a chunk map (candidate slot ->
-      // chunk, written one chunk per wavefront into the bitmap area, which the
-      // candidate path does not use) gives each slot its source address
-      uint16_t* cmap = (uint16_t*)S.bitmap;
-      {
-        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll 1
-        for (int c = wave; c < nch; c += SEL_WAVES) {
-          const int o = S.off[c], cnt = S.off[c + 1] - o;
-          for (int e = lane; e < cnt; e += 64) cmap[o + e] = (uint16_t)c;
-        }
-      }
-      __syncthreads();
-      {
-        uint64_t bk[LB];
-        int32_t bj[LB];
-#pragma unroll
-        for (int u = 0; u < LB; ++u) {
-          const int i = u * SEL_THREADS + threadIdx.x;
-          const int c = i < total ? cmap[i] : 0;
-          const int64_t a = i < total ? ((int64_t)r * NCH + c) * CAP + (i - S.off[c]) : 0;
-          bk[u] = W.ckey[a];
-          bj[u] = W.cidx[a];
-        }
-#pragma unroll
-        for (int u = 0; u < LB; ++u) {
-          const int i = u * SEL_THREADS + threadIdx.x;
-          if (i < total) {
-            ckey_l[i] = bk[u];
-            cidx_l[i] = bj[u];
-            if (nb > 0) atomicAdd(&S.hist[(bk[u] >> shift) & ((1ull << nb) - 1ull)], 1u);
-          }
-        }
-      }
-      __syncthreads();
-      LdsSrc src{ckey_l, cidx_l, total};
       Thr th;
       th.Tj = 0x7FFFFFFF;
       int rem = kk, ties = 0;
-      bool have = false;
+      bool have = false, tie_break = false;
       if (nb == 0) {
         // every candidate has the same key
-        th.T = gmax; th.low = 0; ties = rem; have = true;
+        th.T = gmax; th.low = 0; ties = rem; have = true; tie_break = total > rem;
       } else {
-        // digit holding the rem-th largest (bins counted from the top)
-        constexpr int BPT = 2048 / SEL_THREADS;
-        const int nbins = 1 << nb;
-        const int top = nbins - 1 - BPT * (int)threadIdx.x;
-        int cnt[BPT], mine = 0;
+        // digit holding the rem-th largest, found by one wavefront: lane l
+        // holds the 32 bins nbins-1-32l .. nbins-32-32l (counted from the top)
+        if (wave == 0) {
+          const int nbins = 1 << nb;
+          const int hi = nbins - 1 - 32 * lane;
+          uint32_t hb32[32];
+          if (hi >= 31) {
+            const uint4* hp = (const uint4*)&S.hist[hi - 31];
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) { cnt[i] = (top - i >= 0) ? (int)S.hist[top - i] : 0; mine += cnt[i]; }
-        int tot;
-        int above = block_scan(mine, &tot, S);
+            for (int q = 0; q < 8; ++q) {
+              const uint4 h = hp[q];
+              hb32[4 * q] = h.x; hb32[4 * q + 1] = h.y; hb32[4 * q + 2] = h.z; hb32[4 * q + 3] = h.w;
+            }
+          } else {
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-          if (top - i >= 0 && above < rem && above + cnt[i] >= rem) { S.bcast[0] = top - i; S.bcast[1] = above; S.bcast[2] = cnt[i]; }
-          above += cnt[i];
+            for (int q = 0; q < 32; ++q) hb32[q] = (hi - 31 + q >= 0) ? S.hist[hi - 31 + q] : 0u;
+          }
+          int cnt32 = 0;
+#pragma unroll
+          for (int q = 0; q < 32; ++q) cnt32 += (int)hb32[q];
+          const int inc = wave_incl_scan_dpp(cnt32);
+          if (inc - cnt32 < rem && inc >= rem) {
+            int above = inc - cnt32;
+            bool found = false;
+#pragma unroll
+            for (int q = 31; q >= 0; --q) {
+              const int cb = (int)hb32[q];
+              if (!found && above + cb >= rem) {
+                S.bcast[0] = hi - 31 + q; S.bcast[1] = above; S.bcast[2] = cb;
+                found = true;
+              }
+              above += cb;
+            }
+          }
         }
         __syncthreads();
         int dsel = S.bcast[0], indig = S.bcast[2];
         rem -= S.bcast[1];
         prefix |= (uint64_t)dsel << shift;
         mask |= (uint64_t)((1u << nb) - 1u) << shift;
-        __syncthreads();
         // narrow down until the threshold is exact
         while (!have) {
           if (indig == rem) {                     // the whole bin is in
             th.T = prefix; th.low = shift; ties = rem; have = true;
-            if (shift == 0) th.low = 0;
           } else if (shift == 0) {                // a full key with more ties than needed
-            th.T = prefix; th.low = 0; ties = rem; have = true;
+            th.T = prefix; th.low = 0; ties = rem; have = true; tie_break = true;
           } else if (indig <= 64) {               // few items: rank them exactly
             resolve_bin(src, prefix, mask, rem, S);
             // exact: the rem-th item of the bin is (T, Tj); ties up to Tj are in
@@ -381,7 +474,6 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
             radix_digit(src, prefix, mask, shift, nb2, rem, S);
             dsel = S.bcast[0]; indig = S.bcast[2];
             const int above2 = S.bcast[1];
-            __syncthreads();
             rem -= above2;
             prefix |= (uint64_t)dsel << shift;
             mask |= (uint64_t)((1u << nb2) - 1u) << shift;
@@ -389,24 +481,20 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
         }
       }
       // certification: no excluded entry may reach the threshold
-      int unsafe = 0;
-#pragma unroll
-      for (int i = 0; i < CPTH; ++i) {
-        const int c = i * SEL_THREADS + threadIdx.x;
-        const uint64_t m = mv[i];
-        if (c < nch && m != 0) {
-          if (th.low > 0) unsafe |= (m >> th.low) >= (th.T >> th.low);
-          else unsafe |= m >= th.T;
-        }
+      bool unsafe = false;
+      if (c0 < nch && mv[0] != 0) {
+        if (th.low > 0) unsafe = (mv[0] >> th.low) >= (th.T >> th.low);
+        else unsafe = mv[0] >= th.T;
       }
-      unsafe = __syncthreads_or(unsafe);
-      if (!unsafe) {
-        emit_in_order(ckey_l, cidx_l, total, th, ties, A.k, out, sout, S);
-        done = true;
-      }
+      done = emit_regs(bk, bj, vm, th, tie_break ? ties : -1, unsafe, A.k, out, sout, S);
     }
   }
-  if (!done) select_streamed<DT, HP>(A, r, n, kk, out, sout, S, tbuf, wl, ql, false);
+  if (!done) {
+    __syncthreads();
+    if (threadIdx.x < 32) wl[threadIdx.x] = wv;
+    __syncthreads();
+    select_streamed<DT, HP>(A, r, n, kk, out, sout, S, tbuf, wl, ql, false);
+  }
 }
 
 // ------------------------------------------------------------------------

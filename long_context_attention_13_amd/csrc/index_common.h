@@ -38,23 +38,35 @@ struct MxQuery {
   int dq, qmin, qmax;
 };
 
+// The query operand is loaded in two steps: mx_query_issue requests this
+// lane's bytes (unconditionally, from row 0 where the lane has no query block,
+// so the request count is fixed), mx_query_finish masks them and derives the
+// exponent spread.
+struct MxQueryRaw {
+  int4 v;
+  int sa;
+  bool valid;
+};
 template <int HP>
-__device__ __forceinline__ void mx_load_query(const IndexArgs& A, const Rows& rw, MxQuery& Q) {
+__device__ __forceinline__ MxQueryRaw mx_query_issue(const IndexArgs& A, const Rows& rw) {
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, kb = lane >> 4;
   const int q = row / HP, h = row % HP;
   const int rq = q == 0 ? rw.r[0] : rw.r[1];     // (no dynamic indexing: keeps rw in registers)
-  const bool valid = (q < 2) && rq >= 0 && h < A.H && kb * 32 < A.d;
-  Q.a[0] = Q.a[1] = Q.a[2] = Q.a[3] = 0;
-  Q.sa = 127;
-  int smin = 1000, smax = -1000;
-  if (valid) {
-    const int64_t qrow = (int64_t)rq * A.H + h;
-    const int4 v = *(const int4*)((const uint8_t*)A.qi + qrow * (A.d / 2) + kb * 16);
-    Q.a[0] = v.x; Q.a[1] = v.y; Q.a[2] = v.z; Q.a[3] = v.w;
-    Q.sa = A.qi_scale[qrow * (A.d / 32) + kb];
-    smin = smax = Q.sa;
-  }
+  MxQueryRaw R;
+  R.valid = (q < 2) && rq >= 0 && h < A.H && kb * 32 < A.d;
+  const int64_t qrow = R.valid ? (int64_t)rq * A.H + h : 0;
+  const int kbc = R.valid ? kb : 0;
+  R.v = *(const int4*)((const uint8_t*)A.qi + qrow * (A.d / 2) + kbc * 16);
+  R.sa = A.qi_scale[qrow * (A.d / 32) + kbc];
+  return R;
+}
+
+__device__ __forceinline__ void mx_query_finish(const MxQueryRaw& R, MxQuery& Q) {
+  const bool valid = R.valid;
+  Q.a[0] = valid ? R.v.x : 0; Q.a[1] = valid ? R.v.y : 0; Q.a[2] = valid ? R.v.z : 0; Q.a[3] = valid ? R.v.w : 0;
+  Q.sa = valid ? R.sa : 127;
+  int smin = valid ? Q.sa : 1000, smax = valid ? Q.sa : -1000;
   // per (query, head): spread of the block exponents over the 4 lanes of a row
   int rmin = smin, rmax = smax;
   rmin = min(rmin, __shfl_xor(rmin, 16, WAVE)); rmax = max(rmax, __shfl_xor(rmax, 16, WAVE));
@@ -68,6 +80,11 @@ __device__ __forceinline__ void mx_load_query(const IndexArgs& A, const Rows& rw
     gmax = max(gmax, __shfl_xor(gmax, o, WAVE));
   }
   Q.dq = dq; Q.qmin = gmin; Q.qmax = gmax;
+}
+
+template <int HP>
+__device__ __forceinline__ void mx_load_query(const IndexArgs& A, const Rows& rw, MxQuery& Q) {
+  mx_query_finish(mx_query_issue<HP>(A, rw), Q);
 }
 
 struct MxTiles {
@@ -349,6 +366,12 @@ struct SelShared {
   uint32_t bitmap[BITMAP_BITS / 32];
   uint64_t rkey[64];           // items of the threshold bin, resolved exactly
   int32_t rj[64];
+  uint32_t rank[64];
+  uint32_t woff[SEL_WAVES];        // exclusive prefix of per-wavefront counts
+  uint32_t ecnt[LB * SEL_WAVES];   // emission: items above the threshold per (pass, wavefront)
+  uint32_t epre[LB * SEL_WAVES];   // and their exclusive prefix
+  uint32_t ecnt2[LB * SEL_WAVES];  // tied items per (pass, wavefront)
+  uint32_t epre2[LB * SEL_WAVES];
   int nres;
   int bcast[8];
   uint64_t bcast64[4];
@@ -394,7 +417,7 @@ __device__ __forceinline__ int block_scan(int v, int* tot, SelShared& S) {
 // for_each(fn(key, j)).  Returns via S.bcast: [0] digit, [1] count above,
 // [2] count in digit.
 template <class Src>
-__device__ void radix_digit(Src& src, uint64_t prefix, uint64_t mask, int shift, int nb, int rem, SelShared& S) {
+__device__ __forceinline__ void radix_digit(Src& src, uint64_t prefix, uint64_t mask, int shift, int nb, int rem, SelShared& S) {
   constexpr int BPT = 2048 / SEL_THREADS;       // bins per thread
   const int nbins = 1 << nb;
   for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
@@ -475,8 +498,9 @@ __device__ __forceinline__ bool selected(const Thr& th, uint64_t key, int j) {
 // (key & mask) == prefix are gathered in LDS and the rem-th of them in the
 // order (key desc, j asc) is found by counting, per item, the items before it.
 template <class Src>
-__device__ void resolve_bin(Src& src, uint64_t prefix, uint64_t mask, int rem, SelShared& S) {
+__device__ __forceinline__ void resolve_bin(Src& src, uint64_t prefix, uint64_t mask, int rem, SelShared& S) {
   if (threadIdx.x == 0) S.nres = 0;
+  if (threadIdx.x < 64) S.rank[threadIdx.x] = 0;
   __syncthreads();
   src.for_each([&](uint64_t key, int j) {
     if (key != 0 && (key & mask) == prefix) {
@@ -486,18 +510,29 @@ __device__ void resolve_bin(Src& src, uint64_t prefix, uint64_t mask, int rem, S
   });
   __syncthreads();
   const int n = min(S.nres, 64);
-  if (threadIdx.x < 64) {
-    const int i = threadIdx.x;
-    int rank = 0;
-    const uint64_t ki = i < n ? S.rkey[i] : 0;
-    const int ji = i < n ? S.rj[i] : 0;
-    const uint32_t klo = (uint32_t)ki, khi = (uint32_t)(ki >> 32);
-    for (int m = 0; m < n; ++m) {
-      const uint64_t km = ((uint64_t)readlane_u32(khi, m) << 32) | readlane_u32(klo, m);
-      const int jm = (int)readlane_u32((uint32_t)ji, m);
-      rank += (km > ki) || (km == ki && jm < ji);
+  {
+    // thread (g, i): items before item i among items m = g*MPG .. g*MPG+MPG-1
+    constexpr int MPG = 64 / SEL_WAVES;
+    const int i = threadIdx.x & 63, g = threadIdx.x >> 6;
+    if (i < n) {
+      const uint64_t ki = S.rkey[i];
+      const int ji = S.rj[i];
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < MPG; ++t) {
+        const int m = g * MPG + t;
+        if (m < n) {
+          const uint64_t km = S.rkey[m];
+          cnt += (km > ki) || (km == ki && S.rj[m] < ji);
+        }
+      }
+      if (cnt) atomicAdd(&S.rank[i], (uint32_t)cnt);
     }
-    if (i < n && rank == rem - 1) { S.bcast64[0] = ki; S.bcast[3] = ji; }
+  }
+  __syncthreads();
+  if (threadIdx.x < n && (int)S.rank[threadIdx.x] == rem - 1) {
+    S.bcast64[0] = S.rkey[threadIdx.x];
+    S.bcast[3] = S.rj[threadIdx.x];
   }
   __syncthreads();
 }
@@ -608,14 +643,16 @@ __device__ void emit_sorted(Src& src, const Thr& th, int n, int k, int32_t* out,
   }
 }
 
-// Source over candidates held in registers.
-// Source over candidates held in LDS.
-struct LdsSrc {
-  const uint64_t* key;
-  const int32_t* j;
-  int n;
+// Candidates held in registers: item u of this thread is present when bit u
+// of vm is set.
+struct RegSrc {
+  uint64_t (&key)[LB];
+  int32_t (&j)[LB];
+  uint32_t vm;
   template <class F> __device__ __forceinline__ void for_each(F&& f) {
-    for (int i = threadIdx.x; i < n; i += SEL_THREADS) f(key[i], j[i]);
+#pragma unroll
+    for (int u = 0; u < LB; ++u)
+      if ((vm >> u) & 1u) f(key[u], j[u]);
   }
 };
 
@@ -679,66 +716,71 @@ __device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n
 // the selection flags of contiguous slices keeps that order, so no sorting is
 // needed.  Items equal to the threshold key are taken in array (= index)
 // order until `ties` of them are in.
-__device__ void emit_in_order(const uint64_t* key, const int32_t* jj, int total, const Thr& th, int ties, int k,
-                              int32_t* out, double* sout, SelShared& S) {
-  const int per = (total + SEL_THREADS - 1) / SEL_THREADS;
-  const int i0 = threadIdx.x * per, i1 = min(total, i0 + per);
-  if (th.low == 0 && th.Tj != 0x7FFFFFFF) {
-    // exact threshold (T, Tj): key > T, or key == T and j <= Tj
-    int nsel = 0;
-    for (int i = i0; i < i1; ++i) nsel += key[i] > th.T || (key[i] == th.T && jj[i] <= th.Tj);
-    int tot;
-    int pos = block_scan(nsel, &tot, S);
-    for (int i = i0; i < i1; ++i) {
-      const uint64_t kv = key[i];
-      if (kv > th.T || (kv == th.T && jj[i] <= th.Tj)) {
-        if (pos < k) {
-          out[pos] = jj[i];
-          if (sout) sout[pos] = key_score(kv);
-        }
-        ++pos;
-      }
+// Emission, in ascending candidate order, of the register-held items that th
+// selects, when no excluded entry is unsafe (block-wide OR of `unsafe`).  With
+// ties >= 0 (a full key T with more ties than places) the items equal to T
+// are taken in candidate order until `ties` of them are in.  Item i =
+// u*SEL_THREADS + tid belongs to pass u; one exchange of per-(pass, wavefront)
+// counts of items above the threshold and of tied items gives every item its
+// output position.  Returns false (nothing written) when unsafe.
+__device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_t (&bj)[LB], uint32_t vm,
+                                          const Thr& th, int ties, bool unsafe, int k, int32_t* out, double* sout,
+                                          SelShared& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t fa = 0, fe = 0;
+#pragma unroll
+  for (int u = 0; u < LB; ++u) {
+    bool a = false, e = false;
+    if ((vm >> u) & 1u) {
+      if (ties >= 0) { a = bk[u] > th.T; e = bk[u] == th.T; }
+      else a = selected(th, bk[u], bj[u]);
     }
-    for (int i = tot + threadIdx.x; i < k; i += SEL_THREADS) {
-      out[i] = -1;
-      if (sout) sout[i] = 0.0;
+    fa |= (uint32_t)a << u;
+    fe |= (uint32_t)e << u;
+    const uint64_t ba = __ballot(a), be = __ballot(e);
+    if (lane == 0) {
+      S.ecnt[u * SEL_WAVES + wave] = (uint32_t)__popcll(ba);
+      S.ecnt2[u * SEL_WAVES + wave] = (uint32_t)__popcll(be);
     }
-    return;
   }
-  int nt = 0;
-  for (int i = i0; i < i1; ++i) nt += (th.low == 0 && key[i] == th.T);
-  int tt;
-  int tie_before = block_scan(nt, &tt, S);
-  int nsel = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint64_t kv = key[i];
-    bool f;
-    if (th.low > 0) f = kv != 0 && (kv >> th.low) >= (th.T >> th.low);
-    else if (kv == th.T) { f = tie_before < ties; ++tie_before; }
-    else f = kv > th.T;
-    nsel += f;
+  if (unsafe) S.bcast[6] = 1;
+  __syncthreads();
+  if (S.bcast[6]) return false;
+  if (wave == 0) {
+    // exclusive prefixes over (pass, wavefront), two entries per lane
+    static_assert(LB * SEL_WAVES == 128, "two prefix entries per lane");
+    const int a0 = (int)S.ecnt[2 * lane], a1 = (int)S.ecnt[2 * lane + 1];
+    const int ia = wave_incl_scan_dpp(a0 + a1);
+    S.epre[2 * lane] = (uint32_t)(ia - a0 - a1);
+    S.epre[2 * lane + 1] = (uint32_t)(ia - a1);
+    const int e0 = (int)S.ecnt2[2 * lane], e1 = (int)S.ecnt2[2 * lane + 1];
+    const int ie = wave_incl_scan_dpp(e0 + e1);
+    S.epre2[2 * lane] = (uint32_t)(ie - e0 - e1);
+    S.epre2[2 * lane + 1] = (uint32_t)(ie - e1);
+    if (lane == 63) { S.bcast[5] = ia; S.bcast[2] = ie; }
   }
-  int tot;
-  int pos = block_scan(nsel, &tot, S);
-  tie_before -= nt;   // rewind for the write pass
-  for (int i = i0; i < i1; ++i) {
-    const uint64_t kv = key[i];
-    bool f;
-    if (th.low > 0) f = kv != 0 && (kv >> th.low) >= (th.T >> th.low);
-    else if (kv == th.T) { f = tie_before < ties; ++tie_before; }
-    else f = kv > th.T;
-    if (f) {
-      if (pos < k) {
-        out[pos] = jj[i];
-        if (sout) sout[pos] = key_score(kv);
+  __syncthreads();
+  const int tot = S.bcast[5] + (ties >= 0 ? min(S.bcast[2], ties) : 0);
+#pragma unroll
+  for (int u = 0; u < LB; ++u) {
+    const bool a = (fa >> u) & 1u, e = (fe >> u) & 1u;
+    const uint64_t ba = __ballot(a), be = __ballot(e);
+    if (a || e) {
+      const int pa = (int)S.epre[u * SEL_WAVES + wave] + lanes_below(ba);
+      int pe = 0;
+      if (ties >= 0) pe = (int)S.epre2[u * SEL_WAVES + wave] + lanes_below(be);
+      const int pos = pa + (ties >= 0 ? min(pe, ties) : 0);
+      if ((a || pe < ties) && pos < k) {
+        out[pos] = bj[u];
+        if (sout) sout[pos] = key_score(bk[u]);
       }
-      ++pos;
     }
   }
   for (int i = tot + threadIdx.x; i < k; i += SEL_THREADS) {
     out[i] = -1;
     if (sout) sout[i] = 0.0;
   }
+  return true;
 }
 
 // The prefill path (index_prefill.hip): many query rows per sequence.
