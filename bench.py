@@ -66,6 +66,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
+    ap.add_argument("--prefill-only", action="store_true", help="run only the chunked-prefill leg")
     ap.add_argument("--serial", action="store_true", help="run the decode step on one stream, eagerly")
     ap.add_argument("--no-graph", action="store_true", help="issue the three-stream step eagerly")
     ap.add_argument("--prefill-steps", type=int, default=5)
@@ -446,6 +447,9 @@ def main():
               f"note, not a measured path.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.prefill_only:
+        print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}))
+        return
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
