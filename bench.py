@@ -67,8 +67,9 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="run only the chunked-prefill leg")
-    ap.add_argument("--serial", action="store_true", help="run the decode step on one stream, eagerly")
-    ap.add_argument("--no-graph", action="store_true", help="issue the three-stream step eagerly")
+    ap.add_argument("--unbatched", action="store_true",
+                    help="issue the step as the nine single calls instead of the batched calls")
+    ap.add_argument("--no-graph", action="store_true", help="issue the steps eagerly instead of replaying a graph")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 3 times (a known-size kernel "
@@ -173,12 +174,24 @@ class Workload:
         self.ws_idx = torch.empty(lca.index_topk_ws(B, 1, H_I, d_I, N, self.k), dtype=torch.uint8, device=dev)
         self.ws_csa = torch.empty(max(lca.attend_ws(B, 1, Hq, D, self.k, 128), 16), dtype=torch.uint8, device=dev)
         self.ws_hca = torch.empty(max(lca.attend_ws(B, 1, Hq, D, N2, 256), 16), dtype=torch.uint8, device=dev)
-        # side streams (default priority) for the branches that do not depend on the indexer
-        self.s_csa = torch.cuda.Stream(device=dev)
-        self.s_hca = torch.cuda.Stream(device=dev)
-        self.ev_start = torch.cuda.Event()
-        self.ev_ent = torch.cuda.Event()
-        self.ev_hca = torch.cuda.Event()
+        # the batched form of the step: one compress launch for the three new blocks and one
+        # attention launch (+ one merge) for both branches; job arrays built once per copy
+        import ctypes
+        self.cjobs, self.ajobs, self._jobs = [], [], []
+        for c in range(copies):
+            cj = [lca.compress_job(self.win_csa, self.gate_csa, self.bias_csa, 4, self.csa_tok0, self.one,
+                                   self.csa_row0, 1, self.ent[c], lca.FP8E4M3, self.ent_sc[c]),
+                  lca.compress_job(self.win_keys, self.gate_i, self.bias_i, 4, self.csa_tok0, self.one,
+                                   self.csa_row0, 1, self.key[c], lca.MXFP4, self.key_sc[c]),
+                  lca.compress_job(self.win_hca, self.gate_hca, self.bias_hca, 128, self.hca_tok0, self.one,
+                                   self.hca_row0, 1, self.hca[c], lca.FP8E4M3, self.hca_sc[c])]
+            aj = [lca.attend_job(True, self.q_csa, self.ent[c], self.ent_sc[c], self.idx, self.win_csa, self.wb_csa,
+                                 self.wl, self.sink_csa, self.tau, self.out_csa, ws=self.ws_csa),
+                  lca.attend_job(False, self.q_hca, self.hca[c], self.hca_sc[c], self.n_hca, self.win_hca,
+                                 self.wb_hca, self.wl, self.sink_hca, self.tau, self.out_hca, ws=self.ws_hca)]
+            self._jobs.append((cj, aj))
+            self.cjobs.append((lca.CompressJob * 3)(*cj))
+            self.ajobs.append((lca.AttendJob * 2)(*aj))
         torch.cuda.synchronize()
 
     # -- the hot path ------------------------------------------------------
@@ -207,38 +220,18 @@ class Workload:
         self.index(c)
         self.attend(c)
 
-    def step_streams(self, c, ev_idx=None):
-        """The same step with its independent branches on separate streams: the CSA
-        entry block on one side stream, HCA compression + HCA attention on another,
-        and the indexer keys -> indexer -> CSA attention chain on the current stream,
-        which joins both branches before the step ends."""
+    def step_batched(self, c, ev_idx=None):
+        """The same step in three library calls: compress_batch (CSA entry block, indexer key
+        block, HCA block), the indexer, attend_batch (CSA and HCA branches)."""
         import torch
         lca = self.lca
-        main = torch.cuda.current_stream()
-        self.ev_start.record(main)
-        self.s_csa.wait_event(self.ev_start)
-        self.s_hca.wait_event(self.ev_start)
-        with torch.cuda.stream(self.s_csa):
-            lca.csa_compress(self.win_csa, self.gate_csa, self.bias_csa, 4, self.csa_tok0, self.one, self.csa_row0,
-                             1, self.ent[c], lca.FP8E4M3, self.ent_sc[c])
-            self.ev_ent.record(self.s_csa)
-        with torch.cuda.stream(self.s_hca):
-            lca.hca_compress(self.win_hca, self.gate_hca, self.bias_hca, 128, self.hca_tok0, self.one,
-                             self.hca_row0, 1, self.hca[c], lca.FP8E4M3, self.hca_sc[c])
-            lca.hca_attend(self.q_hca, self.hca[c], self.hca_sc[c], self.n_hca, self.win_hca, self.wb_hca, self.wl,
-                           self.sink_hca, self.tau, self.out_hca, ws=self.ws_hca)
-            self.ev_hca.record(self.s_hca)
-        lca.csa_compress(self.win_keys, self.gate_i, self.bias_i, 4, self.csa_tok0, self.one, self.csa_row0, 1,
-                         self.key[c], lca.MXFP4, self.key_sc[c])
+        lca.compress_batch(self.cjobs[c])
         if ev_idx is not None:
-            ev_idx[0].record(main)
+            ev_idx[0].record(torch.cuda.current_stream())
         self.index(c)
         if ev_idx is not None:
-            ev_idx[1].record(main)
-        main.wait_event(self.ev_ent)
-        lca.sparse_mqa_attend(self.q_csa, self.ent[c], self.ent_sc[c], self.idx, self.win_csa, self.wb_csa, self.wl,
-                              self.sink_csa, self.tau, self.out_csa, ws=self.ws_csa)
-        main.wait_event(self.ev_hca)
+            ev_idx[1].record(torch.cuda.current_stream())
+        lca.attend_batch(self.ajobs[c])
 
     # -- algorithmic bytes -------------------------------------------------
     def index_bytes(self) -> float:
@@ -462,20 +455,19 @@ def main():
     wl = Workload(args.copies)
     stream = torch.cuda.current_stream()
     C = args.copies
-    run = wl.step if args.serial else wl.step_streams
+    run = wl.step if args.unbatched else wl.step_batched
     for s in range(args.warmup):
         run(s % C)
     torch.cuda.synchronize()
     graphs = None
-    if not args.serial and not args.no_graph:
-        # one captured graph holds C consecutive three-stream steps (one per
-        # cache copy, each joined before the next starts); replaying it issues
-        # C steps without per-launch host work
+    if not args.no_graph:
+        # one captured graph holds C consecutive steps (one per cache copy);
+        # replaying it issues C steps without per-launch host work
         args.steps = -(-args.steps // C) * C
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for c in range(C):
-                wl.step_streams(c)
+                run(c)
         graphs = [g]
         for _ in range(max(1, args.warmup // C)):
             g.replay()
@@ -492,14 +484,14 @@ def main():
         if graphs is not None:
             if c == 0:
                 graphs[0].replay()
-        elif args.serial:
+        elif args.unbatched:
             wl.compress(c)
             ev_idx[s][0].record(stream)
             wl.index(c)
             ev_idx[s][1].record(stream)
             wl.attend(c)
         else:
-            wl.step_streams(c, ev_idx[s])
+            wl.step_batched(c, ev_idx[s])
     end.record(stream)
     t_host = time.perf_counter() - t_host
     torch.cuda.synchronize()
@@ -509,11 +501,14 @@ def main():
         # the indexer call on its stream
         for s in range(args.steps):
             c = s % C
-            wl.compress(c)
-            ev_idx[s][0].record(stream)
-            wl.index(c)
-            ev_idx[s][1].record(stream)
-            wl.attend(c)
+            if args.unbatched:
+                wl.compress(c)
+                ev_idx[s][0].record(stream)
+                wl.index(c)
+                ev_idx[s][1].record(stream)
+                wl.attend(c)
+            else:
+                wl.step_batched(c, ev_idx[s])
         torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
@@ -540,7 +535,8 @@ def main():
                                "CSA 262144 FP8 entries + MXFP4 indexer (8x128) top-1024, HCA 8192 FP8 entries, "
                                "window 128, 64 query heads, head_dim 128",
                    "global_batch": wl.B, "seq_len": int(wl.L.max()), "parallelism": "single GPU"},
-        "schedule": ("serial" if args.serial else "3 streams (CSA entries | HCA branch | keys->indexer->CSA)")
+        "schedule": ("9 single calls" if args.unbatched else
+                     "compress_batch (3 blocks) -> indexer -> attend_batch (CSA + HCA)")
                     + (f", graph of {C} steps replayed" if graphs is not None else ", eager"),
         "host_issue_us_per_step": round(t_host / args.steps * 1e6, 1),
         "step_hbm_gbs": round(step_gbs, 1),

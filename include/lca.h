@@ -71,7 +71,7 @@ typedef enum lca_dtype {
   LCA_MXFP4 = 3
 } lca_dtype;
 
-#define LCA_ABI_VERSION 1
+#define LCA_ABI_VERSION 2
 
 /* Version of this ABI (LCA_ABI_VERSION). */
 int32_t lca_abi_version(void);
@@ -120,6 +120,32 @@ lca_status lca_hca_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const
                             const int32_t* nblk, const int64_t* dst_row0, int32_t B,
                             int32_t nblk_max, int32_t D, void* dst, lca_dtype dst_dt,
                             void* dst_scale, int64_t dst_rows, float* pooled, void* stream);
+
+/*
+ * lca_compress_batch -- several compress calls in one launch (for example the
+ * CSA entry block, the indexer-key block and the HCA block of one decode
+ * step).  Each job is the argument list of lca_csa_compress /
+ * lca_hca_compress with the same meaning, layouts and caller guarantees, and
+ * its result is bit-identical to that single call.  [Same passages as
+ * lca_csa_compress.]
+ *   jobs     host array of njobs descriptors, read during the call only;
+ *            1 <= njobs <= LCA_MAX_COMPRESS_JOBS.
+ * Each job is validated as a single call with 1 <= m <= 1024; all jobs must
+ * share x_dt and D (LCA_ENOTSUP otherwise).  Jobs must not write overlapping
+ * destination, scale or pooled rows (they run concurrently).  On any invalid
+ * job nothing is enqueued and the message names the job.
+ */
+#define LCA_MAX_COMPRESS_JOBS 8
+typedef struct lca_compress_job {
+  const void* x; lca_dtype x_dt; int64_t x_rows;
+  const float* gate; const float* pos_bias; int32_t m;
+  const int32_t* x_tok0; const int32_t* nblk; const int64_t* dst_row0;
+  int32_t B; int32_t nblk_max; int32_t D;
+  void* dst; lca_dtype dst_dt; void* dst_scale; int64_t dst_rows;
+  float* pooled;
+} lca_compress_job;
+
+lca_status lca_compress_batch(const lca_compress_job* jobs, int32_t njobs, void* stream);
 
 /*
  * lca_lightning_index_topk -- lightning-indexer scores and top-k selection.
@@ -205,6 +231,40 @@ lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dty
                           const int32_t* win_begin, const int32_t* win_len, const float* sink,
                           float scale, int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out,
                           lca_dtype out_dt, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * lca_attend_batch -- several attention calls in one launch (one attention
+ * launch and at most one merge launch for all jobs), for example the CSA and
+ * HCA branches of one decode step.  Each job is the argument list of
+ * lca_sparse_mqa_attend (sparse = 1: idx, k) or lca_hca_attend (sparse = 0:
+ * n_elig) with the same meaning, layouts, workspace and caller guarantees,
+ * and its result is bit-identical to that single call.  [Same passages as
+ * the two single calls.]
+ *   jobs     host array of njobs descriptors, read during the call only;
+ *            1 <= njobs <= LCA_MAX_ATTEND_JOBS.
+ * Each job is validated as its single call; in addition every job takes bf16
+ * q and window and bf16 or FP8 entries, all jobs share kv_dt and Hq, and no
+ * job may be a dense call with many query rows per sequence and no split
+ * (the chunked-prefill shape, which the single call runs with grouped rows):
+ * LCA_ENOTSUP otherwise.  Jobs must not share output, lse or workspace
+ * memory.  On any invalid job nothing is enqueued and the message names it.
+ */
+#define LCA_MAX_ATTEND_JOBS 4
+typedef struct lca_attend_job {
+  int32_t sparse;
+  const void* q; lca_dtype q_dt;
+  const void* kv; lca_dtype kv_dt; const float* kv_scale; int64_t N_cap;
+  const int32_t* idx; int32_t k;
+  const int32_t* n_elig;
+  const void* win; lca_dtype win_dt; int64_t W_buf;
+  const int32_t* win_begin; const int32_t* win_len;
+  const float* sink; float scale;
+  int32_t B; int32_t Tq; int32_t Hq; int32_t D;
+  void* out; lca_dtype out_dt; float* lse;
+  void* ws; size_t ws_bytes;
+} lca_attend_job;
+
+lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* stream);
 
 /* Workspace bytes for the attention calls.  n_kv_max is k for
  * lca_sparse_mqa_attend and N_cap for lca_hca_attend; W_buf the window buffer

@@ -21,9 +21,21 @@ LIB_PATH = os.path.join(HERE, "liblca.so")
 F32, BF16, FP8E4M3, MXFP4 = 0, 1, 2, 3
 STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA_EWORKSPACE"}
 
-EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress",
+EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
-           "lca_hca_attend", "lca_attend_ws"]
+           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws"]
+MAX_COMPRESS_JOBS = 8
+MAX_ATTEND_JOBS = 4
+
+
+class CompressJob(ctypes.Structure):
+    """lca_compress_job: the argument list of one compress call."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_dt", ctypes.c_int32), ("x_rows", ctypes.c_int64),
+                ("gate", ctypes.c_void_p), ("pos_bias", ctypes.c_void_p), ("m", ctypes.c_int32),
+                ("x_tok0", ctypes.c_void_p), ("nblk", ctypes.c_void_p), ("dst_row0", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("nblk_max", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dst", ctypes.c_void_p), ("dst_dt", ctypes.c_int32), ("dst_scale", ctypes.c_void_p),
+                ("dst_rows", ctypes.c_int64), ("pooled", ctypes.c_void_p)]
 
 
 class LcaError(RuntimeError):
@@ -52,6 +64,10 @@ def load(path: str = LIB_PATH):
     for name in ("lca_csa_compress", "lca_hca_compress"):
         getattr(L, name).restype = i32
         getattr(L, name).argtypes = comp
+    L.lca_attend_batch.restype = i32
+    L.lca_attend_batch.argtypes = [ctypes.POINTER(AttendJob), i32, vp]
+    L.lca_compress_batch.restype = i32
+    L.lca_compress_batch.argtypes = [ctypes.POINTER(CompressJob), i32, vp]
     L.lca_lightning_index_topk.restype = i32
     L.lca_lightning_index_topk.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i64,
                                            i32, vp, vp, vp, sz, vp]
@@ -125,6 +141,62 @@ def hca_compress(x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max, dst, ds
     """As csa_compress, for m' up to 1024 (see lca_hca_compress)."""
     _compress(load().lca_hca_compress, x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max,
               dst, dst_dt, dst_scale, pooled, stream)
+
+
+def compress_job(x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max, dst, dst_dt, dst_scale=None,
+                 pooled=None) -> CompressJob:
+    """One job of compress_batch, with the arguments of csa_compress / hca_compress.  The job
+    holds references to its tensors, so they stay allocated while the job object is alive
+    (keep it until compress_batch has been called)."""
+    B, x_rows, D = x.shape
+    ptr = lambda t: None if t is None else t.data_ptr()
+    job = CompressJob(ptr(x), dtype_of(x), x_rows, ptr(gate), ptr(pos_bias), int(m), ptr(x_tok0), ptr(nblk),
+                      ptr(dst_row0), B, int(nblk_max), D, ptr(dst), int(dst_dt), ptr(dst_scale), dst.shape[1],
+                      ptr(pooled))
+    job._keep = (x, gate, pos_bias, x_tok0, nblk, dst_row0, dst, dst_scale, pooled)
+    return job
+
+
+def compress_batch(jobs, stream=None):
+    """Several compress calls in one launch (see lca_compress_batch); jobs from compress_job(),
+    or a ctypes array of them built once (e.g. for a step that is issued many times)."""
+    arr = jobs if isinstance(jobs, ctypes.Array) else (CompressJob * len(jobs))(*jobs)
+    _check(load().lca_compress_batch(arr, len(arr), _stream(stream)))
+
+
+class AttendJob(ctypes.Structure):
+    """lca_attend_job: the argument list of one sparse_mqa_attend / hca_attend call."""
+    _fields_ = [("sparse", ctypes.c_int32), ("q", ctypes.c_void_p), ("q_dt", ctypes.c_int32),
+                ("kv", ctypes.c_void_p), ("kv_dt", ctypes.c_int32), ("kv_scale", ctypes.c_void_p),
+                ("N_cap", ctypes.c_int64), ("idx", ctypes.c_void_p), ("k", ctypes.c_int32),
+                ("n_elig", ctypes.c_void_p), ("win", ctypes.c_void_p), ("win_dt", ctypes.c_int32),
+                ("W_buf", ctypes.c_int64), ("win_begin", ctypes.c_void_p), ("win_len", ctypes.c_void_p),
+                ("sink", ctypes.c_void_p), ("scale", ctypes.c_float), ("B", ctypes.c_int32), ("Tq", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("D", ctypes.c_int32), ("out", ctypes.c_void_p), ("out_dt", ctypes.c_int32),
+                ("lse", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+def attend_job(sparse, q, kv, kv_scale, idx_or_n, win, win_begin, win_len, sink, scale, out, lse=None,
+               ws=None) -> AttendJob:
+    """One job of attend_batch: the arguments of sparse_mqa_attend (sparse=True, idx) or
+    hca_attend (sparse=False, n_elig).  The job holds references to its tensors, so they stay
+    allocated while the job object is alive (keep it until attend_batch has been called)."""
+    B, Tq, Hq, D = q.shape
+    ptr = lambda t: None if t is None else t.data_ptr()
+    job = AttendJob(1 if sparse else 0, ptr(q), dtype_of(q), ptr(kv), dtype_of(kv, kv_scale), ptr(kv_scale),
+                    kv.shape[1], ptr(idx_or_n) if sparse else None, idx_or_n.shape[-1] if sparse else 0,
+                    None if sparse else ptr(idx_or_n), ptr(win), dtype_of(win), win.shape[1], ptr(win_begin),
+                    ptr(win_len), ptr(sink), float(scale), B, Tq, Hq, D, ptr(out), dtype_of(out), ptr(lse),
+                    ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
+    job._keep = (q, kv, kv_scale, idx_or_n, win, win_begin, win_len, sink, out, lse, ws)
+    return job
+
+
+def attend_batch(jobs, stream=None):
+    """Several attention calls in one launch (see lca_attend_batch); jobs from attend_job(),
+    or a ctypes array of them built once."""
+    arr = jobs if isinstance(jobs, ctypes.Array) else (AttendJob * len(jobs))(*jobs)
+    _check(load().lca_attend_batch(arr, len(arr), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

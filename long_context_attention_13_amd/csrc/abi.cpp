@@ -40,11 +40,14 @@ lca_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-lca_status compress_common(const char* name, int mmax, const void* x, lca_dtype x_dt, int64_t x_rows,
-                           const float* gate, const float* pos_bias, int32_t m, const int32_t* x_tok0,
-                           const int32_t* nblk, const int64_t* dst_row0, int32_t B, int32_t nblk_max,
-                           int32_t D, void* dst, lca_dtype dst_dt, void* dst_scale, int64_t dst_rows,
-                           float* pooled, void* stream) {
+// Validation of one compress call; on success *out holds the launch
+// arguments (B = 0 when there is nothing to do).
+lca_status compress_check(const char* name, int mmax, const void* x, lca_dtype x_dt, int64_t x_rows,
+                          const float* gate, const float* pos_bias, int32_t m, const int32_t* x_tok0,
+                          const int32_t* nblk, const int64_t* dst_row0, int32_t B, int32_t nblk_max,
+                          int32_t D, void* dst, lca_dtype dst_dt, void* dst_scale, int64_t dst_rows,
+                          float* pooled, lca::CompressArgs* out) {
+  *out = lca::CompressArgs{};
   REQ(B >= 0 && nblk_max >= 0, LCA_EINVAL, "%s: B and nblk_max must be >= 0", name);
   REQ(m >= 1 && m <= mmax, LCA_ENOTSUP, "%s: m=%d outside [1, %d]", name, m, mmax);
   REQ(D == 64 || D == 128, LCA_ENOTSUP, "%s: D=%d (supported: 64, 128)", name, D);
@@ -56,6 +59,7 @@ lca_status compress_common(const char* name, int mmax, const void* x, lca_dtype 
       (long long)nblk_max * m, (long long)x_rows);
   REQ(nblk_max <= dst_rows, LCA_EINVAL, "%s: nblk_max=%d exceeds dst_rows=%lld", name, nblk_max,
       (long long)dst_rows);
+  out->x_dt = (int)x_dt; out->D = D;
   if (B == 0 || nblk_max == 0) return ok();
   PTR(x); PTR(gate); PTR(pos_bias); PTR(x_tok0); PTR(nblk); PTR(dst_row0); PTR(dst);
   if (dst_dt == LCA_FP8E4M3 || dst_dt == LCA_MXFP4) {
@@ -64,17 +68,33 @@ lca_status compress_common(const char* name, int mmax, const void* x, lca_dtype 
     REQ(dst_scale == nullptr, LCA_EINVAL, "%s: dst_scale must be NULL for F32/BF16 output", name);
   }
   if (pooled) REQ(aligned16(pooled), LCA_EINVAL, "%s: pooled must be 16-byte aligned", name);
-  lca::CompressArgs a{x, (int)x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0,
-                      B, nblk_max, D, dst, (int)dst_dt, dst_scale, dst_rows, pooled};
+  *out = lca::CompressArgs{x, (int)x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0,
+                           B, nblk_max, D, dst, (int)dst_dt, dst_scale, dst_rows, pooled};
+  return ok();
+}
+
+lca_status compress_common(const char* name, int mmax, const void* x, lca_dtype x_dt, int64_t x_rows,
+                           const float* gate, const float* pos_bias, int32_t m, const int32_t* x_tok0,
+                           const int32_t* nblk, const int64_t* dst_row0, int32_t B, int32_t nblk_max,
+                           int32_t D, void* dst, lca_dtype dst_dt, void* dst_scale, int64_t dst_rows,
+                           float* pooled, void* stream) {
+  lca::CompressArgs a;
+  const lca_status st = compress_check(name, mmax, x, x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0, B,
+                                       nblk_max, D, dst, dst_dt, dst_scale, dst_rows, pooled, &a);
+  if (st != LCA_OK || a.B == 0) return st;
   return hip_status(lca::launch_compress(a, (hipStream_t)stream), name);
 }
 
-lca_status attend_common(const char* name, int sparse, const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,
-                         const float* kv_scale, int64_t N_cap, const int32_t* idx, int32_t k,
-                         const int32_t* n_elig, const void* win, lca_dtype win_dt, int64_t W_buf,
-                         const int32_t* win_begin, const int32_t* win_len, const float* sink, float scale,
-                         int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,
-                         void* ws, size_t ws_bytes, void* stream) {
+// Validation of one attention call; on success *out holds the launch
+// arguments (B*Tq = 0 when there is nothing to do).
+lca_status attend_check(const char* name, int sparse, const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,
+                        const float* kv_scale, int64_t N_cap, const int32_t* idx, int32_t k,
+                        const int32_t* n_elig, const void* win, lca_dtype win_dt, int64_t W_buf,
+                        const int32_t* win_begin, const int32_t* win_len, const float* sink, float scale,
+                        int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,
+                        void* ws, size_t ws_bytes, lca::AttendArgs* outa) {
+  *outa = lca::AttendArgs{};
+  outa->q_dt = (int)q_dt; outa->kv_dt = (int)kv_dt; outa->win_dt = (int)win_dt; outa->Hq = Hq; outa->D = D;
   REQ(B >= 0 && Tq >= 0, LCA_EINVAL, "%s: B and Tq must be >= 0", name);
   REQ(D == 128, LCA_ENOTSUP, "%s: D=%d (supported: 128)", name, D);
   REQ(Hq == 16 || Hq == 32 || Hq == 64, LCA_ENOTSUP, "%s: Hq=%d (supported: 16, 32, 64)", name, Hq);
@@ -99,12 +119,26 @@ lca_status attend_common(const char* name, int sparse, const void* q, lca_dtype 
     REQ(ws != nullptr && aligned16(ws), LCA_EWORKSPACE, "%s: workspace of %zu bytes required", name, need);
     REQ(ws_bytes >= need, LCA_EWORKSPACE, "%s: workspace too small (%zu < %zu)", name, ws_bytes, need);
   }
-  lca::AttendArgs a{};
+  lca::AttendArgs& a = *outa;
   a.q = q; a.q_dt = (int)q_dt; a.kv = kv; a.kv_dt = (int)kv_dt; a.kv_scale = kv_scale; a.N_cap = N_cap;
   a.sparse = sparse; a.idx = idx; a.k = k; a.n_elig = n_elig; a.win = win; a.win_dt = (int)win_dt; a.W_buf = W_buf;
   a.win_begin = win_begin; a.win_len = win_len; a.sink = sink; a.scale = scale;
   a.B = B; a.Tq = Tq; a.Hq = Hq; a.D = D; a.out = out; a.out_dt = (int)out_dt; a.lse = lse;
   a.ws = ws; a.ws_bytes = ws_bytes;
+  return ok();
+}
+
+lca_status attend_common(const char* name, int sparse, const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,
+                         const float* kv_scale, int64_t N_cap, const int32_t* idx, int32_t k,
+                         const int32_t* n_elig, const void* win, lca_dtype win_dt, int64_t W_buf,
+                         const int32_t* win_begin, const int32_t* win_len, const float* sink, float scale,
+                         int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  lca::AttendArgs a;
+  const lca_status st = attend_check(name, sparse, q, q_dt, kv, kv_dt, kv_scale, N_cap, idx, k, n_elig, win, win_dt,
+                                     W_buf, win_begin, win_len, sink, scale, B, Tq, Hq, D, out, out_dt, lse, ws,
+                                     ws_bytes, &a);
+  if (st != LCA_OK || (int64_t)a.B * a.Tq == 0) return st;
   return hip_status(lca::launch_attend(a, (hipStream_t)stream), name);
 }
 
@@ -130,6 +164,27 @@ lca_status lca_hca_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const
                             lca_dtype dst_dt, void* dst_scale, int64_t dst_rows, float* pooled, void* stream) {
   return compress_common("lca_hca_compress", 1024, x, x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0,
                          B, nblk_max, D, dst, dst_dt, dst_scale, dst_rows, pooled, stream);
+}
+
+lca_status lca_compress_batch(const lca_compress_job* jobs, int32_t njobs, void* stream) {
+  REQ(njobs >= 1 && njobs <= LCA_MAX_COMPRESS_JOBS, LCA_EINVAL, "lca_compress_batch: njobs=%d outside [1, %d]",
+      njobs, LCA_MAX_COMPRESS_JOBS);
+  REQ(jobs != nullptr, LCA_EINVAL, "lca_compress_batch: jobs is NULL");
+  static_assert(LCA_MAX_COMPRESS_JOBS == lca::MAX_COMPRESS_JOBS, "job limits agree");
+  lca::CompressBatch bt{};
+  bt.njobs = njobs;
+  for (int j = 0; j < njobs; ++j) {
+    const lca_compress_job& J = jobs[j];
+    char name[64];
+    snprintf(name, sizeof(name), "lca_compress_batch: job %d", j);
+    const lca_status st = compress_check(name, 1024, J.x, J.x_dt, J.x_rows, J.gate, J.pos_bias, J.m, J.x_tok0, J.nblk,
+                                         J.dst_row0, J.B, J.nblk_max, J.D, J.dst, J.dst_dt, J.dst_scale, J.dst_rows,
+                                         J.pooled, &bt.job[j]);
+    if (st != LCA_OK) return st;
+    REQ(J.x_dt == jobs[0].x_dt && J.D == jobs[0].D, LCA_ENOTSUP,
+        "lca_compress_batch: job %d has x_dt/D different from job 0", j);
+  }
+  return hip_status(lca::launch_compress_batch(bt, (hipStream_t)stream), "lca_compress_batch");
 }
 
 size_t lca_index_topk_ws(int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int64_t N_cap, int32_t k) {
@@ -178,6 +233,45 @@ lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8
   a.n_elig = n_elig; a.B = B; a.Tq = Tq; a.H = H_I; a.d = d_I; a.N_cap = N_cap; a.k = k;
   a.idx_out = idx_out; a.score_out = score_out; a.ws = ws; a.ws_bytes = ws_bytes;
   return hip_status(lca::launch_index(a, (hipStream_t)stream), name);
+}
+
+lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* stream) {
+  REQ(njobs >= 1 && njobs <= LCA_MAX_ATTEND_JOBS, LCA_EINVAL, "lca_attend_batch: njobs=%d outside [1, %d]", njobs,
+      LCA_MAX_ATTEND_JOBS);
+  REQ(jobs != nullptr, LCA_EINVAL, "lca_attend_batch: jobs is NULL");
+  static_assert(LCA_MAX_ATTEND_JOBS == lca::MAX_ATTEND_JOBS, "job limits agree");
+  lca::AttendBatch bt{};
+  bt.njobs = njobs;
+  for (int j = 0; j < njobs; ++j) {
+    const lca_attend_job& J = jobs[j];
+    char name[64];
+    snprintf(name, sizeof(name), "lca_attend_batch: job %d", j);
+    REQ(J.sparse == 0 || J.sparse == 1, LCA_EINVAL, "%s: sparse must be 0 or 1", name);
+    const bool rows = (int64_t)J.B * J.Tq > 0;
+    if (J.sparse) {
+      REQ(!rows || J.k <= 0 || (J.idx != nullptr && aligned16(J.idx)), LCA_EINVAL,
+          "%s: idx must be a non-null 16-byte aligned pointer", name);
+    } else {
+      REQ(!rows || (J.n_elig != nullptr && aligned16(J.n_elig)), LCA_EINVAL,
+          "%s: n_elig must be a non-null 16-byte aligned pointer", name);
+    }
+    const lca_status st = attend_check(name, J.sparse, J.q, J.q_dt, J.kv, J.kv_dt, J.kv_scale, J.N_cap,
+                                       J.sparse ? J.idx : nullptr, J.sparse ? J.k : 0, J.sparse ? nullptr : J.n_elig,
+                                       J.win, J.win_dt, J.W_buf, J.win_begin, J.win_len, J.sink, J.scale, J.B, J.Tq,
+                                       J.Hq, J.D, J.out, J.out_dt, J.lse, J.ws, J.ws_bytes, &bt.job[j]);
+    if (st != LCA_OK) return st;
+    lca::AttendArgs& a = bt.job[j];
+    if ((int64_t)J.B * J.Tq == 0) {
+      // nothing to do for this job: keep a launchable descriptor with no rows
+      a.B = 0; a.Tq = 0; a.sparse = 1; a.k = 0; a.Hq = J.Hq; a.D = J.D;
+    }
+    REQ(J.q_dt == LCA_BF16 && J.win_dt == LCA_BF16 && (J.kv_dt == LCA_BF16 || J.kv_dt == LCA_FP8E4M3), LCA_ENOTSUP,
+        "%s: batched attention takes bf16 queries and windows and bf16 or FP8 entries", name);
+    REQ(J.kv_dt == jobs[0].kv_dt && J.Hq == jobs[0].Hq, LCA_ENOTSUP, "%s: kv_dt/Hq differ from job 0", name);
+    REQ((int64_t)J.B * J.Tq == 0 || lca::attend_batchable(a), LCA_ENOTSUP,
+        "%s: dense rows grouped per sequence (many query rows, no split) are not batched; use lca_hca_attend", name);
+  }
+  return hip_status(lca::launch_attend_batch(bt, (hipStream_t)stream), "lca_attend_batch");
 }
 
 size_t lca_attend_ws(int32_t B, int32_t Tq, int32_t Hq, int32_t D, int64_t n_kv_max, int64_t W_buf) {

@@ -350,18 +350,28 @@ __device__ __forceinline__ void mt_store(const MtRegs<KVDT, CPT>& R, __bf16* Kl,
   }
 }
 
+template <int QB>
+struct MtShared {
+  __align__(16) __bf16 Kl[MT_TE * MT_KROW];
+  __align__(16) __bf16 Vt[128 * MT_VROW];
+  __align__(16) float sclo[MT_TE];
+  __align__(16) float schi[MT_TE];
+  __align__(16) int okl[MT_TE];
+  int idxl[QB == 1 ? 2048 : 1];
+};
+
+// Split `split` of query-row group `grp` of one attention call.
 template <int KVDT, int HQ, int QB>
-__global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void attend_mfma_kernel(AttendArgs A, int S, int split_items, float* part_ml,
-                                                                  float* part_o) {
+__device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int split_items, float* part_ml,
+                                                 float* part_o, int split, int grp, MtShared<QB>& sm) {
   // QB query rows of one sequence share each staged tile (dense lists only):
   // the workgroup's list is entries 0 .. max n_elig - 1 followed by the union
   // of the rows' window slices, and every row masks what is not its own.
   constexpr int NT = HQ * 4 * QB;                  // threads (HQ/16 waves per row)
   constexpr int CPT = (MT_TASKS + NT - 1) / NT;    // staging tasks per thread and tile
-  const int split = blockIdx.x;
   const int ngrp = (A.Tq + QB - 1) / QB;
-  const int b = blockIdx.y / ngrp;
-  const int t0r = (blockIdx.y % ngrp) * QB;
+  const int b = grp / ngrp;
+  const int t0r = (grp % ngrp) * QB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int qrow = wave / (HQ / 16);                // this wave's row within the group
@@ -389,12 +399,12 @@ __global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void atten
   const int p0 = split * split_items;
   const int p1 = S == 1 ? L : min(L, p0 + split_items);
 
-  __shared__ __align__(16) __bf16 Kl[MT_TE * MT_KROW];
-  __shared__ __align__(16) __bf16 Vt[128 * MT_VROW];
-  __shared__ __align__(16) float sclo[MT_TE];
-  __shared__ __align__(16) float schi[MT_TE];
-  __shared__ __align__(16) int okl[MT_TE];
-  __shared__ int idxl[QB == 1 ? 2048 : 1];
+  __bf16* Kl = sm.Kl;
+  __bf16* Vt = sm.Vt;
+  float* sclo = sm.sclo;
+  float* schi = sm.schi;
+  int* okl = sm.okl;
+  int* idxl = sm.idxl;
 
   // the selected indices of this split's entry range, staged once
   const int e_lo = p0, e_hi = min(p1, nkv);
@@ -554,16 +564,21 @@ __global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void atten
 // ------------------------------------------------------------------------
 // merge: combine the split partials of one row in split order with the sink
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, const float* part_ml,
-                                                           const float* part_o) {
-  // one workgroup per (row, head); thread d owns output dim d.  Every load
-  // (the split maxima and sums, and the first MG_PRE splits' outputs) is
-  // issued before any of them is used.
+struct MgShared {
+  float wsp[1024];
+  float red[2][2];
+};
+
+// one workgroup per (row, head) = blk; thread d owns output dim d.  Every load
+// (the split maxima and sums, and the first MG_PRE splits' outputs) is issued
+// before any of them is used.
+__device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S, const float* part_ml,
+                                                  const float* part_o, int blk, MgShared& sm) {
   constexpr int MG_PRE = 64;
-  const int r = blockIdx.x / A.Hq, h = blockIdx.x % A.Hq;
+  const int r = blk / A.Hq, h = blk % A.Hq;
   const int d = threadIdx.x;
-  __shared__ float wsp[1024];
-  __shared__ float red[2][2];
+  float* wsp = sm.wsp;
+  auto& red = sm.red;
   const float sk = A.sink[h] * LOG2E;                       // partial maxima are base-2 logits
   const int64_t base0 = (int64_t)r * S * A.Hq + h;          // partial (r, s, h) = base0 + s*Hq
   const int64_t ost = (int64_t)A.Hq * A.D;
@@ -616,6 +631,38 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, 
   const float o = o0 + o1;
   store_out(A, ((int64_t)r * A.Hq + h) * A.D + d, o / Z);
   if (A.lse && d == 0) A.lse[(int64_t)r * A.Hq + h] = (M + log2f(Z)) * LN2;
+}
+
+template <int KVDT, int HQ, int QB>
+__global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void attend_mfma_kernel(
+    AttendArgs A, int S, int split_items, float* part_ml, float* part_o) {
+  __shared__ MtShared<QB> sm;
+  attend_mfma_body<KVDT, HQ, QB>(A, S, split_items, part_ml, part_o, blockIdx.x, blockIdx.y, sm);
+}
+
+__global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, const float* part_ml,
+                                                           const float* part_o) {
+  __shared__ MgShared sm;
+  attend_merge_body(A, S, part_ml, part_o, blockIdx.x, sm);
+}
+
+// Several attention calls in one launch: block x of the grid is block
+// x - blk0[j] of job j, i.e. split (x - blk0[j]) % S[j] of row (x - blk0[j]) / S[j].
+template <int KVDT, int HQ>
+__global__ __launch_bounds__(HQ * 4, HQ * 4 == 256 ? 2 : 1) void attend_mfma_batch_kernel(AttendBatch bt) {
+  __shared__ MtShared<1> sm;
+  int j = 0;
+  while (j + 1 < bt.njobs && (int)blockIdx.x >= bt.blk0[j + 1]) ++j;
+  const int local = (int)blockIdx.x - bt.blk0[j];
+  const int S = bt.S[j];
+  attend_mfma_body<KVDT, HQ, 1>(bt.job[j], S, bt.items[j], bt.ml[j], bt.po[j], local % S, local / S, sm);
+}
+
+__global__ __launch_bounds__(128) void attend_merge_batch_kernel(AttendBatch bt) {
+  __shared__ MgShared sm;
+  int j = 0;
+  while (j + 1 < bt.njobs && (int)blockIdx.x >= bt.mblk0[j + 1]) ++j;
+  attend_merge_body(bt.job[j], bt.S[j], bt.ml[j], bt.po[j], (int)blockIdx.x - bt.mblk0[j], sm);
 }
 
 // ------------------------------------------------------------------------
@@ -690,6 +737,57 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   else e = a.q_dt == DT_F32 ? launch_kv<DT_F32>(a, s, P, ml, po) : launch_kv<DT_BF16>(a, s, P, ml, po);
   if (e != hipSuccess || P.S == 1) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, P.S, ml, po);
+  return hipGetLastError();
+}
+
+// A call the batch launcher can take: the bf16-MFMA path in its one-row,
+// split layout (not the grouped dense-prefill layout).
+bool attend_batchable(const AttendArgs& a) {
+  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8);
+  if (!mfma) return false;
+  const int64_t R = (int64_t)a.B * a.Tq;
+  const Plan P = att_plan(R, a.sparse ? a.k : a.N_cap, a.W_buf);
+  const int qb = a.Hq == 16 ? att_qb<16>() : a.Hq == 32 ? att_qb<32>() : att_qb<64>();
+  return !(!a.sparse && P.S == 1 && a.Tq >= 2 * qb);
+}
+
+hipError_t launch_attend_batch(const AttendBatch& in, hipStream_t s) {
+  AttendBatch bt = in;
+  int nb = 0, nm = 0;
+  for (int j = 0; j < bt.njobs; ++j) {
+    const AttendArgs& a = bt.job[j];
+    const int64_t R = (int64_t)a.B * a.Tq;
+    const Plan P = att_plan(R, a.sparse ? a.k : a.N_cap, a.W_buf);
+    bt.S[j] = P.S;
+    bt.items[j] = P.items;
+    bt.ml[j] = P.S > 1 ? (float*)a.ws : nullptr;
+    bt.po[j] = P.S > 1 ? (float*)((char*)a.ws + align256(sizeof(float) * R * P.S * a.Hq * 2)) : nullptr;
+    bt.blk0[j] = nb;
+    bt.mblk0[j] = nm;
+    nb += (int)(R * P.S);
+    nm += P.S > 1 ? (int)(R * a.Hq) : 0;
+  }
+  bt.blk0[bt.njobs] = nb;
+  bt.mblk0[bt.njobs] = nm;
+  if (nb == 0) return hipSuccess;
+  const bool fp8 = bt.job[0].kv_dt == DT_FP8;
+  switch (bt.job[0].Hq) {
+    case 16:
+      if (fp8) hipLaunchKernelGGL((attend_mfma_batch_kernel<DT_FP8, 16>), dim3(nb), dim3(64), 0, s, bt);
+      else hipLaunchKernelGGL((attend_mfma_batch_kernel<DT_BF16, 16>), dim3(nb), dim3(64), 0, s, bt);
+      break;
+    case 32:
+      if (fp8) hipLaunchKernelGGL((attend_mfma_batch_kernel<DT_FP8, 32>), dim3(nb), dim3(128), 0, s, bt);
+      else hipLaunchKernelGGL((attend_mfma_batch_kernel<DT_BF16, 32>), dim3(nb), dim3(128), 0, s, bt);
+      break;
+    default:
+      if (fp8) hipLaunchKernelGGL((attend_mfma_batch_kernel<DT_FP8, 64>), dim3(nb), dim3(256), 0, s, bt);
+      else hipLaunchKernelGGL((attend_mfma_batch_kernel<DT_BF16, 64>), dim3(nb), dim3(256), 0, s, bt);
+      break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nm == 0) return e;
+  hipLaunchKernelGGL(attend_merge_batch_kernel, dim3(nm), dim3(128), 0, s, bt);
   return hipGetLastError();
 }
 

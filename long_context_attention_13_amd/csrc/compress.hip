@@ -24,14 +24,20 @@ namespace lca {
 // are then added in LDS in group order, and thread d < D encodes channel d.
 constexpr int PE_THREADS = 128;
 
+struct PeShared {
+  float wgt[1024];                              // gate weights of the block
+  float red[2][PE_THREADS / WAVE];
+  __align__(16) float part[1024];               // [G][D] group partials
+};
+
+// Block i of sequence b of one compress call.
 template <int XDT, int ODT, int D>
-__global__ __launch_bounds__(PE_THREADS) void pool_encode_kernel(CompressArgs a) {
+__device__ __forceinline__ void pool_encode_block(const CompressArgs& a, int b, int i, PeShared& S) {
   constexpr int CPL = XDT == DT_F32 ? 4 : 8;    // channels per 16-byte piece
   constexpr int NCK = D / CPL;                  // pieces per token row
   constexpr int G = PE_THREADS / NCK;           // token groups
   constexpr int TB = 16;                        // token loads in flight per thread and batch
-  const int b = blockIdx.y;
-  const int i = blockIdx.x;
+  static_assert(G * D <= 1024, "group partials fit");
   const int nblk = a.nblk[b];
   const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * a.m;
   if (i >= nblk) return;
@@ -39,9 +45,9 @@ __global__ __launch_bounds__(PE_THREADS) void pool_encode_kernel(CompressArgs a)
   const int ck = tid % NCK, grp = tid / NCK;
   const int m = a.m;
 
-  __shared__ float wgt[1024];
-  __shared__ float red[2][PE_THREADS / WAVE];
-  __shared__ __align__(16) float part[G][D];
+  float* wgt = S.wgt;
+  auto& red = S.red;
+  float (*part)[D] = (float (*)[D])S.part;
 
   const char* xrow = (const char*)a.x + (((int64_t)b * a.x_rows + tok0) * D + ck * CPL) * (XDT == DT_F32 ? 4 : 2);
   const int64_t rstride = (int64_t)D * (XDT == DT_F32 ? 4 : 2);
@@ -155,6 +161,27 @@ __global__ __launch_bounds__(PE_THREADS) void pool_encode_kernel(CompressArgs a)
   }
 }
 
+template <int XDT, int ODT, int D>
+__global__ __launch_bounds__(PE_THREADS) void pool_encode_kernel(CompressArgs a) {
+  __shared__ PeShared S;
+  pool_encode_block<XDT, ODT, D>(a, blockIdx.y, blockIdx.x, S);
+}
+
+// Several compress calls in one launch: blockIdx.z is the job; every job has
+// the input type XDT and width D, the output type is taken per job.
+template <int XDT, int D>
+__global__ __launch_bounds__(PE_THREADS) void pool_encode_batch_kernel(CompressBatch bt) {
+  __shared__ PeShared S;
+  const CompressArgs& a = bt.job[blockIdx.z];
+  if ((int)blockIdx.y >= a.B || (int)blockIdx.x >= a.nblk_max) return;
+  switch (a.dst_dt) {
+    case DT_F32: pool_encode_block<XDT, DT_F32, D>(a, blockIdx.y, blockIdx.x, S); break;
+    case DT_BF16: pool_encode_block<XDT, DT_BF16, D>(a, blockIdx.y, blockIdx.x, S); break;
+    case DT_FP8: pool_encode_block<XDT, DT_FP8, D>(a, blockIdx.y, blockIdx.x, S); break;
+    default: pool_encode_block<XDT, DT_MXFP4, D>(a, blockIdx.y, blockIdx.x, S); break;
+  }
+}
+
 template <int XDT, int ODT>
 static hipError_t launch_d(const CompressArgs& a, hipStream_t s) {
   dim3 grid(a.nblk_max, a.B);
@@ -176,6 +203,22 @@ static hipError_t launch_o(const CompressArgs& a, hipStream_t s) {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.nblk_max == 0 || a.B == 0) return hipSuccess;
   return a.x_dt == DT_F32 ? launch_o<DT_F32>(a, s) : launch_o<DT_BF16>(a, s);
+}
+
+hipError_t launch_compress_batch(const CompressBatch& bt, hipStream_t s) {
+  int gx = 0, gy = 0;
+  for (int j = 0; j < bt.njobs; ++j) {
+    gx = bt.job[j].nblk_max > gx ? bt.job[j].nblk_max : gx;
+    gy = bt.job[j].B > gy ? bt.job[j].B : gy;
+  }
+  if (bt.njobs == 0 || gx == 0 || gy == 0) return hipSuccess;
+  const dim3 grid(gx, gy, bt.njobs);
+  const bool f32 = bt.job[0].x_dt == DT_F32, d64 = bt.job[0].D == 64;
+  if (f32 && d64) hipLaunchKernelGGL((pool_encode_batch_kernel<DT_F32, 64>), grid, dim3(PE_THREADS), 0, s, bt);
+  else if (f32) hipLaunchKernelGGL((pool_encode_batch_kernel<DT_F32, 128>), grid, dim3(PE_THREADS), 0, s, bt);
+  else if (d64) hipLaunchKernelGGL((pool_encode_batch_kernel<DT_BF16, 64>), grid, dim3(PE_THREADS), 0, s, bt);
+  else hipLaunchKernelGGL((pool_encode_batch_kernel<DT_BF16, 128>), grid, dim3(PE_THREADS), 0, s, bt);
+  return hipGetLastError();
 }
 
 }  // namespace lca

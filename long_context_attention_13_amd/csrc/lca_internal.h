@@ -19,6 +19,13 @@ struct CompressArgs {
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
+constexpr int MAX_COMPRESS_JOBS = 8;
+struct CompressBatch {                // jobs share x_dt and D
+  CompressArgs job[MAX_COMPRESS_JOBS];
+  int njobs;
+};
+hipError_t launch_compress_batch(const CompressBatch& bt, hipStream_t s);
+
 struct IndexArgs {
   const void* qi; int dt; const uint8_t* qi_scale;
   const float* w;
@@ -46,5 +53,17 @@ struct AttendArgs {
 };
 size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W_buf);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+constexpr int MAX_ATTEND_JOBS = 4;
+struct AttendBatch {                  // jobs share kv_dt and Hq; plans filled by the launcher
+  AttendArgs job[MAX_ATTEND_JOBS];
+  int S[MAX_ATTEND_JOBS], items[MAX_ATTEND_JOBS];
+  float* ml[MAX_ATTEND_JOBS];
+  float* po[MAX_ATTEND_JOBS];
+  int blk0[MAX_ATTEND_JOBS + 1], mblk0[MAX_ATTEND_JOBS + 1];
+  int njobs;
+};
+bool attend_batchable(const AttendArgs& a);
+hipError_t launch_attend_batch(const AttendBatch& bt, hipStream_t s);
 
 }  // namespace lca

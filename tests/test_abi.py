@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.lca_abi_version() == 1
+    assert L.lca_abi_version() == 2
 
 
 def compress(L, **kw):
@@ -129,3 +129,69 @@ def test_errors_are_thread_local(L):
     t.join()
     assert seen == [b""]
     assert L.lca_last_error() != b""
+
+
+def batch_job(**kw):
+    a = dict(x=FAKE, x_dt=lca.BF16, x_rows=256, gate=FAKE, pos_bias=FAKE, m=4, x_tok0=FAKE, nblk=FAKE,
+             dst_row0=FAKE, B=2, nblk_max=1, D=128, dst=FAKE, dst_dt=lca.FP8E4M3, dst_scale=FAKE,
+             dst_rows=16, pooled=None)
+    a.update(kw)
+    return lca.CompressJob(*a.values())
+
+
+def compress_batch(L, jobs, n=None):
+    arr = (lca.CompressJob * max(1, len(jobs)))(*jobs)
+    return L.lca_compress_batch(arr, len(jobs) if n is None else n, None)
+
+
+def test_compress_batch_validation(L):
+    ok3 = [batch_job(), batch_job(dst_dt=lca.MXFP4), batch_job(m=128, x_rows=256)]
+    assert compress_batch(L, [batch_job(B=0)] * 3) == 0          # nothing to do, no GPU touched
+    assert compress_batch(L, ok3, n=0) == 1
+    assert compress_batch(L, ok3 * 3, n=9) == 1                   # more than LCA_MAX_COMPRESS_JOBS
+    assert L.lca_compress_batch(None, 1, None) == 1
+    bad = list(ok3)
+    bad[1] = batch_job(m=2048)                                    # m above 1024
+    assert compress_batch(L, bad) == 2
+    assert b"job 1" in L.lca_last_error()
+    bad[1] = batch_job(dst=None)
+    assert compress_batch(L, bad) == 1
+    bad[1] = batch_job(D=64)                                      # D differs from job 0
+    assert compress_batch(L, bad) == 2
+    bad[1] = batch_job(x_dt=lca.F32)                              # x_dt differs from job 0
+    assert compress_batch(L, bad) == 2
+    bad[2] = batch_job(nblk_max=100)                              # nblk_max*m exceeds x_rows
+    assert compress_batch(L, bad) in (1, 2)
+
+
+def attend_job(**kw):
+    a = dict(sparse=1, q=FAKE, q_dt=lca.BF16, kv=FAKE, kv_dt=lca.FP8E4M3, kv_scale=FAKE, N_cap=1024, idx=FAKE,
+             k=64, n_elig=None, win=FAKE, win_dt=lca.BF16, W_buf=128, win_begin=FAKE, win_len=FAKE, sink=FAKE,
+             scale=0.088, B=1, Tq=1, Hq=64, D=128, out=FAKE, out_dt=lca.BF16, lse=None, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return lca.AttendJob(*a.values())
+
+
+def attend_batch(L, jobs, n=None):
+    arr = (lca.AttendJob * max(1, len(jobs)))(*jobs)
+    return L.lca_attend_batch(arr, len(jobs) if n is None else n, None)
+
+
+def test_attend_batch_validation(L):
+    dense = dict(sparse=0, idx=None, k=0, n_elig=FAKE)
+    assert attend_batch(L, [attend_job(B=0), attend_job(B=0, **dense)]) == 0   # nothing to do
+    assert attend_batch(L, [attend_job()], n=0) == 1
+    assert attend_batch(L, [attend_job()] * 5) == 1                           # more than LCA_MAX_ATTEND_JOBS
+    assert L.lca_attend_batch(None, 1, None) == 1
+    assert attend_batch(L, [attend_job(), attend_job(sparse=2)]) == 1
+    assert attend_batch(L, [attend_job(), attend_job(idx=None)]) == 1
+    assert b"job 1" in L.lca_last_error()
+    assert attend_batch(L, [attend_job(), attend_job(n_elig=None, **{k: v for k, v in dense.items()
+                                                                     if k != "n_elig"})]) == 1
+    assert attend_batch(L, [attend_job(), attend_job(Hq=32)]) == 2          # Hq differs from job 0
+    assert attend_batch(L, [attend_job(), attend_job(kv_dt=lca.BF16, kv_scale=None)]) == 2
+    assert attend_batch(L, [attend_job(q_dt=lca.F32)]) == 2                  # not the bf16 MFMA path
+    # the chunked-prefill dense shape (many rows, no split) stays with lca_hca_attend
+    assert attend_batch(L, [attend_job(Tq=8192, W_buf=8319, N_cap=2048, **dense)]) == 2
+    assert attend_batch(L, [attend_job(k=1024, ws=None)]) == 4               # split partials need workspace

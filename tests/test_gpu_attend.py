@@ -151,3 +151,69 @@ def test_dense_row_groups(Hq, kv_dt):
                        lca.BF16)
     assert_rows_close(o, ro, 2e-2, "out")
     assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
+
+
+@pytest.mark.parametrize("kv_dt,Hq", [(lca.FP8E4M3, 64), (lca.BF16, 16)])
+def test_batch_equals_single_calls(kv_dt, Hq):
+    """lca_attend_batch over a sparse job with splits, a dense job with splits,
+    a short job without splits and an empty job gives the bytes of the single
+    calls (outputs and LSE)."""
+    d = dev()
+    g = torch.Generator(device=d)
+    g.manual_seed(404 + Hq)
+    B, D, N_cap, W = 2, 128, 5000, 128
+    rn = lambda *s: torch.randn(*s, generator=g, device=d)
+
+    def cache():
+        x = rn(B, N_cap, D)
+        if kv_dt == lca.BF16:
+            return x.to(torch.bfloat16), None
+        codes = torch.empty(B, N_cap, D, dtype=torch.uint8, device=d)
+        sc = torch.empty(B, N_cap, D // 64, device=d)
+        i32 = lambda v: torch.full((B,), v, dtype=torch.int32, device=d)
+        lca.csa_compress(x, torch.zeros(B, N_cap, device=d), torch.zeros(1, device=d), 1, i32(0), i32(N_cap),
+                         torch.zeros(B, dtype=torch.int64, device=d), N_cap, codes, lca.FP8E4M3, sc)
+        return codes, sc
+
+    kv, kv_sc = cache()
+    win = rn(B, 3 * W, D).to(torch.bfloat16)
+    sink = rn(Hq)
+    tau = 1 / math.sqrt(D)
+    idx = torch.stack([torch.randperm(N_cap, generator=g, device=d)[:700] for _ in range(B)]).to(torch.int32)
+    idx[1, 5:40] = -1
+    idx = idx.sort(dim=-1).values.view(B, 1, 700)
+    idx_short = idx[:, :, :16].contiguous()
+    n = torch.tensor([[N_cap], [3001]], dtype=torch.int32, device=d)
+    wb = torch.tensor([[0], [W]], dtype=torch.int32, device=d)
+    wl = torch.tensor([[W], [W - 5]], dtype=torch.int32, device=d)
+    wl_s = torch.tensor([[40], [0]], dtype=torch.int32, device=d)
+    win_s = win[:, :100].contiguous()               # 16 + 100 items: a single split
+    wb_s = torch.zeros(B, 1, dtype=torch.int32, device=d)
+    specs = [(True, idx, win, wb, wl, True), (False, n, win, wb, wl, False),
+             (True, idx_short, win_s, wb_s, wl_s, True)]
+    single, batch, jobs = [], [], []
+    for sparse, sel, win, wb, wlen, with_lse in specs:
+        q = rn(B, 1, Hq, D).to(torch.bfloat16)
+        nmax = sel.shape[-1] if sparse else N_cap
+        for lst in (single, batch):
+            out = torch.full((B, 1, Hq, D), 3.0, device=d).to(torch.bfloat16)
+            lse = torch.full((B, 1, Hq), 5.0, device=d) if with_lse else None
+            ws = empty_ws(lca.attend_ws(B, 1, Hq, D, nmax, win.shape[1]))
+            lst.append((out, lse, ws))
+        out, lse, ws = single[-1]
+        fn = lca.sparse_mqa_attend if sparse else lca.hca_attend
+        fn(q, kv, kv_sc, sel, win, wb, wlen, sink, tau, out, lse, ws=ws)
+        out, lse, ws = batch[-1]
+        jobs.append(lca.attend_job(sparse, q, kv, kv_sc, sel, win, wb, wlen, sink, tau, out, lse, ws))
+    # an empty job (no query rows)
+    q0 = torch.empty(0, 1, Hq, D, dtype=torch.bfloat16, device=d)
+    assert lca.attend_ws(B, 1, Hq, D, 16, 100) == 0
+    jobs.append(lca.attend_job(True, q0, kv, kv_sc, idx[:0], win, wb[:0], wl[:0], sink, tau,
+                               torch.empty(0, 1, Hq, D, dtype=torch.bfloat16, device=d)))
+    lca.attend_batch(jobs)                      # each job keeps its own query and index arrays alive
+    torch.cuda.synchronize()
+    del jobs
+    for j, (a, b) in enumerate(zip(single, batch)):
+        assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)), f"job {j} out"
+        if a[1] is not None:
+            assert torch.equal(a[1], b[1]), f"job {j} lse"

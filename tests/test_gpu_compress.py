@@ -188,3 +188,53 @@ def test_pooled_encoding_is_a_correct_rounding(dst_dt):
     assert (err <= tol).all(), (i, got[i], ref[i], tol[i])
     frac_equal = (codes == rc).mean()
     assert frac_equal > 0.999, frac_equal
+
+
+def test_batch_equals_single_calls():
+    """lca_compress_batch: CSA FP8 (m = 4), indexer keys MXFP4 with pooled rows
+    (m = 4), HCA FP8 (m = 128) and a bf16 cache (m = 16) in one launch give
+    the bytes of the four single calls; rows no job writes are untouched."""
+    d = dev()
+    g = torch.Generator(device=d)
+    g.manual_seed(91)
+    B, D, rows = 3, 128, 12
+    x = torch.randn(B, 2048, D, generator=g, device=d).to(torch.bfloat16)
+    gate = torch.randn(B, 2048, generator=g, device=d)
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=d)
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=d)
+    specs = [  # (m, dst_dt, nblk, tok0, row0, pooled)
+        (4, lca.FP8E4M3, [5, 0, 3], [0, 7, 100], [0, 4, 9], False),
+        (4, lca.MXFP4, [1, 5, 2], [3, 0, 64], [11, 0, 2], True),
+        (128, lca.FP8E4M3, [2, 1, 0], [0, 129, 5], [1, 10, 0], False),
+        (16, lca.BF16, [4, 4, 4], [16, 0, 33], [0, 8, 3], True),
+    ]
+
+    def dst_of(dt):
+        if dt == lca.FP8E4M3:
+            return (torch.full((B, rows, D), 0x5A, dtype=torch.uint8, device=d),
+                    torch.full((B, rows, D // 64), -3.0, device=d))
+        if dt == lca.MXFP4:
+            return (torch.full((B, rows, D // 2), 0x5A, dtype=torch.uint8, device=d),
+                    torch.full((B, rows, D // 32), 7, dtype=torch.uint8, device=d))
+        return torch.full((B, rows, D), -2.0, device=d).to(torch.bfloat16), None
+
+    single, batch, jobs = [], [], []
+    for m, dt, nb, t0, r0, pooled in specs:
+        bias = torch.randn(m, generator=g, device=d)
+        args = (x, gate, bias, m, i32(t0), i32(nb), i64(r0), max(nb))
+        outs = []
+        for dst_list in (single, batch):
+            dst, sc = dst_of(dt)
+            pl = torch.full((B, max(nb), D), 9.0, device=d) if pooled else None
+            dst_list.append((dst, sc, pl))
+        dst, sc, pl = single[-1]
+        (lca.hca_compress if m > 64 else lca.csa_compress)(*args, dst, dt, sc, pl)
+        dst, sc, pl = batch[-1]
+        jobs.append(lca.compress_job(*args, dst, dt, sc, pl))
+    lca.compress_batch(jobs)                    # each job keeps its own index arrays and bias alive
+    torch.cuda.synchronize()
+    del jobs
+    for j, (a, b) in enumerate(zip(single, batch)):
+        for ta, tb in zip(a, b):
+            if ta is not None:
+                assert torch.equal(ta.view(torch.uint8), tb.view(torch.uint8)), f"job {j}"
