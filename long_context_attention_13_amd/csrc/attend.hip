@@ -28,7 +28,9 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Split plan: one split per row when there are enough rows to fill the GPU on
 // their own; otherwise the list is cut into splits of 64 items (one tile)
 // while that stays within one workgroup per compute unit, else 128 or 256
-// (the split size depends only on the shape, never on the data).
+// (the split size depends only on the shape, never on the data; the list
+// length is bounded by capacity, and splits past a row's actual list return
+// at once).
 struct Plan { int S; int items; };
 
 static Plan att_plan(int64_t R, int64_t n_kv_max, int64_t W_buf) {
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   const int L = nkv + A.win_len[r];
   const int p0 = split * split_items;
   const int p1 = S == 1 ? L : min(L, p0 + split_items);
+  if (S > 1 && p0 >= L) return;             // an empty split: the merge does not read it
 
   __shared__ float qs[HQ][D];
   __shared__ float kvs[ATT_TE][D + 1];
@@ -398,6 +401,7 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
   const int64_t wbase = (int64_t)b * A.W_buf + wlo;
   const int p0 = split * split_items;
   const int p1 = S == 1 ? L : min(L, p0 + split_items);
+  if (S > 1 && p0 >= L) return;             // an empty split: the merge does not read it
 
   __bf16* Kl = sm.Kl;
   __bf16* Vt = sm.Vt;
@@ -569,18 +573,22 @@ struct MgShared {
   float red[2][2];
 };
 
-// one workgroup per (row, head) = blk; thread d owns output dim d.  Every load
-// (the split maxima and sums, and the first MG_PRE splits' outputs) is issued
-// before any of them is used.
-__device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S, const float* part_ml,
-                                                  const float* part_o, int blk, MgShared& sm) {
+// one workgroup per (row, head) = blk; thread d owns output dim d.  Only the
+// splits that hold items of the row's list (length L = list + window) are
+// read: a later split is empty and contributes nothing.  Every load (the split
+// maxima and sums, and the first MG_PRE splits' outputs) is issued before any
+// of them is used.
+__device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all, int split_items,
+                                                  const float* part_ml, const float* part_o, int blk, MgShared& sm) {
   constexpr int MG_PRE = 64;
   const int r = blk / A.Hq, h = blk % A.Hq;
   const int d = threadIdx.x;
+  const int L = (A.sparse ? A.k : A.n_elig[r]) + A.win_len[r];
+  const int S = min(S_all, (L + split_items - 1) / split_items);
   float* wsp = sm.wsp;
   auto& red = sm.red;
   const float sk = A.sink[h] * LOG2E;                       // partial maxima are base-2 logits
-  const int64_t base0 = (int64_t)r * S * A.Hq + h;          // partial (r, s, h) = base0 + s*Hq
+  const int64_t base0 = (int64_t)r * S_all * A.Hq + h;      // partial (r, s, h) = base0 + s*Hq
   const int64_t ost = (int64_t)A.Hq * A.D;
   const float* po = part_o + base0 * A.D + d;
   float ov[MG_PRE];
@@ -640,10 +648,10 @@ __global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void atten
   attend_mfma_body<KVDT, HQ, QB>(A, S, split_items, part_ml, part_o, blockIdx.x, blockIdx.y, sm);
 }
 
-__global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, const float* part_ml,
+__global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, int split_items, const float* part_ml,
                                                            const float* part_o) {
   __shared__ MgShared sm;
-  attend_merge_body(A, S, part_ml, part_o, blockIdx.x, sm);
+  attend_merge_body(A, S, split_items, part_ml, part_o, blockIdx.x, sm);
 }
 
 // Several attention calls in one launch: block x of the grid is block
@@ -662,7 +670,7 @@ __global__ __launch_bounds__(128) void attend_merge_batch_kernel(AttendBatch bt)
   __shared__ MgShared sm;
   int j = 0;
   while (j + 1 < bt.njobs && (int)blockIdx.x >= bt.mblk0[j + 1]) ++j;
-  attend_merge_body(bt.job[j], bt.S[j], bt.ml[j], bt.po[j], (int)blockIdx.x - bt.mblk0[j], sm);
+  attend_merge_body(bt.job[j], bt.S[j], bt.items[j], bt.ml[j], bt.po[j], (int)blockIdx.x - bt.mblk0[j], sm);
 }
 
 // ------------------------------------------------------------------------
@@ -736,7 +744,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (mfma) e = a.kv_dt == DT_FP8 ? launch_mfma<DT_FP8>(a, s, P, ml, po) : launch_mfma<DT_BF16>(a, s, P, ml, po);
   else e = a.q_dt == DT_F32 ? launch_kv<DT_F32>(a, s, P, ml, po) : launch_kv<DT_BF16>(a, s, P, ml, po);
   if (e != hipSuccess || P.S == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, P.S, ml, po);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, P.S, P.items, ml, po);
   return hipGetLastError();
 }
 
