@@ -583,8 +583,9 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
   constexpr int MG_PRE = 64;
   const int r = blk / A.Hq, h = blk % A.Hq;
   const int d = threadIdx.x;
+  // the row's list length is requested with the partials, which are read for
+  // every planned split (all inside the workspace) and masked once it arrives
   const int L = (A.sparse ? A.k : A.n_elig[r]) + A.win_len[r];
-  const int S = min(S_all, (L + split_items - 1) / split_items);
   float* wsp = sm.wsp;
   auto& red = sm.red;
   const float sk = A.sink[h] * LOG2E;                       // partial maxima are base-2 logits
@@ -593,14 +594,18 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
   const float* po = part_o + base0 * A.D + d;
   float ov[MG_PRE];
 #pragma unroll
-  for (int i = 0; i < MG_PRE; ++i) ov[i] = i < S ? po[i * ost] : 0.f;
+  for (int i = 0; i < MG_PRE; ++i) ov[i] = i < S_all ? po[i * ost] : 0.f;
   float mv[8], lv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int s = d + 128 * i;
-    mv[i] = s < S ? part_ml[(base0 + (int64_t)s * A.Hq) * 2] : -INFINITY;
-    lv[i] = s < S ? part_ml[(base0 + (int64_t)s * A.Hq) * 2 + 1] : 0.f;
+    mv[i] = s < S_all ? part_ml[(base0 + (int64_t)s * A.Hq) * 2] : -INFINITY;
+    lv[i] = s < S_all ? part_ml[(base0 + (int64_t)s * A.Hq) * 2 + 1] : 0.f;
   }
+  const int S = min(S_all, (L + split_items - 1) / split_items);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (d + 128 * i >= S) { mv[i] = -INFINITY; lv[i] = 0.f; }
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 8; ++i) mx = fmaxf(mx, mv[i]);
