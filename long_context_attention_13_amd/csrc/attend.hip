@@ -397,12 +397,6 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
     }
     if (whi < wlo) whi = wlo;
   }
-  const int L = nkv + (whi - wlo);
-  const int64_t wbase = (int64_t)b * A.W_buf + wlo;
-  const int p0 = split * split_items;
-  const int p1 = S == 1 ? L : min(L, p0 + split_items);
-  if (S > 1 && p0 >= L) return;             // an empty split: the merge does not read it
-
   __bf16* Kl = sm.Kl;
   __bf16* Vt = sm.Vt;
   float* sclo = sm.sclo;
@@ -410,10 +404,20 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
   int* okl = sm.okl;
   int* idxl = sm.idxl;
 
-  // the selected indices of this split's entry range, staged once
-  const int e_lo = p0, e_hi = min(p1, nkv);
-  if (QB == 1 && A.sparse)
-    for (int i = tid; i < e_hi - e_lo; i += NT) idxl[i] = A.idx[(int64_t)r * A.k + e_lo + i];
+  // the selected indices of this split's entry range, staged once; their
+  // bound does not depend on the window, so they are requested together with
+  // the row's window bounds
+  const int p0 = split * split_items;
+  const int e_lo = p0;
+  if (QB == 1 && A.sparse) {
+    const int e_end = min(p0 + split_items, A.k);
+    for (int i = tid; i < e_end - e_lo; i += NT) idxl[i] = A.idx[(int64_t)r * A.k + e_lo + i];
+  }
+
+  const int L = nkv + (whi - wlo);
+  const int64_t wbase = (int64_t)b * A.W_buf + wlo;
+  const int p1 = S == 1 ? L : min(L, p0 + split_items);
+  if (S > 1 && p0 >= L) return;             // an empty split: the merge does not read it
 
   // Q^T operand: this lane's head = (wave % (HQ/16))*16 + col, dims 32*ks + 8*g .. +7
   const int head = (wave % (HQ / 16)) * 16 + col;
