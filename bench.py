@@ -68,7 +68,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="run only the chunked-prefill leg")
     ap.add_argument("--unbatched", action="store_true",
-                    help="issue the step as the nine single calls instead of the batched calls")
+                    help="issue the step as the nine single calls instead of the decode-step call")
+    ap.add_argument("--three-calls", action="store_true",
+                    help="issue the step as compress_batch, the indexer and attend_batch instead of the "
+                         "decode-step call")
     ap.add_argument("--no-graph", action="store_true", help="issue the steps eagerly instead of replaying a graph")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -177,7 +180,7 @@ class Workload:
         # the batched form of the step: one compress launch for the three new blocks and one
         # attention launch (+ one merge) for both branches; job arrays built once per copy
         import ctypes
-        self.cjobs, self.ajobs, self._jobs = [], [], []
+        self.cjobs, self.ajobs, self.ijobs, self._jobs = [], [], [], []
         for c in range(copies):
             cj = [lca.compress_job(self.win_csa, self.gate_csa, self.bias_csa, 4, self.csa_tok0, self.one,
                                    self.csa_row0, 1, self.ent[c], lca.FP8E4M3, self.ent_sc[c]),
@@ -189,9 +192,12 @@ class Workload:
                                  self.wl, self.sink_csa, self.tau, self.out_csa, ws=self.ws_csa),
                   lca.attend_job(False, self.q_hca, self.hca[c], self.hca_sc[c], self.n_hca, self.win_hca,
                                  self.wb_hca, self.wl, self.sink_hca, self.tau, self.out_hca, ws=self.ws_hca)]
-            self._jobs.append((cj, aj))
+            ij = lca.index_job(self.qi, self.qi_sc, self.w, self.key[c], self.key_sc[c], self.n_csa, self.k,
+                               self.idx, self.ws_idx)
+            self._jobs.append((cj, aj, ij))
             self.cjobs.append((lca.CompressJob * 3)(*cj))
             self.ajobs.append((lca.AttendJob * 2)(*aj))
+            self.ijobs.append(ij)
         torch.cuda.synchronize()
 
     # -- the hot path ------------------------------------------------------
@@ -232,6 +238,12 @@ class Workload:
         if ev_idx is not None:
             ev_idx[1].record(torch.cuda.current_stream())
         lca.attend_batch(self.ajobs[c])
+
+    def step_fused(self, c):
+        """The same step as one library call (decode_step): the compress launch, the indexer
+        scan with the HCA branch's attention blocks in the same launch, the selection, the
+        CSA attention and the merge of both branches."""
+        self.lca.decode_step(self.cjobs[c], self.ijobs[c], self.ajobs[c])
 
     # -- algorithmic bytes -------------------------------------------------
     def index_bytes(self) -> float:
@@ -455,7 +467,7 @@ def main():
     wl = Workload(args.copies)
     stream = torch.cuda.current_stream()
     C = args.copies
-    run = wl.step if args.unbatched else wl.step_batched
+    run = wl.step if args.unbatched else wl.step_batched if args.three_calls else wl.step_fused
     for s in range(args.warmup):
         run(s % C)
     torch.cuda.synchronize()
@@ -490,15 +502,19 @@ def main():
             wl.index(c)
             ev_idx[s][1].record(stream)
             wl.attend(c)
-        else:
+        elif args.three_calls:
             wl.step_batched(c, ev_idx[s])
+        else:
+            wl.step_fused(c)
     end.record(stream)
     t_host = time.perf_counter() - t_host
     torch.cuda.synchronize()
-    if graphs is not None:
-        # events cannot be recorded inside a captured graph here: the indexer's
-        # launch duration comes from the same steps run eagerly, events around
-        # the indexer call on its stream
+    roof_eager = graphs is not None or not (args.unbatched or args.three_calls)
+    if roof_eager:
+        # events cannot be recorded inside a captured graph here, and the decode-step
+        # call runs the indexer's scan inside one launch with the HCA attention: the
+        # indexer's launch duration comes from the same steps run eagerly as separate
+        # calls, events around the indexer call on its stream
         for s in range(args.steps):
             c = s % C
             if args.unbatched:
@@ -536,7 +552,8 @@ def main():
                                "window 128, 64 query heads, head_dim 128",
                    "global_batch": wl.B, "seq_len": int(wl.L.max()), "parallelism": "single GPU"},
         "schedule": ("9 single calls" if args.unbatched else
-                     "compress_batch (3 blocks) -> indexer -> attend_batch (CSA + HCA)")
+                     "compress_batch (3 blocks) -> indexer -> attend_batch (CSA + HCA)" if args.three_calls else
+                     "decode_step (compress, indexer scan + HCA attention, selection, CSA attention, merge)")
                     + (f", graph of {C} steps replayed" if graphs is not None else ", eager"),
         "host_issue_us_per_step": round(t_host / args.steps * 1e6, 1),
         "step_hbm_gbs": round(step_gbs, 1),
@@ -545,7 +562,8 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "avg_launch_us": round(idx_ms * 1e3, 2), "algorithmic_bytes": int(idx_bytes),
-                     "timed_in": "eager pass of the same steps" if graphs is not None else "the timed steps"},
+                     "timed_in": "eager pass of the same steps as separate calls" if roof_eager
+                     else "the timed steps"},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)

@@ -266,6 +266,32 @@ typedef struct lca_attend_job {
 
 lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* stream);
 
+/*
+ * lca_decode_step -- one decode step of the layer pair in one call:
+ * lca_compress_batch(cjobs), then lca_lightning_index_topk(*ijob), then
+ * lca_attend_batch(ajobs), with the results of those three calls issued in
+ * that order (bit-identical), and with fewer dependent launches: the dense
+ * attention jobs (sparse = 0) run beside the indexer's scan, since they read
+ * nothing the indexer writes.  [release notes (agentlenshq.com), 壓縮稀疏注意力
+ * (CSA) / 重度壓縮注意力 (HCA): only the CSA branch depends on the top-k.]
+ *   cjobs    0 <= ncjobs <= LCA_MAX_COMPRESS_JOBS compress jobs (as lca_compress_batch)
+ *   ijob     the indexer call's arguments (as lca_lightning_index_topk)
+ *   ajobs    0 <= najobs <= LCA_MAX_ATTEND_JOBS attention jobs (as lca_attend_batch)
+ * Each part is validated as its own call.  Dense attention jobs must not
+ * read or write memory the indexer job writes (idx_out, score_out, its
+ * workspace); sparse jobs may read idx_out.  Host arrays are read during the
+ * call only.
+ */
+typedef struct lca_index_job {
+  const void* qi; lca_dtype qi_dt; const uint8_t* qi_scale; const float* w;
+  const void* ki; lca_dtype ki_dt; const uint8_t* ki_scale; const int32_t* n_elig;
+  int32_t B; int32_t Tq; int32_t H_I; int32_t d_I; int64_t N_cap; int32_t k;
+  int32_t* idx_out; double* score_out; void* ws; size_t ws_bytes;
+} lca_index_job;
+
+lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
+                           const lca_attend_job* ajobs, int32_t najobs, void* stream);
+
 /* Workspace bytes for the attention calls.  n_kv_max is k for
  * lca_sparse_mqa_attend and N_cap for lca_hca_attend; W_buf the window buffer
  * rows. */

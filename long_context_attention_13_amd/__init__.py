@@ -23,7 +23,7 @@ STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA
 
 EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
-           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws"]
+           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step"]
 MAX_COMPRESS_JOBS = 8
 MAX_ATTEND_JOBS = 4
 
@@ -64,6 +64,9 @@ def load(path: str = LIB_PATH):
     for name in ("lca_csa_compress", "lca_hca_compress"):
         getattr(L, name).restype = i32
         getattr(L, name).argtypes = comp
+    L.lca_decode_step.restype = i32
+    L.lca_decode_step.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
+                                  ctypes.POINTER(AttendJob), i32, vp]
     L.lca_attend_batch.restype = i32
     L.lca_attend_batch.argtypes = [ctypes.POINTER(AttendJob), i32, vp]
     L.lca_compress_batch.restype = i32
@@ -197,6 +200,38 @@ def attend_batch(jobs, stream=None):
     or a ctypes array of them built once."""
     arr = jobs if isinstance(jobs, ctypes.Array) else (AttendJob * len(jobs))(*jobs)
     _check(load().lca_attend_batch(arr, len(arr), _stream(stream)))
+
+
+class IndexJob(ctypes.Structure):
+    """lca_index_job: the argument list of one lightning_index_topk call."""
+    _fields_ = [("qi", ctypes.c_void_p), ("qi_dt", ctypes.c_int32), ("qi_scale", ctypes.c_void_p),
+                ("w", ctypes.c_void_p), ("ki", ctypes.c_void_p), ("ki_dt", ctypes.c_int32),
+                ("ki_scale", ctypes.c_void_p), ("n_elig", ctypes.c_void_p), ("B", ctypes.c_int32),
+                ("Tq", ctypes.c_int32), ("H_I", ctypes.c_int32), ("d_I", ctypes.c_int32), ("N_cap", ctypes.c_int64),
+                ("k", ctypes.c_int32), ("idx_out", ctypes.c_void_p), ("score_out", ctypes.c_void_p),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+def index_job(qi, qi_scale, w, ki, ki_scale, n_elig, k, idx_out, ws, score_out=None) -> IndexJob:
+    """The indexer part of decode_step, with the arguments of lightning_index_topk (the job
+    keeps its tensors alive while it is)."""
+    B, Tq, H = qi.shape[0], qi.shape[1], qi.shape[2]
+    dt = F32 if qi_scale is None else MXFP4
+    d = qi.shape[3] if dt == F32 else qi.shape[3] * 2
+    ptr = lambda t: None if t is None else t.data_ptr()
+    job = IndexJob(ptr(qi), dt, ptr(qi_scale), ptr(w), ptr(ki), dt, ptr(ki_scale), ptr(n_elig), B, Tq, H, d,
+                   ki.shape[1], int(k), ptr(idx_out), ptr(score_out), ptr(ws),
+                   0 if ws is None else ws.numel() * ws.element_size())
+    job._keep = (qi, qi_scale, w, ki, ki_scale, n_elig, idx_out, ws, score_out)
+    return job
+
+
+def decode_step(cjobs, ijob, ajobs, stream=None):
+    """One decode step (see lca_decode_step): compress jobs, the indexer job, attention jobs;
+    job lists may be prebuilt ctypes arrays."""
+    ca = cjobs if isinstance(cjobs, ctypes.Array) else (CompressJob * max(1, len(cjobs)))(*cjobs)
+    aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
+    _check(load().lca_decode_step(ca, len(cjobs), ctypes.byref(ijob), aa, len(ajobs), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -166,24 +166,40 @@ lca_status lca_hca_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const
                          B, nblk_max, D, dst, dst_dt, dst_scale, dst_rows, pooled, stream);
 }
 
-lca_status lca_compress_batch(const lca_compress_job* jobs, int32_t njobs, void* stream) {
-  REQ(njobs >= 1 && njobs <= LCA_MAX_COMPRESS_JOBS, LCA_EINVAL, "lca_compress_batch: njobs=%d outside [1, %d]",
-      njobs, LCA_MAX_COMPRESS_JOBS);
-  REQ(jobs != nullptr, LCA_EINVAL, "lca_compress_batch: jobs is NULL");
+}  // extern "C"
+
+namespace {
+
+lca_status compress_batch_check(const char* who, const lca_compress_job* jobs, int32_t njobs, int min_jobs,
+                                lca::CompressBatch* out) {
+  REQ(njobs >= min_jobs && njobs <= LCA_MAX_COMPRESS_JOBS, LCA_EINVAL, "%s: njobs=%d outside [%d, %d]", who, njobs,
+      min_jobs, LCA_MAX_COMPRESS_JOBS);
+  REQ(njobs == 0 || jobs != nullptr, LCA_EINVAL, "%s: jobs is NULL", who);
   static_assert(LCA_MAX_COMPRESS_JOBS == lca::MAX_COMPRESS_JOBS, "job limits agree");
-  lca::CompressBatch bt{};
+  lca::CompressBatch& bt = *out;
+  bt = lca::CompressBatch{};
   bt.njobs = njobs;
   for (int j = 0; j < njobs; ++j) {
     const lca_compress_job& J = jobs[j];
-    char name[64];
-    snprintf(name, sizeof(name), "lca_compress_batch: job %d", j);
+    char name[96];
+    snprintf(name, sizeof(name), "%s: compress job %d", who, j);
     const lca_status st = compress_check(name, 1024, J.x, J.x_dt, J.x_rows, J.gate, J.pos_bias, J.m, J.x_tok0, J.nblk,
                                          J.dst_row0, J.B, J.nblk_max, J.D, J.dst, J.dst_dt, J.dst_scale, J.dst_rows,
                                          J.pooled, &bt.job[j]);
     if (st != LCA_OK) return st;
-    REQ(J.x_dt == jobs[0].x_dt && J.D == jobs[0].D, LCA_ENOTSUP,
-        "lca_compress_batch: job %d has x_dt/D different from job 0", j);
+    REQ(J.x_dt == jobs[0].x_dt && J.D == jobs[0].D, LCA_ENOTSUP, "%s: x_dt/D differ from job 0", name);
   }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_compress_batch(const lca_compress_job* jobs, int32_t njobs, void* stream) {
+  lca::CompressBatch bt;
+  const lca_status st = compress_batch_check("lca_compress_batch", jobs, njobs, 1, &bt);
+  if (st != LCA_OK) return st;
   return hip_status(lca::launch_compress_batch(bt, (hipStream_t)stream), "lca_compress_batch");
 }
 
@@ -192,12 +208,17 @@ size_t lca_index_topk_ws(int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int64_
   return lca::index_ws_bytes(B, Tq, H_I, d_I, N_cap, k, lca::DT_MXFP4 /* same layout for both types */);
 }
 
-lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8_t* qi_scale, const float* w,
-                                    const void* ki, lca_dtype ki_dt, const uint8_t* ki_scale,
-                                    const int32_t* n_elig, int32_t B, int32_t Tq, int32_t H_I, int32_t d_I,
-                                    int64_t N_cap, int32_t k, int32_t* idx_out, double* score_out, void* ws,
-                                    size_t ws_bytes, void* stream) {
-  const char* name = "lca_lightning_index_topk";
+}  // extern "C"
+
+namespace {
+
+// Validation of one indexer call; on success *out holds the launch arguments
+// (B*Tq = 0 when there is nothing to do).
+lca_status index_check(const char* name, const void* qi, lca_dtype qi_dt, const uint8_t* qi_scale, const float* w,
+                       const void* ki, lca_dtype ki_dt, const uint8_t* ki_scale, const int32_t* n_elig, int32_t B,
+                       int32_t Tq, int32_t H_I, int32_t d_I, int64_t N_cap, int32_t k, int32_t* idx_out,
+                       double* score_out, void* ws, size_t ws_bytes, lca::IndexArgs* out) {
+  *out = lca::IndexArgs{};
   REQ(B >= 0 && Tq >= 0, LCA_EINVAL, "%s: B and Tq must be >= 0", name);
   REQ(k >= 1 && k <= 2048, LCA_EINVAL, "%s: k=%d outside [1, 2048]", name, k);
   REQ(N_cap >= 0 && N_cap < (1ll << 31), LCA_EINVAL, "%s: N_cap out of range", name);
@@ -228,24 +249,46 @@ lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8
   const size_t need = lca_index_topk_ws(B, Tq, H_I, d_I, N_cap, k);
   REQ(ws != nullptr && aligned16(ws), LCA_EWORKSPACE, "%s: workspace of %zu bytes required", name, need);
   REQ(ws_bytes >= need, LCA_EWORKSPACE, "%s: workspace too small (%zu < %zu)", name, ws_bytes, need);
-  lca::IndexArgs a{};
+  lca::IndexArgs& a = *out;
   a.qi = qi; a.dt = (int)qi_dt; a.qi_scale = qi_scale; a.w = w; a.ki = ki; a.ki_scale = ki_scale;
   a.n_elig = n_elig; a.B = B; a.Tq = Tq; a.H = H_I; a.d = d_I; a.N_cap = N_cap; a.k = k;
   a.idx_out = idx_out; a.score_out = score_out; a.ws = ws; a.ws_bytes = ws_bytes;
-  return hip_status(lca::launch_index(a, (hipStream_t)stream), name);
+  return ok();
 }
 
-lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* stream) {
-  REQ(njobs >= 1 && njobs <= LCA_MAX_ATTEND_JOBS, LCA_EINVAL, "lca_attend_batch: njobs=%d outside [1, %d]", njobs,
-      LCA_MAX_ATTEND_JOBS);
-  REQ(jobs != nullptr, LCA_EINVAL, "lca_attend_batch: jobs is NULL");
+}  // namespace
+
+extern "C" {
+
+lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8_t* qi_scale, const float* w,
+                                    const void* ki, lca_dtype ki_dt, const uint8_t* ki_scale,
+                                    const int32_t* n_elig, int32_t B, int32_t Tq, int32_t H_I, int32_t d_I,
+                                    int64_t N_cap, int32_t k, int32_t* idx_out, double* score_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  lca::IndexArgs a;
+  const lca_status st = index_check("lca_lightning_index_topk", qi, qi_dt, qi_scale, w, ki, ki_dt, ki_scale, n_elig,
+                                    B, Tq, H_I, d_I, N_cap, k, idx_out, score_out, ws, ws_bytes, &a);
+  if (st != LCA_OK || (int64_t)a.B * a.Tq == 0) return st;
+  return hip_status(lca::launch_index(a, (hipStream_t)stream), "lca_lightning_index_topk");
+}
+
+}  // extern "C"
+
+namespace {
+
+lca_status attend_batch_check(const char* who, const lca_attend_job* jobs, int32_t njobs, int min_jobs,
+                              lca::AttendBatch* out) {
+  REQ(njobs >= min_jobs && njobs <= LCA_MAX_ATTEND_JOBS, LCA_EINVAL, "%s: njobs=%d outside [%d, %d]", who, njobs,
+      min_jobs, LCA_MAX_ATTEND_JOBS);
+  REQ(njobs == 0 || jobs != nullptr, LCA_EINVAL, "%s: jobs is NULL", who);
   static_assert(LCA_MAX_ATTEND_JOBS == lca::MAX_ATTEND_JOBS, "job limits agree");
-  lca::AttendBatch bt{};
+  lca::AttendBatch& bt = *out;
+  bt = lca::AttendBatch{};
   bt.njobs = njobs;
   for (int j = 0; j < njobs; ++j) {
     const lca_attend_job& J = jobs[j];
-    char name[64];
-    snprintf(name, sizeof(name), "lca_attend_batch: job %d", j);
+    char name[96];
+    snprintf(name, sizeof(name), "%s: attention job %d", who, j);
     REQ(J.sparse == 0 || J.sparse == 1, LCA_EINVAL, "%s: sparse must be 0 or 1", name);
     const bool rows = (int64_t)J.B * J.Tq > 0;
     if (J.sparse) {
@@ -271,7 +314,36 @@ lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* str
     REQ((int64_t)J.B * J.Tq == 0 || lca::attend_batchable(a), LCA_ENOTSUP,
         "%s: dense rows grouped per sequence (many query rows, no split) are not batched; use lca_hca_attend", name);
   }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* stream) {
+  lca::AttendBatch bt;
+  const lca_status st = attend_batch_check("lca_attend_batch", jobs, njobs, 1, &bt);
+  if (st != LCA_OK) return st;
   return hip_status(lca::launch_attend_batch(bt, (hipStream_t)stream), "lca_attend_batch");
+}
+
+lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
+                           const lca_attend_job* ajobs, int32_t najobs, void* stream) {
+  const char* name = "lca_decode_step";
+  lca::CompressBatch cb;
+  lca_status st = compress_batch_check(name, cjobs, ncjobs, 0, &cb);
+  if (st != LCA_OK) return st;
+  REQ(ijob != nullptr, LCA_EINVAL, "%s: ijob is NULL", name);
+  const lca_index_job& I = *ijob;
+  lca::IndexArgs ia;
+  st = index_check("lca_decode_step: index job", I.qi, I.qi_dt, I.qi_scale, I.w, I.ki, I.ki_dt, I.ki_scale, I.n_elig,
+                   I.B, I.Tq, I.H_I, I.d_I, I.N_cap, I.k, I.idx_out, I.score_out, I.ws, I.ws_bytes, &ia);
+  if (st != LCA_OK) return st;
+  lca::AttendBatch ab;
+  st = attend_batch_check(name, ajobs, najobs, 0, &ab);
+  if (st != LCA_OK) return st;
+  return hip_status(lca::launch_decode_step(cb, ia, ab, (hipStream_t)stream), name);
 }
 
 size_t lca_attend_ws(int32_t B, int32_t Tq, int32_t Hq, int32_t D, int64_t n_kv_max, int64_t W_buf) {

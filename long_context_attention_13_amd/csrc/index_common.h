@@ -21,7 +21,6 @@ constexpr int MAXCH = 1024;        // chunks per row the candidate path handles
 constexpr int KROW = 20;           // LDS floats per key in the transpose buffer (16 + pad)
 constexpr int BITMAP_BITS = 1 << 18;
 
-static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------------------
 // Query state of one wavefront (up to two query rows of one sequence).

@@ -65,5 +65,15 @@ struct AttendBatch {                  // jobs share kv_dt and Hq; plans filled b
 };
 bool attend_batchable(const AttendArgs& a);
 hipError_t launch_attend_batch(const AttendBatch& bt, hipStream_t s);
+// the stages of launch_attend_batch: plans (splits, partial buffers, block
+// offsets), the attention launch over bt's blocks, the merge launch
+void attend_batch_plan(AttendBatch& bt);
+hipError_t launch_attend_batch_mfma(const AttendBatch& bt, hipStream_t s);
+hipError_t launch_attend_batch_merge(const AttendBatch& bt, hipStream_t s);
+
+// One decode step: the compress jobs, the indexer call, the attention jobs, in
+// that order and with the results of the three calls; the dense attention jobs
+// may run beside the indexer's scan.
+hipError_t launch_decode_step(const CompressBatch& cb, const IndexArgs& ia, const AttendBatch& ab, hipStream_t s);
 
 }  // namespace lca

@@ -195,3 +195,32 @@ def test_attend_batch_validation(L):
     # the chunked-prefill dense shape (many rows, no split) stays with lca_hca_attend
     assert attend_batch(L, [attend_job(Tq=8192, W_buf=8319, N_cap=2048, **dense)]) == 2
     assert attend_batch(L, [attend_job(k=1024, ws=None)]) == 4               # split partials need workspace
+
+
+def index_job(**kw):
+    a = dict(qi=FAKE, qi_dt=lca.MXFP4, qi_scale=FAKE, w=FAKE, ki=FAKE, ki_dt=lca.MXFP4, ki_scale=FAKE, n_elig=FAKE,
+             B=1, Tq=1, H_I=8, d_I=128, N_cap=1024, k=64, idx_out=FAKE, score_out=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lca.IndexJob(*a.values())
+
+
+def decode_step(L, cjobs, ij, ajobs, nc=None, na=None):
+    ca = (lca.CompressJob * max(1, len(cjobs)))(*cjobs)
+    aa = (lca.AttendJob * max(1, len(ajobs)))(*ajobs)
+    return L.lca_decode_step(ca, len(cjobs) if nc is None else nc, None if ij is None else ctypes.byref(ij), aa,
+                             len(ajobs) if na is None else na, None)
+
+
+def test_decode_step_validation(L):
+    assert decode_step(L, [], index_job(B=0), []) == 0                       # nothing to do
+    assert decode_step(L, [batch_job(B=0)], index_job(B=0), [attend_job(B=0)]) == 0
+    assert decode_step(L, [], None, []) == 1
+    assert decode_step(L, [batch_job()] * 9, index_job(B=0), []) == 1
+    assert decode_step(L, [], index_job(B=0), [attend_job()] * 5) == 1
+    assert decode_step(L, [], index_job(k=0), []) == 1
+    assert b"index job" in L.lca_last_error()
+    assert decode_step(L, [batch_job(m=2048)], index_job(B=0), []) == 2
+    assert b"compress job 0" in L.lca_last_error()
+    assert decode_step(L, [], index_job(B=0), [attend_job(), attend_job(Hq=32)]) == 2
+    assert b"attention job 1" in L.lca_last_error()
+    assert decode_step(L, [], index_job(ws=None), []) == 4
