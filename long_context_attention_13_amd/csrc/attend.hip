@@ -254,6 +254,10 @@ template <int KVDT, int HQ>
 static void launch_mfma_h(const AttendArgs& a, hipStream_t s, Plan P, float* ml, float* po) {
   constexpr int QB = att_qb<HQ>();
   if (!a.sparse && P.S == 1 && a.Tq >= 2 * QB) {
+    if (attend_dense_wide_applies(a)) {
+      (void)launch_attend_dense_wide(a, s);   // the caller reads hipGetLastError
+      return;
+    }
     dim3 grid(1, (unsigned)(a.B * ((a.Tq + QB - 1) / QB)));
     hipLaunchKernelGGL((attend_mfma_kernel<KVDT, HQ, QB>), grid, dim3(HQ * 4 * QB), 0, s, a, 1, P.items, ml, po);
   } else {

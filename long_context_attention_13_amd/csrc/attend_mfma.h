@@ -471,4 +471,10 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
   if (A.lse && d == 0) A.lse[(int64_t)r * A.Hq + h] = (M + log2f(Z)) * LN2;
 }
 
+// The dense attention of many query rows of one sequence with 64 heads and
+// bf16 entries, a wavefront per row (attend_dense.hip): used for the grouped
+// (single-split) dense layout when it applies.
+bool attend_dense_wide_applies(const AttendArgs& a);
+hipError_t launch_attend_dense_wide(const AttendArgs& a, hipStream_t s);
+
 }  // namespace lca

@@ -130,11 +130,12 @@ def test_empty_lists_give_sink_only():
     np.testing.assert_allclose(l, np.broadcast_to(sink, l.shape), rtol=1e-6)
 
 
-@pytest.mark.parametrize("Hq,kv_dt", [(64, lca.FP8E4M3), (16, lca.BF16)])
+@pytest.mark.parametrize("Hq,kv_dt", [(64, lca.FP8E4M3), (64, lca.BF16), (16, lca.BF16)])
 def test_dense_row_groups(Hq, kv_dt):
-    """Dense prefill rows processed in groups that share staged tiles: a
-    ragged last group, rows of two sequences, n_elig from 0 up, windows that
-    start short (sequence start), an empty window and windows in any order."""
+    """Dense prefill rows processed in groups that share staged tiles (64 heads
+    with bf16 entries: a wavefront per row and all heads): a ragged last group,
+    rows of two sequences, n_elig from 0 up, windows that start short
+    (sequence start), an empty window and windows in any order."""
     B, Tq, N_cap, W = 2, 301, 700, 128
     W_buf = W - 1 + Tq
     g, q, kv, kv_sc, win, sink = make(71 + Hq, B, Tq, Hq, N_cap, W_buf, kv_dt, lca.BF16)
