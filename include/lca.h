@@ -244,9 +244,10 @@ lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dty
  *            1 <= njobs <= LCA_MAX_ATTEND_JOBS.
  * Each job is validated as its single call; in addition every job takes bf16
  * q and window and bf16 or FP8 entries, all jobs share kv_dt and Hq, and no
- * job may be a dense call with many query rows per sequence and no split
- * (the chunked-prefill shape, which the single call runs with grouped rows):
- * LCA_ENOTSUP otherwise.  Jobs must not share output, lse or workspace
+ * job may have the chunked-prefill shape (many query rows and no split: a
+ * dense call with several rows per sequence, or a sparse call with bf16
+ * entries and 64 heads, which the single call runs with kernels of their
+ * own): LCA_ENOTSUP otherwise.  Jobs must not share output, lse or workspace
  * memory.  On any invalid job nothing is enqueued and the message names it.
  */
 #define LCA_MAX_ATTEND_JOBS 4

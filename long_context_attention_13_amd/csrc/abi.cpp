@@ -312,7 +312,7 @@ lca_status attend_batch_check(const char* who, const lca_attend_job* jobs, int32
         "%s: batched attention takes bf16 queries and windows and bf16 or FP8 entries", name);
     REQ(J.kv_dt == jobs[0].kv_dt && J.Hq == jobs[0].Hq, LCA_ENOTSUP, "%s: kv_dt/Hq differ from job 0", name);
     REQ((int64_t)J.B * J.Tq == 0 || lca::attend_batchable(a), LCA_ENOTSUP,
-        "%s: dense rows grouped per sequence (many query rows, no split) are not batched; use lca_hca_attend", name);
+        "%s: prefill-shaped calls (many query rows, no split) are not batched; use the single call", name);
   }
   return ok();
 }

@@ -260,6 +260,8 @@ static void launch_mfma_h(const AttendArgs& a, hipStream_t s, Plan P, float* ml,
     }
     dim3 grid(1, (unsigned)(a.B * ((a.Tq + QB - 1) / QB)));
     hipLaunchKernelGGL((attend_mfma_kernel<KVDT, HQ, QB>), grid, dim3(HQ * 4 * QB), 0, s, a, 1, P.items, ml, po);
+  } else if (a.sparse && P.S == 1 && attend_sparse_wide_applies(a)) {
+    (void)launch_attend_sparse_wide(a, s);   // the caller reads hipGetLastError
   } else {
     dim3 grid(P.S, (unsigned)(a.B * a.Tq));
     hipLaunchKernelGGL((attend_mfma_kernel<KVDT, HQ, 1>), grid, dim3(HQ * 4), 0, s, a, P.S, P.items, ml, po);
@@ -297,14 +299,16 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 }
 
 // A call the batch launcher can take: the bf16-MFMA path in its one-row,
-// split layout (not the grouped dense-prefill layout).
+// split layout (not a prefill-shaped call -- many rows, no split -- which
+// the single call runs with the grouped dense layout or the wide kernels).
 bool attend_batchable(const AttendArgs& a) {
   const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8);
   if (!mfma) return false;
   const int64_t R = (int64_t)a.B * a.Tq;
   const Plan P = att_plan(R, a.sparse ? a.k : a.N_cap, a.W_buf);
   const int qb = a.Hq == 16 ? att_qb<16>() : a.Hq == 32 ? att_qb<32>() : att_qb<64>();
-  return !(!a.sparse && P.S == 1 && a.Tq >= 2 * qb);
+  if (a.sparse) return !(P.S == 1 && attend_sparse_wide_applies(a));
+  return !(P.S == 1 && a.Tq >= 2 * qb);
 }
 
 void attend_batch_plan(AttendBatch& bt) {

@@ -476,5 +476,8 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
 // (single-split) dense layout when it applies.
 bool attend_dense_wide_applies(const AttendArgs& a);
 hipError_t launch_attend_dense_wide(const AttendArgs& a, hipStream_t s);
+// The same for the sparse lists of many query rows (one list per row).
+bool attend_sparse_wide_applies(const AttendArgs& a);
+hipError_t launch_attend_sparse_wide(const AttendArgs& a, hipStream_t s);
 
 }  // namespace lca

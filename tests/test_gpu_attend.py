@@ -120,6 +120,30 @@ def test_prefill_rows_with_sliding_windows():
     assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse sparse")
 
 
+@pytest.mark.parametrize("out_dt", [lca.BF16, lca.F32])
+def test_sparse_prefill_rows_64_heads(out_dt):
+    """Sparse rows of a prefill chunk with 64 heads and bf16 entries (one
+    workgroup per row, no split): lists of 200 selected entries (not a whole
+    number of tiles), -1 padding in some rows and a row with no entry, rows
+    of two sequences, windows that slide, start short or are empty."""
+    B, Tq, Hq, N_cap, W = 2, 150, 64, 700, 128
+    W_buf = W - 1 + Tq
+    g, q, kv, kv_sc, win, sink = make(83, B, Tq, Hq, N_cap, W_buf, lca.BF16, lca.BF16)
+    wb = np.stack([np.arange(Tq), np.arange(Tq)]).astype(np.int32)
+    wl = np.full((B, Tq), W, np.int32)
+    wl[1, :30] = np.arange(30)                  # the second sequence starts inside the chunk
+    wb[1, :30] += W - 1 - np.arange(30)
+    wl[0, 11] = 0                               # an empty window
+    sel = np.stack([np.stack([np.sort(g.choice(N_cap, 200, replace=False)) for _ in range(Tq)])
+                    for _ in range(B)]).astype(np.int32)
+    sel[0, 3, 150:] = -1                        # a short list, padded
+    sel[1, 7, :] = -1                           # no selected entry at all
+    o, l, ro, rl = run(True, q, lca.BF16, kv, lca.BF16, None, sel, win, lca.BF16, wb, wl, sink,
+                       1 / math.sqrt(128), out_dt)
+    assert_rows_close(o, ro, 2e-2, "out")
+    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
+
+
 def test_empty_lists_give_sink_only():
     B, Hq = 2, 16
     g, q, kv, kv_sc, win, sink = make(61, B, 1, Hq, 64, 8, lca.F32, lca.F32)
