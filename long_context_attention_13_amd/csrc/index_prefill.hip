@@ -441,8 +441,19 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
 }
 
 // ------------------------------------------------------------------------
-// Select pass: one wavefront per row.
+// Select pass: one workgroup of PS_NW wavefronts per row.  The candidate
+// lists are gathered into LDS, every thread holds PS_CPT of them in
+// registers (item tid + PS_NT*m), and the phases -- radix select of the
+// fp32 threshold, certification, band re-score, ascending emission through a
+// bitmap over [0, n) -- are split over the workgroup; the band re-score (at
+// most 64 entries) is wavefront 0's.  Every decision is the same in every
+// wavefront (all read the same LDS), so the exits are uniform.
 // ------------------------------------------------------------------------
+constexpr int PS_NW = 4;
+constexpr int PS_NT = PS_NW * 64;
+constexpr int PS_CPT = PF_CAND / PS_NT;   // candidates per thread
+static_assert(PS_CPT * PS_NT == PF_CAND, "candidates split evenly");
+
 struct PfSelShared {
   uint32_t cs[PF_CAND];     // candidate scores (fp32 bits); then the MFMA transpose
                             // buffer, then the bitmap (the scores live in registers)
@@ -450,32 +461,36 @@ struct PfSelShared {
   uint32_t hist[256];
   float wl[32];
   int32_t bj[PF_BAND];
+  uint32_t rmax[PS_NW], rmin[PS_NW];
+  int nin, nband, wsum[PS_NW];
 };
 static_assert(sizeof(float) * WBUF <= sizeof(uint32_t) * PF_CAND, "transpose buffer fits the score array");
 static_assert(PF_NMAX / 32 <= PF_CAND, "bitmap fits the score array");
 
 template <int HP>
-__global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int KC) {
+__global__ __launch_bounds__(PS_NT) void pf_select_kernel(IndexArgs A, PfWs W, int KC) {
   extern __shared__ __align__(16) char smem[];
   PfSelShared& L = *(PfSelShared*)smem;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t r = blockIdx.x;
   const int n = A.n_elig[r];
   const int kk = min(n, A.k);
   int32_t* out = A.idx_out + r * A.k;
   double* sout = A.score_out ? A.score_out + r * A.k : nullptr;
   auto enqueue = [&]() {
-    if (lane == 0) {
+    if (tid == 0) {
       const int p = atomicAdd(&W.queue[0], 1);
       W.queue[1 + p] = (int)r;
     }
   };
   if (n <= A.k) {
-    for (int i = lane; i < A.k; i += 64) out[i] = i < n ? i : -1;
+    for (int i = tid; i < A.k; i += PS_NT) out[i] = i < n ? i : -1;
     if (sout) enqueue();                  // scores of every entry: the fallback computes them
     return;
   }
   if (W.flags[r] != 0) { enqueue(); return; }
+  // list counts and offsets: the same in every wavefront
   const int nl = ((n + KC - 1) / KC) * 4;                 // lists (key range, lane group)
   const int cl = lane < nl ? W.cnt[r * PF_NKC * 4 + lane] : 0;
   if (__ballot(cl > PF_LCAP)) { enqueue(); return; }
@@ -485,10 +500,10 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
   const int loff = incl - cl;
   // gather the lists into LDS with direct global->LDS dword loads: the high
   // halves (scores) into cs, the low halves (indices) into cj, every list at
-  // its flat offset; all loads are in flight at once
+  // its flat offset; wavefront w takes lists w, w + PS_NW, ...
   const uint32_t* lw = (const uint32_t*)(W.cand + r * PF_NKC * 4 * PF_LCAP);
 #pragma unroll 1
-  for (int Lx = 0; Lx < nl; ++Lx) {
+  for (int Lx = wave; Lx < nl; Lx += PS_NW) {
     const int cn = __builtin_amdgcn_readlane(cl, Lx);
     const int o = __builtin_amdgcn_readlane(loff, Lx);
     const uint32_t* src = lw + (int64_t)Lx * PF_LCAP * 2;
@@ -503,45 +518,52 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
-  wave_lds_sync();
-  uint32_t sv[PF_CPL];
+  __syncthreads();
+  uint32_t sv[PS_CPT];
 #pragma unroll
-  for (int m = 0; m < PF_CPL; ++m) {
-    const int i = lane + 64 * m;
+  for (int m = 0; m < PS_CPT; ++m) {
+    const int i = tid + PS_NT * m;
     sv[m] = i < total ? L.cs[i] : 0u;
   }
   // exact radix select (8-bit digits) of the kk-th largest s32, from the first
   // byte where the largest and smallest candidate differ
   uint32_t vmax = 0, vmin = ~0u;
 #pragma unroll
-  for (int m = 0; m < PF_CPL; ++m) {
-    if (lane + 64 * m < total) { vmax = max(vmax, sv[m]); vmin = min(vmin, sv[m]); }
+  for (int m = 0; m < PS_CPT; ++m) {
+    if (tid + PS_NT * m < total) { vmax = max(vmax, sv[m]); vmin = min(vmin, sv[m]); }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, o, WAVE));
     vmin = min(vmin, (uint32_t)__shfl_xor((int)vmin, o, WAVE));
   }
+  if (lane == 0) { L.rmax[wave] = vmax; L.rmin[wave] = vmin; }
+  for (int i = tid; i < 256; i += PS_NT) L.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < PS_NW; ++w) { vmax = max(vmax, L.rmax[w]); vmin = min(vmin, L.rmin[w]); }
   const int top = vmax == vmin ? 0 : (31 - __clz(vmax ^ vmin)) / 8 * 8;
   uint32_t mask = top == 24 ? 0u : ~((1u << (top + 8)) - 1u);
   uint32_t prefix = vmax & mask;
   int rem = kk;
 #pragma unroll 1
   for (int shift = top; shift >= 0; shift -= 8) {
-    for (int i = lane; i < 256; i += 64) L.hist[i] = 0;
-    wave_lds_sync();
 #pragma unroll
-    for (int m = 0; m < PF_CPL; ++m) {
-      const int i = lane + 64 * m;
+    for (int m = 0; m < PS_CPT; ++m) {
+      const int i = tid + PS_NT * m;
       if (i < total && (sv[m] & mask) == prefix) atomicAdd(&L.hist[(sv[m] >> shift) & 255u], 1u);
     }
-    wave_lds_sync();
+    __syncthreads();
+    // every wavefront finds the same digit from the same histogram
     int above;
     const int d = pf_hist_digit(L.hist, rem, &above);
     rem -= above;
     prefix |= (uint32_t)d << shift;
     mask |= 255u << shift;
-    wave_lds_sync();
+    __syncthreads();
+    if (shift > 0)
+      for (int i = tid; i < 256; i += PS_NT) L.hist[i] = 0;
+    __syncthreads();
   }
   const double eps = (double)(A.H + 1) * 0x1p-24 * 1.001;
   const double Td = (double)__uint_as_float(prefix);
@@ -549,76 +571,96 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
   if (!(Td * (1.0 - eps) >= t * (1.0 + eps))) { enqueue(); return; }
   const double hi = Td * (1.0 + eps) / (1.0 - eps);
   const double lo = Td * (1.0 - eps) / (1.0 + eps);
-  // definitely-in count and the band
-  int nin = 0, nband = 0;
+  // definitely-in count and the band (its order does not matter: the band
+  // is ranked by (score, index) and emitted through the bitmap)
+  if (tid == 0) { L.nin = 0; L.nband = 0; }
+  __syncthreads();
+  int nin = 0;
 #pragma unroll
-  for (int m = 0; m < PF_CPL; ++m) {
-    const int i = lane + 64 * m;
+  for (int m = 0; m < PS_CPT; ++m) {
+    const int i = tid + PS_NT * m;
     const double x = (double)__uint_as_float(sv[m]);
     const bool valid = i < total;
     nin += __popcll(__ballot(valid && x > hi));
     const bool inb = valid && x >= lo && x <= hi;
     const uint64_t bm = __ballot(inb);
-    if (inb) {
-      const int p = nband + lanes_below(bm);
-      if (p < PF_BAND) L.bj[p] = L.cj[i];
+    if (bm) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&L.nband, __popcll(bm));
+      base = __shfl(base, 0, WAVE);
+      if (inb) {
+        const int p = base + lanes_below(bm);
+        if (p < PF_BAND) L.bj[p] = L.cj[i];
+      }
     }
-    nband += __popcll(bm);
   }
+  if (lane == 0) atomicAdd(&L.nin, nin);
+  if (lane < 32 && wave == 0) L.wl[lane] = lane < A.H ? A.w[r * A.H + lane] : 0.f;
+  __syncthreads();
+  const int nband = L.nband;
+  nin = L.nin;
   const int need = kk - nin;
   if (nband > PF_BAND || need < 1 || need > nband) { enqueue(); return; }
-  // exact scores of the band (MFMA dots are exact here: the score pass checked
-  // the envelope; a key outside it would have flagged the row)
+  // exact scores of the band, wavefront 0 (MFMA dots are exact here: the
+  // score pass checked the envelope; a key outside it would have flagged the row)
   Rows rw;
   rw.b = (int)(r / A.Tq);
   rw.r[0] = (int)r; rw.r[1] = -1;
   rw.n[0] = nband; rw.n[1] = 0;
-  if (lane < 32) L.wl[lane] = lane < A.H ? A.w[r * A.H + lane] : 0.f;
-  wave_lds_sync();
   MxQuery Q;
-  mx_load_query<HP>(A, rw, Q);
-  const int jm = lane < nband ? L.bj[lane] : 0;
-  uint64_t key;
-  {
-    MxTiles T;
-    bool ix;
-    MxW<HP, 1> W;
-    mx_load_weights<HP, 1>(L.wl, W);
-    mx_load_gather(A, rw.b, jm, nband, T);
-    mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, W, &key, ix);
-    if (ix) key = mx_score_exact(A, (int)r, rw.b, jm, L.wl);
-    if (lane >= nband) key = 0;
-  }
-  int rank = 0;
+  int jm = 0;
+  bool bsel = false;
+  if (wave == 0) {
+    mx_load_query<HP>(A, rw, Q);
+    jm = lane < nband ? L.bj[lane] : 0;
+    uint64_t key;
+    {
+      MxTiles T;
+      bool ix;
+      MxW<HP, 1> Wt;
+      mx_load_weights<HP, 1>(L.wl, Wt);
+      mx_load_gather(A, rw.b, jm, nband, T);
+      mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, Wt, &key, ix);
+      if (ix) key = mx_score_exact(A, (int)r, rw.b, jm, L.wl);
+      if (lane >= nband) key = 0;
+    }
+    int rank = 0;
 #pragma unroll 1
-  for (int e = 0; e < nband; ++e) {
-    const uint64_t ke = ((uint64_t)readlane_u32((uint32_t)(key >> 32), e) << 32) | readlane_u32((uint32_t)key, e);
-    const int je = (int)readlane_u32((uint32_t)jm, e);
-    rank += (ke > key) || (ke == key && je < jm);
+    for (int e = 0; e < nband; ++e) {
+      const uint64_t ke = ((uint64_t)readlane_u32((uint32_t)(key >> 32), e) << 32) | readlane_u32((uint32_t)key, e);
+      const int je = (int)readlane_u32((uint32_t)jm, e);
+      rank += (ke > key) || (ke == key && je < jm);
+    }
+    bsel = lane < nband && rank < need;
   }
-  const bool bsel = lane < nband && rank < need;
+  __syncthreads();                        // the transpose buffer becomes the bitmap
   // ascending emission through a bitmap over [0, n)
   uint32_t* bitmap = L.cs;
   const int nw = (n + 31) >> 5;
-  for (int i = lane; i < nw; i += 64) bitmap[i] = 0;
-  wave_lds_sync();
+  for (int i = tid; i < nw; i += PS_NT) bitmap[i] = 0;
+  __syncthreads();
 #pragma unroll
-  for (int m = 0; m < PF_CPL; ++m) {
-    const int i = lane + 64 * m;
+  for (int m = 0; m < PS_CPT; ++m) {
+    const int i = tid + PS_NT * m;
     if (i < total && (double)__uint_as_float(sv[m]) > hi) {
       const int j = L.cj[i];
       atomicOr(&bitmap[j >> 5], 1u << (j & 31));
     }
   }
   if (bsel) atomicOr(&bitmap[jm >> 5], 1u << (jm & 31));
-  wave_lds_sync();
-  const int wpl = (nw + 63) >> 6;
-  const int w0 = lane * wpl, w1 = min(nw, w0 + wpl);
+  __syncthreads();
+  // thread t owns words [t*wpt, (t+1)*wpt); the workgroup scan of their
+  // counts gives each its first output position
+  const int wpt = (nw + PS_NT - 1) / PS_NT;
+  const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
   int mine = 0;
   for (int w = w0; w < w1; ++w) mine += __popc(bitmap[w]);
-  int pos = wave_incl_scan_dpp(mine) - mine;
+  const int winc = wave_incl_scan_dpp(mine);
+  if (lane == 63) L.wsum[wave] = winc;
+  __syncthreads();
+  int pos = winc - mine;
+  for (int w = 0; w < wave; ++w) pos += L.wsum[w];
   int32_t* outl = L.cj;
-  wave_lds_sync();
   for (int w = w0; w < w1; ++w) {
     uint32_t bits = bitmap[w];
     while (bits) {
@@ -626,28 +668,30 @@ __global__ __launch_bounds__(64) void pf_select_kernel(IndexArgs A, PfWs W, int 
       bits &= bits - 1;
       if (pos < A.k) {
         out[pos] = w * 32 + bit;
-        outl[pos] = w * 32 + bit;
+        if (sout) outl[pos] = w * 32 + bit;
       }
       ++pos;
     }
   }
   if (sout) {
-    // exact scores of every selected entry, 64 at a time
-    wave_lds_sync();
+    // exact scores of every selected entry, 64 at a time, wavefront 0
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll 1
-    for (int i0 = 0; i0 < kk; i0 += 64) {
-      const int cntr = min(64, kk - i0);
-      const int je = lane < cntr ? outl[i0 + lane] : 0;
-      rw.n[0] = cntr;
-      MxTiles T;
-      bool ix;
-      uint64_t k2;
-      MxW<HP, 1> W;
-      mx_load_weights<HP, 1>(L.wl, W);
-      mx_load_gather(A, rw.b, je, cntr, T);
-      mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, W, &k2, ix);
-      if (ix) k2 = mx_score_exact(A, (int)r, rw.b, je, L.wl);
-      if (lane < cntr) sout[i0 + lane] = key_score(k2);
+      for (int i0 = 0; i0 < kk; i0 += 64) {
+        const int cntr = min(64, kk - i0);
+        const int je = lane < cntr ? outl[i0 + lane] : 0;
+        rw.n[0] = cntr;
+        MxTiles T;
+        bool ix;
+        uint64_t k2;
+        MxW<HP, 1> Wt;
+        mx_load_weights<HP, 1>(L.wl, Wt);
+        mx_load_gather(A, rw.b, je, cntr, T);
+        mx_score_round<HP, 1>(A, rw, Q, T, 0, (float*)L.cs, Wt, &k2, ix);
+        if (ix) k2 = mx_score_exact(A, (int)r, rw.b, je, L.wl);
+        if (lane < cntr) sout[i0 + lane] = key_score(k2);
+      }
     }
   }
 }
@@ -695,7 +739,7 @@ static hipError_t launch_pf(const IndexArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((pf_score_kernel<HP>), dim3((unsigned)((a.Tq + PF_QROWS - 1) / PF_QROWS), PF_NKC, (unsigned)a.B),
                      dim3(256), (size_t)2 * PF_STAGE_B, s, a, W, KC);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((pf_select_kernel<HP>), dim3((unsigned)R), dim3(64), sizeof(PfSelShared), s, a, W, KC);
+  hipLaunchKernelGGL((pf_select_kernel<HP>), dim3((unsigned)R), dim3(PS_NT), sizeof(PfSelShared), s, a, W, KC);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned fg = (unsigned)(R < PF_FALLBACK_GRID ? R : PF_FALLBACK_GRID);
   hipLaunchKernelGGL((pf_fallback_kernel<HP>), dim3(fg), dim3(SEL_THREADS), select_smem(a.dt, a.H, a.d), s, a, W);
