@@ -28,7 +28,7 @@ namespace lca {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int DW_ROWS = 4;                   // query rows per workgroup
-constexpr int DW_NT = 512;                   // threads: (row, half of the heads) per wavefront
+constexpr int DW_NT = DW_ROWS * 128;         // threads: (row, half of the heads) per wavefront
 constexpr int DW_KROW = 136;                 // bf16 per staged K row (128 + pad)
 constexpr int DW_VROW = 72;                  // bf16 per staged V^T row (64 + pad)
 
@@ -43,44 +43,57 @@ struct DwShared {
 // column of item e of a tile in the staged V^T rows: bits 2 and 3 swapped
 __device__ __forceinline__ int dw_col(int e) { return (e & ~15) | (e & 3) | ((e & 4) << 1) | ((e & 8) >> 1); }
 
-// One staging task per thread: items 2*pr, 2*pr + 1 of the tile, dims
-// 8*cq .. +7 (pr = t % 32, cq = t / 32).  An item is an entry (kind 0), a
-// window token (1) or nothing (-1); each load reads a valid row.
+// Staging of a tile by NT threads: task (pr, cq) = items 2*pr, 2*pr + 1 of
+// the tile, dims 8*cq .. +7 (32 x 16 tasks); thread t takes pr = t % 32 and
+// cq = t / 32 + (NT / 32) * c.  An item is an entry (kind 0), a window token
+// (1) or nothing (-1); each load reads a valid row.
+template <int NT>
 struct DwRegs {
-  int4 v[2];
+  int4 v[512 / NT][2];
   int kind[2];
 };
 
-__device__ __forceinline__ void dw_fetch(const AttendArgs& A, int b, int64_t wbase, int nkv, int t0, int L, DwRegs& R) {
-  const int t = threadIdx.x, pr = t & 31, cq = t >> 5;
+template <int NT>
+__device__ __forceinline__ void dw_fetch(const AttendArgs& A, int b, int64_t wbase, int nkv, int t0, int L,
+                                         DwRegs<NT>& R) {
+  const int t = threadIdx.x, pr = t & 31, cq0 = t >> 5;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int p = t0 + 2 * pr + u;
     const int kind = p < L ? (p < nkv ? (p < A.N_cap ? 0 : -1) : 1) : -1;
     const uint16_t* row = kind == 1 ? (const uint16_t*)A.win + (wbase + (p - nkv)) * 128
                                     : (const uint16_t*)A.kv + ((int64_t)b * A.N_cap + (kind == 0 ? p : 0)) * 128;
-    R.v[u] = *(const int4*)(row + cq * 8);
+#pragma unroll
+    for (int c = 0; c < 512 / NT; ++c) R.v[c][u] = *(const int4*)(row + (cq0 + (NT / 32) * c) * 8);
     R.kind[u] = kind;
   }
 }
 
-__device__ __forceinline__ void dw_store(const DwRegs& R, DwShared::Tile& T) {
-  const int t = threadIdx.x, pr = t & 31, cq = t >> 5;
-  int4 v[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    v[u] = R.kind[u] >= 0 ? R.v[u] : make_int4(0, 0, 0, 0);
-    *(int4*)&T.Kl[(2 * pr + u) * DW_KROW + cq * 8] = v[u];
-    if (cq == 0) T.okl[2 * pr + u] = R.kind[u] >= 0;
-  }
-  // V^T: dword (row d, column pair) = dim d of items 2pr (low half) and 2pr + 1
+template <int NT>
+__device__ __forceinline__ void dw_store(const DwRegs<NT>& R, DwShared::Tile& T) {
+  const int t = threadIdx.x, pr = t & 31, cq0 = t >> 5;
   uint32_t* vt = (uint32_t*)T.Vt + dw_col(2 * pr) / 2;
-  const uint32_t* a = (const uint32_t*)&v[0];
-  const uint32_t* c = (const uint32_t*)&v[1];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    vt[(cq * 8 + 2 * q) * (DW_VROW / 2)] = __builtin_amdgcn_perm(c[q], a[q], 0x05040100u);
-    vt[(cq * 8 + 2 * q + 1) * (DW_VROW / 2)] = __builtin_amdgcn_perm(c[q], a[q], 0x07060302u);
+  for (int c = 0; c < 512 / NT; ++c) {
+    const int cq = cq0 + (NT / 32) * c;
+    int4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      v[u] = R.kind[u] >= 0 ? R.v[c][u] : make_int4(0, 0, 0, 0);
+      *(int4*)&T.Kl[(2 * pr + u) * DW_KROW + cq * 8] = v[u];
+    }
+    // V^T: dword (row d, column pair) = dim d of items 2pr (low half) and 2pr + 1
+    const uint32_t* a = (const uint32_t*)&v[0];
+    const uint32_t* e = (const uint32_t*)&v[1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      vt[(cq * 8 + 2 * q) * (DW_VROW / 2)] = __builtin_amdgcn_perm(e[q], a[q], 0x05040100u);
+      vt[(cq * 8 + 2 * q + 1) * (DW_VROW / 2)] = __builtin_amdgcn_perm(e[q], a[q], 0x07060302u);
+    }
+  }
+  if (cq0 == 0) {
+    T.okl[2 * pr] = R.kind[0] >= 0;
+    T.okl[2 * pr + 1] = R.kind[1] >= 0;
   }
 }
 
@@ -176,7 +189,7 @@ __device__ __forceinline__ void dw_finish(const AttendArgs& A, int r, int head, 
   if (A.lse && h == 0) A.lse[(int64_t)r * 64 + head] = (M + log2f(Z)) * LN2;
 }
 
-__global__ __launch_bounds__(DW_NT, 1) void attend_dense_wide_kernel(AttendArgs A) {
+__global__ __launch_bounds__(DW_NT, 512 / DW_NT) void attend_dense_wide_kernel(AttendArgs A) {
   __shared__ DwShared sm;
   const int ngrp = (A.Tq + DW_ROWS - 1) / DW_ROWS;
   const int b = blockIdx.x / ngrp;
@@ -226,7 +239,7 @@ __global__ __launch_bounds__(DW_NT, 1) void attend_dense_wide_kernel(AttendArgs 
   // wavefront is done with the tile before the current one, and tile t0 is
   // written), tile t0 + 64 goes to the other buffer, tile t0 + 128 is
   // requested, and tile t0 is computed
-  DwRegs R;
+  DwRegs<DW_NT> R;
   if (L > 0) {
     dw_fetch(A, b, wbase, nkv, 0, L, R);
     dw_store(R, sm.t[0]);
