@@ -39,7 +39,7 @@
 namespace lca {
 
 constexpr int PF_QROWS = 64;          // query rows per score workgroup (16 per wavefront)
-constexpr int PF_STAGE = 512;         // keys per LDS stage
+constexpr int PF_STAGE = 256;         // keys per LDS stage (3 workgroups per CU: the registers allow 3, the LDS 4)
 constexpr int PF_CODE_B = PF_STAGE * 64;
 constexpr int PF_STAGE_B = PF_CODE_B + PF_STAGE * 4;
 constexpr int PF_NKC = 16;            // key ranges per row
@@ -340,14 +340,14 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
     const int sj = j0 + st * PF_STAGE;
     char* base = smem + (st & 1) * PF_STAGE_B;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int ci = wave * 512 + u * 64 + lane;
+    for (int u = 0; u < PF_STAGE / 64; ++u) {
+      const int ci = wave * PF_STAGE + u * 64 + lane;
       const int tile = ci >> 6, blk = (ci >> 4) & 3, kt = ci & 15;
       const int j = min(sj + tile * 16 + kt, (int)A.N_cap - 1);
       __builtin_amdgcn_global_load_lds((const void*)(kbase + (int64_t)j * 64 + blk * 16),
-                                       (void*)(base + (wave * 512 + u * 64) * 16), 16, 0, 0);
+                                       (void*)(base + (wave * PF_STAGE + u * 64) * 16), 16, 0, 0);
     }
-    if (wave < 2) {
+    if (wave * 64 + lane < PF_STAGE / 4) {      // 16 bytes = the scales of 4 keys a lane
       const int j = min(sj + 4 * (wave * 64 + lane), (int)A.N_cap - 4);
       __builtin_amdgcn_global_load_lds((const void*)(sbase + (int64_t)j * 4),
                                        (void*)(base + PF_CODE_B + wave * 64 * 16), 16, 0, 0);
