@@ -2,7 +2,8 @@
 and lca_attend_batch issued in that order: with the HCA attention running
 inside the indexer's scan launch (FP8 entries, one query row per sequence;
 bf16 entries, two rows per sequence so that two rows share a scan wavefront),
-with an indexer that has no scan (a short cache: the unfused order), and
+with an indexer that has no scan (a short cache: the unfused order), with
+rows written by the step's own compress jobs that decide its results, and
 captured in a graph.  Inputs are seeded N(0, 1)."""
 import math
 
@@ -132,3 +133,37 @@ def test_step_graph_replays():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(st.outputs(), ref)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i}"
+
+
+def test_step_reads_rows_written_in_the_step():
+    """The newest indexer key row and HCA row are written by the step's own
+    compress jobs: before the step they hold zeros, and their raw tokens are
+    scaled so that the new rows decide the results (the key row is selected,
+    the HCA row dominates the HCA attention).  A scan or HCA split that read
+    the rows before they were written would differ from the three calls."""
+    st = Step(919)
+    N, N2, W = st.key.shape[1], st.hca.shape[1], 128
+    st.win_keys[:, W - 4:W] *= 40.0
+    st.win[:, :128] *= 8.0
+
+    def stale():
+        st.key[:, N - 1].zero_()
+        st.key_sc[:, N - 1].fill_(127)
+        st.hca[:, N2 - 1].zero_()
+        if st.hca_sc is not None:
+            st.hca_sc[:, N2 - 1].fill_(1.0)
+
+    stale()
+    st.three_calls()
+    torch.cuda.synchronize()
+    ref = st.outputs()
+    assert bool((ref[4][0, 0] == N - 1).any()), "the new key row is selected"
+    stale()
+    st.clobber()
+    for rep in range(2):
+        st.step()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(st.outputs(), ref)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"step {rep}: output {i}"
+        stale()
+        st.clobber()
