@@ -726,22 +726,27 @@ __device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_
                                           const Thr& th, int ties, bool unsafe, int k, int32_t* out, double* sout,
                                           SelShared& S) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // per slot: taken (a) or a tie at a full key (e), without branches; the
+  // wavefront's 2*LB counts go to lanes 0 .. 2*LB-1 and one LDS store
   uint32_t fa = 0, fe = 0;
+  int cnts = 0;
+  const bool tmode = ties >= 0;
+  const uint64_t Thi = th.low > 0 ? th.T >> th.low : 0ull;
 #pragma unroll
   for (int u = 0; u < LB; ++u) {
-    bool a = false, e = false;
-    if ((vm >> u) & 1u) {
-      if (ties >= 0) { a = bk[u] > th.T; e = bk[u] == th.T; }
-      else a = selected(th, bk[u], bj[u]);
-    }
+    const uint64_t key = bk[u];
+    const bool valid = (vm >> u) & 1u;
+    const bool gt = key > th.T, eq = key == th.T;
+    const bool sel = key != 0 && (th.low > 0 ? (key >> th.low) >= Thi : (gt || (eq && bj[u] <= th.Tj)));
+    const bool a = valid && (tmode ? gt : sel);
+    const bool e = valid && tmode && eq;
     fa |= (uint32_t)a << u;
     fe |= (uint32_t)e << u;
-    const uint64_t ba = __ballot(a), be = __ballot(e);
-    if (lane == 0) {
-      S.ecnt[u * SEL_WAVES + wave] = (uint32_t)__popcll(ba);
-      S.ecnt2[u * SEL_WAVES + wave] = (uint32_t)__popcll(be);
-    }
+    const int ca = __popcll(__ballot(a)), ce = __popcll(__ballot(e));
+    cnts = lane == u ? ca : (lane == LB + u ? ce : cnts);
   }
+  if (lane < LB) S.ecnt[lane * SEL_WAVES + wave] = (uint32_t)cnts;
+  else if (lane < 2 * LB) S.ecnt2[(lane - LB) * SEL_WAVES + wave] = (uint32_t)cnts;
   if (unsafe) S.bcast[6] = 1;
   __syncthreads();
   if (S.bcast[6]) return false;
