@@ -74,6 +74,8 @@ def parse():
                          "decode-step call")
     ap.add_argument("--no-graph", action="store_true", help="issue the steps eagerly instead of replaying a graph")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--mtp", default="2,4",
+                    help="query tokens per sequence of the multi-token decode legs (comma list; empty: none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 3 times (a known-size kernel "
                          "that scales the HBM byte counters of a profiler run)")
@@ -83,7 +85,7 @@ def parse():
 class Workload:
     """Device buffers of the layer-pair decode workload."""
 
-    def __init__(self, copies: int, seed: int = 1004):
+    def __init__(self, copies: int, seed: int = 1004, Tq: int = 1):
         import torch
         import long_context_attention_13_amd as lca
         import synth
@@ -99,6 +101,7 @@ class Workload:
         self.N, self.N2 = N, N2
         L = c["L"]
         self.L = L
+        self.Tq = Tq
         self.tau = c["tau"]
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
@@ -133,21 +136,34 @@ class Workload:
             self.hca.append(h); self.hca_sc.append(hs)
         torch.cuda.synchronize()
 
-        # queries and the indexer query (MXFP4, encoded by the library)
-        qi32 = t(c["qi"].reshape(B, H_I, d_I))
-        self.qi = torch.empty(B, 1, H_I, d_I // 2, dtype=torch.uint8, device=dev)
-        self.qi_sc = torch.empty(B, 1, H_I, d_I // 32, dtype=torch.uint8, device=dev)
-        lca.csa_compress(qi32, torch.zeros(B, H_I, device=dev), bias1, 1, zeros_B,
-                         torch.full((B,), H_I, dtype=torch.int32, device=dev), zeros_B64, H_I,
-                         self.qi.view(B, H_I, d_I // 2), lca.MXFP4, self.qi_sc.view(B, H_I, d_I // 32))
-        self.w = t(c["w"])
-        self.q_csa = bf(c["q_csa"])
-        self.q_hca = bf(c["q_hca"])
+        # queries and the indexer query (MXFP4, encoded by the library); with
+        # Tq > 1 query tokens per sequence (multi-token decode) the queries
+        # are drawn N(0,1) / U(0,1) on the GPU, query t at position L - Tq + t
+        if Tq == 1:
+            qi32 = t(c["qi"].reshape(B, H_I, d_I))
+            self.w = t(c["w"])
+            self.q_csa = bf(c["q_csa"])
+            self.q_hca = bf(c["q_hca"])
+        else:
+            qi32 = torch.randn(B, Tq * H_I, d_I, generator=g, device=dev)
+            self.w = torch.rand(B, Tq, H_I, generator=g, device=dev)
+            self.q_csa = torch.randn(B, Tq, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+            self.q_hca = torch.randn(B, Tq, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+        self.qi = torch.empty(B, Tq, H_I, d_I // 2, dtype=torch.uint8, device=dev)
+        self.qi_sc = torch.empty(B, Tq, H_I, d_I // 32, dtype=torch.uint8, device=dev)
+        lca.csa_compress(qi32, torch.zeros(B, Tq * H_I, device=dev), bias1, 1, zeros_B,
+                         torch.full((B,), Tq * H_I, dtype=torch.int32, device=dev), zeros_B64, Tq * H_I,
+                         self.qi.view(B, Tq * H_I, d_I // 2), lca.MXFP4, self.qi_sc.view(B, Tq * H_I, d_I // 32))
         self.sink_csa = t(c["sink_csa"])
         self.sink_hca = t(c["sink_hca"])
         # raw buffers: CSA window (128 tokens), indexer raw keys (128), HCA buffer (256 tokens:
         # the previous 128 + the window) so the newest complete 128-block is always inside
         self.win_csa = bf(c["win_csa"])
+        # the CSA attention's window buffer holds the Tq - 1 tokens before the
+        # last 128 too (the compress jobs read the last 128)
+        self.win_att = self.win_csa if Tq == 1 else bf(np.concatenate(
+            [np.random.default_rng(seed + Tq).standard_normal((B, Tq - 1, D)).astype(np.float32), c["win_csa"]],
+            axis=1))
         self.win_keys = bf(c["win_keys"])
         hbuf = np.concatenate([c["win_hca"][:, ::-1], c["win_hca"]], axis=1)   # 256 tokens
         self.win_hca = bf(hbuf)
@@ -157,26 +173,32 @@ class Workload:
         self.bias_csa = t(c["bias_csa"])
         self.bias_i = t(c["bias_i"])
         self.bias_hca = t(c["bias_hca"])
-        # per-sequence positions
+        # per-sequence positions: query t sees the blocks complete at its
+        # position L - Tq + t (the compress jobs write the newest ones)
         n_csa = (L // 4).astype(np.int32)
         n_hca = (L // 128).astype(np.int32)
-        self.n_csa = t(n_csa.reshape(B, 1))
-        self.n_hca = t(n_hca.reshape(B, 1))
+        pos1 = L[:, None] - Tq + 1 + np.arange(Tq)[None]          # tokens up to query t
+        self.n_csa = t((pos1 // 4).astype(np.int32))
+        self.n_hca = t((pos1 // 128).astype(np.int32))
         self.csa_tok0 = t((124 - L % 4).astype(np.int32))
         self.csa_row0 = t((n_csa - 1).astype(np.int64))
         self.hca_tok0 = t((128 - L % 128).astype(np.int32))
         self.hca_row0 = t((n_hca - 1).astype(np.int64))
         self.one = torch.ones(B, dtype=torch.int32, device=dev)
-        self.wb_csa = torch.zeros(B, 1, dtype=torch.int32, device=dev)
-        self.wl = torch.full((B, 1), W, dtype=torch.int32, device=dev)
-        self.wb_hca = torch.full((B, 1), 128, dtype=torch.int32, device=dev)
+        # query t: window rows [t, t + W) of the CSA buffer and
+        # [128 - (Tq - 1) + t, +W) of the HCA buffer
+        tt = torch.arange(Tq, dtype=torch.int32, device=dev)[None].repeat(B, 1)
+        self.wb_csa = tt.clone()
+        self.wl = torch.full((B, Tq), W, dtype=torch.int32, device=dev)
+        self.wb_hca = tt + (128 - (Tq - 1))
         # outputs and workspaces
-        self.idx = torch.empty(B, 1, self.k, dtype=torch.int32, device=dev)
-        self.out_csa = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
-        self.out_hca = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
-        self.ws_idx = torch.empty(lca.index_topk_ws(B, 1, H_I, d_I, N, self.k), dtype=torch.uint8, device=dev)
-        self.ws_csa = torch.empty(max(lca.attend_ws(B, 1, Hq, D, self.k, 128), 16), dtype=torch.uint8, device=dev)
-        self.ws_hca = torch.empty(max(lca.attend_ws(B, 1, Hq, D, N2, 256), 16), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(B, Tq, self.k, dtype=torch.int32, device=dev)
+        self.out_csa = torch.empty(B, Tq, Hq, D, dtype=torch.bfloat16, device=dev)
+        self.out_hca = torch.empty(B, Tq, Hq, D, dtype=torch.bfloat16, device=dev)
+        self.ws_idx = torch.empty(lca.index_topk_ws(B, Tq, H_I, d_I, N, self.k), dtype=torch.uint8, device=dev)
+        self.ws_csa = torch.empty(max(lca.attend_ws(B, Tq, Hq, D, self.k, 128 + Tq - 1), 16), dtype=torch.uint8,
+                                  device=dev)
+        self.ws_hca = torch.empty(max(lca.attend_ws(B, Tq, Hq, D, N2, 256), 16), dtype=torch.uint8, device=dev)
         # the batched form of the step: one compress launch for the three new blocks and one
         # attention launch (+ one merge) for both branches; job arrays built once per copy
         import ctypes
@@ -188,7 +210,7 @@ class Workload:
                                    self.csa_row0, 1, self.key[c], lca.MXFP4, self.key_sc[c]),
                   lca.compress_job(self.win_hca, self.gate_hca, self.bias_hca, 128, self.hca_tok0, self.one,
                                    self.hca_row0, 1, self.hca[c], lca.FP8E4M3, self.hca_sc[c])]
-            aj = [lca.attend_job(True, self.q_csa, self.ent[c], self.ent_sc[c], self.idx, self.win_csa, self.wb_csa,
+            aj = [lca.attend_job(True, self.q_csa, self.ent[c], self.ent_sc[c], self.idx, self.win_att, self.wb_csa,
                                  self.wl, self.sink_csa, self.tau, self.out_csa, ws=self.ws_csa),
                   lca.attend_job(False, self.q_hca, self.hca[c], self.hca_sc[c], self.n_hca, self.win_hca,
                                  self.wb_hca, self.wl, self.sink_hca, self.tau, self.out_hca, ws=self.ws_hca)]
@@ -216,7 +238,7 @@ class Workload:
 
     def attend(self, c):
         lca = self.lca
-        lca.sparse_mqa_attend(self.q_csa, self.ent[c], self.ent_sc[c], self.idx, self.win_csa, self.wb_csa, self.wl,
+        lca.sparse_mqa_attend(self.q_csa, self.ent[c], self.ent_sc[c], self.idx, self.win_att, self.wb_csa, self.wl,
                               self.sink_csa, self.tau, self.out_csa, ws=self.ws_csa)
         lca.hca_attend(self.q_hca, self.hca[c], self.hca_sc[c], self.n_hca, self.win_hca, self.wb_hca, self.wl,
                        self.sink_hca, self.tau, self.out_hca, ws=self.ws_hca)
@@ -370,6 +392,37 @@ class PrefillWorkload:
         items_csa = np.minimum(self.k, (p + 1) // 4) + 128
         items_hca = (p + 1) // 128 + 128
         return float((items_csa + items_hca).sum()) * self.Hq * self.D * 4
+
+
+def run_mtp(Tq: int, copies: int, steps: int):
+    """Multi-token decode: the same layer pair with Tq query tokens per
+    sequence per step (one decode_step call, a graph of `copies` steps
+    replayed); decode tokens/s counts B * Tq tokens a step."""
+    import torch
+    wl = Workload(copies, Tq=Tq)
+    for c in range(copies):
+        wl.step_fused(c)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in range(copies):
+            wl.step_fused(c)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * copies)
+    out = {"Tq": Tq, "decode_tokens_per_s": round(wl.B * Tq / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "steps": reps * copies, "schedule": "decode_step, graph of %d steps replayed" % copies,
+           "queries": "N(0,1) bf16 / MXFP4, weights U(0,1); query t at position L - Tq + t"}
+    del wl
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_prefill(steps: int, warmup: int):
@@ -567,9 +620,11 @@ def main():
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
+    del wl
+    torch.cuda.empty_cache()
+    if args.mtp:
+        res["mtp"] = [run_mtp(int(tq), args.copies, 50) for tq in args.mtp.split(",")]
     if not args.no_prefill:
-        del wl
-        torch.cuda.empty_cache()
         res["prefill"] = run_prefill(args.prefill_steps, 2)
     print(json.dumps(res))
 

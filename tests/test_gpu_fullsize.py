@@ -3,7 +3,8 @@ configuration bench.py times.
 
 - 1M-token CSA+HCA layer pair (4 sequences, 262144 FP8 entries + MXFP4 keys,
   top-1024; 8192 FP8 HCA entries): every row's index set bit-exact and both
-  attentions within rtol 2e-2 (the oracle computes all 4 rows in seconds).
+  attentions within rtol 2e-2 (the oracle computes all 4 rows in seconds);
+  the same with 4 query tokens per sequence (multi-token decode).
 - 131072-token CSA decode (16 sequences, 32768 entries, top-512): all rows.
 - 65536-token HCA decode in bf16 (8 sequences): cache build (pooled rows vs the
   oracle) and attention over the oracle-built cache.
@@ -71,6 +72,43 @@ def test_layer_pair_1m_full():
             ("csa", c["q_csa"], ent, ent_sc, ri, None, c["win_csa"], c["sink_csa"]),
             ("hca", c["q_hca"], hca, hca_sc, None, n_hca, c["win_hca"], c["sink_hca"])]:
         qb, _ = oracle.encode(q, oracle.BF16)
+        wbf, _ = oracle.encode(win, oracle.BF16)
+        o, l = gpu_attend(sel is not None, qb, kv, sc, sel if sel is not None else n, wbf, wb, wl, sink, tau)
+        ro, rl = oracle.attend(oracle.decode(qb, oracle.BF16), kv, oracle.FP8E4M3, sc, sel, n, wbf, oracle.BF16,
+                               wb, wl, sink, tau)
+        assert_rows_close(o, ro, 2e-2, name + " out")
+        assert_rows_close(l[..., None], rl[..., None], 2e-2, name + " lse")
+
+
+def test_layer_pair_1m_multi_token_full():
+    """Multi-token decode on the 1M-token layer pair: 4 query tokens per
+    sequence (query t at position L - 4 + t, its own eligible counts and
+    window slice), seeded N(0,1) queries and U(0,1) head weights; every row's
+    index set bit-exact and both attentions within rtol 2e-2."""
+    c = synth.layer_pair_1m()
+    B, k, W, Hq, H_I, d_I, D = c["B"], c["k"], c["W"], c["Hq"], c["H_I"], c["d_I"], c["D"]
+    Tq = 4
+    L = c["L"]
+    g = np.random.default_rng(4242)
+    kc, ks = oracle.encode(c["keys"], oracle.MXFP4)
+    ent, ent_sc = oracle.encode(c["entries"], oracle.FP8E4M3)
+    hca, hca_sc = oracle.encode(c["hca_entries"], oracle.FP8E4M3)
+    qc, qs = oracle.encode(g.standard_normal((B, Tq, H_I, d_I)).astype(np.float32), oracle.MXFP4)
+    w = g.random((B, Tq, H_I)).astype(np.float32)
+    pos1 = L[:, None] - Tq + 1 + np.arange(Tq)[None]
+    n_csa = (pos1 // 4).astype(np.int32)
+    n_hca = (pos1 // 128).astype(np.int32)
+    gi, gs = gpu_index(qc, qs, w, kc, ks, n_csa, k)
+    ri, rs = oracle.index_topk(oracle.decode(qc, oracle.MXFP4, qs), w, kc, oracle.MXFP4, ks, n_csa, k)
+    assert np.array_equal(gi, ri)
+    assert np.array_equal(gs.view(np.uint64), rs.view(np.uint64))
+    tau = c["tau"]
+    wb = np.tile(np.arange(Tq, dtype=np.int32), (B, 1))
+    wl = np.full((B, Tq), W, np.int32)
+    win = g.standard_normal((B, W + Tq - 1, D)).astype(np.float32)
+    for name, sel, n, kv, sc in [("csa", ri, None, ent, ent_sc), ("hca", None, n_hca, hca, hca_sc)]:
+        qb, _ = oracle.encode(g.standard_normal((B, Tq, Hq, D)).astype(np.float32), oracle.BF16)
+        sink = g.standard_normal(Hq).astype(np.float32)
         wbf, _ = oracle.encode(win, oracle.BF16)
         o, l = gpu_attend(sel is not None, qb, kv, sc, sel if sel is not None else n, wbf, wb, wl, sink, tau)
         ro, rl = oracle.attend(oracle.decode(qb, oracle.BF16), kv, oracle.FP8E4M3, sc, sel, n, wbf, oracle.BF16,
