@@ -74,6 +74,7 @@ def parse():
                          "decode-step call")
     ap.add_argument("--no-graph", action="store_true", help="issue the steps eagerly instead of replaying a graph")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop leg (append + step)")
     ap.add_argument("--mtp", default="2,4",
                     help="query tokens per sequence of the multi-token decode legs (comma list; empty: none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -425,6 +426,82 @@ def run_mtp(Tq: int, copies: int, steps: int):
     return out
 
 
+def run_loop(copies: int, steps: int):
+    """Decode loop: per step and cache copy, decode_append puts one new raw
+    token per sequence into the three rings (CSA KV and indexer keys: m = 4;
+    HCA KV: m = 128; token t at rows t % R and t % R + R) and derives the
+    step's arguments on the device, then decode_step compresses the blocks
+    that just completed (CSA and indexer every 4th step, HCA every 128th),
+    runs the indexer and both attentions over the ring windows.  Lengths start
+    512 tokens below the workload's so every appended token fits the caches;
+    rings and new tokens are N(0,1) bf16, gates N(0,1).  A graph of `copies`
+    steps (one per cache copy) is replayed; decode tokens/s counts B tokens a
+    step."""
+    import ctypes
+    import torch
+    wl = Workload(copies)
+    lca, dev, B, D, d_I, W = wl.lca, wl.dev, wl.B, wl.D, wl.d_I, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(1006)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device=dev)
+    i32 = lambda *sh: torch.zeros(*sh, dtype=torch.int32, device=dev)
+    L0 = torch.from_numpy(wl.L - 512).to(dev)
+    R = {"csa": 128, "key": 4, "hca": 128}
+    m = {"csa": 4, "key": 4, "hca": 128}
+    dim = {"csa": D, "key": d_I, "hca": D}
+    bias = {"csa": wl.bias_csa, "key": wl.bias_i, "hca": wl.bias_hca}
+    ws_csa = torch.empty(lca.attend_ws(B, 1, wl.Hq, D, wl.k, 2 * R["csa"]), dtype=torch.uint8, device=dev)
+    ws_hca = torch.empty(lca.attend_ws(B, 1, wl.Hq, D, wl.N2, 2 * R["hca"]), dtype=torch.uint8, device=dev)
+    keep, plans = [], []
+    for c in range(copies):
+        st = {}
+        for s in R:
+            st[s] = dict(ring=rn(B, 2 * R[s], dim[s]).to(torch.bfloat16), gring=rn(B, 2 * R[s]), len=L0.clone(),
+                         xn=rn(B, dim[s]).to(torch.bfloat16), gn=rn(B), tok0=i32(B), nblk=i32(B),
+                         row0=torch.zeros(B, dtype=torch.int64, device=dev))
+        n_csa, n_hca, wb_c, wl_c, wb_h, wl_h = i32(B, 1), i32(B, 1), i32(B, 1), i32(B, 1), i32(B, 1), i32(B, 1)
+        A = lambda s, **kw: lca.append_job(st[s]["xn"], st[s]["ring"], st[s]["len"], m=m[s], g_new=st[s]["gn"],
+                                           gring=st[s]["gring"], x_tok0=st[s]["tok0"], nblk=st[s]["nblk"],
+                                           dst_row0=st[s]["row0"], **kw)
+        ap = [A("csa", W=W, n_elig=n_csa, win_begin=wb_c, win_len=wl_c), A("key"),
+              A("hca", W=W, n_elig=n_hca, win_begin=wb_h, win_len=wl_h)]
+        Cj = lambda s, dst, dt, sc: lca.compress_job(st[s]["ring"], st[s]["gring"], bias[s], m[s], st[s]["tok0"],
+                                                     st[s]["nblk"], st[s]["row0"], 1, dst, dt, sc)
+        cj = [Cj("csa", wl.ent[c], lca.FP8E4M3, wl.ent_sc[c]), Cj("key", wl.key[c], lca.MXFP4, wl.key_sc[c]),
+              Cj("hca", wl.hca[c], lca.FP8E4M3, wl.hca_sc[c])]
+        ij = lca.index_job(wl.qi, wl.qi_sc, wl.w, wl.key[c], wl.key_sc[c], n_csa, wl.k, wl.idx, wl.ws_idx)
+        aj = [lca.attend_job(True, wl.q_csa, wl.ent[c], wl.ent_sc[c], wl.idx, st["csa"]["ring"], wb_c, wl_c,
+                             wl.sink_csa, wl.tau, wl.out_csa, ws=ws_csa),
+              lca.attend_job(False, wl.q_hca, wl.hca[c], wl.hca_sc[c], n_hca, st["hca"]["ring"], wb_h, wl_h,
+                             wl.sink_hca, wl.tau, wl.out_hca, ws=ws_hca)]
+        keep.append((st, ap, cj, ij, aj))
+        plans.append(((lca.AppendJob * 3)(*ap), (lca.CompressJob * 3)(*cj), ij, (lca.AttendJob * 2)(*aj)))
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    assert reps + 1 <= 512, "appended tokens must fit below the workload's lengths"
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for ap, cj, ij, aj in plans:
+            lca.decode_append(ap)
+            lca.decode_step(cj, ij, aj)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * copies)
+    out = {"decode_tokens_per_s": round(wl.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "steps": reps * copies,
+           "schedule": "decode_append (3 rings) + decode_step, graph of %d steps replayed" % copies,
+           "compression": "when a block completes: CSA and indexer every 4th step, HCA every 128th"}
+    del wl, keep, plans, graph
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_prefill(steps: int, warmup: int):
     import torch
     pw = PrefillWorkload()
@@ -622,6 +699,8 @@ def main():
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
     del wl
     torch.cuda.empty_cache()
+    if not args.no_loop:
+        res["decode_loop"] = run_loop(args.copies, 50)
     if args.mtp:
         res["mtp"] = [run_mtp(int(tq), args.copies, 50) for tq in args.mtp.split(",")]
     if not args.no_prefill:

@@ -71,7 +71,7 @@ typedef enum lca_dtype {
   LCA_MXFP4 = 3
 } lca_dtype;
 
-#define LCA_ABI_VERSION 2
+#define LCA_ABI_VERSION 3
 
 /* Version of this ABI (LCA_ABI_VERSION). */
 int32_t lca_abi_version(void);
@@ -292,6 +292,49 @@ typedef struct lca_index_job {
 
 lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
                            const lca_attend_job* ajobs, int32_t najobs, void* stream);
+
+/*
+ * lca_decode_append -- the token append of a decode loop, for several raw-token
+ * streams in one launch (for example a CSA layer's raw KV, its indexer's raw
+ * keys and an HCA layer's raw KV): each sequence's new token goes into the
+ * stream's ring, and the step's arguments for lca_decode_step are derived on
+ * the device, so that one captured step can be replayed step after step.
+ * [release notes (agentlenshq.com), 壓縮稀疏注意力 (CSA): the most recent
+ * tokens stay uncompressed in a sliding window, and a block of m tokens
+ * becomes one compressed entry once it is complete (m = 4 for CSA, 128 for
+ * HCA).]
+ * Ring: token t of sequence b is stored at rows t % R and t % R + R of
+ * ring[b] ([B][2R][D]) and of gring[b] ([B][2R]), so that every run of at most
+ * R consecutive tokens (a block being compressed, the window) is contiguous.
+ *   x_new    [B][D] device, the new tokens (x_dt: bf16 or f32; the ring's type)
+ *   g_new    [B] fp32 device, their gate logits, with gring; both NULL: no gate ring
+ *   len      [B] int64 device: tokens before the call; the call adds 1
+ *   R        ring rows, >= max(1, m, W)
+ *   m        compression block of the stream (0: not compressed)
+ *   W        window of the stream's attention (0: no window outputs needed)
+ * Outputs, for L = len + 1 tokens (device, each may be NULL):
+ *   nblk[b] = 1 when L % m == 0 (a block completed), else 0
+ *   x_tok0[b] = ring row of token L - m (the completed block's first token)
+ *   dst_row0[b] = L / m - 1 (its cache row);  n_elig[b] = L / m
+ *   win_begin[b], win_len[b]: ring rows of the last min(L, W) tokens
+ * These are the x_tok0 / nblk / dst_row0 of a compress job with x = ring,
+ * x_rows = 2R, gate = gring, nblk_max = 1, and the n_elig / win_begin /
+ * win_len of an attention or indexer job with win = ring, W_buf = 2R, Tq = 1.
+ * Jobs must not share len, rings or outputs.  Errors: LCA_EINVAL (null or
+ * misaligned x_new/ring, null len, bad sizes), LCA_ENOTSUP (D not 64/128,
+ * x_dt not bf16/f32).
+ */
+#define LCA_MAX_APPEND_JOBS 8
+typedef struct lca_append_job {
+  const void* x_new; lca_dtype x_dt; const float* g_new;
+  void* ring; float* gring; int64_t R;
+  int64_t* len; int32_t m; int32_t W;
+  int32_t* x_tok0; int32_t* nblk; int64_t* dst_row0; int32_t* n_elig;
+  int32_t* win_begin; int32_t* win_len;
+  int32_t B; int32_t D;
+} lca_append_job;
+
+lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* stream);
 
 /* Workspace bytes for the attention calls.  n_kv_max is k for
  * lca_sparse_mqa_attend and N_cap for lca_hca_attend; W_buf the window buffer

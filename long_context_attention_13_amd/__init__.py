@@ -23,9 +23,10 @@ STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA
 
 EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
-           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step"]
+           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append"]
 MAX_COMPRESS_JOBS = 8
 MAX_ATTEND_JOBS = 4
+MAX_APPEND_JOBS = 8
 
 
 class CompressJob(ctypes.Structure):
@@ -67,6 +68,8 @@ def load(path: str = LIB_PATH):
     L.lca_decode_step.restype = i32
     L.lca_decode_step.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
                                   ctypes.POINTER(AttendJob), i32, vp]
+    L.lca_decode_append.restype = i32
+    L.lca_decode_append.argtypes = [ctypes.POINTER(AppendJob), i32, vp]
     L.lca_attend_batch.restype = i32
     L.lca_attend_batch.argtypes = [ctypes.POINTER(AttendJob), i32, vp]
     L.lca_compress_batch.restype = i32
@@ -232,6 +235,36 @@ def decode_step(cjobs, ijob, ajobs, stream=None):
     ca = cjobs if isinstance(cjobs, ctypes.Array) else (CompressJob * max(1, len(cjobs)))(*cjobs)
     aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
     _check(load().lca_decode_step(ca, len(cjobs), ctypes.byref(ijob), aa, len(ajobs), _stream(stream)))
+
+
+class AppendJob(ctypes.Structure):
+    """lca_append_job: one raw-token stream of decode_append."""
+    _fields_ = [("x_new", ctypes.c_void_p), ("x_dt", ctypes.c_int32), ("g_new", ctypes.c_void_p),
+                ("ring", ctypes.c_void_p), ("gring", ctypes.c_void_p), ("R", ctypes.c_int64),
+                ("len", ctypes.c_void_p), ("m", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("x_tok0", ctypes.c_void_p), ("nblk", ctypes.c_void_p), ("dst_row0", ctypes.c_void_p),
+                ("n_elig", ctypes.c_void_p), ("win_begin", ctypes.c_void_p), ("win_len", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+def append_job(x_new, ring, length, m=0, W=0, g_new=None, gring=None, x_tok0=None, nblk=None, dst_row0=None,
+               n_elig=None, win_begin=None, win_len=None) -> AppendJob:
+    """One stream of decode_append: x_new [B, D] new tokens, ring [B, 2R, D] (gring [B, 2R]),
+    length [B] int64 tokens so far; the outputs are the step arguments named in lca.h (the job
+    keeps its tensors alive while it is)."""
+    B, R2, D = ring.shape
+    ptr = lambda t: None if t is None else t.data_ptr()
+    job = AppendJob(ptr(x_new), dtype_of(x_new), ptr(g_new), ptr(ring), ptr(gring), R2 // 2, ptr(length), int(m),
+                    int(W), ptr(x_tok0), ptr(nblk), ptr(dst_row0), ptr(n_elig), ptr(win_begin), ptr(win_len), B, D)
+    job._keep = (x_new, g_new, ring, gring, length, x_tok0, nblk, dst_row0, n_elig, win_begin, win_len)
+    return job
+
+
+def decode_append(jobs, stream=None):
+    """Append one token per sequence to each stream (see lca_decode_append); jobs from
+    append_job(), or a ctypes array of them built once."""
+    arr = jobs if isinstance(jobs, ctypes.Array) else (AppendJob * len(jobs))(*jobs)
+    _check(load().lca_decode_append(arr, len(arr), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

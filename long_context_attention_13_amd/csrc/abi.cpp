@@ -346,6 +346,43 @@ lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const 
   return hip_status(lca::launch_decode_step(cb, ia, ab, (hipStream_t)stream), name);
 }
 
+lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* stream) {
+  const char* who = "lca_decode_append";
+  REQ(njobs >= 1 && njobs <= LCA_MAX_APPEND_JOBS, LCA_EINVAL, "%s: njobs=%d outside [1, %d]", who, njobs,
+      LCA_MAX_APPEND_JOBS);
+  REQ(jobs != nullptr, LCA_EINVAL, "%s: jobs is NULL", who);
+  static_assert(LCA_MAX_APPEND_JOBS == lca::MAX_APPEND_JOBS, "job limits agree");
+  lca::AppendBatch bt{};
+  bt.njobs = njobs;
+  for (int j = 0; j < njobs; ++j) {
+    const lca_append_job& J = jobs[j];
+    char name[96];
+    snprintf(name, sizeof(name), "%s: append job %d", who, j);
+    REQ(J.B >= 0 && J.B <= (1 << 20), LCA_EINVAL, "%s: B=%d out of range", name, J.B);
+    REQ(J.D == 64 || J.D == 128, LCA_ENOTSUP, "%s: D=%d (64 or 128)", name, J.D);
+    REQ(J.x_dt == LCA_BF16 || J.x_dt == LCA_F32, LCA_ENOTSUP, "%s: x_dt must be bf16 or f32", name);
+    REQ(J.m >= 0 && J.m <= 1024, LCA_EINVAL, "%s: m=%d outside [0, 1024]", name, J.m);
+    REQ(J.W >= 0, LCA_EINVAL, "%s: W=%d negative", name, J.W);
+    REQ(J.R >= 1 && J.R >= J.m && J.R >= J.W && J.R < (1ll << 30), LCA_EINVAL,
+        "%s: R=%lld must be >= max(1, m, W)", name, (long long)J.R);
+    REQ((J.g_new == nullptr) == (J.gring == nullptr), LCA_EINVAL, "%s: g_new and gring go together", name);
+    REQ((J.win_begin == nullptr) == (J.win_len == nullptr), LCA_EINVAL, "%s: win_begin and win_len go together",
+        name);
+    if (J.B > 0) {
+      REQ(J.x_new != nullptr && aligned16(J.x_new), LCA_EINVAL, "%s: x_new must be a non-null 16-byte aligned pointer",
+          name);
+      REQ(J.ring != nullptr && aligned16(J.ring), LCA_EINVAL, "%s: ring must be a non-null 16-byte aligned pointer",
+          name);
+      REQ(J.len != nullptr, LCA_EINVAL, "%s: len is NULL", name);
+    }
+    lca::AppendArgs& a = bt.job[j];
+    a.x_new = J.x_new; a.x_dt = (int)J.x_dt; a.g_new = J.g_new; a.ring = J.ring; a.gring = J.gring; a.R = J.R;
+    a.len = J.len; a.m = J.m; a.W = J.W; a.x_tok0 = J.x_tok0; a.nblk = J.nblk; a.dst_row0 = J.dst_row0;
+    a.n_elig = J.n_elig; a.win_begin = J.win_begin; a.win_len = J.win_len; a.B = J.B; a.D = J.D;
+  }
+  return hip_status(lca::launch_decode_append(bt, (hipStream_t)stream), who);
+}
+
 size_t lca_attend_ws(int32_t B, int32_t Tq, int32_t Hq, int32_t D, int64_t n_kv_max, int64_t W_buf) {
   if (B <= 0 || Tq <= 0) return 0;
   return lca::attend_ws_bytes(B, Tq, Hq, D, n_kv_max, W_buf);

@@ -71,6 +71,23 @@ void attend_batch_plan(AttendBatch& bt);
 hipError_t launch_attend_batch_mfma(const AttendBatch& bt, hipStream_t s);
 hipError_t launch_attend_batch_merge(const AttendBatch& bt, hipStream_t s);
 
+// Token append of a decode loop (one new token per sequence and stream into
+// a doubled ring of R rows, and the step's derived arguments).
+struct AppendArgs {
+  const void* x_new; int x_dt; const float* g_new;
+  void* ring; float* gring; int64_t R;
+  int64_t* len; int m; int W;
+  int32_t* x_tok0; int32_t* nblk; int64_t* dst_row0; int32_t* n_elig;
+  int32_t* win_begin; int32_t* win_len;
+  int B, D;
+};
+constexpr int MAX_APPEND_JOBS = 8;
+struct AppendBatch {
+  AppendArgs job[MAX_APPEND_JOBS];
+  int njobs;
+};
+hipError_t launch_decode_append(const AppendBatch& bt, hipStream_t s);
+
 // One decode step: the compress jobs, the indexer call, the attention jobs, in
 // that order and with the results of the three calls; the dense attention jobs
 // may run beside the indexer's scan.

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.lca_abi_version() == 2
+    assert L.lca_abi_version() == 3
 
 
 def compress(L, **kw):
@@ -224,3 +224,35 @@ def test_decode_step_validation(L):
     assert decode_step(L, [], index_job(B=0), [attend_job(), attend_job(Hq=32)]) == 2
     assert b"attention job 1" in L.lca_last_error()
     assert decode_step(L, [], index_job(ws=None), []) == 4
+
+
+def append_job(**kw):
+    a = dict(x_new=FAKE, x_dt=lca.BF16, g_new=FAKE, ring=FAKE, gring=FAKE, R=256, len=FAKE, m=4, W=128,
+             x_tok0=FAKE, nblk=FAKE, dst_row0=FAKE, n_elig=FAKE, win_begin=FAKE, win_len=FAKE, B=2, D=128)
+    a.update(kw)
+    return lca.AppendJob(*a.values())
+
+
+def decode_append(L, jobs, n=None):
+    arr = (lca.AppendJob * max(1, len(jobs)))(*jobs)
+    return L.lca_decode_append(arr, len(jobs) if n is None else n, None)
+
+
+def test_decode_append_validation(L):
+    assert decode_append(L, [append_job(B=0)]) == 0                        # nothing to launch
+    assert decode_append(L, [append_job(B=0, x_new=None, ring=None, len=None)]) == 0
+    assert decode_append(L, []) == 1
+    assert decode_append(L, [append_job()] * 9) == 1
+    assert L.lca_decode_append(None, 1, None) == 1
+    assert decode_append(L, [append_job(x_new=None)]) == 1
+    assert b"x_new" in L.lca_last_error()
+    assert decode_append(L, [append_job(B=0), append_job(ring=FAKE + 2)]) == 1
+    assert b"append job 1" in L.lca_last_error()
+    assert decode_append(L, [append_job(len=None)]) == 1
+    assert decode_append(L, [append_job(R=127)]) == 1                       # R < W
+    assert decode_append(L, [append_job(m=128, W=0, R=64)]) == 1            # R < m
+    assert decode_append(L, [append_job(gring=None)]) == 1                  # gate without its ring
+    assert decode_append(L, [append_job(win_len=None)]) == 1
+    assert decode_append(L, [append_job(m=-1)]) == 1
+    assert decode_append(L, [append_job(D=96)]) == 2
+    assert decode_append(L, [append_job(x_dt=lca.FP8E4M3)]) == 2
