@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="issue the steps eagerly instead of replaying a graph")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop leg (append + step)")
+    ap.add_argument("--loop-only", action="store_true", help="run only the decode-loop leg")
     ap.add_argument("--mtp", default="2,4",
                     help="query tokens per sequence of the multi-token decode legs (comma list; empty: none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -584,6 +585,9 @@ def main():
     import torch
     if args.prefill_only:
         print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}))
+        return
+    if args.loop_only:
+        print(json.dumps({"decode_loop": run_loop(args.copies, args.steps)}))
         return
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
