@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop leg (append + step)")
     ap.add_argument("--loop-only", action="store_true", help="run only the decode-loop leg")
+    ap.add_argument("--no-schedule", action="store_true", help="skip the 61-layer schedule leg")
+    ap.add_argument("--schedule-only", action="store_true", help="run only the 61-layer schedule leg")
     ap.add_argument("--mtp", default="2,4",
                     help="query tokens per sequence of the multi-token decode legs (comma list; empty: none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -503,6 +505,128 @@ def run_loop(copies: int, steps: int):
     return out
 
 
+def run_schedule(steps: int):
+    """The attention layers of the 61-layer V4-Pro model and its MTP block
+    (layers 0-1 HCA, 2..60 alternating CSA / HCA, MTP block window-only), at
+    the layer-pair workload's sizes: 4 sequences at ~1M tokens, every CSA layer
+    with its own 262144-row FP8 entry cache and MXFP4 keys (top-1024), every HCA
+    layer its own 8192-row FP8 cache, every layer its own raw-token rings.
+    One step = per layer one decode_append and one decode_step (CSA: compress,
+    indexer, sparse attention; HCA: compress, dense attention; MTP block: the
+    window-only attention), layer after layer; the whole step is one captured
+    graph, replayed.  Lengths start 64 tokens below the layer-pair workload's.
+    Caches, rings, queries and new tokens are N(0,1) (MXFP4 / FP8 encoded by
+    the library), head weights U(0,1)."""
+    import torch
+    import long_context_attention_13_amd as lca
+    import synth
+    dev = torch.device("cuda:0")
+    c = synth.layer_pair_1m(draw_caches=False)
+    B, D, d_I, H_I, Hq, k, W = c["B"], c["D"], c["d_I"], c["H_I"], c["Hq"], c["k"], c["W"]
+    N, N2, tau = c["N_cap"], c["N2_cap"], c["tau"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device=dev)
+    i32 = lambda *sh: torch.zeros(*sh, dtype=torch.int32, device=dev)
+    z32, z64 = i32(B), torch.zeros(B, dtype=torch.int64, device=dev)
+    bias1 = torch.zeros(1, device=dev)
+    L0 = torch.from_numpy(c["L"] - 64).to(dev)
+
+    def encode(rows, dim, dt):
+        dst = torch.empty(B, rows, dim if dt == lca.FP8E4M3 else dim // 2, dtype=torch.uint8, device=dev)
+        sc = torch.empty(B, rows, dim // 64 if dt == lca.FP8E4M3 else dim // 32,
+                         dtype=torch.float32 if dt == lca.FP8E4M3 else torch.uint8, device=dev)
+        step = 1 << 16
+        for r0 in range(0, rows, step):
+            n = min(step, rows - r0)
+            lca.csa_compress(rn(B, n, dim), torch.zeros(B, n, device=dev), bias1, 1, z32,
+                             torch.full((B,), n, dtype=torch.int32, device=dev), z64 + r0, n, dst, dt, sc)
+        return dst, sc
+
+    ws_i = torch.empty(lca.index_topk_ws(B, 1, H_I, d_I, N, k), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(lca.attend_ws(B, 1, Hq, D, k, 256), dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(lca.attend_ws(B, 1, Hq, D, N2, 256), dtype=torch.uint8, device=dev)
+    ws_w = torch.empty(max(16, lca.attend_ws(B, 1, Hq, D, 0, 256)), dtype=torch.uint8, device=dev)
+    kinds = synth.v4_pro_layer_kinds()
+    layers, keep = [], []
+    for kind in kinds:
+        def stream(dim, m, R, Wn):
+            t = dict(ring=rn(B, 2 * R, dim).to(torch.bfloat16), len=L0.clone(), xn=rn(B, dim).to(torch.bfloat16))
+            kw = dict(m=m, W=Wn)
+            if m > 0:
+                t.update(gring=rn(B, 2 * R), gn=rn(B), tok0=i32(B), nblk=i32(B),
+                         row0=torch.zeros(B, dtype=torch.int64, device=dev), bias=rn(m) * 0.1)
+                kw.update(g_new=t["gn"], gring=t["gring"], x_tok0=t["tok0"], nblk=t["nblk"], dst_row0=t["row0"])
+            return t, kw
+        n, wb, wln = i32(B, 1), i32(B, 1), i32(B, 1)
+        q, sink = rn(B, 1, Hq, D).to(torch.bfloat16), rn(Hq)
+        out = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
+        if kind == "csa":
+            kv, kw = stream(D, 4, 128, W)
+            key, kwk = stream(d_I, 4, 4, 0)
+            apps = [lca.append_job(kv["xn"], kv["ring"], kv["len"], n_elig=n, win_begin=wb, win_len=wln, **kw),
+                    lca.append_job(key["xn"], key["ring"], key["len"], **kwk)]
+            ent, ent_sc = encode(N, D, lca.FP8E4M3)
+            kc, ks = encode(N, d_I, lca.MXFP4)
+            qi = torch.empty(B, 1, H_I, d_I // 2, dtype=torch.uint8, device=dev)
+            qs = torch.empty(B, 1, H_I, d_I // 32, dtype=torch.uint8, device=dev)
+            lca.csa_compress(rn(B, H_I, d_I), torch.zeros(B, H_I, device=dev), bias1, 1, z32,
+                             torch.full((B,), H_I, dtype=torch.int32, device=dev), z64, H_I,
+                             qi.view(B, H_I, d_I // 2), lca.MXFP4, qs.view(B, H_I, d_I // 32))
+            w = torch.rand(B, 1, H_I, generator=g, device=dev)
+            idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
+            cj = [lca.compress_job(kv["ring"], kv["gring"], kv["bias"], 4, kv["tok0"], kv["nblk"], kv["row0"], 1,
+                                   ent, lca.FP8E4M3, ent_sc),
+                  lca.compress_job(key["ring"], key["gring"], key["bias"], 4, key["tok0"], key["nblk"], key["row0"],
+                                   1, kc, lca.MXFP4, ks)]
+            ij = lca.index_job(qi, qs, w, kc, ks, n, k, idx, ws_i)
+            aj = lca.attend_job(True, q, ent, ent_sc, idx, kv["ring"], wb, wln, sink, tau, out, ws=ws_c)
+            keep.append((kv, key, ent, ent_sc, kc, ks, qi, qs, w, idx))
+        elif kind == "hca":
+            kv, kw = stream(D, 128, 128, W)
+            apps = [lca.append_job(kv["xn"], kv["ring"], kv["len"], n_elig=n, win_begin=wb, win_len=wln, **kw)]
+            ent, ent_sc = encode(N2, D, lca.FP8E4M3)
+            cj = [lca.compress_job(kv["ring"], kv["gring"], kv["bias"], 128, kv["tok0"], kv["nblk"], kv["row0"], 1,
+                                   ent, lca.FP8E4M3, ent_sc)]
+            ij = None
+            aj = lca.attend_job(False, q, ent, ent_sc, n, kv["ring"], wb, wln, sink, tau, out, ws=ws_h)
+            keep.append((kv, ent, ent_sc))
+        else:
+            kv, kw = stream(D, 0, 128, W)
+            apps = [lca.append_job(kv["xn"], kv["ring"], kv["len"], win_begin=wb, win_len=wln, **kw)]
+            cj, ij = [], None
+            aj = lca.attend_job(True, q, None, None, None, kv["ring"], wb, wln, sink, tau, out, ws=ws_w)
+            keep.append((kv,))
+        keep.append((n, wb, wln, q, sink, out, apps, cj, ij, aj))
+        layers.append(((lca.AppendJob * len(apps))(*apps), cj, ij, [aj]))
+    torch.cuda.synchronize()
+    reps = max(1, steps)
+    assert reps + 1 <= 64, "appended tokens must fit below the layer-pair workload's lengths"
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for ap, cj, ij, aj in layers:
+            lca.decode_append(ap)
+            lca.decode_step(cj, ij, aj)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    out = {"layers": "61 attention layers (0-1 HCA, 2-60 alternating CSA/HCA: 30 CSA, 31 HCA) + MTP block "
+                     "(window only)",
+           "decode_tokens_per_s": round(B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "steps": reps,
+           "schedule": "per layer decode_append + decode_step, layer after layer; one graph per step",
+           "cache_gb": round(sum(t.numel() * t.element_size() for grp in keep for t in grp
+                                 if isinstance(t, torch.Tensor)) / 1e9, 2)}
+    del layers, keep, graph
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_prefill(steps: int, warmup: int):
     import torch
     pw = PrefillWorkload()
@@ -585,6 +709,9 @@ def main():
     import torch
     if args.prefill_only:
         print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}))
+        return
+    if args.schedule_only:
+        print(json.dumps({"v4_pro_schedule": run_schedule(args.steps)}))
         return
     if args.loop_only:
         print(json.dumps({"decode_loop": run_loop(args.copies, args.steps)}))
@@ -705,6 +832,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_loop:
         res["decode_loop"] = run_loop(args.copies, 50)
+    if not args.no_schedule:
+        res["v4_pro_schedule"] = run_schedule(10)
     if args.mtp:
         res["mtp"] = [run_mtp(int(tq), args.copies, 50) for tq in args.mtp.split(",")]
     if not args.no_prefill:

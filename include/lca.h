@@ -233,6 +233,23 @@ lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dty
                           lca_dtype out_dt, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lca_window_attend -- attention over the sliding window and the sink alone,
+ * with no compressed entries: the attention of the multi-token-prediction
+ * block that follows the 61 CSA/HCA layers of V4-Pro.  [release notes
+ * (agentlenshq.com), 架構實現: the final MTP block of V4-Pro uses only
+ * sliding-window attention.]  The softmax of lca_sparse_mqa_attend with an
+ * empty selection (k = 0, no entry cache); arguments as there, workspace
+ * lca_attend_ws(B, Tq, Hq, D, 0, W_buf).  In lca_attend_batch and
+ * lca_decode_step the same job is sparse = 1, k = 0, kv = NULL, N_cap = 0.
+ * Supported: D = 128; Hq in {16, 32, 64}.
+ */
+lca_status lca_window_attend(const void* q, lca_dtype q_dt, const void* win, lca_dtype win_dt,
+                             int64_t W_buf, const int32_t* win_begin, const int32_t* win_len,
+                             const float* sink, float scale, int32_t B, int32_t Tq, int32_t Hq,
+                             int32_t D, void* out, lca_dtype out_dt, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * lca_attend_batch -- several attention calls in one launch (one attention
  * launch and at most one merge launch for all jobs), for example the CSA and
  * HCA branches of one decode step.  Each job is the argument list of
@@ -276,7 +293,8 @@ lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* str
  * nothing the indexer writes.  [release notes (agentlenshq.com), 壓縮稀疏注意力
  * (CSA) / 重度壓縮注意力 (HCA): only the CSA branch depends on the top-k.]
  *   cjobs    0 <= ncjobs <= LCA_MAX_COMPRESS_JOBS compress jobs (as lca_compress_batch)
- *   ijob     the indexer call's arguments (as lca_lightning_index_topk)
+ *   ijob     the indexer call's arguments (as lca_lightning_index_topk), or
+ *            NULL for a step without an indexer (an HCA or window-only layer)
  *   ajobs    0 <= najobs <= LCA_MAX_ATTEND_JOBS attention jobs (as lca_attend_batch)
  * Each part is validated as its own call.  Dense attention jobs must not
  * read or write memory the indexer job writes (idx_out, score_out, its

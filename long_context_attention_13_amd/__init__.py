@@ -23,7 +23,7 @@ STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA
 
 EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
-           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append"]
+           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append", "lca_window_attend"]
 MAX_COMPRESS_JOBS = 8
 MAX_ATTEND_JOBS = 4
 MAX_APPEND_JOBS = 8
@@ -87,6 +87,9 @@ def load(path: str = LIB_PATH):
                                  i32, i32, i32, vp, i32, vp, vp, sz, vp]
     L.lca_attend_ws.restype = sz
     L.lca_attend_ws.argtypes = [i32, i32, i32, i32, i64, i64]
+    L.lca_window_attend.restype = i32
+    L.lca_window_attend.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp, f32, i32, i32, i32, i32, vp, i32, vp, vp, sz,
+                                    vp]
     _lib = L
     return L
 
@@ -185,12 +188,16 @@ class AttendJob(ctypes.Structure):
 def attend_job(sparse, q, kv, kv_scale, idx_or_n, win, win_begin, win_len, sink, scale, out, lse=None,
                ws=None) -> AttendJob:
     """One job of attend_batch: the arguments of sparse_mqa_attend (sparse=True, idx) or
-    hca_attend (sparse=False, n_elig).  The job holds references to its tensors, so they stay
-    allocated while the job object is alive (keep it until attend_batch has been called)."""
+    hca_attend (sparse=False, n_elig); kv=None with sparse=True and idx_or_n=None is a
+    window_attend job.  The job holds references to its tensors, so they stay allocated while
+    the job object is alive (keep it until attend_batch has been called)."""
     B, Tq, Hq, D = q.shape
     ptr = lambda t: None if t is None else t.data_ptr()
-    job = AttendJob(1 if sparse else 0, ptr(q), dtype_of(q), ptr(kv), dtype_of(kv, kv_scale), ptr(kv_scale),
-                    kv.shape[1], ptr(idx_or_n) if sparse else None, idx_or_n.shape[-1] if sparse else 0,
+    if kv is None and not (sparse and idx_or_n is None):
+        raise ValueError("kv=None describes a window-only job: sparse=True, idx_or_n=None")
+    job = AttendJob(1 if sparse else 0, ptr(q), dtype_of(q), ptr(kv), BF16 if kv is None else dtype_of(kv, kv_scale),
+                    ptr(kv_scale), 0 if kv is None else kv.shape[1], ptr(idx_or_n) if sparse else None,
+                    (0 if idx_or_n is None else idx_or_n.shape[-1]) if sparse else 0,
                     None if sparse else ptr(idx_or_n), ptr(win), dtype_of(win), win.shape[1], ptr(win_begin),
                     ptr(win_len), ptr(sink), float(scale), B, Tq, Hq, D, ptr(out), dtype_of(out), ptr(lse),
                     ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
@@ -230,11 +237,12 @@ def index_job(qi, qi_scale, w, ki, ki_scale, n_elig, k, idx_out, ws, score_out=N
 
 
 def decode_step(cjobs, ijob, ajobs, stream=None):
-    """One decode step (see lca_decode_step): compress jobs, the indexer job, attention jobs;
-    job lists may be prebuilt ctypes arrays."""
+    """One decode step (see lca_decode_step): compress jobs, the indexer job (None: no
+    indexer), attention jobs; job lists may be prebuilt ctypes arrays."""
     ca = cjobs if isinstance(cjobs, ctypes.Array) else (CompressJob * max(1, len(cjobs)))(*cjobs)
     aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
-    _check(load().lca_decode_step(ca, len(cjobs), ctypes.byref(ijob), aa, len(ajobs), _stream(stream)))
+    ij = None if ijob is None else ctypes.byref(ijob)
+    _check(load().lca_decode_step(ca, len(cjobs), ij, aa, len(ajobs), _stream(stream)))
 
 
 class AppendJob(ctypes.Structure):
@@ -315,4 +323,13 @@ def hca_attend(q, kv, kv_scale, n_elig, win, win_begin, win_len, sink, scale, ou
         _p(q), dtype_of(q), _p(kv), dtype_of(kv, kv_scale), _p(kv_scale), kv.shape[1], _p(n_elig),
         _p(win), dtype_of(win), win.shape[1], _p(win_begin), _p(win_len), _p(sink), float(scale),
         B, Tq, Hq, D, _p(out), dtype_of(out), _p(lse), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def window_attend(q, win, win_begin, win_len, sink, scale, out, lse=None, ws=None, stream=None):
+    """Attention over the window rows and the sink only (see lca_window_attend)."""
+    B, Tq, Hq, D = q.shape
+    _check(load().lca_window_attend(
+        _p(q), dtype_of(q), _p(win), dtype_of(win), win.shape[1], _p(win_begin), _p(win_len), _p(sink),
+        float(scale), B, Tq, Hq, D, _p(out), dtype_of(out), _p(lse), _p(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))

@@ -334,12 +334,13 @@ lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const 
   lca::CompressBatch cb;
   lca_status st = compress_batch_check(name, cjobs, ncjobs, 0, &cb);
   if (st != LCA_OK) return st;
-  REQ(ijob != nullptr, LCA_EINVAL, "%s: ijob is NULL", name);
-  const lca_index_job& I = *ijob;
-  lca::IndexArgs ia;
-  st = index_check("lca_decode_step: index job", I.qi, I.qi_dt, I.qi_scale, I.w, I.ki, I.ki_dt, I.ki_scale, I.n_elig,
-                   I.B, I.Tq, I.H_I, I.d_I, I.N_cap, I.k, I.idx_out, I.score_out, I.ws, I.ws_bytes, &ia);
-  if (st != LCA_OK) return st;
+  lca::IndexArgs ia{};                 // no index job: B = 0
+  if (ijob != nullptr) {
+    const lca_index_job& I = *ijob;
+    st = index_check("lca_decode_step: index job", I.qi, I.qi_dt, I.qi_scale, I.w, I.ki, I.ki_dt, I.ki_scale,
+                     I.n_elig, I.B, I.Tq, I.H_I, I.d_I, I.N_cap, I.k, I.idx_out, I.score_out, I.ws, I.ws_bytes, &ia);
+    if (st != LCA_OK) return st;
+  }
   lca::AttendBatch ab;
   st = attend_batch_check(name, ajobs, najobs, 0, &ab);
   if (st != LCA_OK) return st;
@@ -399,6 +400,15 @@ lca_status lca_sparse_mqa_attend(const void* q, lca_dtype q_dt, const void* kv, 
   REQ(k >= 0 && k <= 2048, LCA_EINVAL, "%s: k=%d outside [0, 2048]", name, k);
   return attend_common(name, 1, q, q_dt, kv, kv_dt, kv_scale, N_cap, idx, k, nullptr, win, win_dt,
                        W_buf, win_begin, win_len, sink, scale, B, Tq, Hq, D, out, out_dt, lse, ws, ws_bytes,
+                       stream);
+}
+
+lca_status lca_window_attend(const void* q, lca_dtype q_dt, const void* win, lca_dtype win_dt, int64_t W_buf,
+                             const int32_t* win_begin, const int32_t* win_len, const float* sink, float scale,
+                             int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return attend_common("lca_window_attend", 1, q, q_dt, nullptr, LCA_BF16, nullptr, 0, nullptr, 0, nullptr, win,
+                       win_dt, W_buf, win_begin, win_len, sink, scale, B, Tq, Hq, D, out, out_dt, lse, ws, ws_bytes,
                        stream);
 }
 

@@ -19,6 +19,9 @@ is Gaussian or uniform noise with these shapes):
                      [0.9 * 2^20, 2^20]: 262144 FP8 CSA entries + MXFP4 keys,
                      top-1024; 8192 FP8 HCA entries; window 128; 64 heads
   prefill_chunk      8192 new bf16 tokens after a 262144-token cache
+  v4_pro schedule    the attention layers of the 61-layer model and its MTP
+                     block (v4_pro_layer_kinds), each layer with caches of the
+                     layer_pair_1m shapes and its own raw-token rings
 
 Distributions: KV, gates, queries, raw keys ~ N(0,1); positional bias ~
 N(0, 0.1^2); indexer head weights ~ U(0,1); sinks ~ N(0,1); the small fp32
@@ -158,3 +161,11 @@ def prefill_chunk(seed: int = SEEDS["prefill_chunk"], ctx: int = 262144, T: int 
     out["sink_hca"] = normal(g, (Hq,))
     out["q"] = normal(g, (1, T, Hq, D))
     return out
+
+
+def v4_pro_layer_kinds(n_layers: int = 61) -> list:
+    """Attention kind of every layer of the 61-layer V4-Pro model, then its MTP
+    block: layers 0 and 1 "hca", layers 2 .. n_layers-1 alternating "csa" and
+    "hca" starting with "csa", and "window" (sliding-window attention only)
+    for the MTP block.  A configuration list, not arithmetic."""
+    return ["hca", "hca"] + ["csa" if (l - 2) % 2 == 0 else "hca" for l in range(2, n_layers)] + ["window"]

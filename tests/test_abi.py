@@ -214,7 +214,8 @@ def decode_step(L, cjobs, ij, ajobs, nc=None, na=None):
 def test_decode_step_validation(L):
     assert decode_step(L, [], index_job(B=0), []) == 0                       # nothing to do
     assert decode_step(L, [batch_job(B=0)], index_job(B=0), [attend_job(B=0)]) == 0
-    assert decode_step(L, [], None, []) == 1
+    assert decode_step(L, [], None, []) == 0                                  # no indexer
+    assert decode_step(L, [batch_job(B=0)], None, [attend_job(B=0)]) == 0
     assert decode_step(L, [batch_job()] * 9, index_job(B=0), []) == 1
     assert decode_step(L, [], index_job(B=0), [attend_job()] * 5) == 1
     assert decode_step(L, [], index_job(k=0), []) == 1
@@ -236,6 +237,26 @@ def append_job(**kw):
 def decode_append(L, jobs, n=None):
     arr = (lca.AppendJob * max(1, len(jobs)))(*jobs)
     return L.lca_decode_append(arr, len(jobs) if n is None else n, None)
+
+
+def test_window_attend_validation(L):
+    a = dict(q=FAKE, q_dt=lca.BF16, win=FAKE, win_dt=lca.BF16, W_buf=256, win_begin=FAKE, win_len=FAKE, sink=FAKE,
+             scale=0.088, B=2, Tq=1, Hq=64, D=128, out=FAKE, out_dt=lca.BF16, lse=None, ws=FAKE, ws_bytes=1 << 30,
+             stream=None)
+
+    def call(**kw):
+        b = dict(a)
+        b.update(kw)
+        return L.lca_window_attend(*b.values())
+    assert call(B=0) == 0
+    assert call(win=None) == 1
+    assert b"win must be" in L.lca_last_error()
+    assert call(Hq=48) == 2
+    assert call(D=64) == 2
+    assert call(q_dt=lca.FP8E4M3) == 2
+    need = L.lca_attend_ws(2, 1, 64, 128, 0, 256)
+    if need > 0:
+        assert call(ws=None) == 4
 
 
 def test_decode_append_validation(L):
