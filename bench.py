@@ -481,26 +481,35 @@ def run_loop(copies: int, steps: int):
         plans.append(((lca.AppendJob * 3)(*ap), (lca.CompressJob * 3)(*cj), ij, (lca.AttendJob * 2)(*aj)))
     torch.cuda.synchronize()
     reps = max(1, steps // copies)
-    assert reps + 1 <= 512, "appended tokens must fit below the workload's lengths"
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for ap, cj, ij, aj in plans:
-            lca.decode_append(ap)
-            lca.decode_step(cj, ij, aj)
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    assert 2 * (reps + 1) <= 512, "appended tokens must fit below the workload's lengths"
+    ms = {}
+    for fused in (True, False):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for ap, cj, ij, aj in plans:
+                if fused:
+                    lca.decode_loop_step(ap, cj, ij, aj)
+                else:
+                    lca.decode_append(ap)
+                    lca.decode_step(cj, ij, aj)
         graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / (reps * copies)
-    out = {"decode_tokens_per_s": round(wl.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[fused] = e0.elapsed_time(e1) / (reps * copies)
+        del graph
+    out = {"decode_tokens_per_s": round(wl.B / (ms[True] * 1e-3), 1), "ms_per_step": round(ms[True], 4),
            "steps": reps * copies,
-           "schedule": "decode_append (3 rings) + decode_step, graph of %d steps replayed" % copies,
+           "schedule": "decode_loop_step (3 ring appends inside the compress launch, then the decode step), "
+                       "graph of %d steps replayed" % copies,
+           "two_calls": {"decode_tokens_per_s": round(wl.B / (ms[False] * 1e-3), 1),
+                         "ms_per_step": round(ms[False], 4), "schedule": "decode_append + decode_step"},
            "compression": "when a block completes: CSA and indexer every 4th step, HCA every 128th"}
-    del wl, keep, plans, graph
+    del wl, keep, plans
     torch.cuda.empty_cache()
     return out
 
@@ -601,28 +610,38 @@ def run_schedule(steps: int):
         layers.append(((lca.AppendJob * len(apps))(*apps), cj, ij, [aj]))
     torch.cuda.synchronize()
     reps = max(1, steps)
-    assert reps + 1 <= 64, "appended tokens must fit below the layer-pair workload's lengths"
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for ap, cj, ij, aj in layers:
-            lca.decode_append(ap)
-            lca.decode_step(cj, ij, aj)
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    assert 2 * (reps + 1) <= 64, "appended tokens must fit below the layer-pair workload's lengths"
+    ms = {}
+    for fused in (True, False):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for ap, cj, ij, aj in layers:
+                if fused:
+                    lca.decode_loop_step(ap, cj, ij, aj)
+                else:
+                    lca.decode_append(ap)
+                    lca.decode_step(cj, ij, aj)
         graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[fused] = e0.elapsed_time(e1) / reps
+        del graph
     out = {"layers": "61 attention layers (0-1 HCA, 2-60 alternating CSA/HCA: 30 CSA, 31 HCA) + MTP block "
                      "(window only)",
-           "decode_tokens_per_s": round(B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "steps": reps,
-           "schedule": "per layer decode_append + decode_step, layer after layer; one graph per step",
+           "decode_tokens_per_s": round(B / (ms[True] * 1e-3), 1), "ms_per_step": round(ms[True], 4),
+           "steps": reps,
+           "schedule": "per layer one decode_loop_step, layer after layer; one graph per step",
+           "two_calls": {"decode_tokens_per_s": round(B / (ms[False] * 1e-3), 1),
+                         "ms_per_step": round(ms[False], 4),
+                         "schedule": "per layer decode_append + decode_step"},
            "cache_gb": round(sum(t.numel() * t.element_size() for grp in keep for t in grp
                                  if isinstance(t, torch.Tensor)) / 1e9, 2)}
-    del layers, keep, graph
+    del layers, keep
     torch.cuda.empty_cache()
     return out
 

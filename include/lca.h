@@ -354,6 +354,27 @@ typedef struct lca_append_job {
 
 lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* stream);
 
+/*
+ * lca_decode_loop_step -- one step of a decode loop in one call:
+ * lca_decode_append(app) followed by lca_decode_step(cjobs, ijob, ajobs), with
+ * the same results, and the appends run inside the compress launch (one
+ * dependent launch less).  [Sources as lca_decode_append and lca_decode_step.]
+ * A compress job whose x is an append job's ring is that stream's block
+ * compression: it must take x_tok0, nblk and dst_row0 from that append job,
+ * have nblk_max = 1, the append job's B, m, x_dt and D, and x_rows = 2R; its
+ * workgroup appends the token, then compresses.  Append jobs that no compress
+ * job reads (for example a window-only stream) get workgroups of their own in
+ * the same launch.  No two compress jobs may read one append job's ring, and
+ * no compress job may read a ring through any other pointer.
+ *   app      0 <= napp <= LCA_MAX_APPEND_JOBS append jobs (as lca_decode_append)
+ *   cjobs, ijob (may be NULL), ajobs   as lca_decode_step
+ * Errors: those of the two calls; LCA_EINVAL when a compress job breaks the
+ * pairing rules above.
+ */
+lca_status lca_decode_loop_step(const lca_append_job* app, int32_t napp, const lca_compress_job* cjobs,
+                                int32_t ncjobs, const lca_index_job* ijob, const lca_attend_job* ajobs,
+                                int32_t najobs, void* stream);
+
 /* Workspace bytes for the attention calls.  n_kv_max is k for
  * lca_sparse_mqa_attend and N_cap for lca_hca_attend; W_buf the window buffer
  * rows. */

@@ -23,7 +23,8 @@ STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA
 
 EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
-           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append", "lca_window_attend"]
+           "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append", "lca_window_attend",
+           "lca_decode_loop_step"]
 MAX_COMPRESS_JOBS = 8
 MAX_ATTEND_JOBS = 4
 MAX_APPEND_JOBS = 8
@@ -68,6 +69,9 @@ def load(path: str = LIB_PATH):
     L.lca_decode_step.restype = i32
     L.lca_decode_step.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
                                   ctypes.POINTER(AttendJob), i32, vp]
+    L.lca_decode_loop_step.restype = i32
+    L.lca_decode_loop_step.argtypes = [ctypes.POINTER(AppendJob), i32, ctypes.POINTER(CompressJob), i32,
+                                       ctypes.POINTER(IndexJob), ctypes.POINTER(AttendJob), i32, vp]
     L.lca_decode_append.restype = i32
     L.lca_decode_append.argtypes = [ctypes.POINTER(AppendJob), i32, vp]
     L.lca_attend_batch.restype = i32
@@ -273,6 +277,17 @@ def decode_append(jobs, stream=None):
     append_job(), or a ctypes array of them built once."""
     arr = jobs if isinstance(jobs, ctypes.Array) else (AppendJob * len(jobs))(*jobs)
     _check(load().lca_decode_append(arr, len(arr), _stream(stream)))
+
+
+def decode_loop_step(ajobs_append, cjobs, ijob, ajobs, stream=None):
+    """decode_append(ajobs_append) then decode_step(cjobs, ijob, ajobs) in one call, the appends
+    inside the compress launch (see lca_decode_loop_step); lists or prebuilt ctypes arrays."""
+    pa = ajobs_append if isinstance(ajobs_append, ctypes.Array) else \
+        (AppendJob * max(1, len(ajobs_append)))(*ajobs_append)
+    ca = cjobs if isinstance(cjobs, ctypes.Array) else (CompressJob * max(1, len(cjobs)))(*cjobs)
+    aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
+    ij = None if ijob is None else ctypes.byref(ijob)
+    _check(load().lca_decode_loop_step(pa, len(ajobs_append), ca, len(cjobs), ij, aa, len(ajobs), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

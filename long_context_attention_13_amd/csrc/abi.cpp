@@ -344,16 +344,21 @@ lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const 
   lca::AttendBatch ab;
   st = attend_batch_check(name, ajobs, najobs, 0, &ab);
   if (st != LCA_OK) return st;
-  return hip_status(lca::launch_decode_step(cb, ia, ab, (hipStream_t)stream), name);
+  return hip_status(lca::launch_decode_step(nullptr, nullptr, cb, ia, ab, (hipStream_t)stream), name);
 }
 
-lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* stream) {
-  const char* who = "lca_decode_append";
-  REQ(njobs >= 1 && njobs <= LCA_MAX_APPEND_JOBS, LCA_EINVAL, "%s: njobs=%d outside [1, %d]", who, njobs,
-      LCA_MAX_APPEND_JOBS);
-  REQ(jobs != nullptr, LCA_EINVAL, "%s: jobs is NULL", who);
+}  // extern "C"
+
+namespace {
+
+lca_status append_batch_check(const char* who, const lca_append_job* jobs, int32_t njobs, int min_jobs,
+                              lca::AppendBatch* out) {
+  REQ(njobs >= min_jobs && njobs <= LCA_MAX_APPEND_JOBS, LCA_EINVAL, "%s: njobs=%d outside [%d, %d]", who, njobs,
+      min_jobs, LCA_MAX_APPEND_JOBS);
+  REQ(njobs == 0 || jobs != nullptr, LCA_EINVAL, "%s: jobs is NULL", who);
   static_assert(LCA_MAX_APPEND_JOBS == lca::MAX_APPEND_JOBS, "job limits agree");
-  lca::AppendBatch bt{};
+  lca::AppendBatch& bt = *out;
+  bt = lca::AppendBatch{};
   bt.njobs = njobs;
   for (int j = 0; j < njobs; ++j) {
     const lca_append_job& J = jobs[j];
@@ -381,7 +386,62 @@ lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* st
     a.len = J.len; a.m = J.m; a.W = J.W; a.x_tok0 = J.x_tok0; a.nblk = J.nblk; a.dst_row0 = J.dst_row0;
     a.n_elig = J.n_elig; a.win_begin = J.win_begin; a.win_len = J.win_len; a.B = J.B; a.D = J.D;
   }
-  return hip_status(lca::launch_decode_append(bt, (hipStream_t)stream), who);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* stream) {
+  lca::AppendBatch bt;
+  const lca_status st = append_batch_check("lca_decode_append", jobs, njobs, 1, &bt);
+  if (st != LCA_OK) return st;
+  return hip_status(lca::launch_decode_append(bt, (hipStream_t)stream), "lca_decode_append");
+}
+
+lca_status lca_decode_loop_step(const lca_append_job* app, int32_t napp, const lca_compress_job* cjobs,
+                                int32_t ncjobs, const lca_index_job* ijob, const lca_attend_job* ajobs,
+                                int32_t najobs, void* stream) {
+  const char* name = "lca_decode_loop_step";
+  lca::AppendBatch apb;
+  lca_status st = append_batch_check(name, app, napp, 0, &apb);
+  if (st != LCA_OK) return st;
+  lca::CompressBatch cb;
+  st = compress_batch_check(name, cjobs, ncjobs, 0, &cb);
+  if (st != LCA_OK) return st;
+  // pair every compress job that reads an append job's ring with that append
+  lca::AppendMap mp{};
+  bool used[LCA_MAX_APPEND_JOBS] = {};
+  for (int j = 0; j < ncjobs; ++j) {
+    const lca::CompressArgs& c = cb.job[j];
+    mp.of[j] = -1;
+    for (int a = 0; a < napp; ++a) {
+      const lca::AppendArgs& A = apb.job[a];
+      if (A.ring != c.x) continue;
+      REQ(!used[a], LCA_EINVAL, "%s: compress jobs %d and another read the ring of append job %d", name, j, a);
+      REQ(c.x_tok0 == A.x_tok0 && c.nblk == A.nblk && c.dst_row0 == A.dst_row0, LCA_EINVAL,
+          "%s: compress job %d reads the ring of append job %d but not its x_tok0 / nblk / dst_row0", name, j, a);
+      REQ(c.nblk_max == 1 && c.B == A.B && c.m == A.m && c.x_rows == 2 * A.R && c.x_dt == A.x_dt && c.D == A.D,
+          LCA_EINVAL, "%s: compress job %d and append job %d disagree (nblk_max 1, B, m, x_rows = 2R, x_dt, D)",
+          name, j, a);
+      used[a] = true;
+      mp.of[j] = a;
+    }
+  }
+  for (int a = 0; a < napp; ++a)
+    if (!used[a]) mp.extra[mp.nextra++] = a;
+  lca::IndexArgs ia{};
+  if (ijob != nullptr) {
+    const lca_index_job& I = *ijob;
+    st = index_check("lca_decode_loop_step: index job", I.qi, I.qi_dt, I.qi_scale, I.w, I.ki, I.ki_dt, I.ki_scale,
+                     I.n_elig, I.B, I.Tq, I.H_I, I.d_I, I.N_cap, I.k, I.idx_out, I.score_out, I.ws, I.ws_bytes, &ia);
+    if (st != LCA_OK) return st;
+  }
+  lca::AttendBatch ab;
+  st = attend_batch_check(name, ajobs, najobs, 0, &ab);
+  if (st != LCA_OK) return st;
+  return hip_status(lca::launch_decode_step(&apb, &mp, cb, ia, ab, (hipStream_t)stream), name);
 }
 
 size_t lca_attend_ws(int32_t B, int32_t Tq, int32_t Hq, int32_t D, int64_t n_kv_max, int64_t W_buf) {

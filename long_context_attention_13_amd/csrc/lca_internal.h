@@ -88,9 +88,24 @@ struct AppendBatch {
 };
 hipError_t launch_decode_append(const AppendBatch& bt, hipStream_t s);
 
+// The appends of a decode-loop step run in the compress launch: compress job
+// j appends for append job of[j] (-1: none) before it compresses (the job
+// reads that stream's ring and takes its block arguments from the append);
+// the append jobs extra[0 .. nextra) that no compress job reads get blocks of
+// their own in the same launch.
+struct AppendMap {
+  int of[MAX_COMPRESS_JOBS];
+  int extra[MAX_APPEND_JOBS];
+  int nextra;
+};
+hipError_t launch_append_compress(const AppendBatch& ab, const AppendMap& mp, const CompressBatch& cb,
+                                  hipStream_t s);
+
 // One decode step: the compress jobs, the indexer call, the attention jobs, in
 // that order and with the results of the three calls; the dense attention jobs
 // may run beside the indexer's scan.
-hipError_t launch_decode_step(const CompressBatch& cb, const IndexArgs& ia, const AttendBatch& ab, hipStream_t s);
+// With `app` (and its map) the appends run first, in the compress launch.
+hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const CompressBatch& cb,
+                              const IndexArgs& ia, const AttendBatch& ab, hipStream_t s);
 
 }  // namespace lca

@@ -76,9 +76,13 @@ static AttendBatch sub_batch(const AttendBatch& all, bool dense) {
   return sub;
 }
 
-hipError_t launch_decode_step(const CompressBatch& cb, const IndexArgs& ia, const AttendBatch& ab, hipStream_t s) {
+hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const CompressBatch& cb,
+                              const IndexArgs& ia, const AttendBatch& ab, hipStream_t s) {
   hipError_t e;
-  if (cb.njobs > 0) {
+  if (app != nullptr) {
+    e = launch_append_compress(*app, *mp, cb, s);
+    if (e != hipSuccess) return e;
+  } else if (cb.njobs > 0) {
     e = launch_compress_batch(cb, s);
     if (e != hipSuccess) return e;
   }

@@ -277,3 +277,33 @@ def test_decode_append_validation(L):
     assert decode_append(L, [append_job(m=-1)]) == 1
     assert decode_append(L, [append_job(D=96)]) == 2
     assert decode_append(L, [append_job(x_dt=lca.FP8E4M3)]) == 2
+
+
+def test_decode_loop_step_validation(L):
+    def call(apps, cjobs, ij=None, ajobs=()):
+        pa = (lca.AppendJob * max(1, len(apps)))(*apps)
+        ca = (lca.CompressJob * max(1, len(cjobs)))(*cjobs)
+        aa = (lca.AttendJob * max(1, len(ajobs)))(*ajobs)
+        return L.lca_decode_loop_step(pa, len(apps), ca, len(cjobs), None if ij is None else ctypes.byref(ij), aa,
+                                      len(ajobs), None)
+    RING, TOK0, NBLK, ROW0 = FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5
+    app = lambda **kw: append_job(ring=RING, x_tok0=TOK0, nblk=NBLK, dst_row0=ROW0, R=128, m=4, **kw)
+    cj = lambda **kw: batch_job(**{**dict(x=RING, x_tok0=TOK0, nblk=NBLK, dst_row0=ROW0, x_rows=256, m=4), **kw})
+    # nothing to launch (every job has B = 0): accepted without a GPU
+    assert call([app(B=0)], [cj(B=0)]) == 0
+    assert call([], []) == 0
+    assert call([app(B=0)], []) == 0
+    # pairing rules
+    assert call([app()], [cj(nblk=FAKE * 6)]) == 1
+    assert b"x_tok0 / nblk / dst_row0" in L.lca_last_error()
+    assert call([app()], [cj(nblk_max=2)]) == 1
+    assert call([app()], [cj(x_rows=512)]) == 1
+    assert call([app()], [cj(m=128)]) == 1
+    assert call([app()], [cj(B=1)]) == 1
+    assert call([app()], [cj(), cj()]) == 1
+    assert b"read the ring of append job 0" in L.lca_last_error()
+    # the parts are validated as their own calls
+    assert call([app(D=96)], []) == 2
+    assert call([app()] * 9, []) == 1
+    assert call([app(B=0)], [cj(B=0)], index_job(k=0)) == 1
+    assert b"index job" in L.lca_last_error()

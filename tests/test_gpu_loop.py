@@ -16,7 +16,9 @@ checks:
   keys bit-exact: their raw values are multiples of 1/16 with equal gates, so
   fp32 pooling is exact; FP8 rows a correct rounding of the oracle's pooling);
 - the same loop captured once as a graph (append + step) and replayed with
-  new inputs copied in before each replay ends with the eager loop's bytes.
+  new inputs copied in before each replay ends with the eager loop's bytes,
+  both as the two calls and as one lca_decode_loop_step (the appends inside
+  the compress launch).
 
 Two cases: long sequences (the indexer's chunked scan runs beside the HCA
 attention) starting at different phases of the 4- and 128-token blocks, and
@@ -202,9 +204,12 @@ class Device:
         self.q_csa.copy_(self.all_qc[i])
         self.q_hca.copy_(self.all_qh[i])
 
-    def step(self):
-        lca.decode_append(self.appends)
-        lca.decode_step(self.cjobs, self.ijob, self.ajobs)
+    def step(self, fused=False):
+        if fused:
+            lca.decode_loop_step(self.appends, self.cjobs, self.ijob, self.ajobs)
+        else:
+            lca.decode_append(self.appends)
+            lca.decode_step(self.cjobs, self.ijob, self.ajobs)
 
     def state(self):
         ts = [self.ent, self.ent_sc, self.key, self.key_sc, self.hca, self.hca_sc, self.idx, self.score,
@@ -312,16 +317,19 @@ def test_decode_loop(case):
     check_final_state(lp, dv)
     eager = dv.state()
 
-    # the same loop as one captured step replayed S times
-    dv2 = Device(lp)
-    dv2.load_inputs(0)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        dv2.step()
-    torch.cuda.synchronize()
-    for i in range(S):
-        dv2.load_inputs(i)
-        graph.replay()
-    torch.cuda.synchronize()
-    for j, (a, b) in enumerate(zip(dv2.state(), eager)):
-        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"graph loop: state {j}"
+    # the same loop as one captured step replayed S times: the two calls, and
+    # decode_loop_step (the appends inside the compress launch)
+    for fused in (False, True):
+        dv2 = Device(lp)
+        dv2.load_inputs(0)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dv2.step(fused)
+        torch.cuda.synchronize()
+        for i in range(S):
+            dv2.load_inputs(i)
+            graph.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(dv2.state(), eager)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"graph loop (fused={fused}): state {j}"
+        del graph, dv2

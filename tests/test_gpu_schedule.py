@@ -10,7 +10,8 @@ and a 128-block in every layer.  At every step every layer's index set and
 scores are bit-exact and its attention is within rtol 2e-2 of the oracle on
 caches the host assembles (oracle codecs, oracle pooling of the host-held
 token history) and windows cut from that history; the captured schedule step
-replayed five times ends with the eager loop's bytes.  lca_window_attend is
+replayed five times ends with the eager loop's bytes, issued per layer as
+the two calls and as one lca_decode_loop_step.  lca_window_attend is
 also checked on its own against the oracle on ragged windows."""
 import math
 
@@ -201,9 +202,12 @@ class LayerDev:
             self.qi_sc.copy_(self.all_qs[i])
             self.w.copy_(self.all_w[i])
 
-    def issue(self):
-        lca.decode_append(self.appends)
-        lca.decode_step(self.cjobs, self.ijob, [self.ajob])
+    def issue(self, fused=False):
+        if fused:
+            lca.decode_loop_step(self.appends, self.cjobs, self.ijob, [self.ajob])
+        else:
+            lca.decode_append(self.appends)
+            lca.decode_step(self.cjobs, self.ijob, [self.ajob])
 
     def state(self):
         ts = [self.out, self.lse] + [t["ring"] for t in self.st] + [t["len"] for t in self.st]
@@ -254,22 +258,24 @@ def test_v4_pro_schedule_loop():
             check_layer(ly, dv, i, L, f"step {i} layer {j} ({ly.kind})")
     eager = [dv.state() for dv in devs]
 
-    devs2 = [LayerDev(ly) for ly in layers]
-    for dv in devs2:
-        dv.load_inputs(0)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    for fused in (False, True):
+        devs2 = [LayerDev(ly) for ly in layers]
         for dv in devs2:
-            dv.issue()
-    torch.cuda.synchronize()
-    for i in range(S):
-        for dv in devs2:
-            dv.load_inputs(i)
-        graph.replay()
-    torch.cuda.synchronize()
-    for j, dv in enumerate(devs2):
-        for a, b in zip(dv.state(), eager[j]):
-            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"graph: layer {j}"
+            dv.load_inputs(0)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for dv in devs2:
+                dv.issue(fused)
+        torch.cuda.synchronize()
+        for i in range(S):
+            for dv in devs2:
+                dv.load_inputs(i)
+            graph.replay()
+        torch.cuda.synchronize()
+        for j, dv in enumerate(devs2):
+            for a, b in zip(dv.state(), eager[j]):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"graph (fused={fused}): layer {j}"
+        del graph, devs2
 
 
 @pytest.mark.parametrize("Hq_,q_dt", [(64, "bf16"), (16, "f32")])
