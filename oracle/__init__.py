@@ -62,6 +62,8 @@ def lib():
         L.orc_encode.argtypes = [vp, i64, i32, vp, vp]
         L.orc_pool.restype = None
         L.orc_pool.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        L.orc_pool_variant.restype = None
+        L.orc_pool_variant.argtypes = [vp, vp, i32, vp, i64, i32, i32, i32, vp]
         L.orc_index_score.restype = dbl
         L.orc_index_score.argtypes = [vp, vp, vp, i32, i32]
         L.orc_select_topk.restype = None
@@ -175,6 +177,26 @@ def pool(x, gate, bias, m):
     out = np.empty((nblk, D), np.float64)
     if nblk:
         lib().orc_pool(_p(x), _p(gate), _p(bias), nblk, int(m), int(D), _p(out))
+    return out
+
+
+def pool_variant(x, gate, bias, m, overlap=0):
+    """Pooling variants (see orc_pool_variant): x [T, D]; gate [T] (one logit per
+    token) or [T, D] (per channel); bias [m + overlap] or [m + overlap, D]
+    matching the gate; block j pools positions j*m - overlap .. j*m + m - 1 that
+    exist.  Returns [T // m, D] float64."""
+    x = _c(x, np.float64)
+    gate = _c(gate, np.float64)
+    bias = _c(bias, np.float64)
+    T, D = x.shape
+    pc = 1 if gate.ndim == 2 else 0
+    assert gate.shape == ((T, D) if pc else (T,))
+    assert bias.shape == ((m + overlap, D) if pc else (m + overlap,))
+    assert 0 <= overlap <= m
+    nblk = T // m
+    out = np.empty((nblk, D), np.float64)
+    if nblk:
+        lib().orc_pool_variant(_p(x), _p(gate), pc, _p(bias), nblk, int(m), int(overlap), int(D), _p(out))
     return out
 
 

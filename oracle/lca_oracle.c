@@ -266,6 +266,43 @@ void orc_pool(const double* x, const double* gate, const double* bias,
 }
 
 /* ------------------------------------------------------------------------- */
+/* O1 variants.  The pages name softmax-gated pooling with a learned          */
+/* positional bias [RN-CSA] but give neither the gate's shape nor whether     */
+/* blocks overlap; orc_pool takes one logit per token and disjoint blocks.    */
+/* These are the two alternatives, alone or together:                         */
+/*  - gate_pc = 1: one logit per token and channel, gate[t][d], with a bias   */
+/*    per block position and channel, bias[u][d]; one softmax per channel;    */
+/*  - overlap o (0 <= o <= m): block j pools the positions jm - o .. jm+m-1   */
+/*    that exist (positions below 0 are left out of the softmax); the bias    */
+/*    index of position t is u = t - (jm - o), so bias has m + o rows.        */
+/* For block j and channel d, over the existing positions t_u:               */
+/*   a_u = gate(t_u, d) + bias(u, d);  w_u = exp(a_u - max a) / sum exp(..)  */
+/*   c_j[d] = sum_u w_u * x[t_u][d]     (sums in increasing u)               */
+/* ------------------------------------------------------------------------- */
+void orc_pool_variant(const double* x, const double* gate, int gate_pc, const double* bias,
+                      int64_t nblk, int m, int o, int D, double* out) {
+  int64_t j;
+  double* a = (double*)malloc(sizeof(double) * (size_t)(m + o));
+  for (j = 0; j < nblk; ++j) {
+    const int64_t t0 = j * m - o;                       /* position of u = 0 */
+    const int u0 = t0 < 0 ? (int)(-t0) : 0;             /* first existing u */
+    int d, u;
+    for (d = 0; d < D; ++d) {
+      double amax = -INFINITY, z = 0.0, c = 0.0;
+      for (u = u0; u < m + o; ++u) {
+        const int64_t t = t0 + u;
+        a[u] = (gate_pc ? gate[t * D + d] : gate[t]) + (gate_pc ? bias[(int64_t)u * D + d] : bias[u]);
+        if (a[u] > amax) amax = a[u];
+      }
+      for (u = u0; u < m + o; ++u) z += exp(a[u] - amax);
+      for (u = u0; u < m + o; ++u) c += (exp(a[u] - amax) / z) * x[(t0 + u) * D + d];
+      out[j * D + d] = c;
+    }
+  }
+  free(a);
+}
+
+/* ------------------------------------------------------------------------- */
 /* O3: lightning-indexer score of entry j for one query [RN-CSA]             */
 /*   r_h = max(0, sum_i q[h][i] * k[j][i])    (left to right over i)         */
 /*   s_j = sum_h w[h] * r_h                   (left to right over h)         */
