@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop leg (append + step)")
     ap.add_argument("--loop-only", action="store_true", help="run only the decode-loop leg")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 61-layer schedule leg")
+    ap.add_argument("--no-variants", action="store_true", help="skip the compression-variant leg")
+    ap.add_argument("--variants-only", action="store_true", help="run only the compression-variant leg")
     ap.add_argument("--schedule-only", action="store_true", help="run only the 61-layer schedule leg")
     ap.add_argument("--mtp", default="2,4",
                     help="query tokens per sequence of the multi-token decode legs (comma list; empty: none)")
@@ -646,6 +648,50 @@ def run_schedule(steps: int):
     return out
 
 
+def run_variants(reps: int = 20):
+    """Compression of a prefill chunk (8192 new bf16 tokens, D = 128, one
+    sequence) with the pooling variants: one logit per token or per channel,
+    disjoint or overlapping blocks (overlap = m), for the CSA stream (m = 4,
+    2048 FP8 rows) and the HCA stream (m = 128, 64 FP8 rows).  Each variant is
+    one compress_batch call, timed with HIP events over `reps` calls.
+    Algorithmic bytes = the tokens once (2 B per value) + the gates once (4 B
+    per token, or per token and channel) + the FP8 rows with their scales."""
+    import torch
+    import long_context_attention_13_amd as lca
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1008)
+    T, D = 8192, 128
+    out = []
+    for m in (4, 128):
+        for pc in (0, 1):
+            for o in (0, m):
+                n = T // m
+                x = torch.randn(1, T + o, D, generator=g, device=dev).to(torch.bfloat16)
+                gate = torch.randn(*((1, T + o, D) if pc else (1, T + o)), generator=g, device=dev)
+                bias = torch.randn(*((m + o, D) if pc else (m + o,)), generator=g, device=dev) * 0.1
+                dst = torch.empty(1, n, D, dtype=torch.uint8, device=dev)
+                sc = torch.empty(1, n, D // 64, device=dev)
+                i32 = lambda v: torch.full((1,), v, dtype=torch.int32, device=dev)
+                job = lca.compress_job(x, gate, bias, m, i32(0), i32(n), torch.zeros(1, dtype=torch.int64, device=dev),
+                                       n, dst, lca.FP8E4M3, sc, overlap=o)
+                arr = (lca.CompressJob * 1)(job)
+                lca.compress_batch(arr)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    lca.compress_batch(arr)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                nbytes = T * D * 2 + T * (D if pc else 1) * 4 + n * (D + 8)
+                out.append({"m": m, "gate": "per channel" if pc else "per token", "overlap": o,
+                            "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+                del x, gate, bias, dst, sc, job, arr
+    return out
+
+
 def run_prefill(steps: int, warmup: int):
     import torch
     pw = PrefillWorkload()
@@ -728,6 +774,9 @@ def main():
     import torch
     if args.prefill_only:
         print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}))
+        return
+    if args.variants_only:
+        print(json.dumps({"compress_variants": run_variants()}))
         return
     if args.schedule_only:
         print(json.dumps({"v4_pro_schedule": run_schedule(args.steps)}))
@@ -853,6 +902,8 @@ def main():
         res["decode_loop"] = run_loop(args.copies, 50)
     if not args.no_schedule:
         res["v4_pro_schedule"] = run_schedule(10)
+    if not args.no_variants:
+        res["compress_variants"] = run_variants()
     if args.mtp:
         res["mtp"] = [run_mtp(int(tq), args.copies, 50) for tq in args.mtp.split(",")]
     if not args.no_prefill:

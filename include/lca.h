@@ -134,6 +134,21 @@ lca_status lca_hca_compress(const void* x, lca_dtype x_dt, int64_t x_rows, const
  * share x_dt and D (LCA_ENOTSUP otherwise).  Jobs must not write overlapping
  * destination, scale or pooled rows (they run concurrently).  On any invalid
  * job nothing is enqueued and the message names the job.
+ *
+ * Two pooling variants, per job (both 0 = the single calls' pooling).  The
+ * pages name softmax-gated pooling with a learned positional bias but give
+ * neither the gate's shape nor whether blocks overlap:
+ *   gate_pc = 1   one logit per token and channel: gate [B][x_rows][D] fp32,
+ *                 pos_bias [m + overlap][D]; one softmax per channel:
+ *                 c[d] = sum_u softmax_u(gate[b][t_u][d] + pos_bias[u][d]) x[b][t_u][d]
+ *   overlap = o   (0 <= o <= m, m + o <= 1024) block i pools the m + o tokens
+ *                 t_u = x_tok0[b] + i*m + u, u = 0 .. m+o-1: the o tokens
+ *                 before the block and its m tokens (x_tok0 points o rows
+ *                 before the first block's first token); pos_bias has m + o
+ *                 rows.  For the first entry of a sequence (dst_row0[b] + i
+ *                 == 0) the o leading tokens do not exist: they are neither
+ *                 read nor weighted.  Caller guarantees
+ *                 x_tok0[b] + nblk[b]*m + o <= x_rows.
  */
 #define LCA_MAX_COMPRESS_JOBS 8
 typedef struct lca_compress_job {
@@ -143,6 +158,7 @@ typedef struct lca_compress_job {
   int32_t B; int32_t nblk_max; int32_t D;
   void* dst; lca_dtype dst_dt; void* dst_scale; int64_t dst_rows;
   float* pooled;
+  int32_t gate_pc; int32_t overlap;
 } lca_compress_job;
 
 lca_status lca_compress_batch(const lca_compress_job* jobs, int32_t njobs, void* stream);
@@ -326,13 +342,16 @@ lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const 
  * R consecutive tokens (a block being compressed, the window) is contiguous.
  *   x_new    [B][D] device, the new tokens (x_dt: bf16 or f32; the ring's type)
  *   g_new    [B] fp32 device, their gate logits, with gring; both NULL: no gate ring
+ *            (gate_pc = 1: one logit per channel, g_new [B][D], gring [B][2R][D])
  *   len      [B] int64 device: tokens before the call; the call adds 1
  *   R        ring rows, >= max(1, m, W)
  *   m        compression block of the stream (0: not compressed)
  *   W        window of the stream's attention (0: no window outputs needed)
  * Outputs, for L = len + 1 tokens (device, each may be NULL):
  *   nblk[b] = 1 when L % m == 0 (a block completed), else 0
- *   x_tok0[b] = ring row of token L - m (the completed block's first token)
+ *   x_tok0[b] = ring row of token L - m - overlap (the first token of the
+ *            completed block's span; overlap 0 .. m as in the compress jobs,
+ *            R >= m + overlap)
  *   dst_row0[b] = L / m - 1 (its cache row);  n_elig[b] = L / m
  *   win_begin[b], win_len[b]: ring rows of the last min(L, W) tokens
  * These are the x_tok0 / nblk / dst_row0 of a compress job with x = ring,
@@ -350,6 +369,7 @@ typedef struct lca_append_job {
   int32_t* x_tok0; int32_t* nblk; int64_t* dst_row0; int32_t* n_elig;
   int32_t* win_begin; int32_t* win_len;
   int32_t B; int32_t D;
+  int32_t overlap; int32_t gate_pc;
 } lca_append_job;
 
 lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* stream);

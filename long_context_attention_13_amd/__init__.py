@@ -37,7 +37,8 @@ class CompressJob(ctypes.Structure):
                 ("x_tok0", ctypes.c_void_p), ("nblk", ctypes.c_void_p), ("dst_row0", ctypes.c_void_p),
                 ("B", ctypes.c_int32), ("nblk_max", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("dst", ctypes.c_void_p), ("dst_dt", ctypes.c_int32), ("dst_scale", ctypes.c_void_p),
-                ("dst_rows", ctypes.c_int64), ("pooled", ctypes.c_void_p)]
+                ("dst_rows", ctypes.c_int64), ("pooled", ctypes.c_void_p), ("gate_pc", ctypes.c_int32),
+                ("overlap", ctypes.c_int32)]
 
 
 class LcaError(RuntimeError):
@@ -157,15 +158,16 @@ def hca_compress(x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max, dst, ds
 
 
 def compress_job(x, gate, pos_bias, m, x_tok0, nblk, dst_row0, nblk_max, dst, dst_dt, dst_scale=None,
-                 pooled=None) -> CompressJob:
-    """One job of compress_batch, with the arguments of csa_compress / hca_compress.  The job
-    holds references to its tensors, so they stay allocated while the job object is alive
-    (keep it until compress_batch has been called)."""
+                 pooled=None, overlap=0) -> CompressJob:
+    """One job of compress_batch, with the arguments of csa_compress / hca_compress; a gate of
+    shape [B, x_rows, D] selects per-channel gates (pos_bias [m + overlap, D]), overlap > 0
+    overlapping blocks (see lca_compress_batch).  The job holds references to its tensors, so
+    they stay allocated while the job object is alive (keep it until the call)."""
     B, x_rows, D = x.shape
     ptr = lambda t: None if t is None else t.data_ptr()
     job = CompressJob(ptr(x), dtype_of(x), x_rows, ptr(gate), ptr(pos_bias), int(m), ptr(x_tok0), ptr(nblk),
                       ptr(dst_row0), B, int(nblk_max), D, ptr(dst), int(dst_dt), ptr(dst_scale), dst.shape[1],
-                      ptr(pooled))
+                      ptr(pooled), 1 if gate.dim() == 3 else 0, int(overlap))
     job._keep = (x, gate, pos_bias, x_tok0, nblk, dst_row0, dst, dst_scale, pooled)
     return job
 
@@ -256,18 +258,20 @@ class AppendJob(ctypes.Structure):
                 ("len", ctypes.c_void_p), ("m", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("x_tok0", ctypes.c_void_p), ("nblk", ctypes.c_void_p), ("dst_row0", ctypes.c_void_p),
                 ("n_elig", ctypes.c_void_p), ("win_begin", ctypes.c_void_p), ("win_len", ctypes.c_void_p),
-                ("B", ctypes.c_int32), ("D", ctypes.c_int32)]
+                ("B", ctypes.c_int32), ("D", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("gate_pc", ctypes.c_int32)]
 
 
 def append_job(x_new, ring, length, m=0, W=0, g_new=None, gring=None, x_tok0=None, nblk=None, dst_row0=None,
-               n_elig=None, win_begin=None, win_len=None) -> AppendJob:
+               n_elig=None, win_begin=None, win_len=None, overlap=0) -> AppendJob:
     """One stream of decode_append: x_new [B, D] new tokens, ring [B, 2R, D] (gring [B, 2R]),
     length [B] int64 tokens so far; the outputs are the step arguments named in lca.h (the job
     keeps its tensors alive while it is)."""
     B, R2, D = ring.shape
     ptr = lambda t: None if t is None else t.data_ptr()
     job = AppendJob(ptr(x_new), dtype_of(x_new), ptr(g_new), ptr(ring), ptr(gring), R2 // 2, ptr(length), int(m),
-                    int(W), ptr(x_tok0), ptr(nblk), ptr(dst_row0), ptr(n_elig), ptr(win_begin), ptr(win_len), B, D)
+                    int(W), ptr(x_tok0), ptr(nblk), ptr(dst_row0), ptr(n_elig), ptr(win_begin), ptr(win_len), B, D,
+                    int(overlap), 1 if gring is not None and gring.dim() == 3 else 0)
     job._keep = (x_new, g_new, ring, gring, length, x_tok0, nblk, dst_row0, n_elig, win_begin, win_len)
     return job
 

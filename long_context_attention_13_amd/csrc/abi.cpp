@@ -46,17 +46,20 @@ lca_status compress_check(const char* name, int mmax, const void* x, lca_dtype x
                           const float* gate, const float* pos_bias, int32_t m, const int32_t* x_tok0,
                           const int32_t* nblk, const int64_t* dst_row0, int32_t B, int32_t nblk_max,
                           int32_t D, void* dst, lca_dtype dst_dt, void* dst_scale, int64_t dst_rows,
-                          float* pooled, lca::CompressArgs* out) {
+                          float* pooled, int32_t gate_pc, int32_t overlap, lca::CompressArgs* out) {
   *out = lca::CompressArgs{};
   REQ(B >= 0 && nblk_max >= 0, LCA_EINVAL, "%s: B and nblk_max must be >= 0", name);
   REQ(m >= 1 && m <= mmax, LCA_ENOTSUP, "%s: m=%d outside [1, %d]", name, m, mmax);
+  REQ(gate_pc == 0 || gate_pc == 1, LCA_EINVAL, "%s: gate_pc=%d (0 or 1)", name, gate_pc);
+  REQ(overlap >= 0 && overlap <= m && m + overlap <= 1024, LCA_EINVAL,
+      "%s: overlap=%d outside [0, m] or m + overlap > 1024", name, overlap);
   REQ(D == 64 || D == 128, LCA_ENOTSUP, "%s: D=%d (supported: 64, 128)", name, D);
   REQ(x_dt == LCA_F32 || x_dt == LCA_BF16, LCA_ENOTSUP, "%s: x_dt must be F32 or BF16", name);
   REQ(dst_dt >= LCA_F32 && dst_dt <= LCA_MXFP4, LCA_ENOTSUP, "%s: unknown dst_dt %d", name, (int)dst_dt);
   REQ(x_rows >= 0 && dst_rows >= 0, LCA_EINVAL, "%s: x_rows and dst_rows must be >= 0", name);
   REQ(B <= 65535, LCA_ENOTSUP, "%s: B=%d exceeds 65535", name, B);
-  REQ((int64_t)nblk_max * m <= x_rows, LCA_EINVAL, "%s: nblk_max*m=%lld exceeds x_rows=%lld", name,
-      (long long)nblk_max * m, (long long)x_rows);
+  REQ((int64_t)nblk_max * m + overlap <= x_rows, LCA_EINVAL, "%s: nblk_max*m + overlap=%lld exceeds x_rows=%lld",
+      name, (long long)nblk_max * m + overlap, (long long)x_rows);
   REQ(nblk_max <= dst_rows, LCA_EINVAL, "%s: nblk_max=%d exceeds dst_rows=%lld", name, nblk_max,
       (long long)dst_rows);
   out->x_dt = (int)x_dt; out->D = D;
@@ -69,7 +72,7 @@ lca_status compress_check(const char* name, int mmax, const void* x, lca_dtype x
   }
   if (pooled) REQ(aligned16(pooled), LCA_EINVAL, "%s: pooled must be 16-byte aligned", name);
   *out = lca::CompressArgs{x, (int)x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0,
-                           B, nblk_max, D, dst, (int)dst_dt, dst_scale, dst_rows, pooled};
+                           B, nblk_max, D, dst, (int)dst_dt, dst_scale, dst_rows, pooled, gate_pc, overlap};
   return ok();
 }
 
@@ -80,7 +83,7 @@ lca_status compress_common(const char* name, int mmax, const void* x, lca_dtype 
                            float* pooled, void* stream) {
   lca::CompressArgs a;
   const lca_status st = compress_check(name, mmax, x, x_dt, x_rows, gate, pos_bias, m, x_tok0, nblk, dst_row0, B,
-                                       nblk_max, D, dst, dst_dt, dst_scale, dst_rows, pooled, &a);
+                                       nblk_max, D, dst, dst_dt, dst_scale, dst_rows, pooled, 0, 0, &a);
   if (st != LCA_OK || a.B == 0) return st;
   return hip_status(lca::launch_compress(a, (hipStream_t)stream), name);
 }
@@ -185,7 +188,7 @@ lca_status compress_batch_check(const char* who, const lca_compress_job* jobs, i
     snprintf(name, sizeof(name), "%s: compress job %d", who, j);
     const lca_status st = compress_check(name, 1024, J.x, J.x_dt, J.x_rows, J.gate, J.pos_bias, J.m, J.x_tok0, J.nblk,
                                          J.dst_row0, J.B, J.nblk_max, J.D, J.dst, J.dst_dt, J.dst_scale, J.dst_rows,
-                                         J.pooled, &bt.job[j]);
+                                         J.pooled, J.gate_pc, J.overlap, &bt.job[j]);
     if (st != LCA_OK) return st;
     REQ(J.x_dt == jobs[0].x_dt && J.D == jobs[0].D, LCA_ENOTSUP, "%s: x_dt/D differ from job 0", name);
   }
@@ -369,8 +372,10 @@ lca_status append_batch_check(const char* who, const lca_append_job* jobs, int32
     REQ(J.x_dt == LCA_BF16 || J.x_dt == LCA_F32, LCA_ENOTSUP, "%s: x_dt must be bf16 or f32", name);
     REQ(J.m >= 0 && J.m <= 1024, LCA_EINVAL, "%s: m=%d outside [0, 1024]", name, J.m);
     REQ(J.W >= 0, LCA_EINVAL, "%s: W=%d negative", name, J.W);
-    REQ(J.R >= 1 && J.R >= J.m && J.R >= J.W && J.R < (1ll << 30), LCA_EINVAL,
-        "%s: R=%lld must be >= max(1, m, W)", name, (long long)J.R);
+    REQ(J.overlap >= 0 && J.overlap <= J.m, LCA_EINVAL, "%s: overlap=%d outside [0, m]", name, J.overlap);
+    REQ(J.gate_pc == 0 || J.gate_pc == 1, LCA_EINVAL, "%s: gate_pc=%d (0 or 1)", name, J.gate_pc);
+    REQ(J.R >= 1 && J.R >= J.m + J.overlap && J.R >= J.W && J.R < (1ll << 30), LCA_EINVAL,
+        "%s: R=%lld must be >= max(1, m + overlap, W)", name, (long long)J.R);
     REQ((J.g_new == nullptr) == (J.gring == nullptr), LCA_EINVAL, "%s: g_new and gring go together", name);
     REQ((J.win_begin == nullptr) == (J.win_len == nullptr), LCA_EINVAL, "%s: win_begin and win_len go together",
         name);
@@ -385,6 +390,7 @@ lca_status append_batch_check(const char* who, const lca_append_job* jobs, int32
     a.x_new = J.x_new; a.x_dt = (int)J.x_dt; a.g_new = J.g_new; a.ring = J.ring; a.gring = J.gring; a.R = J.R;
     a.len = J.len; a.m = J.m; a.W = J.W; a.x_tok0 = J.x_tok0; a.nblk = J.nblk; a.dst_row0 = J.dst_row0;
     a.n_elig = J.n_elig; a.win_begin = J.win_begin; a.win_len = J.win_len; a.B = J.B; a.D = J.D;
+    a.overlap = J.overlap; a.gate_pc = J.gate_pc;
   }
   return ok();
 }
@@ -422,9 +428,12 @@ lca_status lca_decode_loop_step(const lca_append_job* app, int32_t napp, const l
       REQ(!used[a], LCA_EINVAL, "%s: compress jobs %d and another read the ring of append job %d", name, j, a);
       REQ(c.x_tok0 == A.x_tok0 && c.nblk == A.nblk && c.dst_row0 == A.dst_row0, LCA_EINVAL,
           "%s: compress job %d reads the ring of append job %d but not its x_tok0 / nblk / dst_row0", name, j, a);
-      REQ(c.nblk_max == 1 && c.B == A.B && c.m == A.m && c.x_rows == 2 * A.R && c.x_dt == A.x_dt && c.D == A.D,
-          LCA_EINVAL, "%s: compress job %d and append job %d disagree (nblk_max 1, B, m, x_rows = 2R, x_dt, D)",
-          name, j, a);
+      REQ(c.nblk_max == 1 && c.B == A.B && c.m == A.m && c.overlap == A.overlap && c.gate_pc == A.gate_pc &&
+              c.x_rows == 2 * A.R &&
+              c.x_dt == A.x_dt && c.D == A.D,
+          LCA_EINVAL,
+          "%s: compress job %d and append job %d disagree (nblk_max 1, B, m, overlap, gate_pc, x_rows = 2R, x_dt, D)", name,
+          j, a);
       used[a] = true;
       mp.of[j] = a;
     }

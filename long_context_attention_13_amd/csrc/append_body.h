@@ -22,9 +22,16 @@ __device__ __forceinline__ void append_token(const AppendArgs& a, int b) {
     ((uint32_t*)(ring + row0 * a.D * esz))[i] = v;
     ((uint32_t*)(ring + row1 * a.D * esz))[i] = v;
   }
+  if (a.g_new && a.gate_pc) {            // one gate logit per channel
+    for (int i = threadIdx.x; i < a.D; i += blockDim.x) {
+      const float g = a.g_new[(int64_t)b * a.D + i];
+      a.gring[row0 * a.D + i] = g;
+      a.gring[row1 * a.D + i] = g;
+    }
+  }
   __syncthreads();
   if (threadIdx.x != 0) return;
-  if (a.g_new) {
+  if (a.g_new && !a.gate_pc) {
     const float g = a.g_new[b];
     a.gring[row0] = g;
     a.gring[row1] = g;
@@ -33,7 +40,9 @@ __device__ __forceinline__ void append_token(const AppendArgs& a, int b) {
   a.len[b] = L;
   if (a.m > 0) {
     if (a.nblk) a.nblk[b] = (L % a.m == 0) ? 1 : 0;
-    if (a.x_tok0) a.x_tok0[b] = (int32_t)(L >= a.m ? (L - a.m) % a.R : 0);
+    // first ring row of the block's span (its m tokens and the overlap
+    // tokens before them; for the first block those rows are not read)
+    if (a.x_tok0) a.x_tok0[b] = (int32_t)(L >= a.m ? ((L - a.m - a.overlap) % a.R + a.R) % a.R : 0);
     if (a.dst_row0) a.dst_row0[b] = L / a.m - 1 >= 0 ? L / a.m - 1 : 0;
     if (a.n_elig) a.n_elig[b] = (int32_t)(L / a.m);
   }

@@ -18,7 +18,106 @@ struct PeShared {
   float wgt[1024];                              // gate weights of the block
   float red[2][PE_THREADS / WAVE];
   __align__(16) float part[2048];               // [G][D] group partials
+  __align__(16) float part2[2048];              // per-channel gates: [G][D] softmax sums
 };
+
+template <int ODT, int D>
+__device__ __forceinline__ void encode_row(const CompressArgs& a, int b, int i, float c);
+
+// Per-channel gates (gate [B][x_rows][D], bias [m + overlap][D]): one softmax
+// per channel over the block's span.  Thread t handles CPL channels of the
+// tokens of its group, as in pool_encode_block; pass 1 finds each channel's
+// maximum logit (group maxima reduced in LDS), pass 2 accumulates exp-weighted
+// sums and the softmax denominators, reduced in LDS in group order.
+template <int XDT, int ODT, int D>
+__device__ __forceinline__ void pool_encode_block_pc(const CompressArgs& a, int b, int i, PeShared& S) {
+  constexpr int CPL = XDT == DT_F32 ? 4 : 8;
+  constexpr int NCK = D / CPL;
+  constexpr int G = PE_THREADS / NCK;
+  static_assert(G * D <= 2048, "group partials fit");
+  if (i >= a.nblk[b]) return;
+  const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * a.m;
+  const int span = a.m + a.overlap;
+  const int skip = (a.overlap > 0 && a.dst_row0[b] + i == 0) ? a.overlap : 0;
+  const int tid = threadIdx.x;
+  const int ck = tid % NCK, grp = tid / NCK;
+  float (*part)[D] = (float (*)[D])S.part;
+  float (*part2)[D] = (float (*)[D])S.part2;
+  const float* grow = a.gate + ((int64_t)b * a.x_rows + tok0) * D + ck * CPL;
+  const float* brow = a.bias + ck * CPL;
+  auto logits = [&](int u, float* v) {
+    const float4* gp = (const float4*)(grow + (int64_t)u * D);
+    const float4* bp = (const float4*)(brow + (int64_t)u * D);
+#pragma unroll
+    for (int h = 0; h < CPL / 4; ++h) {
+      const float4 g4 = gp[h], b4 = bp[h];
+      v[4 * h] = g4.x + b4.x; v[4 * h + 1] = g4.y + b4.y; v[4 * h + 2] = g4.z + b4.z; v[4 * h + 3] = g4.w + b4.w;
+    }
+  };
+  float mx[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) mx[c] = -INFINITY;
+  for (int u = skip + grp; u < span; u += G) {
+    float v[CPL];
+    logits(u, v);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) mx[c] = fmaxf(mx[c], v[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) part[grp][ck * CPL + c] = mx[c];
+  __syncthreads();
+  if (tid < D) {
+    float m0 = part[0][tid];
+#pragma unroll
+    for (int q = 1; q < G; ++q) m0 = fmaxf(m0, part[q][tid]);
+    S.wgt[tid] = m0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) mx[c] = S.wgt[ck * CPL + c];
+  float acc[CPL], zc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = zc[c] = 0.f;
+  const char* xrow = (const char*)a.x + (((int64_t)b * a.x_rows + tok0) * D + ck * CPL) * (XDT == DT_F32 ? 4 : 2);
+  const int64_t rstride = (int64_t)D * (XDT == DT_F32 ? 4 : 2);
+  for (int u = skip + grp; u < span; u += G) {
+    float v[CPL], xf[CPL];
+    logits(u, v);
+    const int4 xv = *(const int4*)(xrow + u * rstride);
+    if (XDT == DT_F32) {
+      xf[0] = __int_as_float(xv.x); xf[1] = __int_as_float(xv.y);
+      xf[2] = __int_as_float(xv.z); xf[3] = __int_as_float(xv.w);
+    } else {
+      const uint32_t q[4] = {(uint32_t)xv.x, (uint32_t)xv.y, (uint32_t)xv.z, (uint32_t)xv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        xf[2 * k] = __uint_as_float(q[k] << 16);
+        xf[2 * k + 1] = __uint_as_float(q[k] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float e = expf(v[c] - mx[c]);
+      zc[c] += e;
+      acc[c] = fmaf(e, xf[c], acc[c]);
+    }
+  }
+  __syncthreads();                              // part is re-used
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    part[grp][ck * CPL + c] = acc[c];
+    part2[grp][ck * CPL + c] = zc[c];
+  }
+  __syncthreads();
+  if (tid >= D) return;
+  float c = 0.f, z = 0.f;
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    c += part[q][tid];
+    z += part2[q][tid];
+  }
+  encode_row<ODT, D>(a, b, i, c / z);
+}
 
 // Block i of sequence b of one compress call.
 template <int XDT, int ODT, int D>
@@ -28,12 +127,19 @@ __device__ __forceinline__ void pool_encode_block(const CompressArgs& a, int b, 
   constexpr int G = PE_THREADS / NCK;           // token groups
   constexpr int TB = 16;                        // token loads in flight per thread and batch
   static_assert(G * D <= 2048, "group partials fit");
+  if (a.gate_pc) {
+    pool_encode_block_pc<XDT, ODT, D>(a, b, i, S);
+    return;
+  }
   const int nblk = a.nblk[b];
   const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * a.m;
   if (i >= nblk) return;
   const int tid = threadIdx.x;
   const int ck = tid % NCK, grp = tid / NCK;
-  const int m = a.m;
+  const int m = a.m + a.overlap;                 // tokens of the block's span
+  // the first block of a sequence has no tokens before it: its overlap rows
+  // are neither read nor weighted
+  const int skip = (a.overlap > 0 && a.dst_row0[b] + i == 0) ? a.overlap : 0;
 
   float* wgt = S.wgt;
   auto& red = S.red;
@@ -45,14 +151,14 @@ __device__ __forceinline__ void pool_encode_block(const CompressArgs& a, int b, 
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     const int u = grp + t * G;
-    xv[t] = u < m ? *(const int4*)(xrow + u * rstride) : make_int4(0, 0, 0, 0);
+    xv[t] = u >= skip && u < m ? *(const int4*)(xrow + u * rstride) : make_int4(0, 0, 0, 0);
   }
 
   // gate logits + positional bias, block max and sum
   const float* gp = a.gate + (int64_t)b * a.x_rows + tok0;
   float mx = -INFINITY;
   for (int u = tid; u < m; u += PE_THREADS) {
-    const float v = gp[u] + a.bias[u];
+    const float v = u >= skip ? gp[u] + a.bias[u] : -INFINITY;
     wgt[u] = v;
     mx = fmaxf(mx, v);
   }
@@ -64,7 +170,7 @@ __device__ __forceinline__ void pool_encode_block(const CompressArgs& a, int b, 
   for (int w = 1; w < PE_THREADS / WAVE; ++w) mx = fmaxf(mx, red[0][w]);
   float z = 0.0f;
   for (int u = tid; u < m; u += PE_THREADS) {
-    const float e = expf(wgt[u] - mx);
+    const float e = u >= skip ? expf(wgt[u] - mx) : 0.0f;
     wgt[u] = e;
     z += e;
   }
@@ -98,18 +204,18 @@ __device__ __forceinline__ void pool_encode_block(const CompressArgs& a, int b, 
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     const int u = grp + t * G;
-    if (u < m) add(xv[t], wgt[u] * inv_z);
+    if (u >= skip && u < m) add(xv[t], wgt[u] * inv_z);
   }
   for (int t0 = TB; grp + t0 * G < m; t0 += TB) {
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       const int u = grp + (t0 + t) * G;
-      xv[t] = u < m ? *(const int4*)(xrow + u * rstride) : make_int4(0, 0, 0, 0);
+      xv[t] = u >= skip && u < m ? *(const int4*)(xrow + u * rstride) : make_int4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       const int u = grp + (t0 + t) * G;
-      if (u < m) add(xv[t], wgt[u] * inv_z);
+      if (u >= skip && u < m) add(xv[t], wgt[u] * inv_z);
     }
   }
   if (m == 1) {
@@ -126,7 +232,14 @@ __device__ __forceinline__ void pool_encode_block(const CompressArgs& a, int b, 
 #pragma unroll
   for (int q = 0; q < G; ++q) c += part[q][tid];
   if (m == 1) c = part[0][tid];
+  encode_row<ODT, D>(a, b, i, c);
+}
 
+// Thread tid < D writes channel tid of block i's pooled row c in the output
+// encoding (the FP8 and MXFP4 scale groups are whole wavefronts).
+template <int ODT, int D>
+__device__ __forceinline__ void encode_row(const CompressArgs& a, int b, int i, float c) {
+  const int tid = threadIdx.x;
   const int64_t row = (int64_t)b * a.dst_rows + a.dst_row0[b] + i;
   if (a.pooled) a.pooled[((int64_t)b * a.nblk_max + i) * D + tid] = c;
 

@@ -16,6 +16,8 @@ struct CompressArgs {
   int B; int nblk_max; int D;
   void* dst; int dst_dt; void* dst_scale; int64_t dst_rows;
   float* pooled;
+  int gate_pc;                        // 1: gate [B][x_rows][D], bias [m + overlap][D]
+  int overlap;                        // block i pools m + overlap tokens from x_tok0 + i*m
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
@@ -80,6 +82,8 @@ struct AppendArgs {
   int32_t* x_tok0; int32_t* nblk; int64_t* dst_row0; int32_t* n_elig;
   int32_t* win_begin; int32_t* win_len;
   int B, D;
+  int overlap;                        // the stream's compress jobs pool m + overlap tokens
+  int gate_pc;                        // 1: g_new [B][D], gring [B][2R][D]
 };
 constexpr int MAX_APPEND_JOBS = 8;
 struct AppendBatch {

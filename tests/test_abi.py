@@ -136,7 +136,7 @@ def batch_job(**kw):
              dst_row0=FAKE, B=2, nblk_max=1, D=128, dst=FAKE, dst_dt=lca.FP8E4M3, dst_scale=FAKE,
              dst_rows=16, pooled=None)
     a.update(kw)
-    return lca.CompressJob(*a.values())
+    return lca.CompressJob(**a)
 
 
 def compress_batch(L, jobs, n=None):
@@ -231,7 +231,7 @@ def append_job(**kw):
     a = dict(x_new=FAKE, x_dt=lca.BF16, g_new=FAKE, ring=FAKE, gring=FAKE, R=256, len=FAKE, m=4, W=128,
              x_tok0=FAKE, nblk=FAKE, dst_row0=FAKE, n_elig=FAKE, win_begin=FAKE, win_len=FAKE, B=2, D=128)
     a.update(kw)
-    return lca.AppendJob(*a.values())
+    return lca.AppendJob(**a)
 
 
 def decode_append(L, jobs, n=None):
@@ -300,6 +300,7 @@ def test_decode_loop_step_validation(L):
     assert call([app()], [cj(x_rows=512)]) == 1
     assert call([app()], [cj(m=128)]) == 1
     assert call([app()], [cj(B=1)]) == 1
+    assert call([app()], [cj(overlap=2)]) == 1                         # overlap differs
     assert call([app()], [cj(), cj()]) == 1
     assert b"read the ring of append job 0" in L.lca_last_error()
     # the parts are validated as their own calls
@@ -307,3 +308,18 @@ def test_decode_loop_step_validation(L):
     assert call([app()] * 9, []) == 1
     assert call([app(B=0)], [cj(B=0)], index_job(k=0)) == 1
     assert b"index job" in L.lca_last_error()
+
+
+def test_compress_variant_validation(L):
+    def batch(**kw):
+        arr = (lca.CompressJob * 1)(batch_job(**kw))
+        return L.lca_compress_batch(arr, 1, None)
+    assert batch(gate_pc=2) == 1
+    assert batch(overlap=5) == 1                          # overlap > m
+    assert batch(overlap=-1) == 1
+    assert batch(m=1024, overlap=1, x_rows=4096) == 1     # m + overlap > 1024
+    assert batch(nblk_max=64, x_rows=256, overlap=1, dst_rows=64) == 1   # span of the last block
+    assert batch(B=0, gate_pc=1, overlap=4) == 0
+    assert decode_append(L, [append_job(overlap=5)]) == 1
+    assert decode_append(L, [append_job(m=128, W=0, R=128, overlap=1)]) == 1        # R < m + overlap
+    assert decode_append(L, [append_job(B=0, m=128, W=0, R=256, overlap=128)]) == 0
