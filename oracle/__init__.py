@@ -75,7 +75,7 @@ def lib():
         L.orc_attend_row.argtypes = [vp, vp, i64, vp, i64, vp, dbl, i32, i32, vp, vp]
         L.orc_attend.restype = None
         L.orc_attend.argtypes = [vp, vp, i32, vp, i64, vp, i32, vp, vp, i32, i64, vp, vp, vp,
-                                 dbl, i32, i32, i32, i32, vp, vp]
+                                 dbl, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_num_threads.restype = i32
         L.orc_num_threads.argtypes = []
         _lib = L
@@ -266,21 +266,31 @@ def attend_row(q, ent, win, sink, tau):
     return o, lse
 
 
-def attend(q, kv, kv_dt, kv_scale, sel, n_elig, win, win_dt, win_begin, win_len, sink, tau):
+def attend(q, kv, kv_dt, kv_scale, sel, n_elig, win, win_dt, win_begin, win_len, sink, tau, v=None,
+           v_scale=None, win_v=None):
     """q: float64 [B,Tq,Hq,D]; kv storage [B,N_cap,D] (+ fp32 scales per 64);
     sel int32 [B,Tq,k] for sparse attention or None for dense over n_elig;
     win storage [B,W_buf,D]; win_begin/win_len int32 [B,Tq]; sink f32 [Hq].
+    v / v_scale / win_v: separate values in the layouts of kv / kv_scale / win
+    (None: one vector per item is key and value; both v and win_v or neither).
     Returns o float64 [B,Tq,Hq,D], lse float64 [B,Tq,Hq]."""
+    assert (v is None) == (win_v is None)
     q = _c(q, np.float64)
     B, Tq, Hq, D = q.shape
     N_cap = kv.shape[1]
-    if kv_dt == F32:
-        kv = _c(kv, np.float32)
-    elif kv_dt == BF16:
-        kv = _c(kv, np.uint16)
-    else:
-        kv = _c(kv, np.uint8)
-        kv_scale = _c(kv_scale, np.float32)
+
+    def store(a, sc):
+        if kv_dt == F32:
+            return _c(a, np.float32), None
+        if kv_dt == BF16:
+            return _c(a, np.uint16), None
+        return _c(a, np.uint8), _c(sc, np.float32)
+    kv, kv_scale = store(kv, kv_scale)
+    if v is not None:
+        assert v.shape == kv.shape
+        v, v_scale = store(v, v_scale)
+        win_v = _c(win_v, np.float32 if win_dt == F32 else np.uint16)
+        assert win_v.shape == win.shape
     win = _c(win, np.float32 if win_dt == F32 else np.uint16)
     W_buf = win.shape[1]
     k = 0
@@ -296,7 +306,7 @@ def attend(q, kv, kv_dt, kv_scale, sel, n_elig, win, win_dt, win_begin, win_len,
     lse = np.empty((B, Tq, Hq), np.float64)
     lib().orc_attend(_p(q), _p(kv), kv_dt, _p(kv_scale), N_cap, _p(sel), k, _p(n_elig),
                      _p(win), win_dt, W_buf, _p(win_begin), _p(win_len), _p(sink), float(tau),
-                     B, Tq, Hq, D, _p(o), _p(lse))
+                     B, Tq, Hq, D, _p(o), _p(lse), _p(v), _p(v_scale), _p(win_v))
     return o, lse
 
 

@@ -404,9 +404,24 @@ void orc_index_topk(const double* qi, const float* w, const void* keys, int key_
 /* Entries come first (in the order given), then window tokens, in every sum. */
 /*   q   : [Hq][D]; ent: [n_ent][D] (already gathered); win: [n_win][D]      */
 /* ------------------------------------------------------------------------- */
+/* Separate values (a variant; the pages leave K vs V open and the reading   */
+/* above takes K = V): the logits use ent / win as keys, the weighted sums    */
+/* use ent_v / win_v (same shapes) as values.  NULL values: K = V.            */
+void orc_attend_row_kv(const double* q, const double* ent, const double* ent_v, int64_t n_ent,
+                       const double* win, const double* win_v, int64_t n_win, const float* sink,
+                       double tau, int Hq, int D, double* o, double* lse);
+
 void orc_attend_row(const double* q, const double* ent, int64_t n_ent, const double* win,
                     int64_t n_win, const float* sink, double tau, int Hq, int D,
                     double* o, double* lse) {
+  orc_attend_row_kv(q, ent, NULL, n_ent, win, NULL, n_win, sink, tau, Hq, D, o, lse);
+}
+
+void orc_attend_row_kv(const double* q, const double* ent, const double* ent_v, int64_t n_ent,
+                       const double* win, const double* win_v, int64_t n_win, const float* sink,
+                       double tau, int Hq, int D, double* o, double* lse) {
+  if (!ent_v) ent_v = ent;
+  if (!win_v) win_v = win;
   int64_t n = n_ent + n_win, t;
   int h, dd;
   double* l = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
@@ -426,7 +441,7 @@ void orc_attend_row(const double* q, const double* ent, int64_t n_ent, const dou
     for (dd = 0; dd < D; ++dd) {
       double acc = 0.0;
       for (t = 0; t < n; ++t) {
-        const double* v = t < n_ent ? ent + t * D : win + (t - n_ent) * D;
+        const double* v = t < n_ent ? ent_v + t * D : win_v + (t - n_ent) * D;
         double pr = p[t] * v[dd];
         acc = acc + pr;
       }
@@ -446,11 +461,20 @@ void orc_attend_row(const double* q, const double* ent, int64_t n_ent, const dou
  *   win    : storage [B][W_buf][D] of win_dt; row r uses tokens
  *            win_begin[r] .. win_begin[r]+win_len[r]-1 of sequence b
  *   o, lse : float64 [B*Tq][Hq][D], [B*Tq][Hq]                               */
+static void orc_decode_row(const void* src, int dt, const float* scale, int64_t row, int D, double* dst) {
+  if (dt == ORC_F32) orc_decode((const float*)src + row * D, dt, NULL, D, dst);
+  else if (dt == ORC_BF16) orc_decode((const uint16_t*)src + row * D, dt, NULL, D, dst);
+  else orc_decode((const uint8_t*)src + row * D, dt, scale + row * (D / 64), D, dst);
+}
+
+/* v / v_scale / win_v: separate values in the layouts of kv / kv_scale / win
+ * (NULL: one vector per item is key and value). */
 void orc_attend(const double* q, const void* kv, int kv_dt, const float* kv_scale,
                 int64_t N_cap, const int32_t* sel, int k, const int32_t* n_elig,
                 const void* win, int win_dt, int64_t W_buf, const int32_t* win_begin,
                 const int32_t* win_len, const float* sink, double tau, int B, int Tq,
-                int Hq, int D, double* o, double* lse) {
+                int Hq, int D, double* o, double* lse, const void* v, const float* v_scale,
+                const void* win_v) {
   int64_t r, R = (int64_t)B * Tq;
 #pragma omp parallel for schedule(dynamic, 1)
   for (r = 0; r < R; ++r) {
@@ -459,25 +483,28 @@ void orc_attend(const double* q, const void* kv, int kv_dt, const float* kv_scal
     int64_t cap = sel ? k : n_elig[r];
     double* ent = (double*)malloc(sizeof(double) * (size_t)((cap > 0 ? cap : 1) * D));
     double* wv = (double*)malloc(sizeof(double) * (size_t)((nw > 0 ? nw : 1) * D));
+    double* ent_v = v ? (double*)malloc(sizeof(double) * (size_t)((cap > 0 ? cap : 1) * D)) : NULL;
+    double* wv_v = win_v ? (double*)malloc(sizeof(double) * (size_t)((nw > 0 ? nw : 1) * D)) : NULL;
     for (t = 0; t < cap; ++t) {
       int64_t j = sel ? sel[r * k + t] : t;
       int64_t row;
       if (j < 0) continue;
       row = (int64_t)b * N_cap + j;
-      if (kv_dt == ORC_F32) orc_decode((const float*)kv + row * D, kv_dt, NULL, D, ent + ne * D);
-      else if (kv_dt == ORC_BF16) orc_decode((const uint16_t*)kv + row * D, kv_dt, NULL, D, ent + ne * D);
-      else orc_decode((const uint8_t*)kv + row * D, kv_dt, kv_scale + row * (D / 64), D, ent + ne * D);
+      orc_decode_row(kv, kv_dt, kv_scale, row, D, ent + ne * D);
+      if (v) orc_decode_row(v, kv_dt, v_scale, row, D, ent_v + ne * D);
       ne++;
     }
     for (t = 0; t < nw; ++t) {
       int64_t row = (int64_t)b * W_buf + win_begin[r] + t;
-      if (win_dt == ORC_F32) orc_decode((const float*)win + row * D, win_dt, NULL, D, wv + t * D);
-      else orc_decode((const uint16_t*)win + row * D, win_dt, NULL, D, wv + t * D);
+      orc_decode_row(win, win_dt, NULL, row, D, wv + t * D);
+      if (win_v) orc_decode_row(win_v, win_dt, NULL, row, D, wv_v + t * D);
     }
-    orc_attend_row(q + r * Hq * D, ent, ne, wv, nw, sink, tau, Hq, D, o + r * Hq * D,
-                   lse ? lse + r * Hq : NULL);
+    orc_attend_row_kv(q + r * Hq * D, ent, ent_v, ne, wv, wv_v, nw, sink, tau, Hq, D, o + r * Hq * D,
+                      lse ? lse + r * Hq : NULL);
     free(ent);
     free(wv);
+    free(ent_v);
+    free(wv_v);
   }
 }
 

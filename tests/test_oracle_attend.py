@@ -9,6 +9,12 @@
 - permuting the attended set, or splitting it and merging by LSE, changes nothing;
 - top-k = all entries makes sparse attention equal dense attention (the HCA path);
 - k = 0 with a window covering the whole context is full causal attention.
+
+Separate values (the variant with K != V): torch SDPA with different key and
+value tensors (sink as an extra zero-value column); values equal to the keys
+give the shared-KV result bit for bit; the output is linear in the values
+(exactly, on values whose fp32 sums are exact) and the LSE does not depend on
+them.
 """
 import math
 
@@ -182,3 +188,68 @@ def test_pipeline_is_causal():
         pert["x"][p] += 1.0
         o3, _ = decode_step(p=p, **pert)
         assert np.abs(o3 - o).max() > 1e-6
+
+
+# --------------------------------------------------------------------------
+# separate values (a variant: keys and values are different vectors)
+# --------------------------------------------------------------------------
+def batched_inputs(seed, B=2, Tq=2, Hq=4, D=64, N=40, W_buf=24):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((B, Tq, Hq, D))
+    kv = g.standard_normal((B, N, D)).astype(np.float32)
+    v = g.standard_normal((B, N, D)).astype(np.float32)
+    win = g.standard_normal((B, W_buf, D)).astype(np.float32)
+    win_v = g.standard_normal((B, W_buf, D)).astype(np.float32)
+    sel = g.integers(-1, N, (B, Tq, 12)).astype(np.int32)
+    wb = g.integers(0, 8, (B, Tq)).astype(np.int32)
+    wl = g.integers(0, W_buf - 8 + 1, (B, Tq)).astype(np.int32)
+    sink = g.standard_normal(Hq).astype(np.float32)
+    return q, kv, v, win, win_v, sel, wb, wl, sink
+
+
+def test_separate_values_textbook_sdpa():
+    """softmax(tau q K^T) V with K != V against torch SDPA (float64), the sink
+    as an extra zero-value column with its logit as the mask."""
+    q, kv, v, win, win_v, sel, wb, wl, sink = batched_inputs(40)
+    tau = 0.125
+    o, lse = oracle.attend(q, kv, oracle.F32, None, sel, None, win, oracle.F32, wb, wl, sink, tau, v=v, win_v=win_v)
+    B, Tq, Hq, D = q.shape
+    for b in range(B):
+        for t in range(Tq):
+            js = [j for j in sel[b, t] if j >= 0]
+            K = np.concatenate([kv[b, js], win[b, wb[b, t]:wb[b, t] + wl[b, t]], np.zeros((1, D))]).astype(np.float64)
+            V = np.concatenate([v[b, js], win_v[b, wb[b, t]:wb[b, t] + wl[b, t]], np.zeros((1, D))]).astype(np.float64)
+            mask = torch.zeros(1, Hq, 1, K.shape[0], dtype=torch.float64)
+            mask[0, :, 0, -1] = torch.from_numpy(sink.astype(np.float64))
+            qt = torch.from_numpy(q[b, t]).reshape(1, Hq, 1, D)
+            kt = torch.from_numpy(K).reshape(1, 1, -1, D).expand(1, Hq, -1, D).contiguous()
+            vt = torch.from_numpy(V).reshape(1, 1, -1, D).expand(1, Hq, -1, D).contiguous()
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=tau).reshape(Hq, D).numpy()
+            np.testing.assert_allclose(o[b, t], ref, rtol=1e-10, atol=1e-12)
+            rl = torch.logsumexp((qt @ kt.transpose(-1, -2)) * tau + mask, -1).reshape(Hq).numpy()
+            np.testing.assert_allclose(lse[b, t], rl, rtol=1e-12)
+
+
+def test_separate_values_equal_keys_is_shared_kv():
+    q, kv, v, win, win_v, sel, wb, wl, sink = batched_inputs(41)
+    a = oracle.attend(q, kv, oracle.F32, None, sel, None, win, oracle.F32, wb, wl, sink, 0.1)
+    b = oracle.attend(q, kv, oracle.F32, None, sel, None, win, oracle.F32, wb, wl, sink, 0.1, v=kv, win_v=win)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_separate_values_linear_in_v_and_lse_independent_of_v():
+    q, kv, v, win, win_v, sel, wb, wl, sink = batched_inputs(42)
+    n_elig = np.full(sel.shape[:2], 30, np.int32)
+    args = (q, kv, oracle.F32, None, None, n_elig, win, oracle.F32, wb, wl, sink, 0.1)
+    g = np.random.default_rng(43)
+    # quarter-integer values: their fp32 sums are exact, so linearity can be tested tightly
+    v1, w1 = (g.integers(-8, 9, v.shape) / 4).astype(np.float32), (g.integers(-8, 9, win.shape) / 4).astype(np.float32)
+    v2, w2 = (g.integers(-8, 9, v.shape) / 4).astype(np.float32), (g.integers(-8, 9, win.shape) / 4).astype(np.float32)
+    o1, l1 = oracle.attend(*args, v=v1, win_v=w1)
+    o2, l2 = oracle.attend(*args, v=v2, win_v=w2)
+    o12, l12 = oracle.attend(*args, v=v1 + v2, win_v=w1 + w2)
+    np.testing.assert_allclose(o12, o1 + o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(oracle.attend(*args, v=2 * v1, win_v=2 * w1)[0], 2 * o1)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(l1, l12)
