@@ -655,7 +655,10 @@ def run_variants(reps: int = 20):
     2048 FP8 rows) and the HCA stream (m = 128, 64 FP8 rows).  Each variant is
     one compress_batch call, timed with HIP events over `reps` calls.
     Algorithmic bytes = the tokens once (2 B per value) + the gates once (4 B
-    per token, or per token and channel) + the FP8 rows with their scales."""
+    per token, or per token and channel) + the FP8 rows with their scales.
+    Then the attention variant with separate key and value vectors against the
+    shared-KV call at the decode CSA shape (bytes: the selected rows and the
+    window, once for keys and once more for separate values)."""
     import torch
     import long_context_attention_13_amd as lca
     dev = torch.device("cuda:0")
@@ -689,6 +692,48 @@ def run_variants(reps: int = 20):
                 out.append({"m": m, "gate": "per channel" if pc else "per token", "overlap": o,
                             "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
                 del x, gate, bias, dst, sc, job, arr
+    # attention with separate key and value vectors at the decode CSA shape
+    # (4 rows, 64 heads, 1024 selected FP8 entries of 262144 + 128 window
+    # tokens), against the shared-KV call on the same keys
+    B, Hq, N, k = 4, 64, 262144, 1024
+    i32 = lambda v: torch.full((B, 1), v, dtype=torch.int32, device=dev)
+    enc = []
+    for _ in range(2):
+        c = torch.empty(B, N, D, dtype=torch.uint8, device=dev)
+        sc = torch.empty(B, N, D // 64, device=dev)
+        for r0 in range(0, N, 1 << 16):
+            lca.csa_compress(torch.randn(B, 1 << 16, D, generator=g, device=dev), torch.zeros(B, 1 << 16, device=dev),
+                             torch.zeros(1, device=dev), 1, torch.zeros(B, dtype=torch.int32, device=dev),
+                             torch.full((B,), 1 << 16, dtype=torch.int32, device=dev),
+                             torch.full((B,), r0, dtype=torch.int64, device=dev), 1 << 16, c, lca.FP8E4M3, sc)
+        enc.append((c, sc))
+    (K, Ks), (V, Vs) = enc
+    q = torch.randn(B, 1, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+    idx = torch.randint(0, N, (B, 1, k), generator=g, device=dev, dtype=torch.int32)
+    wk = torch.randn(B, 128, D, generator=g, device=dev).to(torch.bfloat16)
+    wv = torch.randn(B, 128, D, generator=g, device=dev).to(torch.bfloat16)
+    sink = torch.randn(Hq, generator=g, device=dev)
+    o = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, lca.attend_ws(B, 1, Hq, D, k, 128)), dtype=torch.uint8, device=dev)
+    calls = {"shared K = V (matrix cores)": lambda: lca.sparse_mqa_attend(q, K, Ks, idx, wk, i32(0), i32(128), sink,
+                                                                           0.088, o, ws=ws),
+             "separate V (vector ALU)": lambda: lca.attend_separate_v(True, q, K, V, Ks, Vs, idx, wk, wv, i32(0),
+                                                                      i32(128), sink, 0.088, o, ws=ws)}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = B * k * (D + 8) * (2 if "separate" in name else 1) + B * 128 * D * 2 * (2 if "separate" in name else 1)
+        out.append({"attention": name, "shape": "4 rows x 64 heads, top-1024 of 262144 FP8 + window 128",
+                    "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    del enc, K, Ks, V, Vs
+    torch.cuda.empty_cache()
     return out
 
 

@@ -249,6 +249,28 @@ lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dty
                           lca_dtype out_dt, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lca_attend_separate_v -- the attention of lca_sparse_mqa_attend (sparse = 1,
+ * idx, k) or lca_hca_attend (sparse = 0, n_elig) with separate key and value
+ * vectors: logits from k / win_k, weighted sums of v / win_v.  A variant: the
+ * pages describe MQA over one compressed entry per block and leave open
+ * whether one vector serves as key and value (the reading of the other calls)
+ * [wiki (chenshi221), 架构创新: MQA over the selected compressed entries].
+ *   k, v     [B][N_cap][D] of kv_dt; FP8: k_scale, v_scale fp32 [B][N_cap][D/64]
+ *   win_k, win_v [B][W_buf][D] of win_dt
+ * Other arguments, workspace and guarantees as lca_sparse_mqa_attend /
+ * lca_hca_attend.  Runs on the fp32 vector-ALU kernel for every storage type
+ * (the matrix-core kernels stage one tile as key and value).
+ */
+lca_status lca_attend_separate_v(int32_t sparse, const void* q, lca_dtype q_dt, const void* k,
+                                 const void* v, lca_dtype kv_dt, const float* k_scale,
+                                 const float* v_scale, int64_t N_cap, const int32_t* idx, int32_t kk,
+                                 const int32_t* n_elig, const void* win_k, const void* win_v,
+                                 lca_dtype win_dt, int64_t W_buf, const int32_t* win_begin,
+                                 const int32_t* win_len, const float* sink, float scale, int32_t B,
+                                 int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * lca_window_attend -- attention over the sliding window and the sink alone,
  * with no compressed entries: the attention of the multi-token-prediction
  * block that follows the 61 CSA/HCA layers of V4-Pro.  [release notes

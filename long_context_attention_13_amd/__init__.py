@@ -24,7 +24,7 @@ STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA
 EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
            "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append", "lca_window_attend",
-           "lca_decode_loop_step"]
+           "lca_decode_loop_step", "lca_attend_separate_v"]
 MAX_COMPRESS_JOBS = 8
 MAX_ATTEND_JOBS = 4
 MAX_APPEND_JOBS = 8
@@ -92,6 +92,9 @@ def load(path: str = LIB_PATH):
                                  i32, i32, i32, vp, i32, vp, vp, sz, vp]
     L.lca_attend_ws.restype = sz
     L.lca_attend_ws.argtypes = [i32, i32, i32, i32, i64, i64]
+    L.lca_attend_separate_v.restype = i32
+    L.lca_attend_separate_v.argtypes = [i32, vp, i32, vp, vp, i32, vp, vp, i64, vp, i32, vp, vp, vp, i32, i64, vp, vp,
+                                        vp, f32, i32, i32, i32, i32, vp, i32, vp, vp, sz, vp]
     L.lca_window_attend.restype = i32
     L.lca_window_attend.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp, f32, i32, i32, i32, i32, vp, i32, vp, vp, sz,
                                     vp]
@@ -351,4 +354,17 @@ def window_attend(q, win, win_begin, win_len, sink, scale, out, lse=None, ws=Non
     _check(load().lca_window_attend(
         _p(q), dtype_of(q), _p(win), dtype_of(win), win.shape[1], _p(win_begin), _p(win_len), _p(sink),
         float(scale), B, Tq, Hq, D, _p(out), dtype_of(out), _p(lse), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def attend_separate_v(sparse, q, k, v, k_scale, v_scale, idx_or_n, win_k, win_v, win_begin, win_len, sink, scale,
+                      out, lse=None, ws=None, stream=None):
+    """sparse_mqa_attend (sparse=True, idx) or hca_attend (sparse=False, n_elig) with separate
+    key and value vectors (see lca_attend_separate_v)."""
+    B, Tq, Hq, D = q.shape
+    _check(load().lca_attend_separate_v(
+        1 if sparse else 0, _p(q), dtype_of(q), _p(k), _p(v), dtype_of(k, k_scale), _p(k_scale), _p(v_scale),
+        k.shape[1], _p(idx_or_n) if sparse else None, idx_or_n.shape[-1] if sparse else 0,
+        None if sparse else _p(idx_or_n), _p(win_k), _p(win_v), dtype_of(win_k), win_k.shape[1], _p(win_begin),
+        _p(win_len), _p(sink), float(scale), B, Tq, Hq, D, _p(out), dtype_of(out), _p(lse), _p(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))

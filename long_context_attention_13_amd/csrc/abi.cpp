@@ -472,6 +472,34 @@ lca_status lca_sparse_mqa_attend(const void* q, lca_dtype q_dt, const void* kv, 
                        stream);
 }
 
+lca_status lca_attend_separate_v(int32_t sparse, const void* q, lca_dtype q_dt, const void* k, const void* v,
+                                 lca_dtype kv_dt, const float* k_scale, const float* v_scale, int64_t N_cap,
+                                 const int32_t* idx, int32_t kk, const int32_t* n_elig, const void* win_k,
+                                 const void* win_v, lca_dtype win_dt, int64_t W_buf, const int32_t* win_begin,
+                                 const int32_t* win_len, const float* sink, float scale, int32_t B, int32_t Tq,
+                                 int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  const char* name = "lca_attend_separate_v";
+  REQ(sparse == 0 || sparse == 1, LCA_EINVAL, "%s: sparse must be 0 or 1", name);
+  REQ(kk >= 0 && kk <= 2048, LCA_EINVAL, "%s: k=%d outside [0, 2048]", name, kk);
+  const bool rows = (int64_t)B * Tq > 0;
+  if (rows && sparse && kk > 0) PTR(idx);
+  if (rows && !sparse) PTR(n_elig);
+  lca::AttendArgs a;
+  const lca_status st = attend_check(name, sparse, q, q_dt, k, kv_dt, k_scale, N_cap, idx, sparse ? kk : 0, n_elig,
+                                     win_k, win_dt, W_buf, win_begin, win_len, sink, scale, B, Tq, Hq, D, out, out_dt,
+                                     lse, ws, ws_bytes, &a);
+  if (st != LCA_OK || !rows) return st;
+  PTR(win_v);
+  if (N_cap > 0) PTR(v);
+  if (kv_dt == LCA_FP8E4M3 && N_cap > 0) PTR(v_scale);
+  if (kv_dt != LCA_FP8E4M3) REQ(v_scale == nullptr, LCA_EINVAL, "%s: v_scale must be NULL unless FP8", name);
+  a.v = N_cap > 0 ? v : win_v;          // non-null marks separate values
+  a.v_scale = v_scale;
+  a.win_v = win_v;
+  return hip_status(lca::launch_attend(a, (hipStream_t)stream), name);
+}
+
 lca_status lca_window_attend(const void* q, lca_dtype q_dt, const void* win, lca_dtype win_dt, int64_t W_buf,
                              const int32_t* win_begin, const int32_t* win_len, const float* sink, float scale,
                              int32_t B, int32_t Tq, int32_t Hq, int32_t D, void* out, lca_dtype out_dt, float* lse,

@@ -49,18 +49,18 @@ __device__ __forceinline__ ListItem list_item(const AttendArgs& A, int b, int r,
 }
 
 template <int KVDT>
-__device__ __forceinline__ float kv_elem(const AttendArgs& A, int64_t row, int d) {
-  if (KVDT == DT_F32) return ((const float*)A.kv)[row * A.D + d];
-  if (KVDT == DT_BF16) return bf16_to_f32(((const uint16_t*)A.kv)[row * A.D + d]);
-  const uint8_t c = ((const uint8_t*)A.kv)[row * A.D + d];
+__device__ __forceinline__ float kv_elem(const void* kv, const float* kv_scale, int64_t row, int D, int d) {
+  if (KVDT == DT_F32) return ((const float*)kv)[row * D + d];
+  if (KVDT == DT_BF16) return bf16_to_f32(((const uint16_t*)kv)[row * D + d]);
+  const uint8_t c = ((const uint8_t*)kv)[row * D + d];
   const float2 v = fp8x2_to_f32((uint32_t)c);
-  return v.x * A.kv_scale[row * (A.D / 64) + d / 64];
+  return v.x * kv_scale[row * (D / 64) + d / 64];
 }
 
 template <int WDT>
-__device__ __forceinline__ float win_elem(const AttendArgs& A, int64_t row, int d) {
-  if (WDT == DT_F32) return ((const float*)A.win)[row * A.D + d];
-  return bf16_to_f32(((const uint16_t*)A.win)[row * A.D + d]);
+__device__ __forceinline__ float win_elem(const void* win, int64_t row, int D, int d) {
+  if (WDT == DT_F32) return ((const float*)win)[row * D + d];
+  return bf16_to_f32(((const uint16_t*)win)[row * D + d]);
 }
 
 template <int QDT>
@@ -70,7 +70,8 @@ __device__ __forceinline__ float q_elem(const AttendArgs& A, int64_t i) {
 }
 
 // ------------------------------------------------------------------------
-// fp32 VALU kernel (any storage types; used for F32 inputs).
+// fp32 VALU kernel (any storage types; used for F32 inputs and for separate
+// values: the value tile is staged beside the key tile).
 // ------------------------------------------------------------------------
 template <int QDT, int KVDT, int WDT, int HQ>
 __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, int S, int split_items, float* part_ml,
@@ -89,6 +90,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
 
   __shared__ float qs[HQ][D];
   __shared__ float kvs[ATT_TE][D + 1];
+  __shared__ float vls[ATT_TE][D + 1];          // values, when they are separate
   __shared__ float lg[HQ][ATT_TE + 1];
   __shared__ float mrun[HQ], lrun[HQ], alpha[HQ];
   __shared__ int valid[ATT_TE];
@@ -106,14 +108,22 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
     for (int i = tid; i < ATT_TE * D; i += ATT_THREADS) {
       const int e = i / D, d = i % D;
       const int p = t0 + e;
-      float v = 0.f;
+      float v = 0.f, vv = 0.f;
       int ok = 0;
       if (p < p1) {
         const ListItem it = list_item(A, b, r, p, nkv);
-        if (it.kind == 0) { v = kv_elem<KVDT>(A, it.row, d); ok = 1; }
-        else if (it.kind == 1) { v = win_elem<WDT>(A, it.row, d); ok = 1; }
+        if (it.kind == 0) {
+          v = kv_elem<KVDT>(A.kv, A.kv_scale, it.row, D, d);
+          if (A.v) vv = kv_elem<KVDT>(A.v, A.v_scale, it.row, D, d);
+          ok = 1;
+        } else if (it.kind == 1) {
+          v = win_elem<WDT>(A.win, it.row, D, d);
+          if (A.v) vv = win_elem<WDT>(A.win_v, it.row, D, d);
+          ok = 1;
+        }
       }
       kvs[e][d] = v;
+      if (A.v) vls[e][d] = vv;
       if (d == 0) valid[e] = ok;
     }
     __syncthreads();
@@ -142,10 +152,11 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
     const float a = alpha[h];
 #pragma unroll
     for (int i = 0; i < DPT; ++i) acc[i] *= a;
+    float (*vals)[D + 1] = A.v ? vls : kvs;
     for (int e = 0; e < ATT_TE; ++e) {
       const float pe = lg[h][e];
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(pe, kvs[e][d0 + i], acc[i]);
+      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(pe, vals[e][d0 + i], acc[i]);
     }
     __syncthreads();
   }
@@ -290,7 +301,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     po = (float*)((char*)a.ws + align256(sizeof(float) * R * P.S * a.Hq * 2));
   }
   hipError_t e;
-  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8);
+  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8) && !a.v;
   if (mfma) e = a.kv_dt == DT_FP8 ? launch_mfma<DT_FP8>(a, s, P, ml, po) : launch_mfma<DT_BF16>(a, s, P, ml, po);
   else e = a.q_dt == DT_F32 ? launch_kv<DT_F32>(a, s, P, ml, po) : launch_kv<DT_BF16>(a, s, P, ml, po);
   if (e != hipSuccess || P.S == 1) return e;
@@ -302,7 +313,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 // split layout (not a prefill-shaped call -- many rows, no split -- which
 // the single call runs with the grouped dense layout or the wide kernels).
 bool attend_batchable(const AttendArgs& a) {
-  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8);
+  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8) && !a.v;
   if (!mfma) return false;
   const int64_t R = (int64_t)a.B * a.Tq;
   const Plan P = att_plan(R, a.sparse ? a.k : a.N_cap, a.W_buf);

@@ -52,6 +52,9 @@ struct AttendArgs {
   int B, Tq, Hq, D;
   void* out; int out_dt; float* lse;
   void* ws; size_t ws_bytes;
+  // separate values (NULL: one vector per item is key and value): layouts of
+  // kv / kv_scale / win; such calls run on the fp32 VALU kernel
+  const void* v; const float* v_scale; const void* win_v;
 };
 size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W_buf);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);

@@ -323,3 +323,25 @@ def test_compress_variant_validation(L):
     assert decode_append(L, [append_job(overlap=5)]) == 1
     assert decode_append(L, [append_job(m=128, W=0, R=128, overlap=1)]) == 1        # R < m + overlap
     assert decode_append(L, [append_job(B=0, m=128, W=0, R=256, overlap=128)]) == 0
+
+
+def test_attend_separate_v_validation(L):
+    a = dict(sparse=1, q=FAKE, q_dt=lca.BF16, k=FAKE, v=FAKE, kv_dt=lca.FP8E4M3, k_scale=FAKE, v_scale=FAKE,
+             N_cap=1024, idx=FAKE, kk=64, n_elig=None, win_k=FAKE, win_v=FAKE, win_dt=lca.BF16, W_buf=256,
+             win_begin=FAKE, win_len=FAKE, sink=FAKE, scale=0.088, B=2, Tq=1, Hq=64, D=128, out=FAKE,
+             out_dt=lca.BF16, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+
+    def call(**kw):
+        b = dict(a)
+        b.update(kw)
+        return L.lca_attend_separate_v(*b.values())
+    assert call(B=0) == 0
+    assert call(v=None) == 1
+    assert b"v must be" in L.lca_last_error()
+    assert call(win_v=None) == 1
+    assert call(v_scale=None) == 1
+    assert call(kv_dt=lca.BF16, k_scale=None) == 1          # v_scale given for bf16
+    assert call(sparse=2) == 1
+    assert call(idx=None) == 1
+    assert call(sparse=0, idx=None, kk=0) == 1              # dense needs n_elig
+    assert call(Hq=48) == 2
