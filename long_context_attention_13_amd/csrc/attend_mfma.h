@@ -403,11 +403,21 @@ struct MgShared {
 // read: a later split is empty and contributes nothing.  Every load (the split
 // maxima and sums, and the first MG_PRE splits' outputs) is issued before any
 // of them is used.
+// `store` false: the unit only takes part in the workgroup's barriers (a
+// workgroup that merges several units, one per 128 threads, with fewer units
+// left than groups).
+// MG_PRE partial outputs are loaded up front, the rest MG_STEP at a time
+// (fewer registers where the merge shares a kernel with other work).
+// Even splits are summed into o0 and odd ones into o1, each in increasing
+// order, whatever MG_PRE and MG_STEP are (both even), so every variant of the
+// body gives the same bits.
+template <int MG_PRE = 64, int MG_STEP = 32>
 __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all, int split_items,
-                                                  const float* part_ml, const float* part_o, int blk, MgShared& sm) {
-  constexpr int MG_PRE = 64;
+                                                  const float* part_ml, const float* part_o, int blk, MgShared& sm,
+                                                  bool store = true) {
+  static_assert(MG_PRE % 2 == 0 && MG_STEP % 2 == 0, "even prefetch and step");
   const int r = blk / A.Hq, h = blk % A.Hq;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x & 127;
   // the row's list length is requested with the partials, which are read for
   // every planned split (all inside the workspace) and masked once it arrives
   const int L = (A.sparse ? A.k : A.n_elig[r]) + A.win_len[r];
@@ -458,15 +468,18 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
     if (i < S) o0 = fmaf(ov[i], wsp[i], o0);
     if (i + 1 < S) o1 = fmaf(ov[i + 1], wsp[i + 1], o1);
   }
-  for (int s0 = MG_PRE; s0 < S; s0 += 32) {
-    float ot[32];
+  for (int s0 = MG_PRE; s0 < S; s0 += MG_STEP) {
+    float ot[MG_STEP];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) ot[i] = s0 + i < S ? po[(s0 + i) * ost] : 0.f;
+    for (int i = 0; i < MG_STEP; ++i) ot[i] = s0 + i < S ? po[(s0 + i) * ost] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
+    for (int i = 0; i < MG_STEP; i += 2) {
       if (s0 + i < S) o0 = fmaf(ot[i], wsp[s0 + i], o0);
+      if (s0 + i + 1 < S) o1 = fmaf(ot[i + 1], wsp[s0 + i + 1], o1);
+    }
   }
   const float o = o0 + o1;
+  if (!store) return;
   store_out(A, ((int64_t)r * A.Hq + h) * A.D + d, o / Z);
   if (A.lse && d == 0) A.lse[(int64_t)r * A.Hq + h] = (M + log2f(Z)) * LN2;
 }

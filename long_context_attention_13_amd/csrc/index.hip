@@ -34,6 +34,7 @@
 //                 re-scoring every entry in streamed passes.  Rows with few
 //                 entries are always done that way.  Output in ascending index
 //                 order through an LDS bitmap.
+#include "attend_mfma.h"
 #include "index_chunk.h"
 
 namespace lca {
@@ -44,9 +45,10 @@ __global__ __launch_bounds__(256) void index_chunk_kernel(IndexArgs A, IdxWs W, 
   index_chunk_body<DT, KPL, HP, NQ>(A, W, NCH, groups_per_b, blockIdx.x, blockIdx.y, sm);
 }
 
+// The selection of query row r (one workgroup of SEL_THREADS threads).
 template <int DT, int HP>
-__global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, IdxWs W, int NCH, int CH) {
-  extern __shared__ __align__(16) char smem[];
+__device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxWs& W, int NCH, int CH, int r,
+                                                  char* smem) {
   SelShared& S = *(SelShared*)smem;
   // the candidate arrays (candidate path) and the scoring buffers (streamed
   // path) share one region
@@ -55,9 +57,8 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
   int32_t* cidx_l = (int32_t*)(region + sizeof(uint64_t) * CMAX);  // [CMAX]
   float* tbuf = (float*)region;                                    // [SEL_WAVES][WBUF]
   float* wl = (float*)(region + 12 * CMAX);                        // [32]
-  const float* ql = (const float*)A.qi + (int64_t)blockIdx.x * A.H * A.d;   // F32 query row (global)
+  const float* ql = (const float*)A.qi + (int64_t)r * A.H * A.d;   // F32 query row (global)
 
-  const int r = blockIdx.x;
   // the row length and head weights first (waits for them then do not wait
   // for the larger requests behind), then the per-chunk summaries
   const int n = A.n_elig[r];
@@ -305,6 +306,38 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, 
   }
 }
 
+template <int DT, int HP>
+__global__ __launch_bounds__(SEL_THREADS) void index_select_kernel(IndexArgs A, IdxWs W, int NCH, int CH) {
+  extern __shared__ __align__(16) char smem[];
+  index_select_body<DT, HP>(A, W, NCH, CH, blockIdx.x, smem);
+}
+
+// The selection of the decode step with the merge of the dense attention
+// jobs' split partials in the same launch (they are complete once the scan
+// launch is, and the selection occupies one workgroup per row): blocks
+// [0, B*Tq) select a row each; each later block merges SEL_THREADS / 128
+// (row, head) units, 128 threads per unit.
+template <int DT, int HP>
+__global__ __launch_bounds__(SEL_THREADS) void index_select_merge_kernel(IndexArgs A, IdxWs W, int NCH, int CH,
+                                                                         AttendBatch mb) {
+  extern __shared__ __align__(16) char smem[];
+  const int nsel = A.B * A.Tq;
+  if ((int)blockIdx.x < nsel) {
+    index_select_body<DT, HP>(A, W, NCH, CH, blockIdx.x, smem);
+    return;
+  }
+  constexpr int UPB = SEL_THREADS / 128;
+  const int units = mb.mblk0[mb.njobs];
+  const int g = threadIdx.x >> 7;
+  int u = ((int)blockIdx.x - nsel) * UPB + g;
+  const bool real = u < units;
+  if (!real) u = units - 1;               // takes part in the barriers only
+  int j = 0;
+  while (j + 1 < mb.njobs && u >= mb.mblk0[j + 1]) ++j;
+  MgShared& sm = ((MgShared*)smem)[g];
+  attend_merge_body<16, 16>(mb.job[j], mb.S[j], mb.items[j], mb.ml[j], mb.po[j], u - mb.mblk0[j], sm, real);
+}
+
 // ------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------
@@ -348,6 +381,17 @@ static hipError_t launch_k(const IndexArgs& a, hipStream_t s) {
 // a fused launch can run (the select then runs on its own).
 bool index_scan_fusable(const IndexArgs& a) {
   return (int64_t)a.B * a.Tq > 0 && !index_prefill_applies(a) && a.dt == DT_MXFP4 && a.H <= 8 && a.N_cap > NDIRECT;
+}
+
+hipError_t launch_index_select_merge(const IndexArgs& a, const ScanPlan& p, const AttendBatch& mb, hipStream_t s) {
+  constexpr int UPB = SEL_THREADS / 128;
+  static_assert(UPB * sizeof(MgShared) <= sizeof(SelShared) + 12 * (size_t)CMAX, "merge units fit the LDS");
+  const int units = mb.mblk0[mb.njobs];
+  const size_t smem = select_smem(DT_MXFP4, a.H, a.d);
+  const unsigned nb = (unsigned)(a.B * a.Tq + (units + UPB - 1) / UPB);
+  hipLaunchKernelGGL((index_select_merge_kernel<DT_MXFP4, 8>), dim3(nb), dim3(SEL_THREADS), smem, s, a, p.W, p.NCH,
+                     p.CH, mb);
+  return hipGetLastError();
 }
 
 hipError_t launch_index_select(const IndexArgs& a, const ScanPlan& p, hipStream_t s) {

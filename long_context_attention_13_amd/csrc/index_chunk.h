@@ -253,5 +253,8 @@ inline ScanPlan index_scan_plan(const IndexArgs& a) {
 
 bool index_scan_fusable(const IndexArgs& a);
 hipError_t launch_index_select(const IndexArgs& a, const ScanPlan& p, hipStream_t s);
+// The same, with the merge of mb's split jobs in the same launch (mb's merge
+// plan filled: S, items, ml, po, mblk0).
+hipError_t launch_index_select_merge(const IndexArgs& a, const ScanPlan& p, const AttendBatch& mb, hipStream_t s);
 
 }  // namespace lca

@@ -1,8 +1,9 @@
 // step.hip -- one decode step of the layer pair with fewer dependent
 // launches: the compress jobs in one launch, the indexer's scan and the dense
 // (HCA) attention splits in one launch (they do not depend on each other),
-// the indexer's select, the sparse (CSA) attention splits, and one merge of
-// every split attention job.  Each part runs the kernel body of its own call
+// the indexer's select with the merge of the dense jobs' splits beside it,
+// the sparse (CSA) attention splits, and the merge of the sparse jobs'
+// splits.  Each part runs the kernel body of its own call
 // (compress.hip, index_chunk.h, attend_mfma.h), so the results are the same
 // bytes as lca_compress_batch, lca_lightning_index_topk and lca_attend_batch
 // issued in that order.
@@ -60,7 +61,7 @@ static void launch_fused_k(const IndexArgs& ia, const ScanPlan& p, const AttendB
 // of their own.
 static AttendBatch sub_batch(const AttendBatch& all, bool dense) {
   AttendBatch sub{};
-  int nb = 0;
+  int nb = 0, nm = 0;
   for (int j = 0; j < all.njobs; ++j) {
     if ((all.job[j].sparse == 0) != dense) continue;
     const int i = sub.njobs++;
@@ -70,9 +71,12 @@ static AttendBatch sub_batch(const AttendBatch& all, bool dense) {
     sub.ml[i] = all.ml[j];
     sub.po[i] = all.po[j];
     sub.blk0[i] = nb;
+    sub.mblk0[i] = nm;
     nb += all.blk0[j + 1] - all.blk0[j];
+    nm += all.mblk0[j + 1] - all.mblk0[j];
   }
   sub.blk0[sub.njobs] = nb;
+  sub.mblk0[sub.njobs] = nm;
   return sub;
 }
 
@@ -109,14 +113,15 @@ hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_index_select(ia, p, s);
+  // the dense jobs' partials are complete: their merge runs beside the select
+  e = launch_index_select_merge(ia, p, dense, s);
   if (e != hipSuccess) return e;
   const AttendBatch sparse = sub_batch(all, false);
   if (sparse.njobs > 0) {
     e = launch_attend_batch_mfma(sparse, s);
     if (e != hipSuccess) return e;
   }
-  return launch_attend_batch_merge(all, s);
+  return launch_attend_batch_merge(sparse, s);
 }
 
 }  // namespace lca
