@@ -940,18 +940,24 @@ def main():
                      else "the timed steps"},
     }
     if not args.no_cpu:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
     del wl
     torch.cuda.empty_cache()
     if not args.no_loop:
+        print("bench: decode loop", file=sys.stderr, flush=True)
         res["decode_loop"] = run_loop(args.copies, 50)
     if not args.no_schedule:
+        print("bench: 61-layer schedule", file=sys.stderr, flush=True)
         res["v4_pro_schedule"] = run_schedule(10)
     if not args.no_variants:
+        print("bench: variants", file=sys.stderr, flush=True)
         res["compress_variants"] = run_variants()
     if args.mtp:
+        print("bench: multi-token decode", file=sys.stderr, flush=True)
         res["mtp"] = [run_mtp(int(tq), args.copies, 50) for tq in args.mtp.split(",")]
     if not args.no_prefill:
+        print("bench: chunked prefill", file=sys.stderr, flush=True)
         res["prefill"] = run_prefill(args.prefill_steps, 2)
     print(json.dumps(res))
 
