@@ -337,7 +337,12 @@ lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* str
  * Each part is validated as its own call.  Dense attention jobs must not
  * read or write memory the indexer job writes (idx_out, score_out, its
  * workspace); sparse jobs may read idx_out.  Host arrays are read during the
- * call only.
+ * call only.  When every compress job has nblk_max = 1, overlap = 0, bf16
+ * input and width 128, the compress jobs run in the scan launch: a compress
+ * job that writes the indexer's keys (dst = ki) or a dense job's entries
+ * (dst = kv) must then write exactly them (its dst_scale too), and the scan
+ * and attention workgroups that read its new row compute that row from the
+ * raw tokens themselves, with the same code (same bytes).
  */
 typedef struct lca_index_job {
   const void* qi; lca_dtype qi_dt; const uint8_t* qi_scale; const float* w;
@@ -399,8 +404,9 @@ lca_status lca_decode_append(const lca_append_job* jobs, int32_t njobs, void* st
 /*
  * lca_decode_loop_step -- one step of a decode loop in one call:
  * lca_decode_append(app) followed by lca_decode_step(cjobs, ijob, ajobs), with
- * the same results, and the appends run inside the compress launch (one
- * dependent launch less).  [Sources as lca_decode_append and lca_decode_step.]
+ * the same results; the appends run inside the compress launch, or in a
+ * launch of their own when the compress jobs join the scan launch (see
+ * lca_decode_step).  [Sources as lca_decode_append and lca_decode_step.]
  * A compress job whose x is an append job's ring is that stream's block
  * compression: it must take x_tok0, nblk and dst_row0 from that append job,
  * have nblk_max = 1, the append job's B, m, x_dt and D, and x_rows = 2R; its

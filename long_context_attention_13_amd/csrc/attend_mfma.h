@@ -63,9 +63,19 @@ struct MtRegs {
   int kind[CPT][2];       // 0 entry, 1 window token, -1 nothing
 };
 
+// An entry row that the attention takes from elsewhere than the entry cache
+// (j < 0: none): the decode step computes the row its own compress job writes
+// in the same launch.  code: the row in kv_dt's layout; sc: its two FP8 scales.
+struct FreshEnt {
+  int j;
+  const uint8_t* code;
+  const float* sc;
+};
+
 template <int KVDT, int NT, int CPT>
 __device__ __forceinline__ void mt_fetch(const AttendArgs& A, int b, int64_t wbase, int nkv, int e_lo, const int* idxl,
-                                         int t0, int p1, MtRegs<KVDT, CPT>& R) {
+                                         int t0, int p1, MtRegs<KVDT, CPT>& R,
+                                         const FreshEnt& fe = FreshEnt{-1, nullptr, nullptr}) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -96,6 +106,15 @@ __device__ __forceinline__ void mt_fetch(const AttendArgs& A, int b, int64_t wba
         } else {
           R.ent[c][u][0] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16);
           R.ent[c][u][1] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16 + 8);
+        }
+        if (kind == 0 && j == fe.j) {
+          if (KVDT == DT_FP8) {
+            R.ent[c][u][0] = *(const int4*)(fe.code + ch * 16);
+            R.sc[c][u] = *(const float2*)fe.sc;
+          } else {
+            R.ent[c][u][0] = *(const int4*)((const uint16_t*)fe.code + ch * 16);
+            R.ent[c][u][1] = *(const int4*)((const uint16_t*)fe.code + ch * 16 + 8);
+          }
         }
       }
       if (t0 + MT_TE > nkv && A.W_buf > 0) {
@@ -187,7 +206,8 @@ struct MtShared {
 // Split `split` of query-row group `grp` of one attention call.
 template <int KVDT, int HQ, int QB>
 __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int split_items, float* part_ml,
-                                                 float* part_o, int split, int grp, MtShared<QB>& sm) {
+                                                 float* part_o, int split, int grp, MtShared<QB>& sm,
+                                                 const FreshEnt& fe = FreshEnt{-1, nullptr, nullptr}) {
   // QB query rows of one sequence share each staged tile (dense lists only):
   // the workgroup's list is entries 0 .. max n_elig - 1 followed by the union
   // of the rows' window slices, and every row masks what is not its own.
@@ -259,12 +279,12 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
   __syncthreads();
 
   MtRegs<KVDT, CPT> R;
-  if (p0 < p1) mt_fetch<KVDT, NT, CPT>(A, b, wbase, nkv, e_lo, idxl, p0, p1, R);
+  if (p0 < p1) mt_fetch<KVDT, NT, CPT>(A, b, wbase, nkv, e_lo, idxl, p0, p1, R, fe);
   for (int t0 = p0; t0 < p1; t0 += MT_TE) {
     __syncthreads();
     mt_store<KVDT, NT, CPT>(R, Kl, Vt, sclo, schi, okl);
     __syncthreads();
-    if (t0 + MT_TE < p1) mt_fetch<KVDT, NT, CPT>(A, b, wbase, nkv, e_lo, idxl, t0 + MT_TE, p1, R);
+    if (t0 + MT_TE < p1) mt_fetch<KVDT, NT, CPT>(A, b, wbase, nkv, e_lo, idxl, t0 + MT_TE, p1, R, fe);
 
     // ---- S^T = K Q^T for 4 subtiles of 16 items: per K-step the four
     // subtiles' fragments are read together and feed four independent

@@ -33,6 +33,32 @@ inline size_t carve_bytes(int64_t R, int64_t NCH) {
          align256(sizeof(uint64_t) * R * NCH * CAP) + align256(sizeof(int32_t) * R * NCH * CAP);
 }
 
+// A key row that the scan takes from elsewhere than the key cache (j < 0:
+// none): the decode step computes the row its own compress job writes in the
+// same launch, and hands the scan that copy (codes and scale bytes, any
+// address space).
+struct FreshKey {
+  int j;
+  const uint8_t* code;
+  const uint8_t* sc;
+};
+
+// Replace, in a round of key tiles loaded for entries [j0, j0 + 64), the
+// operands of entry F.j (the same per-lane layout as mx_load_round).
+__device__ __forceinline__ void mx_patch_round(MxTiles& T, int j0, int jlim, const FreshKey& F, int d) {
+  const int lane = threadIdx.x & 63;
+  const int kb = lane >> 4;
+  const uint32_t kbc = kb * 32 < d ? kb : 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (min(j0 + t * 16 + (lane & 15), jlim - 1) == F.j) {
+      T.code[t] = *(const int4*)(F.code + kbc * 16);
+      T.sc[t] = F.sc[kbc];
+    }
+  }
+  if (min(j0 + lane, jlim - 1) == F.j) T.kscale = mx_scale_word(F.sc, d);
+}
+
 template <int NQ>
 struct ChunkShared {
   __align__(16) float tbuf[4][WBUF];
@@ -46,7 +72,8 @@ struct ChunkShared {
 // Chunk c of query-row group g: one workgroup of 256 threads.
 template <int DT, int KPL, int HP, int NQ>
 __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs& W, int NCH, int groups_per_b,
-                                                 int c, int g, ChunkShared<NQ>& sm) {
+                                                 int c, int g, ChunkShared<NQ>& sm,
+                                                 const FreshKey& F = FreshKey{-1, nullptr, nullptr}) {
   constexpr int CH = 64 * KPL;
   constexpr int RPW = KPL / 4;            // rounds per wavefront
   static_assert(KPL % 4 == 0, "four wavefronts share a chunk");
@@ -109,6 +136,7 @@ __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs
       uint64_t kk[NQ];
       bool ix;
       if (rr + 1 < RPW) mx_load_round(A, R, min(jw + (rr + 1) * 64, jl), jl, nxt);
+      if (F.j >= jw + rr * 64 && F.j < jw + rr * 64 + 64) mx_patch_round(cur, min(jw + rr * 64, jl), jl, F, A.d);
       mx_score_round<HP, NQ>(A, rw, Q, cur, jw + rr * 64, tbuf[wave], Wt, kk, ix);
       if (rr + 1 < RPW) cur = nxt;
 #pragma unroll
@@ -124,10 +152,13 @@ __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           if (kq[q][rr] == 0) continue;
-          const uint8_t* ks = A.ki_scale + ((int64_t)rw.b * A.N_cap + j) * (A.d / 32);
+          const bool fresh = j == F.j;
+          const uint8_t* ks = fresh ? F.sc : A.ki_scale + ((int64_t)rw.b * A.N_cap + j) * (A.d / 32);
           int kmin = 1000, kmax = -1000;
           for (int i = 0; i < A.d / 32; ++i) { kmin = min(kmin, (int)ks[i]); kmax = max(kmax, (int)ks[i]); }
-          if (!mx_exact(Q, kmin, kmax)) kq[q][rr] = mx_score_exact(A, rw.r[q], rw.b, j, wl + q * 16);
+          if (!mx_exact(Q, kmin, kmax))
+            kq[q][rr] = fresh ? mx_score_exact_row(A, rw.r[q], F.code, F.sc, wl + q * 16)
+                              : mx_score_exact(A, rw.r[q], rw.b, j, wl + q * 16);
         }
       }
     }

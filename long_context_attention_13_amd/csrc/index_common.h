@@ -198,14 +198,17 @@ __device__ __forceinline__ double mx_value(const uint8_t* codes, const uint8_t* 
 
 // Exact float64 dot product of query head (row qr, head h) and key row krow,
 // left to right over the elements.
-__device__ __forceinline__ double mx_dot_exact(const IndexArgs& A, int64_t qrow, int64_t krow) {
+__device__ __forceinline__ double mx_dot_exact(const IndexArgs& A, int64_t qrow, const uint8_t* kc,
+                                               const uint8_t* ks) {
   const uint8_t* qc = (const uint8_t*)A.qi + qrow * (A.d / 2);
   const uint8_t* qs = A.qi_scale + qrow * (A.d / 32);
-  const uint8_t* kc = (const uint8_t*)A.ki + krow * (A.d / 2);
-  const uint8_t* ks = A.ki_scale + krow * (A.d / 32);
   double dot = 0.0;
   for (int i = 0; i < A.d; ++i) dot = fma(mx_value(qc, qs, i), mx_value(kc, ks, i), dot);
   return dot;
+}
+
+__device__ __forceinline__ double mx_dot_exact(const IndexArgs& A, int64_t qrow, int64_t krow) {
+  return mx_dot_exact(A, qrow, (const uint8_t*)A.ki + krow * (A.d / 2), A.ki_scale + krow * (A.d / 32));
 }
 
 // One step of the float64 head combine s = sum_h w_h * max(0, dot_h), taken in
@@ -290,6 +293,14 @@ __device__ __forceinline__ uint64_t mx_score_exact(const IndexArgs& A, int qrow,
   double sc = 0.0;
   for (int h = 0; h < A.H; ++h)
     sc = combine_step(sc, mx_dot_exact(A, (int64_t)qrow * A.H + h, (int64_t)b * A.N_cap + j), wlq[h]);
+  return score_key(sc);
+}
+
+// The same for a key row given by its codes and scale bytes.
+__device__ __forceinline__ uint64_t mx_score_exact_row(const IndexArgs& A, int qrow, const uint8_t* kc,
+                                                       const uint8_t* ks, const float* wlq) {
+  double sc = 0.0;
+  for (int h = 0; h < A.H; ++h) sc = combine_step(sc, mx_dot_exact(A, (int64_t)qrow * A.H + h, kc, ks), wlq[h]);
   return score_key(sc);
 }
 

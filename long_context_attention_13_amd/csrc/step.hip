@@ -1,6 +1,8 @@
 // step.hip -- one decode step of the layer pair with fewer dependent
-// launches: the compress jobs in one launch, the indexer's scan and the dense
-// (HCA) attention splits in one launch (they do not depend on each other),
+// launches: the compress jobs, the indexer's scan and the dense (HCA)
+// attention splits in one launch (nothing in it waits for another part: the
+// scan and attention workgroups that read a row the step compresses compute
+// that row themselves),
 // the indexer's select with the merge of the dense jobs' splits beside it,
 // the sparse (CSA) attention splits, and the merge of the sparse jobs'
 // splits.  Each part runs the kernel body of its own call
@@ -12,24 +14,89 @@
 //  the HCA branch attends over every compressed entry and needs no selection,
 //  only the CSA branch waits for the indexer's top-k.]
 #include "attend_mfma.h"
+#include "compress_body.h"
 #include "index_chunk.h"
 
 namespace lca {
+
+// The compress jobs can join the scan launch when nothing in it waits for
+// them: the compress workgroups write the caches, and the scan workgroup
+// whose chunk holds a sequence's new key row (or the attention split whose
+// range holds its new entry) computes that row itself from the raw tokens
+// with the same code, so it reads the bytes the compress job writes.
+struct StepFold {
+  int ncomp;                          // compress workgroups at the front of the grid (0: none)
+  int bmax;                           // workgroups per compress job
+  int key;                            // the compress job writing the indexer keys (-1: none)
+  int ent[MAX_ATTEND_JOBS];           // per dense job: the compress job writing its entries (-1: none)
+};
+
+// Row 0 of `code` / `scale` (any address space) = the row compress job k
+// writes for sequence b (its block 0; bf16 tokens, width 128).
+template <int ODT>
+__device__ __forceinline__ void fresh_row(const CompressArgs& k, int b, void* code, void* scale, int64_t* zero,
+                                          PeShared& pe) {
+  CompressArgs a = k;
+  a.x = (const char*)k.x + (int64_t)b * k.x_rows * 128 * 2;
+  a.gate = k.gate + (int64_t)b * k.x_rows * (k.gate_pc ? 128 : 1);
+  a.x_tok0 = k.x_tok0 + b;
+  a.nblk = k.nblk + b;
+  a.dst_row0 = zero;
+  a.dst = code;
+  a.dst_scale = scale;
+  a.dst_rows = 1;
+  a.pooled = nullptr;
+  a.B = 1;
+  a.nblk_max = 1;
+  pool_encode_block<DT_BF16, ODT, 128>(a, 0, 0, pe);
+}
 
 // Blocks [0, nscan) are the indexer scan (chunk bid % NCH of row group
 // bid / NCH); the rest are the splits of the dense attention jobs in `bt`.
 // Three workgroups per CU (168 VGPRs; the LDS union, 44.8 KB, also fits three):
 // a scan that fills two workgroups per CU leaves the third to the attention.
+// With fd.ncomp > 0 the first fd.ncomp blocks are the compress jobs (job
+// bid / bmax, sequence bid % bmax), in front of the scan and attention blocks.
 template <int KPL, int NQ, int KVDT>
 __global__ __launch_bounds__(256, 3) void step_scan_attend_kernel(IndexArgs A, IdxWs W, int NCH, int gpb, int nscan,
-                                                                  AttendBatch bt) {
+                                                                  AttendBatch bt, CompressBatch cb, StepFold fd) {
   __shared__ union {
     ChunkShared<NQ> ch;
     MtShared<1> at;
+    PeShared pe;
   } sm;
-  const int bid = blockIdx.x;
+  __shared__ __align__(16) uint8_t fresh[256 + 16];
+  __shared__ int64_t zero;
+  int bid = blockIdx.x;
+  if (bid < fd.ncomp) {
+    const CompressArgs& a = cb.job[bid / fd.bmax];
+    const int b = bid % fd.bmax;
+    if (b >= a.B) return;
+    switch (a.dst_dt) {
+      case DT_F32: pool_encode_block<DT_BF16, DT_F32, 128>(a, b, 0, sm.pe); break;
+      case DT_BF16: pool_encode_block<DT_BF16, DT_BF16, 128>(a, b, 0, sm.pe); break;
+      case DT_FP8: pool_encode_block<DT_BF16, DT_FP8, 128>(a, b, 0, sm.pe); break;
+      default: pool_encode_block<DT_BF16, DT_MXFP4, 128>(a, b, 0, sm.pe); break;
+    }
+    return;
+  }
+  bid -= fd.ncomp;
+  if (threadIdx.x == 0) zero = 0;
+  __syncthreads();
   if (bid < nscan) {
-    index_chunk_body<DT_MXFP4, KPL, 8, NQ>(A, W, NCH, gpb, bid % NCH, bid / NCH, sm.ch);
+    const int c = bid % NCH, g = bid / NCH;
+    FreshKey F{-1, fresh, fresh + 64};
+    if (fd.key >= 0) {
+      const CompressArgs& k = cb.job[fd.key];
+      const int b = g / gpb;
+      const int jn = k.nblk[b] > 0 ? (int)k.dst_row0[b] : -1;
+      if (jn >= c * 64 * KPL && jn < (c + 1) * 64 * KPL) {     // uniform over the workgroup
+        fresh_row<DT_MXFP4>(k, b, fresh, fresh + 64, &zero, sm.pe);
+        __syncthreads();
+        F.j = jn;
+      }
+    }
+    index_chunk_body<DT_MXFP4, KPL, 8, NQ>(A, W, NCH, gpb, c, g, sm.ch, F);
     return;
   }
   const int x = bid - nscan;
@@ -37,24 +104,70 @@ __global__ __launch_bounds__(256, 3) void step_scan_attend_kernel(IndexArgs A, I
   while (j + 1 < bt.njobs && x >= bt.blk0[j + 1]) ++j;
   const int local = x - bt.blk0[j];
   const int S = bt.S[j];
-  attend_mfma_body<KVDT, 64, 1>(bt.job[j], S, bt.items[j], bt.ml[j], bt.po[j], local % S, local / S, sm.at);
+  FreshEnt fe{-1, fresh, (const float*)(fresh + 128)};
+  if (fd.ent[j] >= 0) {
+    const CompressArgs& k = cb.job[fd.ent[j]];
+    const AttendArgs& aj = bt.job[j];
+    const int r = local / S, b = r / aj.Tq;
+    const int en = k.nblk[b] > 0 ? (int)k.dst_row0[b] : -1;
+    const int p0 = (local % S) * bt.items[j];
+    if (en >= p0 && en < p0 + bt.items[j] && en < aj.n_elig[r]) {   // uniform over the workgroup
+      fresh_row<KVDT>(k, b, fresh, fresh + 128, &zero, sm.pe);
+      __syncthreads();
+      fe.j = en;
+    }
+  }
+  attend_mfma_body<KVDT, 64, 1>(bt.job[j], S, bt.items[j], bt.ml[j], bt.po[j], local % S, local / S, sm.at, fe);
 }
 
 template <int KPL, int NQ, int KVDT>
-static void launch_fused(const IndexArgs& ia, const ScanPlan& p, const AttendBatch& dense, hipStream_t s) {
+static void launch_fused(const IndexArgs& ia, const ScanPlan& p, const AttendBatch& dense, const CompressBatch& cb,
+                         const StepFold& fd, hipStream_t s) {
   const int nscan = p.NCH * ia.B * p.gpb;
-  const int nb = nscan + dense.blk0[dense.njobs];
+  const int nb = fd.ncomp + nscan + dense.blk0[dense.njobs];
   hipLaunchKernelGGL((step_scan_attend_kernel<KPL, NQ, KVDT>), dim3((unsigned)nb), dim3(256), 0, s, ia, p.W, p.NCH,
-                     p.gpb, nscan, dense);
+                     p.gpb, nscan, dense, cb, fd);
 }
 
 template <int NQ, int KVDT>
-static void launch_fused_k(const IndexArgs& ia, const ScanPlan& p, const AttendBatch& dense, hipStream_t s) {
+static void launch_fused_k(const IndexArgs& ia, const ScanPlan& p, const AttendBatch& dense, const CompressBatch& cb,
+                           const StepFold& fd, hipStream_t s) {
   switch (p.kpl) {
-    case 32: launch_fused<32, NQ, KVDT>(ia, p, dense, s); break;
-    case 16: launch_fused<16, NQ, KVDT>(ia, p, dense, s); break;
-    default: launch_fused<4, NQ, KVDT>(ia, p, dense, s); break;
+    case 32: launch_fused<32, NQ, KVDT>(ia, p, dense, cb, fd, s); break;
+    case 16: launch_fused<16, NQ, KVDT>(ia, p, dense, cb, fd, s); break;
+    default: launch_fused<4, NQ, KVDT>(ia, p, dense, cb, fd, s); break;
   }
+}
+
+// Which compress jobs the scan launch can take (see StepFold); ncomp = 0 when
+// they cannot all be taken (they then run in a launch of their own first).
+static StepFold plan_fold(const CompressBatch& cb, const IndexArgs& ia, const AttendBatch& dense) {
+  StepFold fd{};
+  fd.key = -1;
+  for (int j = 0; j < MAX_ATTEND_JOBS; ++j) fd.ent[j] = -1;
+  int bmax = 0;
+  for (int c = 0; c < cb.njobs; ++c) {
+    const CompressArgs& k = cb.job[c];
+    if (k.B == 0) continue;
+    if (k.nblk_max != 1 || k.overlap != 0 || k.x_dt != DT_BF16 || k.D != 128) return StepFold{0, 0, -1, {-1, -1, -1, -1}};
+    bmax = k.B > bmax ? k.B : bmax;
+    if (k.dst == ia.ki || k.dst_scale == ia.ki_scale) {
+      if (k.dst != ia.ki || k.dst_scale != ia.ki_scale || k.dst_dt != DT_MXFP4 || ia.d != 128 || k.B != ia.B ||
+          fd.key >= 0)
+        return StepFold{0, 0, -1, {-1, -1, -1, -1}};
+      fd.key = c;
+    }
+    for (int j = 0; j < dense.njobs; ++j) {
+      const AttendArgs& a = dense.job[j];
+      if (k.dst != a.kv && !(a.kv_scale && k.dst_scale == a.kv_scale)) continue;
+      if (k.dst != a.kv || k.dst_scale != a.kv_scale || k.dst_dt != a.kv_dt || k.B != a.B || fd.ent[j] >= 0)
+        return StepFold{0, 0, -1, {-1, -1, -1, -1}};
+      fd.ent[j] = c;
+    }
+  }
+  fd.bmax = bmax;
+  fd.ncomp = cb.njobs * bmax;
+  return fd;
 }
 
 // The jobs of `all` selected by `want`, with their plans and block offsets
@@ -83,17 +196,24 @@ static AttendBatch sub_batch(const AttendBatch& all, bool dense) {
 hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const CompressBatch& cb,
                               const IndexArgs& ia, const AttendBatch& ab, hipStream_t s) {
   hipError_t e;
-  if (app != nullptr) {
-    e = launch_append_compress(*app, *mp, cb, s);
-    if (e != hipSuccess) return e;
-  } else if (cb.njobs > 0) {
-    e = launch_compress_batch(cb, s);
-    if (e != hipSuccess) return e;
-  }
   AttendBatch all = ab;
   attend_batch_plan(all);
   const AttendBatch dense = sub_batch(all, true);
   const bool fuse = ab.njobs > 0 && dense.blk0[dense.njobs] > 0 && index_scan_fusable(ia) && all.job[0].Hq == 64;
+  // the compress jobs join the scan launch when they can (the appends, if
+  // any, then run in a launch of their own first); otherwise they run first,
+  // with the appends in the same launch
+  const StepFold fd = fuse ? plan_fold(cb, ia, dense) : StepFold{0, 0, -1, {-1, -1, -1, -1}};
+  if (app != nullptr && fd.ncomp > 0) {
+    e = launch_decode_append(*app, s);
+    if (e != hipSuccess) return e;
+  } else if (app != nullptr) {
+    e = launch_append_compress(*app, *mp, cb, s);
+    if (e != hipSuccess) return e;
+  } else if (cb.njobs > 0 && fd.ncomp == 0) {
+    e = launch_compress_batch(cb, s);
+    if (e != hipSuccess) return e;
+  }
   if (!fuse) {
     e = launch_index(ia, s);
     if (e != hipSuccess) return e;
@@ -105,11 +225,11 @@ hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const
   const ScanPlan p = index_scan_plan(ia);
   const bool fp8 = all.job[0].kv_dt == DT_FP8;
   if (p.nq == 2) {
-    if (fp8) launch_fused_k<2, DT_FP8>(ia, p, dense, s);
-    else launch_fused_k<2, DT_BF16>(ia, p, dense, s);
+    if (fp8) launch_fused_k<2, DT_FP8>(ia, p, dense, cb, fd, s);
+    else launch_fused_k<2, DT_BF16>(ia, p, dense, cb, fd, s);
   } else {
-    if (fp8) launch_fused_k<1, DT_FP8>(ia, p, dense, s);
-    else launch_fused_k<1, DT_BF16>(ia, p, dense, s);
+    if (fp8) launch_fused_k<1, DT_FP8>(ia, p, dense, cb, fd, s);
+    else launch_fused_k<1, DT_BF16>(ia, p, dense, cb, fd, s);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
