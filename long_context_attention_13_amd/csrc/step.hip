@@ -139,29 +139,34 @@ static void launch_fused_k(const IndexArgs& ia, const ScanPlan& p, const AttendB
   }
 }
 
-// Which compress jobs the scan launch can take (see StepFold); ncomp = 0 when
-// they cannot all be taken (they then run in a launch of their own first).
-static StepFold plan_fold(const CompressBatch& cb, const IndexArgs& ia, const AttendBatch& dense) {
+static StepFold no_fold() {
   StepFold fd{};
   fd.key = -1;
   for (int j = 0; j < MAX_ATTEND_JOBS; ++j) fd.ent[j] = -1;
+  return fd;
+}
+
+// Which compress jobs the scan launch can take (see StepFold); ncomp = 0 when
+// they cannot all be taken (they then run in a launch of their own first).
+static StepFold plan_fold(const CompressBatch& cb, const IndexArgs& ia, const AttendBatch& dense) {
+  StepFold fd = no_fold();
   int bmax = 0;
   for (int c = 0; c < cb.njobs; ++c) {
     const CompressArgs& k = cb.job[c];
     if (k.B == 0) continue;
-    if (k.nblk_max != 1 || k.overlap != 0 || k.x_dt != DT_BF16 || k.D != 128) return StepFold{0, 0, -1, {-1, -1, -1, -1}};
+    if (k.nblk_max != 1 || k.overlap != 0 || k.x_dt != DT_BF16 || k.D != 128) return no_fold();
     bmax = k.B > bmax ? k.B : bmax;
     if (k.dst == ia.ki || k.dst_scale == ia.ki_scale) {
       if (k.dst != ia.ki || k.dst_scale != ia.ki_scale || k.dst_dt != DT_MXFP4 || ia.d != 128 || k.B != ia.B ||
           fd.key >= 0)
-        return StepFold{0, 0, -1, {-1, -1, -1, -1}};
+        return no_fold();
       fd.key = c;
     }
     for (int j = 0; j < dense.njobs; ++j) {
       const AttendArgs& a = dense.job[j];
       if (k.dst != a.kv && !(a.kv_scale && k.dst_scale == a.kv_scale)) continue;
       if (k.dst != a.kv || k.dst_scale != a.kv_scale || k.dst_dt != a.kv_dt || k.B != a.B || fd.ent[j] >= 0)
-        return StepFold{0, 0, -1, {-1, -1, -1, -1}};
+        return no_fold();
       fd.ent[j] = c;
     }
   }
@@ -203,7 +208,7 @@ hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const
   // the compress jobs join the scan launch when they can (the appends, if
   // any, then run in a launch of their own first); otherwise they run first,
   // with the appends in the same launch
-  const StepFold fd = fuse ? plan_fold(cb, ia, dense) : StepFold{0, 0, -1, {-1, -1, -1, -1}};
+  const StepFold fd = fuse ? plan_fold(cb, ia, dense) : no_fold();
   if (app != nullptr && fd.ncomp > 0) {
     e = launch_decode_append(*app, s);
     if (e != hipSuccess) return e;
