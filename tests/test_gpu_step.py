@@ -1,7 +1,9 @@
 """lca_decode_step gives the bytes of lca_compress_batch, lca_lightning_index_topk
-and lca_attend_batch issued in that order: with the HCA attention running
-inside the indexer's scan launch (FP8 entries, one query row per sequence;
-bf16 entries, two rows per sequence so that two rows share a scan wavefront),
+and lca_attend_batch issued in that order: with the compress jobs and the HCA
+attention running inside the indexer's scan launch (the scan workgroup and the
+attention split that read a row the step compresses compute it themselves;
+FP8 entries, one query row per sequence; bf16 entries, two rows per sequence
+so that two rows share a scan wavefront),
 with an indexer that has no scan (a short cache: the unfused order), with
 rows written by the step's own compress jobs that decide its results, and
 captured in a graph.  Inputs are seeded N(0, 1)."""
