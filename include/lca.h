@@ -338,12 +338,34 @@ lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* str
  * read or write memory the indexer job writes (idx_out, score_out, its
  * workspace); sparse jobs may read idx_out.  Host arrays are read during the
  * call only.  When every compress job has nblk_max = 1, overlap = 0, bf16
- * input and width 128, the compress jobs run in the scan launch: a compress
- * job that writes the indexer's keys (dst = ki) or a dense job's entries
- * (dst = kv) must then write exactly them (its dst_scale too), and the scan
- * and attention workgroups that read its new row compute that row from the
- * raw tokens themselves, with the same code (same bytes).
+ * input and width 128, and no compress job writes any byte that the scan or
+ * the dense jobs read or write -- except a job that writes exactly the
+ * indexer's key cache (dst = ki, dst_scale = ki_scale, dst_rows = N_cap) or
+ * exactly a dense job's entry cache (dst = kv, dst_scale = kv_scale,
+ * dst_rows = N_cap) -- nor reads any byte they write, the compress jobs run
+ * in the scan launch, and the scan and attention workgroups that read a new
+ * row compute that row from the raw tokens themselves, with the same code
+ * (same bytes).  Otherwise the compress jobs run in a launch of their own
+ * first.  Either way the results are those of the three calls in order.
  */
+/*
+ * lca_decode_step_events -- lca_decode_step with HIP events recorded on
+ * `stream` around its kernel launches, for measurement (same work, same
+ * results).  events[0] is recorded before the first launch and events[i]
+ * after launch i, so the elapsed time between events[i - 1] and events[i] is
+ * the duration of launch i on the stream.  The step makes at most
+ * LCA_MAX_STEP_LAUNCHES launches; their order follows lca_decode_step.
+ *   events   host array of at least LCA_MAX_STEP_LAUNCHES + 1 hipEvent_t
+ *            handles created by the caller (timing enabled to read times)
+ *   names    NULL, or a host array of LCA_MAX_STEP_LAUNCHES pointers that
+ *            receives, per launch, the name of its kernel (static strings)
+ *   nlaunch  receives the number of launches made (events[0 .. *nlaunch] recorded)
+ * Other arguments, validation and errors as lca_decode_step; LCA_EINVAL for a
+ * NULL or short events array or a NULL nlaunch.  Not for use under stream
+ * capture (events are recorded between the launches).
+ */
+#define LCA_MAX_STEP_LAUNCHES 8
+
 typedef struct lca_index_job {
   const void* qi; lca_dtype qi_dt; const uint8_t* qi_scale; const float* w;
   const void* ki; lca_dtype ki_dt; const uint8_t* ki_scale; const int32_t* n_elig;
@@ -353,6 +375,10 @@ typedef struct lca_index_job {
 
 lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
                            const lca_attend_job* ajobs, int32_t najobs, void* stream);
+
+lca_status lca_decode_step_events(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
+                                  const lca_attend_job* ajobs, int32_t najobs, void* const* events, int32_t nevents,
+                                  const char** names, int32_t* nlaunch, void* stream);
 
 /*
  * lca_decode_append -- the token append of a decode loop, for several raw-token

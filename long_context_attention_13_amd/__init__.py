@@ -24,7 +24,8 @@ STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA
 EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
            "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append", "lca_window_attend",
-           "lca_decode_loop_step", "lca_attend_separate_v"]
+           "lca_decode_loop_step", "lca_attend_separate_v", "lca_decode_step_events"]
+MAX_STEP_LAUNCHES = 8
 MAX_COMPRESS_JOBS = 8
 MAX_ATTEND_JOBS = 4
 MAX_APPEND_JOBS = 8
@@ -70,6 +71,10 @@ def load(path: str = LIB_PATH):
     L.lca_decode_step.restype = i32
     L.lca_decode_step.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
                                   ctypes.POINTER(AttendJob), i32, vp]
+    L.lca_decode_step_events.restype = i32
+    L.lca_decode_step_events.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
+                                         ctypes.POINTER(AttendJob), i32, ctypes.POINTER(vp), i32,
+                                         ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i32), vp]
     L.lca_decode_loop_step.restype = i32
     L.lca_decode_loop_step.argtypes = [ctypes.POINTER(AppendJob), i32, ctypes.POINTER(CompressJob), i32,
                                        ctypes.POINTER(IndexJob), ctypes.POINTER(AttendJob), i32, vp]
@@ -252,6 +257,22 @@ def decode_step(cjobs, ijob, ajobs, stream=None):
     aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
     ij = None if ijob is None else ctypes.byref(ijob)
     _check(load().lca_decode_step(ca, len(cjobs), ij, aa, len(ajobs), _stream(stream)))
+
+
+def decode_step_events(cjobs, ijob, ajobs, events, stream=None):
+    """decode_step with HIP events recorded around its launches (see
+    lca_decode_step_events).  events: MAX_STEP_LAUNCHES + 1 torch.cuda.Event
+    objects already created (recorded once); returns the kernel names of the
+    launches made, launch i between events[i] and events[i + 1]."""
+    ca = cjobs if isinstance(cjobs, ctypes.Array) else (CompressJob * max(1, len(cjobs)))(*cjobs)
+    aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
+    ij = None if ijob is None else ctypes.byref(ijob)
+    ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    names = (ctypes.c_char_p * MAX_STEP_LAUNCHES)()
+    n = ctypes.c_int32(0)
+    _check(load().lca_decode_step_events(ca, len(cjobs), ij, aa, len(ajobs), ev, len(events), names,
+                                         ctypes.byref(n), _stream(stream)))
+    return [names[i].decode() for i in range(n.value)]
 
 
 class AppendJob(ctypes.Structure):

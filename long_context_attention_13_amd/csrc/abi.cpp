@@ -350,6 +350,34 @@ lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const 
   return hip_status(lca::launch_decode_step(nullptr, nullptr, cb, ia, ab, (hipStream_t)stream), name);
 }
 
+lca_status lca_decode_step_events(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
+                                  const lca_attend_job* ajobs, int32_t najobs, void* const* events, int32_t nevents,
+                                  const char** names, int32_t* nlaunch, void* stream) {
+  const char* name = "lca_decode_step_events";
+  REQ(events != nullptr && nevents >= LCA_MAX_STEP_LAUNCHES + 1, LCA_EINVAL,
+      "%s: events must hold at least %d event handles", name, LCA_MAX_STEP_LAUNCHES + 1);
+  REQ(nlaunch != nullptr, LCA_EINVAL, "%s: nlaunch is NULL", name);
+  for (int i = 0; i <= LCA_MAX_STEP_LAUNCHES; ++i)
+    REQ(events[i] != nullptr, LCA_EINVAL, "%s: events[%d] is NULL", name, i);
+  lca::CompressBatch cb;
+  lca_status st = compress_batch_check(name, cjobs, ncjobs, 0, &cb);
+  if (st != LCA_OK) return st;
+  lca::IndexArgs ia{};
+  if (ijob != nullptr) {
+    const lca_index_job& I = *ijob;
+    st = index_check("lca_decode_step_events: index job", I.qi, I.qi_dt, I.qi_scale, I.w, I.ki, I.ki_dt, I.ki_scale,
+                     I.n_elig, I.B, I.Tq, I.H_I, I.d_I, I.N_cap, I.k, I.idx_out, I.score_out, I.ws, I.ws_bytes, &ia);
+    if (st != LCA_OK) return st;
+  }
+  lca::AttendBatch ab;
+  st = attend_batch_check(name, ajobs, najobs, 0, &ab);
+  if (st != LCA_OK) return st;
+  lca::LaunchLog lg{(hipEvent_t*)events, LCA_MAX_STEP_LAUNCHES + 1, 0, names};
+  st = hip_status(lca::launch_decode_step(nullptr, nullptr, cb, ia, ab, (hipStream_t)stream, &lg), name);
+  *nlaunch = lg.n;
+  return st;
+}
+
 }  // extern "C"
 
 namespace {

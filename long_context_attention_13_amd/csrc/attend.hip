@@ -23,7 +23,7 @@ constexpr int ATT_TE = 32;         // items per LDS tile (VALU path)
 
 size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W_buf) {
   const int64_t R = (int64_t)B * Tq;
-  const Plan P = att_plan(R, n_kv_max, W_buf);
+  const Plan P = att_plan(Tq, n_kv_max, W_buf);
   if (P.S == 1) return 0;
   return align256(sizeof(float) * R * P.S * Hq * 2) + align256(sizeof(float) * R * P.S * Hq * D);
 }
@@ -293,7 +293,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   const int64_t R = (int64_t)a.B * a.Tq;
   if (R == 0) return hipSuccess;
   const int64_t nkv = a.sparse ? a.k : a.N_cap;
-  const Plan P = att_plan(R, nkv, a.W_buf);
+  const Plan P = att_plan(a.Tq, nkv, a.W_buf);
   float* ml = nullptr;
   float* po = nullptr;
   if (P.S > 1) {
@@ -315,8 +315,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 bool attend_batchable(const AttendArgs& a) {
   const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8) && !a.v;
   if (!mfma) return false;
-  const int64_t R = (int64_t)a.B * a.Tq;
-  const Plan P = att_plan(R, a.sparse ? a.k : a.N_cap, a.W_buf);
+  const Plan P = att_plan(a.Tq, a.sparse ? a.k : a.N_cap, a.W_buf);
   const int qb = a.Hq == 16 ? att_qb<16>() : a.Hq == 32 ? att_qb<32>() : att_qb<64>();
   if (a.sparse) return !(P.S == 1 && attend_sparse_wide_applies(a));
   return !(P.S == 1 && a.Tq >= 2 * qb);
@@ -327,7 +326,7 @@ void attend_batch_plan(AttendBatch& bt) {
   for (int j = 0; j < bt.njobs; ++j) {
     const AttendArgs& a = bt.job[j];
     const int64_t R = (int64_t)a.B * a.Tq;
-    const Plan P = att_plan(R, a.sparse ? a.k : a.N_cap, a.W_buf);
+    const Plan P = att_plan(a.Tq, a.sparse ? a.k : a.N_cap, a.W_buf);
     bt.S[j] = P.S;
     bt.items[j] = P.items;
     bt.ml[j] = P.S > 1 ? (float*)a.ws : nullptr;

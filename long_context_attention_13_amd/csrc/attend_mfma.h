@@ -10,23 +10,26 @@ namespace lca {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-// Split plan: one split per row when there are enough rows to fill the GPU on
-// their own; otherwise the list is cut into splits of 64 items (one tile)
-// while that stays within one workgroup per compute unit, else 128 or 256
-// (the split size depends only on the shape, never on the data; the list
-// length is bounded by capacity, and splits past a row's actual list return
-// at once).
+// Split plan.  One split per row for a call shaped for prefill (at least
+// ATT_PREFILL_TQ query rows per sequence; its dense rows are then grouped to
+// share staged tiles) and for lists of at most two tiles; otherwise a row's
+// list (entries, then window tokens; its length is bounded by the capacity
+// n_kv_max + W_buf) is cut into at most ATT_MAX_SPLITS splits of a whole
+// number of 64-item tiles.  The plan depends on the call's list capacity and
+// query rows per sequence only -- never on the number of sequences, nor on
+// the data -- so a sequence gives the same bits in any batch (splits past a
+// row's actual list return at once and are not merged).
 struct Plan { int S; int items; };
 
-inline Plan att_plan(int64_t R, int64_t n_kv_max, int64_t W_buf) {
+constexpr int ATT_PREFILL_TQ = 64;
+constexpr int ATT_MAX_SPLITS = 16;
+
+inline Plan att_plan(int64_t Tq, int64_t n_kv_max, int64_t W_buf) {
   const int64_t L = n_kv_max + W_buf;
-  if (R >= 256 || L <= 128) return Plan{1, (int)(L < 1 ? 1 : L)};
-  int64_t items = 256;
-  if (R * ((L + 255) / 256) < 256) items = 128;
-  if (R * ((L + 63) / 64) <= 256) items = 64;
-  if ((L + items - 1) / items > 1024) items = ((L + 1023) / 1024 + 63) / 64 * 64;   // merge holds <= 1024 splits
-  const int64_t s = (L + items - 1) / items;
-  return Plan{(int)(s < 1 ? 1 : s), (int)items};
+  if (Tq >= ATT_PREFILL_TQ || L <= 128) return Plan{1, (int)(L < 1 ? 1 : L)};
+  const int64_t tiles = (L + 63) / 64;
+  const int64_t items = (tiles + ATT_MAX_SPLITS - 1) / ATT_MAX_SPLITS * 64;
+  return Plan{(int)((L + items - 1) / items), (int)items};
 }
 
 __device__ __forceinline__ void store_out(const AttendArgs& A, int64_t i, float v) {

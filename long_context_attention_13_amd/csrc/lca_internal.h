@@ -108,11 +108,24 @@ struct AppendMap {
 hipError_t launch_append_compress(const AppendBatch& ab, const AppendMap& mp, const CompressBatch& cb,
                                   hipStream_t s);
 
+// Events recorded on the launch stream around the launches of a decode step
+// (measurement): ev[0] before the first launch, ev[i] after launch i, whose
+// kernel names[i - 1] names.  At most cap - 1 launches are logged.
+struct LaunchLog {
+  hipEvent_t* ev;
+  int cap;
+  int n;
+  const char** names;
+};
+hipError_t log_start(LaunchLog* lg, hipStream_t s);
+hipError_t log_launch(LaunchLog* lg, hipStream_t s, const char* name);
+
 // One decode step: the compress jobs, the indexer call, the attention jobs, in
 // that order and with the results of the three calls; the dense attention jobs
 // may run beside the indexer's scan.
 // With `app` (and its map) the appends run first, in the compress launch.
+// With `lg`, events are recorded around the launches.
 hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const CompressBatch& cb,
-                              const IndexArgs& ia, const AttendBatch& ab, hipStream_t s);
+                              const IndexArgs& ia, const AttendBatch& ab, hipStream_t s, LaunchLog* lg = nullptr);
 
 }  // namespace lca

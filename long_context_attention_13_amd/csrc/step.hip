@@ -146,28 +146,87 @@ static StepFold no_fold() {
   return fd;
 }
 
+// Byte ranges of the buffers the fused launch touches, for the aliasing
+// checks of plan_fold (a null pointer is an empty range).
+struct Span {
+  const char* lo;
+  const char* hi;
+};
+static Span span(const void* p, int64_t bytes) {
+  const char* c = (const char*)p;
+  return p ? Span{c, c + bytes} : Span{nullptr, nullptr};
+}
+static bool overlap(const Span& a, const Span& b) { return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi; }
+static bool same(const Span& a, const Span& b) { return a.lo == b.lo && a.hi == b.hi; }
+static int64_t row_bytes(int dt, int D) { return dt == DT_F32 ? 4 * D : dt == DT_BF16 ? 2 * D : dt == DT_FP8 ? D : D / 2; }
+static int64_t scale_row_bytes(int dt, int D) { return dt == DT_FP8 ? D / 64 * 4 : dt == DT_MXFP4 ? D / 32 : 0; }
+
 // Which compress jobs the scan launch can take (see StepFold); ncomp = 0 when
 // they cannot all be taken (they then run in a launch of their own first).
+// Nothing in the fused launch may read what a compress job writes, except the
+// indexer keys (written as exactly the key cache: same rows, same layout) and
+// a dense job's entries (exactly that job's cache), whose new rows the readers
+// compute themselves; and no compress job may read what the launch writes.
 static StepFold plan_fold(const CompressBatch& cb, const IndexArgs& ia, const AttendBatch& dense) {
   StepFold fd = no_fold();
+  const int64_t R = (int64_t)ia.B * ia.Tq;
+  const Span ki = span(ia.ki, ia.B * ia.N_cap * ia.d / 2), kis = span(ia.ki_scale, ia.B * ia.N_cap * ia.d / 32);
+  // what the scan reads (besides the keys) and writes
+  const Span scan_in[] = {span(ia.qi, R * ia.H * ia.d / 2), span(ia.qi_scale, R * ia.H * ia.d / 32),
+                          span(ia.w, R * ia.H * 4), span(ia.n_elig, R * 4)};
+  const Span scan_out = span(ia.ws, (int64_t)ia.ws_bytes);
   int bmax = 0;
   for (int c = 0; c < cb.njobs; ++c) {
     const CompressArgs& k = cb.job[c];
     if (k.B == 0) continue;
     if (k.nblk_max != 1 || k.overlap != 0 || k.x_dt != DT_BF16 || k.D != 128) return no_fold();
     bmax = k.B > bmax ? k.B : bmax;
-    if (k.dst == ia.ki || k.dst_scale == ia.ki_scale) {
-      if (k.dst != ia.ki || k.dst_scale != ia.ki_scale || k.dst_dt != DT_MXFP4 || ia.d != 128 || k.B != ia.B ||
-          fd.key >= 0)
+    const Span dst = span(k.dst, k.B * k.dst_rows * row_bytes(k.dst_dt, k.D));
+    const Span dsc = span(k.dst_scale, k.B * k.dst_rows * scale_row_bytes(k.dst_dt, k.D));
+    const Span pooled = span(k.pooled, (int64_t)k.B * k.nblk_max * k.D * 4);
+    const Span outs[] = {dst, dsc, pooled};
+    const Span ins[] = {span(k.x, k.B * k.x_rows * k.D * 2), span(k.gate, k.B * k.x_rows * (k.gate_pc ? k.D : 1) * 4),
+                        span(k.bias, (int64_t)(k.m + k.overlap) * (k.gate_pc ? k.D : 1) * 4),
+                        span(k.x_tok0, k.B * 4), span(k.nblk, k.B * 4), span(k.dst_row0, k.B * 8)};
+    for (const Span& in : ins)
+      if (overlap(in, scan_out)) return no_fold();
+    for (const Span& o : outs)
+      for (const Span& r : scan_in)
+        if (overlap(o, r) || overlap(o, scan_out)) return no_fold();
+    // the indexer keys: written exactly as the key cache, or not at all
+    if (overlap(dst, ki) || overlap(dst, kis) || overlap(dsc, ki) || overlap(dsc, kis) || overlap(pooled, ki) ||
+        overlap(pooled, kis)) {
+      if (!same(dst, ki) || !same(dsc, kis) || k.dst_dt != DT_MXFP4 || ia.dt != DT_MXFP4 || ia.d != 128 ||
+          k.B != ia.B || k.dst_rows != ia.N_cap || fd.key >= 0)
         return no_fold();
       fd.key = c;
     }
     for (int j = 0; j < dense.njobs; ++j) {
       const AttendArgs& a = dense.job[j];
-      if (k.dst != a.kv && !(a.kv_scale && k.dst_scale == a.kv_scale)) continue;
-      if (k.dst != a.kv || k.dst_scale != a.kv_scale || k.dst_dt != a.kv_dt || k.B != a.B || fd.ent[j] >= 0)
-        return no_fold();
-      fd.ent[j] = c;
+      const int64_t Ra = (int64_t)a.B * a.Tq;
+      const Span kv = span(a.kv, a.B * a.N_cap * row_bytes(a.kv_dt, a.D));
+      const Span kvs = span(a.kv_scale, a.B * a.N_cap * scale_row_bytes(a.kv_dt, a.D));
+      const Span a_in[] = {span(a.q, Ra * a.Hq * a.D * 2), span(a.win, a.B * a.W_buf * a.D * 2),
+                           span(a.win_begin, Ra * 4), span(a.win_len, Ra * 4), span(a.sink, (int64_t)a.Hq * 4),
+                           span(a.n_elig, Ra * 4)};
+      const Span a_out[] = {span(a.ws, (int64_t)a.ws_bytes), span(a.out, Ra * a.Hq * a.D * (a.out_dt == DT_F32 ? 4 : 2)),
+                            span(a.lse, Ra * a.Hq * 4)};
+      for (const Span& in : ins)
+        for (const Span& w : a_out)
+          if (overlap(in, w)) return no_fold();
+      for (const Span& o : outs) {
+        for (const Span& r : a_in)
+          if (overlap(o, r)) return no_fold();
+        for (const Span& w : a_out)
+          if (overlap(o, w)) return no_fold();
+      }
+      if (overlap(dst, kv) || overlap(dst, kvs) || overlap(dsc, kv) || overlap(dsc, kvs) || overlap(pooled, kv) ||
+          overlap(pooled, kvs)) {
+        if (!same(dst, kv) || !same(dsc, kvs) || k.dst_dt != a.kv_dt || k.B != a.B || k.dst_rows != a.N_cap ||
+            fd.ent[j] >= 0)
+          return no_fold();
+        fd.ent[j] = c;
+      }
     }
   }
   fd.bmax = bmax;
@@ -198,9 +257,29 @@ static AttendBatch sub_batch(const AttendBatch& all, bool dense) {
   return sub;
 }
 
+static bool compress_work(const CompressBatch& cb) {
+  for (int c = 0; c < cb.njobs; ++c)
+    if (cb.job[c].B > 0 && cb.job[c].nblk_max > 0) return true;
+  return false;
+}
+
+hipError_t log_start(LaunchLog* lg, hipStream_t s) {
+  if (lg == nullptr) return hipSuccess;
+  lg->n = 0;
+  return lg->cap > 0 ? hipEventRecord(lg->ev[0], s) : hipSuccess;
+}
+
+hipError_t log_launch(LaunchLog* lg, hipStream_t s, const char* name) {
+  if (lg == nullptr || lg->n + 1 >= lg->cap) return hipSuccess;
+  if (lg->names) lg->names[lg->n] = name;
+  lg->n++;
+  return hipEventRecord(lg->ev[lg->n], s);
+}
+
 hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const CompressBatch& cb,
-                              const IndexArgs& ia, const AttendBatch& ab, hipStream_t s) {
-  hipError_t e;
+                              const IndexArgs& ia, const AttendBatch& ab, hipStream_t s, LaunchLog* lg) {
+  hipError_t e = log_start(lg, s);
+  if (e != hipSuccess) return e;
   AttendBatch all = ab;
   attend_batch_plan(all);
   const AttendBatch dense = sub_batch(all, true);
@@ -211,21 +290,28 @@ hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const
   const StepFold fd = fuse ? plan_fold(cb, ia, dense) : no_fold();
   if (app != nullptr && fd.ncomp > 0) {
     e = launch_decode_append(*app, s);
+    if (e == hipSuccess) e = log_launch(lg, s, "decode_append_kernel");
     if (e != hipSuccess) return e;
   } else if (app != nullptr) {
     e = launch_append_compress(*app, *mp, cb, s);
+    if (e == hipSuccess) e = log_launch(lg, s, "append_compress_kernel");
     if (e != hipSuccess) return e;
   } else if (cb.njobs > 0 && fd.ncomp == 0) {
     e = launch_compress_batch(cb, s);
+    if (e == hipSuccess && compress_work(cb)) e = log_launch(lg, s, "pool_encode_batch_kernel");
     if (e != hipSuccess) return e;
   }
   if (!fuse) {
     e = launch_index(ia, s);
+    if (e == hipSuccess && (int64_t)ia.B * ia.Tq > 0) e = log_launch(lg, s, "index_chunk_kernel + index_select_kernel");
     if (e != hipSuccess) return e;
     if (ab.njobs == 0) return hipSuccess;
     e = launch_attend_batch_mfma(all, s);
+    if (e == hipSuccess && all.blk0[all.njobs] > 0) e = log_launch(lg, s, "attend_mfma_batch_kernel");
     if (e != hipSuccess) return e;
-    return launch_attend_batch_merge(all, s);
+    e = launch_attend_batch_merge(all, s);
+    if (e == hipSuccess && all.mblk0[all.njobs] > 0) e = log_launch(lg, s, "attend_merge_batch_kernel");
+    return e;
   }
   const ScanPlan p = index_scan_plan(ia);
   const bool fp8 = all.job[0].kv_dt == DT_FP8;
@@ -237,16 +323,21 @@ hipError_t launch_decode_step(const AppendBatch* app, const AppendMap* mp, const
     else launch_fused_k<1, DT_BF16>(ia, p, dense, cb, fd, s);
   }
   e = hipGetLastError();
+  if (e == hipSuccess) e = log_launch(lg, s, "step_scan_attend_kernel");
   if (e != hipSuccess) return e;
   // the dense jobs' partials are complete: their merge runs beside the select
   e = launch_index_select_merge(ia, p, dense, s);
+  if (e == hipSuccess) e = log_launch(lg, s, "index_select_merge_kernel");
   if (e != hipSuccess) return e;
   const AttendBatch sparse = sub_batch(all, false);
   if (sparse.njobs > 0) {
     e = launch_attend_batch_mfma(sparse, s);
+    if (e == hipSuccess && sparse.blk0[sparse.njobs] > 0) e = log_launch(lg, s, "attend_mfma_batch_kernel");
     if (e != hipSuccess) return e;
   }
-  return launch_attend_batch_merge(sparse, s);
+  e = launch_attend_batch_merge(sparse, s);
+  if (e == hipSuccess && sparse.mblk0[sparse.njobs] > 0) e = log_launch(lg, s, "attend_merge_batch_kernel");
+  return e;
 }
 
 }  // namespace lca

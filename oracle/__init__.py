@@ -78,6 +78,8 @@ def lib():
                                  dbl, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_num_threads.restype = i32
         L.orc_num_threads.argtypes = []
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -312,3 +314,8 @@ def attend(q, kv, kv_dt, kv_scale, sel, n_elig, win, win_dt, win_begin, win_len,
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (results do not depend on it)."""
+    lib().orc_set_threads(int(n))

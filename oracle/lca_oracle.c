@@ -366,28 +366,33 @@ void orc_index_topk(const double* qi, const float* w, const void* keys, int key_
                     int d, int64_t N_cap, int k, int32_t* idx_out, double* sel_score,
                     double* scores_out) {
   int64_t r, R = (int64_t)B * Tq;
-#pragma omp parallel for schedule(dynamic, 1)
+  /* rows one after another; the entries of a row are scored in parallel (each
+   * score is its own left-to-right evaluation, so the split changes nothing) */
   for (r = 0; r < R; ++r) {
     int b = (int)(r / Tq);
     int64_t n = n_elig[r], j, h;
     double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-    double* kj = (double*)malloc(sizeof(double) * (size_t)d);
     double wd[64];
     for (h = 0; h < H; ++h) wd[h] = (double)w[r * H + h];
-    for (j = 0; j < n; ++j) {
-      int64_t row = (int64_t)b * N_cap + j;
-      if (key_dt == ORC_F32) orc_decode((const float*)keys + row * d, key_dt, NULL, d, kj);
-      else if (key_dt == ORC_BF16) orc_decode((const uint16_t*)keys + row * d, key_dt, NULL, d, kj);
-      else if (key_dt == ORC_FP8E4M3)
-        orc_decode((const uint8_t*)keys + row * d, key_dt, (const float*)key_scale + row * (d / 64), d, kj);
-      else
-        orc_decode((const uint8_t*)keys + row * (d / 2), key_dt, (const uint8_t*)key_scale + row * (d / 32), d, kj);
-      s[j] = orc_index_score(qi + r * H * d, wd, kj, H, d);
-      if (scores_out) scores_out[r * N_cap + j] = s[j];
+#pragma omp parallel
+    {
+      double* kj = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(static)
+      for (j = 0; j < n; ++j) {
+        int64_t row = (int64_t)b * N_cap + j;
+        if (key_dt == ORC_F32) orc_decode((const float*)keys + row * d, key_dt, NULL, d, kj);
+        else if (key_dt == ORC_BF16) orc_decode((const uint16_t*)keys + row * d, key_dt, NULL, d, kj);
+        else if (key_dt == ORC_FP8E4M3)
+          orc_decode((const uint8_t*)keys + row * d, key_dt, (const float*)key_scale + row * (d / 64), d, kj);
+        else
+          orc_decode((const uint8_t*)keys + row * (d / 2), key_dt, (const uint8_t*)key_scale + row * (d / 32), d, kj);
+        s[j] = orc_index_score(qi + r * H * d, wd, kj, H, d);
+        if (scores_out) scores_out[r * N_cap + j] = s[j];
+      }
+      free(kj);
     }
     orc_select_topk(s, n, k, idx_out + r * k, sel_score ? sel_score + r * k : NULL);
     free(s);
-    free(kj);
   }
 }
 
@@ -422,13 +427,17 @@ void orc_attend_row_kv(const double* q, const double* ent, const double* ent_v, 
                        double tau, int Hq, int D, double* o, double* lse) {
   if (!ent_v) ent_v = ent;
   if (!win_v) win_v = win;
-  int64_t n = n_ent + n_win, t;
-  int h, dd;
-  double* l = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-  double* p = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  int64_t n = n_ent + n_win;
+  int h;
+  /* heads are independent: they run in parallel, each with its own buffers */
+#pragma omp parallel for schedule(static)
   for (h = 0; h < Hq; ++h) {
+    double* l = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
     const double* qh = q + (int64_t)h * D;
     double M = (double)sink[h], Z;
+    int64_t t;
+    int dd;
     for (t = 0; t < n; ++t) {
       const double* v = t < n_ent ? ent + t * D : win + (t - n_ent) * D;
       double dot = 0.0;
@@ -448,9 +457,9 @@ void orc_attend_row_kv(const double* q, const double* ent, const double* ent_v, 
       o[(int64_t)h * D + dd] = acc / Z;
     }
     if (lse) lse[h] = M + log(Z);
+    free(l);
+    free(p);
   }
-  free(l);
-  free(p);
 }
 
 /* Batched attention for the two attention calls.  Row r = b*Tq + t.
@@ -476,7 +485,7 @@ void orc_attend(const double* q, const void* kv, int kv_dt, const float* kv_scal
                 int Hq, int D, double* o, double* lse, const void* v, const float* v_scale,
                 const void* win_v) {
   int64_t r, R = (int64_t)B * Tq;
-#pragma omp parallel for schedule(dynamic, 1)
+  /* rows one after another (the heads of a row run in parallel) */
   for (r = 0; r < R; ++r) {
     int b = (int)(r / Tq);
     int64_t ne = 0, nw = win_len[r], t;
@@ -506,6 +515,16 @@ void orc_attend(const double* q, const void* kv, int kv_dt, const float* kv_scal
     free(ent_v);
     free(wv_v);
   }
+}
+
+/* Threads the parallel loops above use (a timing control: results do not
+ * depend on it). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
 }
 
 int orc_num_threads(void) {

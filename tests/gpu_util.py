@@ -33,12 +33,36 @@ def bf16_bits_to_f64(u16):
 
 
 def assert_rows_close(got, ref, rtol, what=""):
-    """|got - ref| <= rtol * (|ref| + max |ref| over the row), row = last dim."""
+    """|got - ref| <= rtol * (|ref| + max |ref| over the row), row = last dim.
+
+    The comparison rule for attention outputs and pooled rows: an element is
+    held to rtol of its own magnitude plus rtol of the largest magnitude in its
+    row (one head's output vector, one pooled entry), so elements near zero in
+    a row of ordinary size are not held to a vanishing bound."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     rowmax = np.abs(ref).max(axis=-1, keepdims=True) if ref.size else ref
     tol = rtol * (np.abs(ref) + rowmax)
+    err = np.abs(got - ref)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside rtol {rtol}; worst at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r} tol {tol[i]!r}")
+
+
+def assert_lse_close(got, ref, rtol, what=""):
+    """Log-sum-exp rows: |got - ref| <= rtol * max(|ref|, 1), element by element.
+
+    The tolerance is relative to the LSE itself (no row floor: each element is
+    its own row); below |lse| = 1 it is relative to the softmax normaliser
+    Z = exp(lse) instead, since |d lse| = |dZ| / Z, so an LSE near zero is not
+    held to a vanishing absolute bound."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    tol = rtol * np.maximum(np.abs(ref), 1.0)
     err = np.abs(got - ref)
     bad = err > tol
     if bad.any():

@@ -227,6 +227,27 @@ def test_decode_step_validation(L):
     assert decode_step(L, [], index_job(ws=None), []) == 4
 
 
+def test_decode_step_events_validation(L):
+    """Argument checks of the measurement form of the decode step (no GPU:
+    every case fails or has nothing to launch before any event is touched)."""
+    n = ctypes.c_int32(-1)
+    names = (ctypes.c_char_p * lca.MAX_STEP_LAUNCHES)()
+    ev = (ctypes.c_void_p * (lca.MAX_STEP_LAUNCHES + 1))(*([FAKE] * (lca.MAX_STEP_LAUNCHES + 1)))
+    ca = (lca.CompressJob * 1)(batch_job(B=0))
+    aa = (lca.AttendJob * 1)(attend_job(B=0))
+    call = lambda evs, nev, nl, ij=index_job(k=0): L.lca_decode_step_events(
+        ca, 1, ctypes.byref(ij), aa, 1, evs, nev, names, nl, None)
+    assert call(None, lca.MAX_STEP_LAUNCHES + 1, ctypes.byref(n)) == 1
+    assert call(ev, lca.MAX_STEP_LAUNCHES, ctypes.byref(n)) == 1               # too few events
+    assert b"event handles" in L.lca_last_error()
+    assert call(ev, lca.MAX_STEP_LAUNCHES + 1, None) == 1
+    ev_null = (ctypes.c_void_p * (lca.MAX_STEP_LAUNCHES + 1))(*([FAKE] * lca.MAX_STEP_LAUNCHES + [None]))
+    assert call(ev_null, lca.MAX_STEP_LAUNCHES + 1, ctypes.byref(n)) == 1
+    assert b"events[8]" in L.lca_last_error()
+    assert call(ev, lca.MAX_STEP_LAUNCHES + 1, ctypes.byref(n)) == 1           # the index job's k = 0
+    assert b"index job" in L.lca_last_error() and n.value == -1
+
+
 def append_job(**kw):
     a = dict(x_new=FAKE, x_dt=lca.BF16, g_new=FAKE, ring=FAKE, gring=FAKE, R=256, len=FAKE, m=4, W=128,
              x_tok0=FAKE, nblk=FAKE, dst_row0=FAKE, n_elig=FAKE, win_begin=FAKE, win_len=FAKE, B=2, D=128)

@@ -12,7 +12,7 @@ import torch
 import long_context_attention_13_amd as lca
 import oracle
 import synth
-from gpu_util import assert_rows_close, dev, empty_ws, to_dev, to_host
+from gpu_util import assert_lse_close, assert_rows_close, dev, empty_ws, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def test_small_fp32_config():
     o, l, ro, rl = run(True, c["q"], lca.F32, kv, lca.F32, None, sel, win, lca.F32,
                        np.zeros((1, 1), np.int32), np.full((1, 1), 128, np.int32), c["sink"], 1.0, lca.F32)
     assert_rows_close(o, ro, 1e-4, "out")
-    assert_rows_close(l[..., None], rl[..., None], 1e-4, "lse")
+    assert_lse_close(l, rl, 1e-4, "lse")
 
 
 @pytest.mark.parametrize("kv_dt,q_dt,out_dt", [(lca.FP8E4M3, lca.BF16, lca.BF16), (lca.BF16, lca.BF16, lca.F32),
@@ -87,7 +87,7 @@ def test_sparse_decode_rows(kv_dt, q_dt, out_dt):
                        1 / math.sqrt(128), out_dt)
     rt = rtol_for(kv_dt, q_dt, out_dt)
     assert_rows_close(o, ro, rt, "out")
-    assert_rows_close(l[..., None], rl[..., None], rt, "lse")
+    assert_lse_close(l, rl, rt, "lse")
 
 
 @pytest.mark.parametrize("kv_dt,N_cap", [(lca.BF16, 512), (lca.FP8E4M3, 8192), (lca.FP8E4M3, 1000)])
@@ -99,7 +99,7 @@ def test_hca_decode_rows(kv_dt, N_cap):
     o, l, ro, rl = run(False, q, lca.BF16, kv, kv_dt, kv_sc, n, win, lca.BF16, np.zeros((B, 1), np.int32), wl,
                        sink, 1 / math.sqrt(128), lca.BF16)
     assert_rows_close(o, ro, 2e-2, "out")
-    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
+    assert_lse_close(l, rl, 2e-2, "lse")
 
 
 def test_prefill_rows_with_sliding_windows():
@@ -117,7 +117,7 @@ def test_prefill_rows_with_sliding_windows():
     o, l, ro, rl = run(True, q, lca.BF16, kv, lca.BF16, None, sel, win, lca.BF16, wb, wl, sink,
                        1 / math.sqrt(128), lca.BF16)
     assert_rows_close(o, ro, 2e-2, "out sparse")
-    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse sparse")
+    assert_lse_close(l, rl, 2e-2, "lse sparse")
 
 
 @pytest.mark.parametrize("out_dt", [lca.BF16, lca.F32])
@@ -141,7 +141,7 @@ def test_sparse_prefill_rows_64_heads(out_dt):
     o, l, ro, rl = run(True, q, lca.BF16, kv, lca.BF16, None, sel, win, lca.BF16, wb, wl, sink,
                        1 / math.sqrt(128), out_dt)
     assert_rows_close(o, ro, 2e-2, "out")
-    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
+    assert_lse_close(l, rl, 2e-2, "lse")
 
 
 def test_empty_lists_give_sink_only():
@@ -175,7 +175,7 @@ def test_dense_row_groups(Hq, kv_dt):
     o, l, ro, rl = run(False, q, lca.BF16, kv, kv_dt, kv_sc, n, win, lca.BF16, wb, wl, sink, 1 / math.sqrt(128),
                        lca.BF16)
     assert_rows_close(o, ro, 2e-2, "out")
-    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
+    assert_lse_close(l, rl, 2e-2, "lse")
 
 
 @pytest.mark.parametrize("kv_dt,Hq", [(lca.FP8E4M3, 64), (lca.BF16, 16)])

@@ -64,8 +64,17 @@ def special_rows(D=128):
     r[:9] = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.1]
     rows.append(r)
     r = np.zeros(D, np.float32)
-    r[3] = 1e-40                       # subnormal amax; FP8 scale underflows
+    r[3] = 1e-40                       # subnormal amax
     r[70] = -3e-39
+    rows.append(r)
+    # FP8 groups whose amax / 448 rounds to 0 in fp32 (scale 2^-149), and a
+    # group where it rounds up to 2^-149 instead
+    t = np.float32(2.0) ** -149
+    r = np.zeros(D, np.float32)
+    r[3], r[10], r[64 + 5], r[64 + 9] = t, -t, 224 * t, -100 * t
+    rows.append(r)
+    r = np.zeros(D, np.float32)
+    r[0], r[1], r[64], r[65] = 100 * t, 3 * t, 225 * t, 7 * t
     rows.append(r)
     rows.append((g.standard_normal(D) * 1e30).astype(np.float32))
     rows.append((g.standard_normal(D) * 1e-30).astype(np.float32))

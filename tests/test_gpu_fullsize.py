@@ -21,7 +21,7 @@ import torch
 import long_context_attention_13_amd as lca
 import oracle
 import synth
-from gpu_util import assert_rows_close, dev, empty_ws, to_dev, to_host
+from gpu_util import assert_lse_close, assert_rows_close, dev, empty_ws, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
@@ -77,7 +77,7 @@ def test_layer_pair_1m_full():
         ro, rl = oracle.attend(oracle.decode(qb, oracle.BF16), kv, oracle.FP8E4M3, sc, sel, n, wbf, oracle.BF16,
                                wb, wl, sink, tau)
         assert_rows_close(o, ro, 2e-2, name + " out")
-        assert_rows_close(l[..., None], rl[..., None], 2e-2, name + " lse")
+        assert_lse_close(l, rl, 2e-2, name + " lse")
 
 
 def test_layer_pair_1m_multi_token_full():
@@ -114,7 +114,7 @@ def test_layer_pair_1m_multi_token_full():
         ro, rl = oracle.attend(oracle.decode(qb, oracle.BF16), kv, oracle.FP8E4M3, sc, sel, n, wbf, oracle.BF16,
                                wb, wl, sink, tau)
         assert_rows_close(o, ro, 2e-2, name + " out")
-        assert_rows_close(l[..., None], rl[..., None], 2e-2, name + " lse")
+        assert_lse_close(l, rl, 2e-2, name + " lse")
 
 
 def test_csa_decode_fp8_full():
@@ -136,7 +136,7 @@ def test_csa_decode_fp8_full():
     ro, rl = oracle.attend(oracle.decode(qb, oracle.BF16), ent, oracle.FP8E4M3, ent_sc, ri, None, wbf, oracle.BF16,
                            wb, wl, c["sink"], c["tau"])
     assert_rows_close(o, ro, 2e-2, "out")
-    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
+    assert_lse_close(l, rl, 2e-2, "lse")
 
 
 def test_hca_decode_bf16_full():
@@ -164,7 +164,7 @@ def test_hca_decode_bf16_full():
     ro, rl = oracle.attend(oracle.decode(qb, oracle.BF16), cache, oracle.BF16, None, None, n, win, oracle.BF16,
                            wb, wl, c["sink"], c["tau"])
     assert_rows_close(o, ro, 2e-2, "out")
-    assert_rows_close(l[..., None], rl[..., None], 2e-2, "lse")
+    assert_lse_close(l, rl, 2e-2, "lse")
 
 
 def test_prefill_chunk_sampled_rows():
@@ -205,4 +205,4 @@ def test_prefill_chunk_sampled_rows():
                                None if sparse else sel_or_n[:, rows], winb, oracle.BF16, wb[:, rows], wl[:, rows],
                                sink, c["tau"])
         assert_rows_close(o[:, rows], ro, 2e-2, name + " out")
-        assert_rows_close(l[:, rows][..., None], rl[..., None], 2e-2, name + " lse")
+        assert_lse_close(l[:, rows], rl, 2e-2, name + " lse")

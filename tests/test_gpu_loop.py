@@ -32,7 +32,7 @@ import torch
 
 import long_context_attention_13_amd as lca
 import oracle
-from gpu_util import assert_rows_close, dev, empty_ws, to_dev, to_host
+from gpu_util import assert_lse_close, assert_rows_close, dev, empty_ws, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
@@ -252,7 +252,7 @@ def check_against_oracle(lp, dv, i, L):
                                wb0, wl, sink, TAU)
         o = oracle.decode(to_host(out), oracle.BF16)
         assert_rows_close(o, ro, 2e-2, f"step {i}: {name} out")
-        assert_rows_close(to_host(lse)[..., None], rl[..., None], 2e-2, f"step {i}: {name} lse")
+        assert_lse_close(to_host(lse), rl, 2e-2, f"step {i}: {name} lse")
 
 
 def check_final_state(lp, dv):

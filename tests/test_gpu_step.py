@@ -137,13 +137,16 @@ def test_step_graph_replays():
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i}"
 
 
-def test_step_reads_rows_written_in_the_step():
+@pytest.mark.parametrize("kv_dt,Tq", [(lca.FP8E4M3, 1), (lca.BF16, 2)])
+def test_step_reads_rows_written_in_the_step(kv_dt, Tq):
     """The newest indexer key row and HCA row are written by the step's own
     compress jobs: before the step they hold zeros, and their raw tokens are
     scaled so that the new rows decide the results (the key row is selected,
     the HCA row dominates the HCA attention).  A scan or HCA split that read
-    the rows before they were written would differ from the three calls."""
-    st = Step(919)
+    the rows before they were written would differ from the three calls.
+    With two query rows per sequence (bf16 entries) the rows share each scan
+    wavefront, and only the second row sees the new key row."""
+    st = Step(919 + Tq, kv_dt, Tq)
     N, N2, W = st.key.shape[1], st.hca.shape[1], 128
     st.win_keys[:, W - 4:W] *= 40.0
     st.win[:, :128] *= 8.0
@@ -159,7 +162,7 @@ def test_step_reads_rows_written_in_the_step():
     st.three_calls()
     torch.cuda.synchronize()
     ref = st.outputs()
-    assert bool((ref[4][0, 0] == N - 1).any()), "the new key row is selected"
+    assert bool((ref[4][0, Tq - 1] == N - 1).any()), "the new key row is selected"
     stale()
     st.clobber()
     for rep in range(2):
@@ -169,3 +172,33 @@ def test_step_reads_rows_written_in_the_step():
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"step {rep}: output {i}"
         stale()
         st.clobber()
+
+
+def test_step_compress_into_key_cache_at_an_offset():
+    """A compress job that writes into the indexer's key cache through an
+    offset pointer (a different row layout: sequence b's row r lands at key
+    row b * (N - 4) + r + 4) is not run beside the scan, which reads those
+    rows: the step still gives the bytes of the three calls in order.  The
+    raw keys of the block are scaled so that the rows it writes are selected."""
+    st = Step(933)
+    N = st.key.shape[1]
+    kv = st.key.view(-1)[4 * 64:].view(st.key.shape[0] * N - 4, 64)[: 2 * (N - 4)].view(2, N - 4, 64)
+    ks = st.key_sc.view(-1)[4 * 4:].view(st.key.shape[0] * N - 4, 4)[: 2 * (N - 4)].view(2, N - 4, 4)
+    d = dev()
+    st.win_keys[:, 128 - 4:128] *= 40.0
+    st.cjobs[1] = lca.compress_job(st.win_keys, torch.randn(2, 256, device=d), torch.randn(4, device=d), 4,
+                                   torch.full((2,), 124, dtype=torch.int32, device=d),
+                                   torch.ones(2, dtype=torch.int32, device=d),
+                                   torch.tensor([N - 40, N - 90], dtype=torch.int64, device=d), 1, kv, lca.MXFP4, ks)
+    key0, ksc0 = st.key.clone(), st.key_sc.clone()
+    st.three_calls()
+    torch.cuda.synchronize()
+    ref = st.outputs()
+    assert bool((ref[4][0, 0] == N - 36).any()), "a row the offset job wrote is selected"
+    st.key.copy_(key0)
+    st.key_sc.copy_(ksc0)
+    st.clobber()
+    st.step()
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(st.outputs(), ref)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"output {i}"

@@ -104,6 +104,36 @@ def test_fp8_scale_rule_and_roundtrip():
     assert np.array_equal(back, c2)
 
 
+def test_fp8_scale_underflow_branch():
+    """Reading of the FP8 scale rule for groups whose amax / 448 rounds to 0 in
+    fp32: the scale is the smallest fp32 subnormal, s = 2^-149, so the group's
+    values become integer multiples of s and their codes are those integers
+    rounded to E4M3 (ties to the even code).  Closed forms, one per group."""
+    t = np.float32(2.0) ** -149
+    v = np.zeros((3, 128), np.float32)
+    v[0, 3], v[0, 10] = t, -t                        # amax = s: codes of +-1
+    v[0, 64 + 5], v[0, 64 + 9] = 224 * t, -100 * t    # 224/448 = 1/2: ties to 0
+    v[1, 0], v[1, 1] = 100 * t, 3 * t                 # 100/448 < 1/2: rounds to 0
+    v[1, 64], v[1, 65] = 225 * t, 7 * t               # 225/448 > 1/2: s = 2^-149 without the branch
+    v[2, 0] = 448 * t                                 # s = fl32(448 s / 448) = s exactly
+    assert np.float32(v[0, 64 + 5] / np.float32(448)) == 0 and np.float32(v[1, 64] / np.float32(448)) == t
+    codes, sc = oracle.encode(v, oracle.FP8E4M3)
+    assert np.array_equal(sc[:, 0], [t, t, t]) and np.array_equal(sc[:, 1], [t, t, np.float32(1)])
+    # E4M3 codes of the integers 1, 3, 7, 100 (a tie between 96 and 104), 224, 225 and 448
+    assert (codes[0, 3], codes[0, 10]) == (0x38, 0xB8)
+    assert (codes[0, 64 + 5], codes[0, 64 + 9]) == (0x76, 0xEC)
+    assert (codes[1, 0], codes[1, 1]) == (0x6C, 0x44)
+    assert (codes[1, 64], codes[1, 65]) == (0x76, 0x4E)
+    assert codes[2, 0] == 0x7E
+    assert np.count_nonzero(codes) == 9
+    # the same codes from torch's E4M3 conversion of v / s
+    q = (v.reshape(-1, 64).astype(np.float64) / sc.reshape(-1, 1).astype(np.float64)).astype(np.float32)
+    assert np.array_equal(codes.reshape(-1, 64), torch_e4m3_codes(q))
+    # decoded values: the code's value times 2^-149 (exact in float64)
+    dec = oracle.decode(codes, oracle.FP8E4M3, sc)
+    assert dec[0, 64 + 9] == -96 * 2.0 ** -149 and dec[1, 64] == 224 * 2.0 ** -149
+
+
 def test_mxfp4_shared_exponent():
     g = np.random.default_rng(5)
     blocks = g.standard_normal((400, 32)).astype(np.float32) * np.float32(4.0) ** g.integers(
