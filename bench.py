@@ -39,22 +39,27 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MXFP4_PEAK_TFLOPS = 10100.0     # dense fp4 matrix peak
 BF16_PEAK_TFLOPS = 2500.0       # dense bf16 matrix peak
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "layer_pair_1m_decode_index_traffic.json")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "layer_pair_1m_decode_traffic.json")
 
 
-def recorded_traffic():
-    """HBM bytes per indexer launch from the committed FETCH_SIZE/WRITE_SIZE
-    counter runs, or None when the kernel sources differ from the ones the
-    counters were taken on."""
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
+    counter runs, or None when there is no record for it or the kernel sources
+    differ from the ones the counters were taken on."""
     import hashlib
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
-    except OSError:
+        recs = json.load(open(TRAFFIC_RECORD))["records"]
+    except (OSError, KeyError, ValueError):
         return None
-    h = hashlib.sha256()
-    for f in rec["kernel_sources"]:
-        h.update(open(os.path.join(ROOT, "long_context_attention_13_amd", f), "rb").read())
-    return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    for rec in recs:
+        if rec["kernel"] != kernel:
+            continue
+        h = hashlib.sha256()
+        for f in rec["kernel_sources"]:
+            h.update(open(os.path.join(ROOT, "long_context_attention_13_amd", f), "rb").read())
+        if h.hexdigest() == rec["sources_sha256"]:
+            return rec["hbm_bytes_per_launch"]
+    return None
 
 
 def parse():
@@ -62,9 +67,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--copies", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-prefill-rows", type=int, default=512,
+                    help="query rows of the chunked-prefill oracle subset")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the small CSA, HCA bf16 and CSA FP8 decode legs")
+    ap.add_argument("--legs-only", action="store_true",
+                    help="run only the small CSA, HCA bf16 and CSA FP8 decode legs")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="run only the chunked-prefill leg")
     ap.add_argument("--unbatched", action="store_true",
@@ -274,21 +285,51 @@ class Workload:
         self.lca.decode_step(self.cjobs[c], self.ijobs[c], self.ajobs[c])
 
     # -- algorithmic bytes -------------------------------------------------
+    # Each byte the step must move once: cache rows read once, gathered
+    # entries once, raw blocks, windows, queries and outputs once.  Split
+    # partials, candidate lists and scores are overheads, not counted.
+    def parts(self) -> dict:
+        B, D, Hq, k, H_I, d_I = self.B, self.D, self.Hq, self.k, self.H_I, self.d_I
+        ent = D + 8                                    # FP8 row + two fp32 scales
+        key = d_I // 2 + d_I // 32                     # MXFP4 row + E8M0 bytes
+        win_c = (128 + self.Tq - 1) * D * 2
+        q = self.Tq * Hq * D * 2                       # bf16 queries of one sequence (= its outputs)
+        return {
+            "comp_in": B * ((4 * D + 4 * d_I + 128 * D) * 2 + (4 + 4 + 128) * 4),
+            "comp_out": B * (ent + key + ent),
+            "idx_in": float((self.L // 4).sum() * key) + B * self.Tq * H_I * (key + 4),
+            "idx_out": B * self.Tq * k * 4,
+            "hca_in": float((self.L // 128).sum() * ent) + B * (128 + self.Tq - 1) * D * 2 + B * q,
+            "hca_out": B * q,
+            "csa_in": B * self.Tq * k * ent + B * win_c + B * q,
+            "csa_out": B * q,
+        }
+
     def index_bytes(self) -> float:
         """Bytes the indexer must move once: every eligible MXFP4 key row (64 B codes
         + 4 B E8M0), the query rows, head weights and the selected indices."""
-        n = self.L // 4
-        return float(n.sum() * (self.d_I // 2 + self.d_I // 32)
-                     + self.B * (self.H_I * (self.d_I // 2 + self.d_I // 32) + self.H_I * 4 + self.k * 4))
+        p = self.parts()
+        return p["idx_in"] + p["idx_out"]
 
     def step_bytes(self) -> float:
-        B, D, Hq, k = self.B, self.D, self.Hq, self.k
-        ent = D + 8                                    # FP8 row + two fp32 scales
-        qo = 2 * Hq * D * 2                            # bf16 q in, bf16 out
-        csa = B * (k * ent + 128 * D * 2 + qo)
-        hca = float((self.L // 128).sum() * ent + B * (128 * D * 2 + qo))
-        comp = B * (4 * D * 2 * 2 + 128 * D * 2 + 3 * ent)  # raw blocks read, rows written
-        return self.index_bytes() + csa + hca + comp
+        return float(sum(self.parts().values()))
+
+    def launch_bytes(self) -> dict:
+        """Algorithmic bytes of each launch of the step, by kernel name."""
+        p = self.parts()
+        return {
+            "step_scan_attend_kernel": p["comp_in"] + p["comp_out"] + p["idx_in"] + p["hca_in"],
+            "index_select_merge_kernel": p["idx_out"] + p["hca_out"],
+            "attend_mfma_batch_kernel": p["csa_in"],
+            "attend_merge_batch_kernel": p["csa_out"],
+            "pool_encode_batch_kernel": p["comp_in"] + p["comp_out"],
+            "index_chunk_kernel + index_select_kernel": p["idx_in"] + p["idx_out"],
+        }
+
+    def copy_mb(self) -> float:
+        """Device bytes of one cache copy (entries, keys, HCA entries)."""
+        return sum(t.numel() * t.element_size() for t in (self.ent[0], self.ent_sc[0], self.key[0], self.key_sc[0],
+                                                         self.hca[0], self.hca_sc[0])) / 1e6
 
 
 class PrefillWorkload:
@@ -777,37 +818,417 @@ def run_prefill(steps: int, warmup: int):
     return res
 
 
-def cpu_baseline(wl, steps):
-    """The float64 oracle on one full layer-pair step, on the host cores."""
+def host_cpu():
+    """Model name and logical CPU count of the host."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def oracle_decode_step(wl, c, host):
+    """The float64 oracle's layer-pair decode step on copy c's inputs: the three
+    newest blocks pooled and encoded, indexer + top-k, both attentions.  The
+    attentions read the caches the GPU step left (which hold its encoded new
+    rows), as the comparison protocol prescribes; returns (idx, out_csa, out_hca)."""
+    import oracle
+    B = wl.B
+    for x, gate, bias, tok, m, dt in host["blocks"]:
+        for b in range(B):
+            t0 = int(tok[b])
+            pooled = oracle.pool(x[b, t0:t0 + m], gate[b, t0:t0 + m], bias, m)
+            oracle.encode(pooled.astype(np.float32)[None], dt)
+    idx, _ = oracle.index_topk(host["qi"], host["w"], host["key"], oracle.MXFP4, host["key_sc"], host["n_csa"], wl.k)
+    o_c, _ = oracle.attend(host["q_csa"], host["ent"], oracle.FP8E4M3, host["ent_sc"], idx, None, host["win_c"],
+                           oracle.BF16, host["wb_c"], host["wl"], host["sink_c"], wl.tau)
+    o_h, _ = oracle.attend(host["q_hca"], host["hca"], oracle.FP8E4M3, host["hca_sc"], None, host["n_hca"],
+                           host["win_h"], oracle.BF16, host["wb_h"], host["wl"], host["sink_h"], wl.tau)
+    return idx, o_c, o_h
+
+
+def cpu_baseline(wl, gpu_out, steps):
+    """The float64 oracle on the layer-pair decode step (compression included),
+    on all the host threads OpenMP is given and on one thread; and its
+    comparison with the GPU step's outputs for the same copy (index sets
+    bit-exact, attention outputs within rtol 2e-2 of the oracle)."""
     import torch
     import oracle
     c = 0
-    B, H_I, d_I = wl.B, wl.H_I, wl.d_I
-    host = lambda t: t.cpu().numpy()
-    ent, ent_sc = host(wl.ent[c]), host(wl.ent_sc[c])
-    key, key_sc = host(wl.key[c]), host(wl.key_sc[c])
-    hca, hca_sc = host(wl.hca[c]), host(wl.hca_sc[c])
-    qi = oracle.decode(host(wl.qi), oracle.MXFP4, host(wl.qi_sc))
-    w = host(wl.w)
-    q_csa = oracle.decode(host(wl.q_csa.view(torch.int16)).view(np.uint16), oracle.BF16)
-    q_hca = oracle.decode(host(wl.q_hca.view(torch.int16)).view(np.uint16), oracle.BF16)
-    win_c = host(wl.win_csa.view(torch.int16)).view(np.uint16)
-    win_h = host(wl.win_hca.view(torch.int16)).view(np.uint16)
-    n_csa, n_hca = host(wl.n_csa), host(wl.n_hca)
-    wb0 = np.zeros((B, 1), np.int32)
-    wl_ = np.full((B, 1), 128, np.int32)
-    wb1 = np.full((B, 1), 128, np.int32)
-    sink_c, sink_h = host(wl.sink_csa), host(wl.sink_hca)
+    host_t = lambda t: t.cpu().numpy()
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    dec = lambda u16: oracle.decode(u16, oracle.BF16)
+    B = wl.B
+    host = dict(key=host_t(wl.key[c]), key_sc=host_t(wl.key_sc[c]), ent=host_t(wl.ent[c]), ent_sc=host_t(wl.ent_sc[c]),
+                hca=host_t(wl.hca[c]), hca_sc=host_t(wl.hca_sc[c]),
+                qi=oracle.decode(host_t(wl.qi), oracle.MXFP4, host_t(wl.qi_sc)), w=host_t(wl.w),
+                q_csa=dec(bits(wl.q_csa)), q_hca=dec(bits(wl.q_hca)), win_c=bits(wl.win_att), win_h=bits(wl.win_hca),
+                n_csa=host_t(wl.n_csa), n_hca=host_t(wl.n_hca), wb_c=host_t(wl.wb_csa), wb_h=host_t(wl.wb_hca),
+                wl=host_t(wl.wl), sink_c=host_t(wl.sink_csa), sink_h=host_t(wl.sink_hca))
+    host["blocks"] = [(dec(bits(wl.win_csa)), host_t(wl.gate_csa), host_t(wl.bias_csa), host_t(wl.csa_tok0), 4,
+                       oracle.FP8E4M3),
+                      (dec(bits(wl.win_keys)), host_t(wl.gate_i), host_t(wl.bias_i), host_t(wl.csa_tok0), 4,
+                       oracle.MXFP4),
+                      (dec(bits(wl.win_hca)), host_t(wl.gate_hca), host_t(wl.bias_hca), host_t(wl.hca_tok0), 128,
+                       oracle.FP8E4M3)]
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     for _ in range(steps):
-        idx, _ = oracle.index_topk(qi, w, key, oracle.MXFP4, key_sc, n_csa, wl.k)
-        oracle.attend(q_csa, ent, oracle.FP8E4M3, ent_sc, idx, None, win_c, oracle.BF16, wb0, wl_, sink_c, wl.tau)
-        oracle.attend(q_hca, hca, oracle.FP8E4M3, hca_sc, None, n_hca, win_h, oracle.BF16, wb1, wl_, sink_h, wl.tau)
-    dt = time.perf_counter() - t0
-    return {"value": round(B * steps / dt, 3), "unit": "decode tokens/s", "cores": min(oracle.num_threads(), B),
-            "kind": "oracle",
-            "sample": f"{steps} full layer-pair decode steps (4 sequences; indexer + top-k + both attentions, "
-                      f"compression excluded); the oracle parallelises over the 4 query rows"}
+        idx, o_c, o_h = oracle_decode_step(wl, c, host)
+    dt_all = (time.perf_counter() - t0) / steps
+    oracle.set_threads(1)
+    t0 = time.perf_counter()
+    oracle_decode_step(wl, c, host)
+    dt_one = time.perf_counter() - t0
+    oracle.set_threads(threads)
+    # parity of the GPU step against the oracle on the same inputs
+    g_idx, g_c, g_h = gpu_out
+    idx_ok = bool(np.array_equal(g_idx, idx))
+    worst = 0.0
+    for got, ref in ((g_c, o_c), (g_h, o_h)):
+        got = oracle.decode(got, oracle.BF16)
+        tol = 2e-2 * (np.abs(ref) + np.abs(ref).max(-1, keepdims=True))
+        worst = max(worst, float((np.abs(got - ref) / tol).max()))
+    model, ncpu = host_cpu()
+    return {"value": round(B / dt_all, 3), "unit": "decode tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cpus": ncpu,
+            "sample": f"{steps} full layer-pair decode step(s) on copy 0 (4 sequences: the three newest blocks "
+                      f"pooled and encoded, indexer + exact top-1024, CSA and HCA attention), float64, "
+                      f"{threads} OpenMP threads",
+            "single_thread": {"value": round(B / dt_one, 3), "unit": "decode tokens/s", "cores": 1,
+                              "sample": "1 full layer-pair decode step"},
+            "parity": {"index_sets_bit_exact": idx_ok, "attention_max_err_over_tol": round(worst, 4),
+                       "rtol": 2e-2, "status": "ok" if idx_ok and worst <= 1.0 else "failed"}}
+
+
+def step_outputs(wl):
+    import torch
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return wl.idx.cpu().numpy(), bits(wl.out_csa), bits(wl.out_hca)
+
+
+def self_check(wl, replay):
+    """The timed form of the step (a graph replay of copy 0's step) against the
+    three library calls issued eagerly on the same inputs: equal bytes."""
+    import torch
+    outs = []
+    for run in (replay, lambda: wl.step_batched(0)):
+        for t in (wl.idx, wl.out_csa, wl.out_hca):
+            t.zero_()
+        run()
+        torch.cuda.synchronize()
+        outs.append(step_outputs(wl))
+    equal = all(np.array_equal(a.view(np.uint8), b.view(np.uint8)) for a, b in zip(*outs))
+    return equal, outs[0]
+
+
+def launch_profile(wl, steps):
+    """Per-launch durations of the decode step, measured live: eager
+    decode_step_events calls over the rotating copies, HIP events recorded by
+    the library between its launches on the launch stream."""
+    import torch
+    lca = wl.lca
+    C = len(wl.ent)
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(lca.MAX_STEP_LAUNCHES + 1)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)           # creates the events
+    torch.cuda.synchronize()
+    names = None
+    for s in range(steps):
+        c = s % C
+        names = lca.decode_step_events(wl.cjobs[c], wl.ijobs[c], wl.ajobs[c], evs[s])
+    torch.cuda.synchronize()
+    out = []
+    for i, name in enumerate(names):
+        ms = [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]
+        out.append({"kernel": name, "us": round(float(np.mean(ms)) * 1e3, 2),
+                    "us_median": round(float(np.median(ms)) * 1e3, 2)})
+    return out
+
+
+def stats_us(ms):
+    a = np.asarray(ms) * 1e3
+    return {"mean": round(float(a.mean()), 2), "median": round(float(np.median(a)), 2),
+            "p10": round(float(np.percentile(a, 10)), 2), "p90": round(float(np.percentile(a, 90)), 2),
+            "samples": int(a.size)}
+
+
+def time_graph(step, reps, setup=None):
+    """Capture step() in a graph and time reps replays with an event after each
+    (per-replay durations in ms)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
+def run_small_csa(reps: int):
+    """Small CSA decode in fp32: 1 sequence of 4096 tokens -> 1024 entries, 16
+    query heads, indexer 4 x 64, top-64, window 128.  Cache and indexer keys
+    built by csa_compress; one step = the newest block pooled into both caches,
+    indexer + top-k (float64 head combine), sparse attention (fp32), captured in
+    a graph."""
+    import torch
+    import long_context_attention_13_amd as lca
+    import synth
+    dev = torch.device("cuda:0")
+    c = synth.small_csa_decode()
+    L, D, d_I, H_I, Hq, k, W = c["L"], c["D"], c["d_I"], c["H_I"], c["Hq"], c["k"], c["W"]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    i32 = lambda v: torch.full((1,), v, dtype=torch.int32, device=dev)
+    i64 = lambda v: torch.full((1,), v, dtype=torch.int64, device=dev)
+    x, gate, bias, xi, gate_i, bias_i = t(c["x"]), t(c["gate"]), t(c["bias"]), t(c["xi"]), t(c["gate_i"]), t(c["bias_i"])
+    N = L // 4
+    ent = torch.empty(1, N, D, device=dev)
+    key = torch.empty(1, N, d_I, device=dev)
+    lca.csa_compress(x, gate, bias, 4, i32(0), i32(N), i64(0), N, ent, lca.F32)
+    lca.csa_compress(xi, gate_i, bias_i, 4, i32(0), i32(N), i64(0), N, key, lca.F32)
+    qi, w, q, sink = t(c["qi"]), t(c["w"]), t(c["q"]), t(c["sink"])
+    n = torch.full((1, 1), N, dtype=torch.int32, device=dev)
+    idx = torch.empty(1, 1, k, dtype=torch.int32, device=dev)
+    out = torch.empty(1, 1, Hq, D, device=dev)
+    ws_i = torch.empty(max(lca.index_topk_ws(1, 1, H_I, d_I, N, k), 16), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(lca.attend_ws(1, 1, Hq, D, k, W), 16), dtype=torch.uint8, device=dev)
+    win = x[:, L - W:].contiguous()                   # the window: the last 128 raw tokens
+    wb = torch.zeros(1, 1, dtype=torch.int32, device=dev)
+    wlen = torch.full((1, 1), W, dtype=torch.int32, device=dev)
+    tok, row, one = i32(L - 4), i64(N - 1), i32(1)
+
+    def step():
+        lca.csa_compress(x, gate, bias, 4, tok, one, row, 1, ent, lca.F32)
+        lca.csa_compress(xi, gate_i, bias_i, 4, tok, one, row, 1, key, lca.F32)
+        lca.lightning_index_topk(qi, None, w, key, None, n, k, idx, ws_i)
+        lca.sparse_mqa_attend(q, ent, None, idx, win, wb, wlen, sink, c["tau"], out, ws=ws_a)
+
+    ms = time_graph(step, reps)
+    st = stats_us(ms)
+    return {"workload": "small_csa_decode: CSA decode fp32, 1 query, 4096 tokens -> 1024 entries, 16 heads, "
+                        "indexer 4x64, top-64, window 128",
+            "us_per_step": st, "decode_tokens_per_s": round(1e6 / st["median"], 1),
+            "schedule": "csa_compress x2 (newest block), lightning_index_topk, sparse_mqa_attend; graph replays",
+            "bound": "latency (0.37 MB per step; a roofline fraction is not meaningful at this size)"}
+
+
+def run_hca_decode(reps: int):
+    """HCA decode in bf16: 8 sequences of 65536 tokens.  The cache build
+    (hca_compress over every token, 128x -> 512 bf16 entries per sequence) is
+    timed as an HBM-bound kernel; the decode step pools the newest block and
+    attends densely over the 512 entries + window 128 (graph replays)."""
+    import torch
+    import long_context_attention_13_amd as lca
+    import synth
+    dev = torch.device("cuda:0")
+    c = synth.hca_decode_bf16()
+    B, L, D, Hq, W, m = c["B"], c["L"], c["D"], c["Hq"], c["W"], c["m"]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = t(c["x"]).to(torch.bfloat16)
+    gate, bias, q, sink = t(c["gate"]), t(c["bias"]), t(c["q"]).to(torch.bfloat16), t(c["sink"])
+    del c["x"]
+    nb = L // m
+    i32 = lambda v: torch.full((B,), v, dtype=torch.int32, device=dev)
+    i64 = lambda v: torch.full((B,), v, dtype=torch.int64, device=dev)
+    cache = torch.empty(B, nb, D, dtype=torch.bfloat16, device=dev)
+    build = lambda: lca.hca_compress(x, gate, bias, m, i32(0), i32(nb), i64(0), nb, cache, lca.BF16)
+    stream = torch.cuda.current_stream()
+    build()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    ev[0].record(stream)
+    for i in range(10):
+        build()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    bms = [ev[i].elapsed_time(ev[i + 1]) for i in range(10)]
+    build_bytes = B * L * D * 2 + B * L * 4 + B * nb * D * 2
+    n = torch.full((B, 1), nb, dtype=torch.int32, device=dev)
+    win = x[:, L - W:].contiguous()                   # the window: the last 128 raw tokens
+    wb = torch.zeros(B, 1, dtype=torch.int32, device=dev)
+    wlen = torch.full((B, 1), W, dtype=torch.int32, device=dev)
+    out = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(lca.attend_ws(B, 1, Hq, D, nb, W), 16), dtype=torch.uint8, device=dev)
+    tok, row, one = i32(L - m), i64(nb - 1), i32(1)
+    attend = lambda: lca.hca_attend(q, cache, None, n, win, wb, wlen, sink, c["tau"], out, ws=ws)
+
+    def step():
+        lca.hca_compress(x, gate, bias, m, tok, one, row, 1, cache, lca.BF16)
+        attend()
+
+    a = stats_us(time_graph(attend, reps))
+    s = stats_us(time_graph(step, reps))
+    bs = stats_us(bms)
+    step_bytes = B * (nb * D * 2 + W * D * 2 + 2 * Hq * D * 2 + m * D * 2 + m * 4 + D * 2)
+    return {"workload": "hca_decode_bf16: 8 sequences x 65536 tokens, m'=128 -> 512 bf16 entries, 64 heads, "
+                        "window 128",
+            "hca_attend_us": a, "decode_step_us": s, "decode_tokens_per_s": round(B * 1e6 / s["median"], 1),
+            "step_algorithmic_mb": round(step_bytes / 1e6, 3),
+            "schedule": "hca_compress (newest block) + hca_attend; graph replays",
+            "cache_build": {"kernel": "pool_encode_kernel (hca_compress, 4096 blocks of 128 tokens)", "us": bs,
+                            "algorithmic_mb": round(build_bytes / 1e6, 2),
+                            "gbs": round(build_bytes / (bs["median"] * 1e-6) / 1e9, 1),
+                            "frac_of_hbm_peak": round(build_bytes / (bs["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def run_csa_fp8(reps: int, copies: int):
+    """CSA decode: 16 sequences of 131072 tokens, 32768 FP8 entries and MXFP4
+    keys (8 x 128) each, top-512, window 128, 64 heads; copies rotate so each
+    step reads HBM.  One step = indexer + top-k and sparse attention (one
+    decode_step call), one graph per copy."""
+    import torch
+    import long_context_attention_13_amd as lca
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1003)
+    B, N, D, d_I, H_I, Hq, k, W = 16, 32768, 128, 128, 8, 64, 512, 128
+    zB, zB64 = torch.zeros(B, dtype=torch.int32, device=dev), torch.zeros(B, dtype=torch.int64, device=dev)
+    bias1 = torch.zeros(1, device=dev)
+
+    def encode(rows, dim, dt):
+        x = torch.randn(B, rows, dim, generator=g, device=dev)
+        if dt == lca.FP8E4M3:
+            dst = torch.empty(B, rows, dim, dtype=torch.uint8, device=dev)
+            sc = torch.empty(B, rows, dim // 64, device=dev)
+        else:
+            dst = torch.empty(B, rows, dim // 2, dtype=torch.uint8, device=dev)
+            sc = torch.empty(B, rows, dim // 32, dtype=torch.uint8, device=dev)
+        lca.csa_compress(x, torch.zeros(B, rows, device=dev), bias1, 1, zB, torch.full((B,), rows, dtype=torch.int32,
+                         device=dev), zB64, rows, dst, dt, sc)
+        return dst, sc
+
+    caches = [encode(N, D, lca.FP8E4M3) + encode(N, d_I, lca.MXFP4) for _ in range(copies)]
+    qi_raw = torch.randn(B, H_I, d_I, generator=g, device=dev)
+    qi = torch.empty(B, 1, H_I, d_I // 2, dtype=torch.uint8, device=dev)
+    qi_sc = torch.empty(B, 1, H_I, d_I // 32, dtype=torch.uint8, device=dev)
+    lca.csa_compress(qi_raw, torch.zeros(B, H_I, device=dev), bias1, 1, zB, torch.full((B,), H_I, dtype=torch.int32,
+                     device=dev), zB64, H_I, qi.view(B, H_I, d_I // 2), lca.MXFP4, qi_sc.view(B, H_I, d_I // 32))
+    w = torch.rand(B, 1, H_I, generator=g, device=dev)
+    q = torch.randn(B, 1, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+    win = torch.randn(B, W, D, generator=g, device=dev).to(torch.bfloat16)
+    sink = torch.randn(Hq, generator=g, device=dev)
+    n = torch.full((B, 1), N, dtype=torch.int32, device=dev)
+    wb = torch.zeros(B, 1, dtype=torch.int32, device=dev)
+    wlen = torch.full((B, 1), W, dtype=torch.int32, device=dev)
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
+    out = torch.empty(B, 1, Hq, D, dtype=torch.bfloat16, device=dev)
+    ws_i = torch.empty(lca.index_topk_ws(B, 1, H_I, d_I, N, k), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(lca.attend_ws(B, 1, Hq, D, k, W), 16), dtype=torch.uint8, device=dev)
+    tau = 1 / math.sqrt(128.0)
+    jobs = []
+    for e, es, kc, ks in caches:
+        jobs.append((lca.index_job(qi, qi_sc, w, kc, ks, n, k, idx, ws_i),
+                     [lca.attend_job(True, q, e, es, idx, win, wb, wlen, sink, tau, out, ws=ws_a)]))
+    stream = torch.cuda.current_stream()
+    graphs = []
+    for ij, aj in jobs:
+        lca.decode_step([], ij, aj)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            lca.decode_step([], ij, aj)
+        graphs.append(gr)
+    for gr in graphs:
+        gr.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        graphs[i % copies].replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    st = stats_us([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    step_bytes = B * (N * (d_I // 2 + d_I // 32) + H_I * (d_I // 2 + d_I // 32) + H_I * 4 + k * 4
+                      + k * (D + 8) + W * D * 2 + 2 * Hq * D * 2)
+    gbs = step_bytes / (st["median"] * 1e-6) / 1e9
+    del caches, jobs, graphs
+    torch.cuda.empty_cache()
+    return {"workload": "csa_decode_fp8: 16 sequences x 131072 tokens, 32768 FP8 entries + MXFP4 indexer keys "
+                        "(8x128), top-512, window 128, 64 heads",
+            "us_per_step": st, "decode_tokens_per_s": round(B * 1e6 / st["median"], 1),
+            "algorithmic_mb_per_step": round(step_bytes / 1e6, 2), "hbm_gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "copies": copies,
+            "schedule": "decode_step (indexer + top-512, sparse attention), one graph per cache copy"}
+
+
+def cpu_prefill_subset(rows: int):
+    """The oracle on a seeded subset of the chunked-prefill queries (the first,
+    the last and rows - 2 others): compression of the whole chunk, indexer +
+    top-1024 and both attentions for those rows, timed and scaled to the 8192
+    queries ("subset x scale"); and the GPU's outputs for the same rows
+    against it."""
+    import torch
+    import oracle
+    pw = PrefillWorkload()
+    pw.compress(); pw.index(); pw.attend()
+    torch.cuda.synchronize()
+    T = pw.T
+    g = np.random.default_rng(1005)
+    sel = np.unique(np.concatenate([[0, T - 1], g.choice(np.arange(1, T - 1), rows - 2, replace=False)]))
+    host = lambda t: t.cpu().numpy()
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    key, key_sc = host(pw.key), host(pw.key_sc)
+    ent, hca = bits(pw.ent), bits(pw.hca)
+    win = bits(pw.win)
+    qi = oracle.decode(host(pw.qi)[:, sel], oracle.MXFP4, host(pw.qi_sc)[:, sel])
+    w = host(pw.w)[:, sel]
+    q = oracle.decode(bits(pw.q)[:, sel], oracle.BF16)
+    n_csa, n_hca = host(pw.n_csa)[:, sel], host(pw.n_hca)[:, sel]
+    wb, wl_ = host(pw.wb)[:, sel], host(pw.wl)[:, sel]
+    sink_c, sink_h = host(pw.sink_csa), host(pw.sink_hca)
+    xw, xi = oracle.decode(win, oracle.BF16), oracle.decode(bits(pw.xi), oracle.BF16)
+    gate, gate_i, gate2 = host(pw.gate), host(pw.gate_i), host(pw.gate2)
+    b4, bi4, b128 = host(pw.bias), host(pw.bias_i), host(pw.bias2)
+    g_idx = host(pw.idx)[:, sel]
+    g_c, g_h = bits(pw.out_csa)[:, sel], bits(pw.out_hca)[:, sel]
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    t_ = 127                                          # the chunk's first raw token in the window buffer
+    for x, gt, bs_, m, dt in ((xw, gate, b4, 4, oracle.BF16), (xi, gate_i, bi4, 4, oracle.MXFP4),
+                              (xw, gate2, b128, 128, oracle.BF16)):
+        pooled = oracle.pool(x[0, t_:t_ + T], gt[0, t_:t_ + T], bs_, m)
+        oracle.encode(pooled.astype(np.float32)[None], dt)
+    t_cmp = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    idx, _ = oracle.index_topk(qi, w, key, oracle.MXFP4, key_sc, n_csa, pw.k)
+    o_c, _ = oracle.attend(q, ent, oracle.BF16, None, idx, None, win, oracle.BF16, wb, wl_, sink_c, pw.tau)
+    o_h, _ = oracle.attend(q, hca, oracle.BF16, None, None, n_hca, win, oracle.BF16, wb, wl_, sink_h, pw.tau)
+    t_rows = time.perf_counter() - t1
+    scale = T / len(sel)
+    total = t_cmp + t_rows * scale
+    worst = 0.0
+    for got, ref in ((g_c, o_c), (g_h, o_h)):
+        got = oracle.decode(got, oracle.BF16)
+        tol = 2e-2 * (np.abs(ref) + np.abs(ref).max(-1, keepdims=True))
+        worst = max(worst, float((np.abs(got - ref) / tol).max()))
+    idx_ok = bool(np.array_equal(g_idx, idx))
+    del pw
+    torch.cuda.empty_cache()
+    model, ncpu = host_cpu()
+    return {"value": round(T / total, 2), "unit": "prefill tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cpus": ncpu,
+            "sample": f"subset x scale: the whole chunk's compression ({t_cmp:.2f} s) + indexer, top-1024 and both "
+                      f"attentions for {len(sel)} of {T} queries ({t_rows:.2f} s, first and last included), "
+                      f"scaled by {scale:.1f}",
+            "parity": {"rows": len(sel), "index_sets_bit_exact": idx_ok,
+                       "attention_max_err_over_tol": round(worst, 4), "rtol": 2e-2,
+                       "status": "ok" if idx_ok and worst <= 1.0 else "failed"}}
 
 
 def main():
@@ -829,6 +1250,10 @@ def main():
     if args.loop_only:
         print(json.dumps({"decode_loop": run_loop(args.copies, args.steps)}))
         return
+    if args.legs_only:
+        print(json.dumps({"small_csa_decode": run_small_csa(200), "hca_decode_bf16": run_hca_decode(200),
+                          "csa_decode_fp8": run_csa_fp8(200, args.copies)}))
+        return
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
@@ -847,66 +1272,56 @@ def main():
     torch.cuda.synchronize()
     graphs = None
     if not args.no_graph:
-        # one captured graph holds C consecutive steps (one per cache copy);
-        # replaying it issues C steps without per-launch host work
-        args.steps = -(-args.steps // C) * C
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for c in range(C):
+        # one captured graph per cache copy, each holding one step; replays
+        # issue a step without per-launch host work
+        graphs = []
+        for c in range(C):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
                 run(c)
-        graphs = [g]
-        for _ in range(max(1, args.warmup // C)):
-            g.replay()
+            graphs.append(g)
+        for s in range(max(args.warmup, C)):
+            graphs[s % C].replay()
         torch.cuda.synchronize()
 
-    # timed region: whole steps, plus events around the indexer call of each step
-    ev_idx = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: whole steps, an event after each
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
+    ev[0].record(stream)
     t_host = time.perf_counter()
     for s in range(args.steps):
-        c = s % C
         if graphs is not None:
-            if c == 0:
-                graphs[0].replay()
-        elif args.unbatched:
-            wl.compress(c)
-            ev_idx[s][0].record(stream)
-            wl.index(c)
-            ev_idx[s][1].record(stream)
-            wl.attend(c)
-        elif args.three_calls:
-            wl.step_batched(c, ev_idx[s])
+            graphs[s % C].replay()
         else:
-            wl.step_fused(c)
-    end.record(stream)
+            run(s % C)
+        ev[s + 1].record(stream)
     t_host = time.perf_counter() - t_host
     torch.cuda.synchronize()
-    roof_eager = graphs is not None or not (args.unbatched or args.three_calls)
-    if roof_eager:
-        # events cannot be recorded inside a captured graph here, and the decode-step
-        # call runs the indexer's scan inside one launch with the HCA attention: the
-        # indexer's launch duration comes from the same steps run eagerly as separate
-        # calls, events around the indexer call on its stream
-        for s in range(args.steps):
-            c = s % C
-            if args.unbatched:
-                wl.compress(c)
-                ev_idx[s][0].record(stream)
-                wl.index(c)
-                ev_idx[s][1].record(stream)
-                wl.attend(c)
-            else:
-                wl.step_batched(c, ev_idx[s])
-        torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    step_ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[args.steps])
     ms_step = total_ms / args.steps
+    value = wl.B * args.steps / (total_ms * 1e-3)
+    step_bytes = wl.step_bytes()
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    print("bench: self-check and per-launch timing", file=sys.stderr, flush=True)
+    # the timed form against the three calls, and the outputs for the oracle check
+    equal, gpu_out = self_check(wl, (lambda: graphs[0].replay()) if graphs is not None else (lambda: run(0)))
+    # per-launch durations (events between the step's launches), eager steps
+    launches = launch_profile(wl, max(args.steps, 50))
+    lb = wl.launch_bytes()
+    for l in launches:
+        b = lb.get(l["kernel"])
+        l["algorithmic_mb"] = None if b is None else round(b / 1e6, 3)
+        l["gbs"] = None if b is None else round(b / (l["us"] * 1e-6) / 1e9, 1)
+    dom = max(launches, key=lambda l: l["us"])
+    dom_bytes = lb.get(dom["kernel"])
+    # the indexer call alone (index_chunk_kernel + index_select_kernel), as three eager calls
+    ev_idx = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s in range(args.steps):
+        wl.step_batched(s % C, ev_idx[s])
+    torch.cuda.synchronize()
     idx_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_idx]))
     idx_bytes = wl.index_bytes()
-    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
-    step_gbs = wl.step_bytes() / (ms_step * 1e-3) / 1e9
-    value = wl.B * args.steps / (total_ms * 1e-3)
 
     res = {
         "metric": "CSA+HCA decode tokens/s at 1M ctx; % peak HBM BW; indexer MFMA util",
@@ -927,23 +1342,46 @@ def main():
                    "global_batch": wl.B, "seq_len": int(wl.L.max()), "parallelism": "single GPU"},
         "schedule": ("9 single calls" if args.unbatched else
                      "compress_batch (3 blocks) -> indexer -> attend_batch (CSA + HCA)" if args.three_calls else
-                     "decode_step (compress, indexer scan + HCA attention, selection, CSA attention, merge)")
-                    + (f", graph of {C} steps replayed" if graphs is not None else ", eager"),
+                     "decode_step (one call)")
+                    + (f", one graph per cache copy ({C} copies, {wl.copy_mb():.0f} MB each) replayed in turn"
+                       if graphs is not None else ", eager"),
+        "step_us": stats_us(step_ms),
         "host_issue_us_per_step": round(t_host / args.steps * 1e6, 1),
+        "step_algorithmic_mb": round(step_bytes / 1e6, 2),
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "lightning_index_topk (index_chunk_kernel + index_select_kernel)",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "avg_launch_us": round(idx_ms * 1e3, 2), "algorithmic_bytes": int(idx_bytes),
-                     "timed_in": "eager pass of the same steps as separate calls" if roof_eager
-                     else "the timed steps"},
+        "parity": {"graph_replay_vs_three_calls": "equal bytes" if equal else "differ",
+                   "status": "ok" if equal else "failed"},
+        "roofline": {"kernel": dom["kernel"], "bound": "hbm",
+                     "achieved": None if dom_bytes is None else round(dom_bytes / (dom["us"] * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": None if dom_bytes is None else round(dom_bytes / (dom["us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                                                  4),
+                     "traffic": recorded_traffic(dom["kernel"]),
+                     "avg_launch_us": dom["us"], "algorithmic_bytes": dom_bytes,
+                     "timed_in": "eager decode_step_events calls over the same rotating copies: HIP events "
+                                 "recorded by the library between the step's launches, on the launch stream"},
+        "launches": launches,
+        "indexer_call": {"kernels": "index_chunk_kernel + index_select_kernel (lightning_index_topk alone)",
+                         "us": round(idx_ms * 1e3, 2), "algorithmic_bytes": int(idx_bytes),
+                         "gbs": round(idx_bytes / (idx_ms * 1e-3) / 1e9, 1),
+                         "frac": round(idx_bytes / (idx_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "timed_in": "three eager calls per step (compress_batch, indexer, attend_batch), events "
+                                     "around the indexer call"},
     }
     if not args.no_cpu:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
-    del wl
+        res["cpu_baseline"] = cpu_baseline(wl, gpu_out, args.cpu_steps)
+        res["parity"]["oracle"] = res["cpu_baseline"]["parity"]
+        if res["cpu_baseline"]["parity"]["status"] != "ok":
+            res["parity"]["status"] = "failed"
+    del wl, graphs
     torch.cuda.empty_cache()
+    if not args.no_legs:
+        print("bench: small CSA, HCA bf16 and CSA FP8 decode legs", file=sys.stderr, flush=True)
+        res["small_csa_decode"] = run_small_csa(200)
+        res["hca_decode_bf16"] = run_hca_decode(200)
+        res["csa_decode_fp8"] = run_csa_fp8(200, args.copies)
     if not args.no_loop:
         print("bench: decode loop", file=sys.stderr, flush=True)
         res["decode_loop"] = run_loop(args.copies, 50)
@@ -959,6 +1397,9 @@ def main():
     if not args.no_prefill:
         print("bench: chunked prefill", file=sys.stderr, flush=True)
         res["prefill"] = run_prefill(args.prefill_steps, 2)
+        if not args.no_cpu:
+            print("bench: chunked prefill oracle subset", file=sys.stderr, flush=True)
+            res["prefill"]["cpu_baseline"] = cpu_prefill_subset(args.cpu_prefill_rows)
     print(json.dumps(res))
 
 

@@ -14,21 +14,23 @@ constexpr float LN2 = 0.6931471805599453f;
 // ATT_PREFILL_TQ query rows per sequence; its dense rows are then grouped to
 // share staged tiles) and for lists of at most two tiles; otherwise a row's
 // list (entries, then window tokens; its length is bounded by the capacity
-// n_kv_max + W_buf) is cut into at most ATT_MAX_SPLITS splits of a whole
-// number of 64-item tiles.  The plan depends on the call's list capacity and
-// query rows per sequence only -- never on the number of sequences, nor on
-// the data -- so a sequence gives the same bits in any batch (splits past a
-// row's actual list return at once and are not merged).
+// n_kv_max + W_buf) is cut into splits of a fixed size: one 64-item tile up
+// to 2048 items, two tiles beyond (decode lists are latency-bound, so short
+// splits spread them over many compute units), larger only when needed to
+// keep a row within the merge's 1024 splits.  The plan depends on the call's
+// list capacity and query rows per sequence only -- never on the number of
+// sequences, nor on the data -- so a sequence gives the same bits in any
+// batch (splits past a row's actual list return at once and are not merged).
 struct Plan { int S; int items; };
 
 constexpr int ATT_PREFILL_TQ = 64;
-constexpr int ATT_MAX_SPLITS = 16;
+constexpr int ATT_MAX_SPLITS = 1024;
 
 inline Plan att_plan(int64_t Tq, int64_t n_kv_max, int64_t W_buf) {
   const int64_t L = n_kv_max + W_buf;
   if (Tq >= ATT_PREFILL_TQ || L <= 128) return Plan{1, (int)(L < 1 ? 1 : L)};
-  const int64_t tiles = (L + 63) / 64;
-  const int64_t items = (tiles + ATT_MAX_SPLITS - 1) / ATT_MAX_SPLITS * 64;
+  int64_t items = L <= 2048 ? 64 : 128;
+  if ((L + items - 1) / items > ATT_MAX_SPLITS) items = (L + 64 * ATT_MAX_SPLITS - 1) / (64 * ATT_MAX_SPLITS) * 64;
   return Plan{(int)((L + items - 1) / items), (int)items};
 }
 
