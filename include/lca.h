@@ -381,6 +381,30 @@ lca_status lca_decode_step_events(const lca_compress_job* cjobs, int32_t ncjobs,
                                   const char** names, int32_t* nlaunch, void* stream);
 
 /*
+ * lca_decode_step_noalloc -- lca_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same call, with every workspace taken from a
+ * scratch array that the library holds in each GPU's memory
+ * (LCA_NOALLOC_SCRATCH_BYTES per device, from the first call on that device
+ * until the process ends) instead of from the jobs' ws / ws_bytes fields,
+ * which are ignored.  Same results as lca_decode_step.  The call uses the
+ * scratch of the current device (the stream must belong to it); it allocates
+ * nothing.
+ *   Errors: those of lca_decode_step; LCA_EWORKSPACE when the step's
+ *   workspaces (the sizes lca_index_topk_ws and lca_attend_ws return, each
+ *   rounded up to 256 bytes) exceed LCA_NOALLOC_SCRATCH_BYTES, before
+ *   anything is enqueued.
+ * Every call on one GPU uses that GPU's scratch, and the scratch keeps the
+ * last call's contents: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.  Nothing in the scratch
+ * needs to start at zero (the kernels initialise what they read).
+ */
+#define LCA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+lca_status lca_decode_step_noalloc(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
+                                   const lca_attend_job* ajobs, int32_t najobs, void* stream);
+
+/*
  * lca_decode_append -- the token append of a decode loop, for several raw-token
  * streams in one launch (for example a CSA layer's raw KV, its indexer's raw
  * keys and an HCA layer's raw KV): each sequence's new token goes into the

@@ -24,7 +24,7 @@ STATUS = {0: "LCA_OK", 1: "LCA_EINVAL", 2: "LCA_ENOTSUP", 3: "LCA_EHIP", 4: "LCA
 EXPORTS = ["lca_abi_version", "lca_last_error", "lca_csa_compress", "lca_hca_compress", "lca_compress_batch",
            "lca_lightning_index_topk", "lca_index_topk_ws", "lca_sparse_mqa_attend",
            "lca_hca_attend", "lca_attend_batch", "lca_attend_ws", "lca_decode_step", "lca_decode_append", "lca_window_attend",
-           "lca_decode_loop_step", "lca_attend_separate_v", "lca_decode_step_events"]
+           "lca_decode_loop_step", "lca_attend_separate_v", "lca_decode_step_events", "lca_decode_step_noalloc"]
 MAX_STEP_LAUNCHES = 8
 MAX_COMPRESS_JOBS = 8
 MAX_ATTEND_JOBS = 4
@@ -71,6 +71,9 @@ def load(path: str = LIB_PATH):
     L.lca_decode_step.restype = i32
     L.lca_decode_step.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
                                   ctypes.POINTER(AttendJob), i32, vp]
+    L.lca_decode_step_noalloc.restype = i32
+    L.lca_decode_step_noalloc.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
+                                          ctypes.POINTER(AttendJob), i32, vp]
     L.lca_decode_step_events.restype = i32
     L.lca_decode_step_events.argtypes = [ctypes.POINTER(CompressJob), i32, ctypes.POINTER(IndexJob),
                                          ctypes.POINTER(AttendJob), i32, ctypes.POINTER(vp), i32,
@@ -257,6 +260,15 @@ def decode_step(cjobs, ijob, ajobs, stream=None):
     aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
     ij = None if ijob is None else ctypes.byref(ijob)
     _check(load().lca_decode_step(ca, len(cjobs), ij, aa, len(ajobs), _stream(stream)))
+
+
+def decode_step_noalloc(cjobs, ijob, ajobs, stream=None):
+    """decode_step with every workspace taken from the library's per-GPU
+    scratch (see lca_decode_step_noalloc); the jobs' ws fields are ignored."""
+    ca = cjobs if isinstance(cjobs, ctypes.Array) else (CompressJob * max(1, len(cjobs)))(*cjobs)
+    aa = ajobs if isinstance(ajobs, ctypes.Array) else (AttendJob * max(1, len(ajobs)))(*ajobs)
+    ij = None if ijob is None else ctypes.byref(ijob)
+    _check(load().lca_decode_step_noalloc(ca, len(cjobs), ij, aa, len(ajobs), _stream(stream)))
 
 
 def decode_step_events(cjobs, ijob, ajobs, events, stream=None):

@@ -26,7 +26,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
-SOURCES = ["compress.hip", "index.hip", "index_prefill.hip", "attend.hip", "attend_dense.hip", "step.hip", "append.hip", "abi.cpp"]
+SOURCES = ["compress.hip", "index.hip", "index_prefill.hip", "attend.hip", "attend_dense.hip", "step.hip", "append.hip", "noalloc.hip", "abi.cpp"]
 # per-source flags: keep MFMA results in ordinary VGPRs (the score kernel's
 # epilogue reads every result; accumulation-register copies would double it)
 EXTRA = {"index_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -28,6 +28,8 @@ lca_status ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 #define REQ(cond, st, ...) \
   do {                      \
     if (!(cond)) return fail(st, __VA_ARGS__); \
@@ -347,6 +349,63 @@ lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const 
   lca::AttendBatch ab;
   st = attend_batch_check(name, ajobs, najobs, 0, &ab);
   if (st != LCA_OK) return st;
+  return hip_status(lca::launch_decode_step(nullptr, nullptr, cb, ia, ab, (hipStream_t)stream), name);
+}
+
+lca_status lca_decode_step_noalloc(const lca_compress_job* cjobs, int32_t ncjobs, const lca_index_job* ijob,
+                                   const lca_attend_job* ajobs, int32_t najobs, void* stream) {
+  const char* name = "lca_decode_step_noalloc";
+  static_assert(LCA_NOALLOC_SCRATCH_BYTES == lca::NOALLOC_SCRATCH_BYTES, "scratch sizes agree");
+  REQ(najobs >= 0 && najobs <= LCA_MAX_ATTEND_JOBS, LCA_EINVAL, "%s: njobs=%d outside [0, %d]", name, najobs,
+      LCA_MAX_ATTEND_JOBS);
+  REQ(najobs == 0 || ajobs != nullptr, LCA_EINVAL, "%s: jobs is NULL", name);
+  // the workspaces, one after another in the scratch (256-byte aligned)
+  lca_index_job I{};
+  lca_attend_job A[LCA_MAX_ATTEND_JOBS];
+  size_t off[1 + LCA_MAX_ATTEND_JOBS] = {}, need = 0;
+  if (ijob != nullptr) {
+    I = *ijob;
+    I.ws_bytes = (I.B > 0 && I.Tq > 0) ? lca_index_topk_ws(I.B, I.Tq, I.H_I, I.d_I, I.N_cap, I.k) : 0;
+    off[0] = need;
+    need += round256(I.ws_bytes);
+  }
+  for (int j = 0; j < najobs; ++j) {
+    A[j] = ajobs[j];
+    const bool rows = (int64_t)A[j].B * A[j].Tq > 0 && A[j].B > 0 && A[j].Tq > 0;
+    A[j].ws_bytes = rows ? lca_attend_ws(A[j].B, A[j].Tq, A[j].Hq, A[j].D, A[j].sparse ? A[j].k : A[j].N_cap,
+                                         A[j].W_buf)
+                         : 0;
+    off[1 + j] = need;
+    need += round256(A[j].ws_bytes);
+  }
+  REQ(need <= LCA_NOALLOC_SCRATCH_BYTES, LCA_EWORKSPACE,
+      "%s: the step needs %zu bytes of scratch; the library holds %zu per device (use lca_decode_step with "
+      "caller workspaces)", name, need, (size_t)LCA_NOALLOC_SCRATCH_BYTES);
+  // validation with stand-in workspace addresses: nothing touches the GPU
+  // before every job is valid
+  const uintptr_t standin = (uintptr_t)1 << 12;
+  I.ws = (void*)(standin + off[0]);
+  for (int j = 0; j < najobs; ++j) A[j].ws = (void*)(standin + off[1 + j]);
+  lca::CompressBatch cb;
+  lca_status st = compress_batch_check(name, cjobs, ncjobs, 0, &cb);
+  if (st != LCA_OK) return st;
+  lca::IndexArgs ia{};
+  if (ijob != nullptr) {
+    st = index_check("lca_decode_step_noalloc: index job", I.qi, I.qi_dt, I.qi_scale, I.w, I.ki, I.ki_dt, I.ki_scale,
+                     I.n_elig, I.B, I.Tq, I.H_I, I.d_I, I.N_cap, I.k, I.idx_out, I.score_out, I.ws, I.ws_bytes, &ia);
+    if (st != LCA_OK) return st;
+  }
+  lca::AttendBatch ab;
+  st = attend_batch_check(name, A, najobs, 0, &ab);
+  if (st != LCA_OK) return st;
+  // the current device's scratch (when a workspace is needed at all)
+  if (need > 0) {
+    void* base = nullptr;
+    st = hip_status(lca::noalloc_scratch(&base), name);
+    if (st != LCA_OK) return st;
+    if (ijob != nullptr) ia.ws = (char*)base + off[0];
+    for (int j = 0; j < najobs; ++j) ab.job[j].ws = (char*)base + off[1 + j];
+  }
   return hip_status(lca::launch_decode_step(nullptr, nullptr, cb, ia, ab, (hipStream_t)stream), name);
 }
 

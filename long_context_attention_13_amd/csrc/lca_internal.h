@@ -108,6 +108,13 @@ struct AppendMap {
 hipError_t launch_append_compress(const AppendBatch& ab, const AppendMap& mp, const CompressBatch& cb,
                                   hipStream_t s);
 
+// Scratch memory of the allocation-free decode step: a file-scope device
+// array of NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.
+// noalloc_scratch returns the current device's copy (its address is resolved
+// once per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Events recorded on the launch stream around the launches of a decode step
 // (measurement): ev[0] before the first launch, ev[i] after launch i, whose
 // kernel names[i - 1] names.  At most cap - 1 launches are logged.

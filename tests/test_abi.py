@@ -248,6 +248,22 @@ def test_decode_step_events_validation(L):
     assert b"index job" in L.lca_last_error() and n.value == -1
 
 
+def test_decode_step_noalloc_validation(L):
+    """The allocation-free step validates as the step does and rejects a step
+    whose workspaces exceed the library's scratch before touching the GPU."""
+    ca = (lca.CompressJob * 1)(batch_job(B=0))
+    aa = (lca.AttendJob * 1)(attend_job(B=0))
+    call = lambda ij, na=1: L.lca_decode_step_noalloc(ca, 1, None if ij is None else ctypes.byref(ij), aa, na, None)
+    big = index_job(B=256, N_cap=1 << 24, k=1024)
+    assert L.lca_index_topk_ws(256, 1, 8, 128, 1 << 24, 1024) > 64 << 20
+    assert call(big) == 4
+    assert b"scratch" in L.lca_last_error()
+    assert call(index_job(k=0)) == 1
+    assert b"index job" in L.lca_last_error()
+    assert call(None, na=5) == 1
+    assert call(index_job(B=0)) == 0                 # nothing to do: no GPU call
+
+
 def append_job(**kw):
     a = dict(x_new=FAKE, x_dt=lca.BF16, g_new=FAKE, ring=FAKE, gring=FAKE, R=256, len=FAKE, m=4, W=128,
              x_tok0=FAKE, nblk=FAKE, dst_row0=FAKE, n_elig=FAKE, win_begin=FAKE, win_len=FAKE, B=2, D=128)
