@@ -69,6 +69,15 @@ struct ChunkShared {
   uint64_t thr_s[NQ], top_s[NQ];
 };
 
+// Rounds of key tiles a wavefront keeps in flight (each round: 64 keys, 21
+// registers per lane): the decode scan is bound by memory latency, so the
+// deeper the ring the closer to the HBM rate.
+constexpr int SCAN_DEPTH = 2;
+constexpr int scan_depth(int KPL, int NQ) {
+  const int d = NQ == 1 ? SCAN_DEPTH : 2;
+  return d < KPL / 4 ? d : (KPL / 4 < 2 ? 2 : KPL / 4);
+}
+
 // Chunk c of query-row group g: one workgroup of 256 threads.
 template <int DT, int KPL, int HP, int NQ>
 __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs& W, int NCH, int groups_per_b,
@@ -106,11 +115,15 @@ __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs
   const int jl = min((int)A.N_cap, jbeg + CH);
   const int jw = jbeg + wave * RPW * 64;    // this wavefront's first entry
   MxRows R{};
-  MxTiles cur, nxt;
+  // SD rounds of key tiles in flight per wavefront (a ring of stages; all
+  // indices are compile-time constants once the round loop is unrolled)
+  constexpr int SD = scan_depth(KPL, NQ);
+  MxTiles st[SD];
   if (DT == DT_MXFP4) {
     R = mx_rows(A, rw.b, min(jw, jl - 1));
     __builtin_amdgcn_sched_barrier(0);
-    mx_load_round(A, R, min(jw, jl), jl, cur);
+#pragma unroll
+    for (int i = 0; i + 1 < SD; ++i) mx_load_round(A, R, min(jw + i * 64, jl), jl, st[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (rw.r[1] < 0) rw.n[1] = 0;
@@ -129,16 +142,16 @@ __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs
     mx_query_finish(QR, Q);
     MxW<HP, NQ> Wt;
     mx_load_weights<HP, NQ>(wl, Wt);
-    // two-stage pipeline: the next round's tiles load while this one is scored
+    // the round SD-1 ahead loads while this one is scored
     uint32_t fix = 0;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       uint64_t kk[NQ];
       bool ix;
-      if (rr + 1 < RPW) mx_load_round(A, R, min(jw + (rr + 1) * 64, jl), jl, nxt);
+      if (rr + SD - 1 < RPW) mx_load_round(A, R, min(jw + (rr + SD - 1) * 64, jl), jl, st[(rr + SD - 1) % SD]);
+      MxTiles& cur = st[rr % SD];
       if (F.j >= jw + rr * 64 && F.j < jw + rr * 64 + 64) mx_patch_round(cur, min(jw + rr * 64, jl), jl, F, A.d);
       mx_score_round<HP, NQ>(A, rw, Q, cur, jw + rr * 64, tbuf[wave], Wt, kk, ix);
-      if (rr + 1 < RPW) cur = nxt;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) kq[q][rr] = kk[q];
       fix |= __ballot(ix) ? 1u << rr : 0u;
