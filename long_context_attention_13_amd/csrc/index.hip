@@ -172,12 +172,18 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
     __syncthreads();
     if (!(flags & 1) && total <= CMAX && total >= kk && gmax >= gmin) {
       // Every thread holds up to LB candidates in registers: item i =
-      // u*SEL_THREADS + tid in candidate order (ascending entry index).
+      // u*SEL_THREADS + tid of the candidates in dense order (ascending entry
+      // index), present when i < total; the slots u >= nu are empty in every
+      // thread and are skipped by all the passes below.
+      const int nu = __builtin_amdgcn_readfirstlane((total + SEL_THREADS - 1) / SEL_THREADS);
       uint64_t bk[LB];
       int32_t bj[LB];
       uint32_t vm = 0;
       if (!(flags & 2)) {
-        // staged layout (slot c*SPEC + e of chunk c): valid when e < count
+        // staged layout (slot c*SPEC + e of chunk c, valid when e < count):
+        // compacted in place to the dense order (all slots read, then the
+        // valid ones written at off[c] + e)
+        int dpos[LB];
 #pragma unroll
         for (int u = 0; u < LB; ++u) {
           const int i = u * SEL_THREADS + threadIdx.x;
@@ -186,7 +192,18 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
           const bool ok = c < nch && e < S.off[cc + 1] - S.off[cc];
           bk[u] = ckey_l[i];
           bj[u] = cidx_l[i];
-          vm |= (uint32_t)ok << u;
+          dpos[u] = ok ? S.off[cc] + e : -1;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < LB; ++u)
+          if (dpos[u] >= 0) { ckey_l[dpos[u]] = bk[u]; cidx_l[dpos[u]] = bj[u]; }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          const int i = u * SEL_THREADS + threadIdx.x;
+          if (u < nu) { bk[u] = ckey_l[i]; bj[u] = cidx_l[i]; }
+          vm |= (uint32_t)(i < total) << u;
         }
       } else {
         // some chunk has more than SPEC candidates: gather all of them in
@@ -209,10 +226,11 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
           vm |= (uint32_t)(i < total) << u;
         }
       }
-      RegSrc src{bk, bj, vm};
-      // first radix digit: the 11 bits below the common prefix of the range
+      RegSrc src{bk, bj, vm, nu};
+      // first radix digit: the (at most) 9 bits below the common prefix of
+      // the range
       const int hb = gmax == gmin ? -1 : 63 - __clzll(gmax ^ gmin);
-      int shift = hb + 1 > 11 ? hb + 1 - 11 : 0;
+      int shift = hb + 1 > 9 ? hb + 1 - 9 : 0;
       const int nb = hb + 1 - shift;
       uint64_t mask = (hb + 1 >= 64) ? 0 : ~((1ull << (hb + 1)) - 1ull);
       uint64_t prefix = gmax & mask;
@@ -227,34 +245,35 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
         th.T = gmax; th.low = 0; ties = rem; have = true; tie_break = total > rem;
       } else {
         // digit holding the rem-th largest, found by one wavefront: lane l
-        // holds the 32 bins nbins-1-32l .. nbins-32-32l (counted from the top)
+        // holds the 8 bins nbins-1-8l .. nbins-8-8l (counted from the top)
         if (wave == 0) {
+          constexpr int BPL = 8;
           const int nbins = 1 << nb;
-          const int hi = nbins - 1 - 32 * lane;
-          uint32_t hb32[32];
-          if (hi >= 31) {
-            const uint4* hp = (const uint4*)&S.hist[hi - 31];
+          const int hi = nbins - 1 - BPL * lane;
+          uint32_t hb8[BPL];
+          if (hi >= BPL - 1) {
+            const uint4* hp = (const uint4*)&S.hist[hi - (BPL - 1)];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < BPL / 4; ++q) {
               const uint4 h = hp[q];
-              hb32[4 * q] = h.x; hb32[4 * q + 1] = h.y; hb32[4 * q + 2] = h.z; hb32[4 * q + 3] = h.w;
+              hb8[4 * q] = h.x; hb8[4 * q + 1] = h.y; hb8[4 * q + 2] = h.z; hb8[4 * q + 3] = h.w;
             }
           } else {
 #pragma unroll
-            for (int q = 0; q < 32; ++q) hb32[q] = (hi - 31 + q >= 0) ? S.hist[hi - 31 + q] : 0u;
+            for (int q = 0; q < BPL; ++q) hb8[q] = (hi - (BPL - 1) + q >= 0) ? S.hist[hi - (BPL - 1) + q] : 0u;
           }
-          int cnt32 = 0;
+          int cnt8 = 0;
 #pragma unroll
-          for (int q = 0; q < 32; ++q) cnt32 += (int)hb32[q];
-          const int inc = wave_incl_scan_dpp(cnt32);
-          if (inc - cnt32 < rem && inc >= rem) {
-            int above = inc - cnt32;
+          for (int q = 0; q < BPL; ++q) cnt8 += (int)hb8[q];
+          const int inc = wave_incl_scan_dpp(cnt8);
+          if (inc - cnt8 < rem && inc >= rem) {
+            int above = inc - cnt8;
             bool found = false;
 #pragma unroll
-            for (int q = 31; q >= 0; --q) {
-              const int cb = (int)hb32[q];
+            for (int q = BPL - 1; q >= 0; --q) {
+              const int cb = (int)hb8[q];
               if (!found && above + cb >= rem) {
-                S.bcast[0] = hi - 31 + q; S.bcast[1] = above; S.bcast[2] = cb;
+                S.bcast[0] = hi - (BPL - 1) + q; S.bcast[1] = above; S.bcast[2] = cb;
                 found = true;
               }
               above += cb;
@@ -295,7 +314,7 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
         if (th.low > 0) unsafe = (mv[0] >> th.low) >= (th.T >> th.low);
         else unsafe = mv[0] >= th.T;
       }
-      done = emit_regs(bk, bj, vm, th, tie_break ? ties : -1, unsafe, A.k, out, sout, S);
+      done = emit_regs(bk, bj, vm, nu, th, tie_break ? ties : -1, unsafe, A.k, out, sout, S);
     }
   }
   if (!done) {

@@ -654,15 +654,18 @@ __device__ void emit_sorted(Src& src, const Thr& th, int n, int k, int32_t* out,
 }
 
 // Candidates held in registers: item u of this thread is present when bit u
-// of vm is set.
+// of vm is set; slots u >= nu (uniform over the workgroup) are empty.
 struct RegSrc {
   uint64_t (&key)[LB];
   int32_t (&j)[LB];
   uint32_t vm;
+  int nu;
   template <class F> __device__ __forceinline__ void for_each(F&& f) {
 #pragma unroll
-    for (int u = 0; u < LB; ++u)
+    for (int u = 0; u < LB; ++u) {
+      if (u >= nu) break;
       if ((vm >> u) & 1u) f(key[u], j[u]);
+    }
   }
 };
 
@@ -733,7 +736,7 @@ __device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n
 // u*SEL_THREADS + tid belongs to pass u; one exchange of per-(pass, wavefront)
 // counts of items above the threshold and of tied items gives every item its
 // output position.  Returns false (nothing written) when unsafe.
-__device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_t (&bj)[LB], uint32_t vm,
+__device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_t (&bj)[LB], uint32_t vm, int nu,
                                           const Thr& th, int ties, bool unsafe, int k, int32_t* out, double* sout,
                                           SelShared& S) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -745,6 +748,7 @@ __device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_
   const uint64_t Thi = th.low > 0 ? th.T >> th.low : 0ull;
 #pragma unroll
   for (int u = 0; u < LB; ++u) {
+    if (u >= nu) break;                   // empty in every thread
     const uint64_t key = bk[u];
     const bool valid = (vm >> u) & 1u;
     const bool gt = key > th.T, eq = key == th.T;
@@ -778,6 +782,7 @@ __device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_
   const int tot = S.bcast[5] + (ties >= 0 ? min(S.bcast[2], ties) : 0);
 #pragma unroll
   for (int u = 0; u < LB; ++u) {
+    if (u >= nu) break;
     const bool a = (fa >> u) & 1u, e = (fe >> u) & 1u;
     const uint64_t ba = __ballot(a), be = __ballot(e);
     if (a || e) {
