@@ -778,9 +778,9 @@ def run_variants(reps: int = 20):
     return out
 
 
-def run_prefill(steps: int, warmup: int):
+def run_prefill(steps: int, warmup: int, ctx: int = 262144):
     import torch
-    pw = PrefillWorkload()
+    pw = PrefillWorkload(ctx=ctx)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         pw.compress(); pw.index(); pw.attend()
@@ -800,8 +800,9 @@ def run_prefill(steps: int, warmup: int):
     t_att = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     t_cmp = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     fl_i, fl_a = pw.index_flops(), pw.attend_flops()
-    res = {"workload": "prefill_chunk: 8192 new bf16 tokens after a 262144-token context, CSA top-1024 "
-                       "(MXFP4 indexer 8x128) + HCA dense, window 128, 64 query heads",
+    res = {"workload": f"prefill_chunk: 8192 new bf16 tokens after a {ctx}-token context ({pw.N} CSA entries, "
+                       f"{pw.N2} HCA entries at the chunk's end), CSA top-1024 (MXFP4 indexer 8x128) + HCA dense, "
+                       "window 128, 64 query heads",
            "prefill_tokens_per_s": round(pw.T / (tot * 1e-3), 1), "ms_per_chunk": round(tot, 4),
            "ms_compress": round(t_cmp, 4), "ms_index": round(t_idx, 4), "ms_attend": round(t_att, 4),
            "indexer_mfma": {"bound": "mfma", "achieved": round(fl_i / (t_idx * 1e-3) / 1e12, 2),
@@ -1239,7 +1240,8 @@ def main():
         sys.exit(2)
     import torch
     if args.prefill_only:
-        print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2)}))
+        print(json.dumps({"prefill": run_prefill(args.prefill_steps, 2),
+                          "prefill_1m": run_prefill(args.prefill_steps, 2, ctx=(1 << 20) - 8192)}))
         return
     if args.variants_only:
         print(json.dumps({"compress_variants": run_variants()}))
@@ -1433,6 +1435,9 @@ def main():
     if not args.no_prefill:
         print("bench: chunked prefill", file=sys.stderr, flush=True)
         res["prefill"] = run_prefill(args.prefill_steps, 2)
+        # the chunk that ends a 1M-token context: 262144 CSA entries (the
+        # indexer's matrix-core path up to 2^20 entries)
+        res["prefill_1m"] = run_prefill(args.prefill_steps, 2, ctx=(1 << 20) - 8192)
         if not args.no_cpu:
             print("bench: chunked prefill oracle subset", file=sys.stderr, flush=True)
             res["prefill"]["cpu_baseline"] = cpu_prefill_subset(args.cpu_prefill_rows)

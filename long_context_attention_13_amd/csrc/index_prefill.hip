@@ -12,7 +12,9 @@
 //   sample  each row scores a strided sample of its eligible keys (one key in
 //           sigma) and takes the 64th largest sampled score, rounded down, as
 //           its candidate threshold t: about 64*sigma entries of the row
-//           reach it.
+//           reach it.  A workgroup samples 16 rows (the MFMA's columns), or
+//           fewer when the rows' samples would not fit its LDS (16 rows up
+//           to 4096 samples a row, 8 up to 8192, ... 2 up to 32768).
 //   score   a workgroup holds 64 query rows (16 per wavefront, the MFMA's
 //           column operand, one operand per indexer head) and streams a range
 //           of keys through LDS in stages of 512 (direct global->LDS loads,
@@ -44,12 +46,13 @@ constexpr int PF_CODE_B = PF_STAGE * 64;
 constexpr int PF_STAGE_B = PF_CODE_B + PF_STAGE * 4;
 constexpr int PF_NKC = 16;            // key ranges per row
 constexpr int PF_LCAP = 96;           // candidates per (row, key range, lane group)
-constexpr int PF_SMAX = 2560;         // sampled keys per row at most
+constexpr int PF_SROWS_LDS = 128 * 1024;     // LDS for the sampled scores of one sample workgroup
+constexpr int PF_SMAX = PF_SROWS_LDS / 2 / 2;  // sampled keys per row at most (2 rows a workgroup)
 constexpr int PF_RANK = 64;           // threshold = PF_RANK-th largest sampled score
 constexpr int PF_CAND = 3840;         // candidates per row the select pass holds
 constexpr int PF_CPL = PF_CAND / 64;  // ... per lane
 constexpr int PF_BAND = 64;           // band entries re-scored exactly
-constexpr int PF_NMAX = 32 * PF_SMAX; // largest key cache the prefill path takes
+constexpr int PF_NMAX = 32 * PF_SMAX; // largest key cache the prefill path takes (2^20 entries)
 constexpr int PF_FALLBACK_GRID = 128;
 constexpr int PF_SWAVES = 8;         // wavefronts of the sample workgroup (16 rows)
 
@@ -177,17 +180,25 @@ __device__ __forceinline__ void wave_lds_sync() {
 // for all 16 rows, keeping the top 16 bits of each fp32 score (rounded down)
 // in LDS; then each wave finds the thresholds of 4 rows.
 // ------------------------------------------------------------------------
+// Rows per sample workgroup: the most of 16, 8, 4, 2 whose samples (srow
+// 16-bit scores a row) fit PF_SROWS_LDS.
+static int pf_sample_rows(int srow) {
+  int sr = 16;
+  while (sr > 2 && (size_t)sr * srow * 2 > (size_t)PF_SROWS_LDS) sr >>= 1;
+  return sr;
+}
+
 template <int HP>
-__global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, PfWs W, int sigma, int srow) {
+__global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, PfWs W, int sigma, int srow, int sr) {
   extern __shared__ __align__(16) char smem[];
-  uint16_t* sc = (uint16_t*)smem;                                  // [16][srow]
-  uint32_t* hist = (uint32_t*)(smem + 16 * srow * 2);              // [PF_SWAVES][256]
+  uint16_t* sc = (uint16_t*)smem;                                  // [sr][srow]
+  uint32_t* hist = (uint32_t*)(smem + (size_t)sr * srow * 2);      // [PF_SWAVES][256]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
-  const int t0 = blockIdx.x * 16;
+  const int t0 = blockIdx.x * sr;
   const int t = t0 + c;
-  const bool rv = t < A.Tq;
+  const bool rv = c < sr && t < A.Tq;            // columns sr .. 15 carry no query
   const int64_t r = (int64_t)b * A.Tq + (rv ? t : 0);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) W.queue[0] = 0;
 
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
       const bool el = si < S && si * sigma < nq && !wneg;
       u[i] = el ? (__float_as_uint(sv[i]) >> 16) : 0u;
     }
-    *(uint2*)(sc + c * srow + tt * 16 + 4 * g) = make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16));
+    if (c < sr) *(uint2*)(sc + c * srow + tt * 16 + 4 * g) = make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16));
     avc = avn;
     kac = kan;
   }
@@ -237,8 +248,7 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
 
   uint32_t* hw = hist + wave * 256;
 #pragma unroll 1
-  for (int qq = 0; qq < 16 / PF_SWAVES; ++qq) {
-    const int cq = wave * (16 / PF_SWAVES) + qq;
+  for (int cq = wave; cq < sr; cq += PF_SWAVES) {
     const int tq = t0 + cq;
     if (tq >= A.Tq) break;
     const int64_t rq = (int64_t)b * A.Tq + tq;
@@ -465,7 +475,7 @@ struct PfSelShared {
   int nin, nband, wsum[PS_NW];
 };
 static_assert(sizeof(float) * WBUF <= sizeof(uint32_t) * PF_CAND, "transpose buffer fits the score array");
-static_assert(PF_NMAX / 32 <= PF_CAND, "bitmap fits the score array");
+constexpr int PF_BM_BITS = PF_CAND * 32;   // entries one bitmap pass of the emission covers
 
 template <int HP>
 __global__ __launch_bounds__(PS_NT) void pf_select_kernel(IndexArgs A, PfWs W, int KC) {
@@ -633,45 +643,61 @@ __global__ __launch_bounds__(PS_NT) void pf_select_kernel(IndexArgs A, PfWs W, i
     }
     bsel = lane < nband && rank < need;
   }
-  __syncthreads();                        // the transpose buffer becomes the bitmap
-  // ascending emission through a bitmap over [0, n)
-  uint32_t* bitmap = L.cs;
-  const int nw = (n + 31) >> 5;
-  for (int i = tid; i < nw; i += PS_NT) bitmap[i] = 0;
-  __syncthreads();
+  // the candidates' indices in registers: the emission below writes the
+  // output list over L.cj
+  int32_t cjv[PS_CPT];
 #pragma unroll
   for (int m = 0; m < PS_CPT; ++m) {
     const int i = tid + PS_NT * m;
-    if (i < total && (double)__uint_as_float(sv[m]) > hi) {
-      const int j = L.cj[i];
-      atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-    }
+    cjv[m] = (i < total && (double)__uint_as_float(sv[m]) > hi) ? L.cj[i] : -1;
   }
-  if (bsel) atomicOr(&bitmap[jm >> 5], 1u << (jm & 31));
-  __syncthreads();
-  // thread t owns words [t*wpt, (t+1)*wpt); the workgroup scan of their
-  // counts gives each its first output position
-  const int wpt = (nw + PS_NT - 1) / PS_NT;
-  const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
-  int mine = 0;
-  for (int w = w0; w < w1; ++w) mine += __popc(bitmap[w]);
-  const int winc = wave_incl_scan_dpp(mine);
-  if (lane == 63) L.wsum[wave] = winc;
-  __syncthreads();
-  int pos = winc - mine;
-  for (int w = 0; w < wave; ++w) pos += L.wsum[w];
+  __syncthreads();                        // the transpose buffer becomes the bitmap
+  // ascending emission through a bitmap over [0, n), PF_BM_BITS entries at a
+  // time (the bitmap lives in the score array)
+  uint32_t* bitmap = L.cs;
   int32_t* outl = L.cj;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = bitmap[w];
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (pos < A.k) {
-        out[pos] = w * 32 + bit;
-        if (sout) outl[pos] = w * 32 + bit;
-      }
-      ++pos;
+  int written = 0;
+#pragma unroll 1
+  for (int seg0 = 0; seg0 < n; seg0 += PF_BM_BITS) {
+    const int nw = (min(n - seg0, PF_BM_BITS) + 31) >> 5;
+    for (int i = tid; i < nw; i += PS_NT) bitmap[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < PS_CPT; ++m) {
+      const int j = cjv[m] - seg0;
+      if (cjv[m] >= 0 && j >= 0 && j < PF_BM_BITS) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
     }
+    if (bsel && jm >= seg0 && jm - seg0 < PF_BM_BITS) atomicOr(&bitmap[(jm - seg0) >> 5], 1u << ((jm - seg0) & 31));
+    __syncthreads();
+    // thread t owns words [t*wpt, (t+1)*wpt); the workgroup scan of their
+    // counts gives each its first output position
+    const int wpt = (nw + PS_NT - 1) / PS_NT;
+    const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
+    int mine = 0;
+    for (int w = w0; w < w1; ++w) mine += __popc(bitmap[w]);
+    const int winc = wave_incl_scan_dpp(mine);
+    if (lane == 63) L.wsum[wave] = winc;
+    __syncthreads();
+    int pos = written + winc - mine;
+    int segtot = 0;
+    for (int w = 0; w < PS_NW; ++w) {
+      if (w < wave) pos += L.wsum[w];
+      segtot += L.wsum[w];
+    }
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = bitmap[w];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (pos < A.k) {
+          out[pos] = seg0 + w * 32 + bit;
+          if (sout) outl[pos] = seg0 + w * 32 + bit;
+        }
+        ++pos;
+      }
+    }
+    written += segtot;
+    __syncthreads();                      // the bitmap and the sums are reused
   }
   if (sout) {
     // exact scores of every selected entry, 64 at a time, wavefront 0
@@ -731,9 +757,10 @@ static hipError_t launch_pf(const IndexArgs& a, hipStream_t s) {
   const int smax = (int)((a.N_cap + sigma - 1) / sigma);
   const int srow = (smax + 63) / 64 * 64;
   const int KC = pf_key_range(a);
-  const size_t smem0 = (size_t)16 * srow * 2 + PF_SWAVES * 256 * 4;
-  hipLaunchKernelGGL((pf_sample_kernel<HP>), dim3((unsigned)((a.Tq + 15) / 16), (unsigned)a.B), dim3(PF_SWAVES * 64), smem0, s,
-                     a, W, sigma, srow);
+  const int sr = pf_sample_rows(srow);
+  const size_t smem0 = (size_t)sr * srow * 2 + PF_SWAVES * 256 * 4;
+  hipLaunchKernelGGL((pf_sample_kernel<HP>), dim3((unsigned)((a.Tq + sr - 1) / sr), (unsigned)a.B),
+                     dim3(PF_SWAVES * 64), smem0, s, a, W, sigma, srow, sr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pf_score_kernel<HP>), dim3((unsigned)((a.Tq + PF_QROWS - 1) / PF_QROWS), PF_NKC, (unsigned)a.B),

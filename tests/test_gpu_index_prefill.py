@@ -69,6 +69,19 @@ def test_causal_rows(H, k):
     check(qc, qs, w, kc, ks, n, k)
 
 
+@pytest.mark.parametrize("N_cap,k", [(262144, 1024), (131072, 512)])
+def test_long_cache_rows(N_cap, k):
+    """Key caches of a ~1M-token context (262144 entries) and of 131072: the
+    sample workgroups take 8 and 4 rows, the emission makes several bitmap
+    passes (rows of 100000 and 245760+ entries cross 122880).  Sampled rows
+    against the oracle."""
+    B, Tq, H = 1, 64, 8
+    qc, qs, w, kc, ks, _ = inputs(300 + k, B, Tq, H, N_cap)
+    n = causal(Tq, 4 * (N_cap - 64), N_cap)[None].copy()
+    n[0, 5], n[0, 9], n[0, 13] = 100000, 122881, 2000
+    check(qc, qs, w, kc, ks, n, k, rows=np.array([0, 5, 9, 13, 40, 63]))
+
+
 def test_short_and_empty_rows():
     """n_elig of 0, 1, around k, and the sample threshold's small-sample case."""
     B, Tq, N_cap, k = 1, 64, 8192, 512
