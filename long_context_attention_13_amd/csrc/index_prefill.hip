@@ -14,7 +14,7 @@
 //           its candidate threshold t: about 64*sigma entries of the row
 //           reach it.  A workgroup samples 16 rows (the MFMA's columns), or
 //           fewer when the rows' samples would not fit its LDS (16 rows up
-//           to 4096 samples a row, 8 up to 8192, ... 2 up to 32768).
+//           to about 4200 samples a row, 8 up to 8400, ... 2 up to 33700).
 //   score   a workgroup holds 64 query rows (16 per wavefront, the MFMA's
 //           column operand, one operand per indexer head) and streams a range
 //           of keys through LDS in stages of 512 (direct global->LDS loads,
@@ -46,13 +46,16 @@ constexpr int PF_CODE_B = PF_STAGE * 64;
 constexpr int PF_STAGE_B = PF_CODE_B + PF_STAGE * 4;
 constexpr int PF_NKC = 16;            // key ranges per row
 constexpr int PF_LCAP = 96;           // candidates per (row, key range, lane group)
-constexpr int PF_SROWS_LDS = 128 * 1024;     // LDS for the sampled scores of one sample workgroup
-constexpr int PF_SMAX = PF_SROWS_LDS / 2 / 2;  // sampled keys per row at most (2 rows a workgroup)
+constexpr int PF_SROWS_LDS = 132 * 1024;     // LDS for the sampled scores of one sample workgroup
+constexpr int PF_SPAD = 16;                  // padding of a row of samples (16-bit scores)
+// sampled keys per row at most: a row of them, rounded up to 64 and padded,
+// fits half of PF_SROWS_LDS (two rows a workgroup)
+constexpr int PF_SMAX = (PF_SROWS_LDS / 2 / 2 - PF_SPAD) / 64 * 64;
 constexpr int PF_RANK = 64;           // threshold = PF_RANK-th largest sampled score
 constexpr int PF_CAND = 3840;         // candidates per row the select pass holds
 constexpr int PF_CPL = PF_CAND / 64;  // ... per lane
 constexpr int PF_BAND = 64;           // band entries re-scored exactly
-constexpr int PF_NMAX = 32 * PF_SMAX; // largest key cache the prefill path takes (2^20 entries)
+constexpr int PF_NMAX = 1 << 20;      // largest key cache the prefill path takes
 constexpr int PF_FALLBACK_GRID = 128;
 constexpr int PF_SWAVES = 8;         // wavefronts of the sample workgroup (16 rows)
 
@@ -258,16 +261,34 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
     float thr = 0.f;
     if (Sq >= PF_RANK && !neg) {
       const uint16_t* v = sc + cq * srow;
-      uint32_t prefix = 0;
+      // exact radix select of the PF_RANK-th largest 16-bit score, digits of
+      // at most 8 bits from the highest bit where the row's samples differ
+      // (their common leading bits -- most of the exponent -- would put
+      // nearly all of them in one bin and serialise the counting)
+      uint32_t vmx = 0, vmn = 0xFFFFu;
+      for (int i = lane; i < Sq; i += 64) {
+        const uint32_t x = v[i];
+        vmx = max(vmx, x);
+        vmn = min(vmn, x);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        vmx = max(vmx, (uint32_t)__shfl_xor((int)vmx, o, WAVE));
+        vmn = min(vmn, (uint32_t)__shfl_xor((int)vmn, o, WAVE));
+      }
+      int hi = vmx == vmn ? -1 : 31 - __clz(vmx ^ vmn);   // highest bit not yet resolved
+      uint32_t prefix = hi < 0 ? vmx : vmx & ~((2u << hi) - 1u);
       int rem = PF_RANK;
 #pragma unroll 1
-      for (int level = 0; level < 2; ++level) {
-        const int shift = level == 0 ? 8 : 0;
+      while (hi >= 0) {
+        const int shift = hi >= 7 ? hi - 7 : 0;
+        const uint32_t dmask = (2u << (hi - shift)) - 1u;     // this digit's bits
+        const uint32_t pmask = ~((2u << hi) - 1u);            // the bits resolved above it
         for (int i = lane; i < 256; i += 64) hw[i] = 0;
         wave_lds_sync();
         for (int i = lane; i < Sq; i += 64) {
           const uint32_t x = v[i];
-          if (level == 0 || (x >> 8) == (prefix >> 8)) atomicAdd(&hw[(x >> shift) & 255u], 1u);
+          if ((x & pmask) == prefix) atomicAdd(&hw[(x >> shift) & dmask], 1u);
         }
         wave_lds_sync();
         int above;
@@ -275,6 +296,7 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
         rem -= above;
         prefix |= (uint32_t)d << shift;
         wave_lds_sync();
+        hi = shift - 1;
       }
       thr = __uint_as_float(prefix << 16);
     }
@@ -335,6 +357,7 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
   int nlim_min = rv ? nlim : 1 << 30;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) nlim_min = min(nlim_min, __shfl_xor(nlim_min, o, WAVE));
+  nlim_min = __builtin_amdgcn_readfirstlane(nlim_min);
   // candidate lists of the wave's 16 rows: uniform base + 32-bit lane offset
   const int64_t r0 = (int64_t)b * A.Tq + blockIdx.x * PF_QROWS + wave * 16;
   char* wlist = (char*)(W.cand + (r0 * PF_NKC + kc) * 4 * PF_LCAP);
@@ -407,16 +430,23 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
       float sc[4];
       pf_combine<HP>(acc, P, sc);
       const int jt = sj + tt * 16;
-      const bool full = jt + 16 <= nlim_min;        // uniform: every key of the tile is eligible for every row
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      // an overflowing list sends the row to the fallback: clamping the slot is enough
+      auto put = [&](int i) {
         const uint32_t j = (uint32_t)(jt + 4 * g + i);
-        if (sc[i] >= thr && (full || (int)j < nlim)) {
-          // an overflowing list sends the row to the fallback: clamping the slot is enough
-          *(uint64_t*)(wlist + lane_off + min(cnt, (uint32_t)PF_LCAP - 1u) * 8u) =
-              ((uint64_t)__float_as_uint(sc[i]) << 32) | j;
-          ++cnt;
-        }
+        *(uint64_t*)(wlist + lane_off + min(cnt, (uint32_t)PF_LCAP - 1u) * 8u) =
+            ((uint64_t)__float_as_uint(sc[i]) << 32) | j;
+        ++cnt;
+      };
+      if (jt + 16 <= nlim_min) {
+        // (uniform) every key of the tile is eligible for every row: the
+        // threshold alone decides
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (sc[i] >= thr) put(i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (sc[i] >= thr && jt + 4 * g + i < nlim) put(i);
       }
     };
     // software pipeline: the next tile's fragment is read from LDS and its
@@ -755,7 +785,9 @@ static hipError_t launch_pf(const IndexArgs& a, hipStream_t s) {
   PfWs W = pf_carve(a.ws, R);
   const int sigma = pf_sigma(a);
   const int smax = (int)((a.N_cap + sigma - 1) / sigma);
-  const int srow = (smax + 63) / 64 * 64;
+  // a row's samples, padded by 8 dwords: the 16 rows' stores of one tile then
+  // spread evenly over the LDS banks
+  const int srow = (smax + 63) / 64 * 64 + PF_SPAD;
   const int KC = pf_key_range(a);
   const int sr = pf_sample_rows(srow);
   const size_t smem0 = (size_t)sr * srow * 2 + PF_SWAVES * 256 * 4;
