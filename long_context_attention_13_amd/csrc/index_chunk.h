@@ -107,7 +107,8 @@ __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs
   rw.n[0] = A.n_elig[rw.r[0]];
   rw.n[1] = A.n_elig[rw.r[1] >= 0 ? rw.r[1] : rw.r[0]];
   const int wq = (threadIdx.x >> 4) & 1, wh = threadIdx.x & 15;
-  const int wrow = (wq < NQ && rw.r[wq] >= 0) ? rw.r[wq] : rw.r[0];
+  const int rwq = wq == 0 ? rw.r[0] : rw.r[1];    // (no dynamic indexing: keeps rw in registers)
+  const int wrow = (wq < NQ && rwq >= 0) ? rwq : rw.r[0];
   const float wv = A.w[(int64_t)wrow * A.H + (wh < A.H ? wh : 0)];
   MxQueryRaw QR{};
   if (DT == DT_MXFP4) QR = mx_query_issue<HP>(A, rw);
@@ -133,7 +134,7 @@ __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs
   const int jlim = max(rw.n[0], rw.n[1]);
   if (jbeg >= jlim) return;                 // uniform over the workgroup
 
-  if (threadIdx.x < 32) wl[threadIdx.x] = (wq < NQ && rw.r[wq] >= 0 && wh < A.H) ? wv : 0.f;
+  if (threadIdx.x < 32) wl[threadIdx.x] = (wq < NQ && rwq >= 0 && wh < A.H) ? wv : 0.f;
   __syncthreads();
 
   uint64_t kq[NQ][RPW];

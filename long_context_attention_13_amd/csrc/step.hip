@@ -53,12 +53,14 @@ __device__ __forceinline__ void fresh_row(const CompressArgs& k, int b, void* co
 
 // Blocks [0, nscan) are the indexer scan (chunk bid % NCH of row group
 // bid / NCH); the rest are the splits of the dense attention jobs in `bt`.
-// Three workgroups per CU (168 VGPRs; the LDS union, 44.8 KB, also fits three):
-// a scan that fills two workgroups per CU leaves the third to the attention.
+// Three workgroups per CU with 2048-key chunks (the long contexts: 168
+// VGPRs; the LDS union, 44.8 KB, also fits three): a scan that fills two
+// workgroups per CU leaves the third to the attention.  The smaller chunks
+// need more registers and take two.
 // With fd.ncomp > 0 the first fd.ncomp blocks are the compress jobs (job
 // bid / bmax, sequence bid % bmax), in front of the scan and attention blocks.
 template <int KPL, int NQ, int KVDT>
-__global__ __launch_bounds__(256, 3) void step_scan_attend_kernel(IndexArgs A, IdxWs W, int NCH, int gpb, int nscan,
+__global__ __launch_bounds__(256, KPL == 32 ? 3 : 2) void step_scan_attend_kernel(IndexArgs A, IdxWs W, int NCH, int gpb, int nscan,
                                                                   AttendBatch bt, CompressBatch cb, StepFold fd) {
   __shared__ union {
     ChunkShared<NQ> ch;
