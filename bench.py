@@ -758,7 +758,7 @@ def run_variants(reps: int = 20):
     ws = torch.empty(max(16, lca.attend_ws(B, 1, Hq, D, k, 128)), dtype=torch.uint8, device=dev)
     calls = {"shared K = V (matrix cores)": lambda: lca.sparse_mqa_attend(q, K, Ks, idx, wk, i32(0), i32(128), sink,
                                                                            0.088, o, ws=ws),
-             "separate V (vector ALU)": lambda: lca.attend_separate_v(True, q, K, V, Ks, Vs, idx, wk, wv, i32(0),
+             "separate V (matrix cores, K and V tiles staged apart)": lambda: lca.attend_separate_v(True, q, K, V, Ks, Vs, idx, wk, wv, i32(0),
                                                                       i32(128), sink, 0.088, o, ws=ws)}
     for name, fn in calls.items():
         fn()

@@ -258,8 +258,10 @@ lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dty
  *   k, v     [B][N_cap][D] of kv_dt; FP8: k_scale, v_scale fp32 [B][N_cap][D/64]
  *   win_k, win_v [B][W_buf][D] of win_dt
  * Other arguments, workspace and guarantees as lca_sparse_mqa_attend /
- * lca_hca_attend.  Runs on the fp32 vector-ALU kernel for every storage type
- * (the matrix-core kernels stage one tile as key and value).
+ * lca_hca_attend.  bf16 queries and windows with bf16 or FP8 entries run on
+ * the matrix-core kernels (each tile's key and value rows staged separately;
+ * with v = k the bytes of the shared-KV call); fp32 storage on the vector-ALU
+ * kernel.
  */
 lca_status lca_attend_separate_v(int32_t sparse, const void* q, lca_dtype q_dt, const void* k,
                                  const void* v, lca_dtype kv_dt, const float* k_scale,

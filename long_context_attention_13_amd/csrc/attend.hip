@@ -208,6 +208,16 @@ __global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void atten
   attend_mfma_body<KVDT, HQ, QB>(A, S, split_items, part_ml, part_o, blockIdx.x, blockIdx.y, sm);
 }
 
+// The same with separate values (lca_attend_separate_v): the value rows and
+// their scales are staged beside the key rows of each tile.
+template <int KVDT, int HQ, int QB>
+__global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void attend_mfma_sv_kernel(
+    AttendArgs A, int S, int split_items, float* part_ml, float* part_o) {
+  __shared__ MtSharedSV<QB> sm;
+  attend_mfma_body<KVDT, HQ, QB, true>(A, S, split_items, part_ml, part_o, blockIdx.x, blockIdx.y, sm.m,
+                                       FreshEnt{-1, nullptr, nullptr}, sm.vsclo, sm.vschi);
+}
+
 __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, int split_items, const float* part_ml,
                                                            const float* part_o) {
   __shared__ MgShared sm;
@@ -264,6 +274,18 @@ static hipError_t launch_kv(const AttendArgs& a, hipStream_t s, Plan P, float* m
 template <int KVDT, int HQ>
 static void launch_mfma_h(const AttendArgs& a, hipStream_t s, Plan P, float* ml, float* po) {
   constexpr int QB = att_qb<HQ>();
+  if (a.v != nullptr) {
+    // separate values: the split kernel, or the row-group kernel for dense
+    // prefill-shaped calls (the wide kernels stage one tile as key and value)
+    if (!a.sparse && P.S == 1 && a.Tq >= 2 * QB) {
+      dim3 grid(1, (unsigned)(a.B * ((a.Tq + QB - 1) / QB)));
+      hipLaunchKernelGGL((attend_mfma_sv_kernel<KVDT, HQ, QB>), grid, dim3(HQ * 4 * QB), 0, s, a, 1, P.items, ml, po);
+    } else {
+      dim3 grid(P.S, (unsigned)(a.B * a.Tq));
+      hipLaunchKernelGGL((attend_mfma_sv_kernel<KVDT, HQ, 1>), grid, dim3(HQ * 4), 0, s, a, P.S, P.items, ml, po);
+    }
+    return;
+  }
   if (!a.sparse && P.S == 1 && a.Tq >= 2 * QB) {
     if (attend_dense_wide_applies(a)) {
       (void)launch_attend_dense_wide(a, s);   // the caller reads hipGetLastError
@@ -301,7 +323,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     po = (float*)((char*)a.ws + align256(sizeof(float) * R * P.S * a.Hq * 2));
   }
   hipError_t e;
-  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8) && !a.v;
+  const bool mfma = a.q_dt == DT_BF16 && a.win_dt == DT_BF16 && (a.kv_dt == DT_BF16 || a.kv_dt == DT_FP8);
   if (mfma) e = a.kv_dt == DT_FP8 ? launch_mfma<DT_FP8>(a, s, P, ml, po) : launch_mfma<DT_BF16>(a, s, P, ml, po);
   else e = a.q_dt == DT_F32 ? launch_kv<DT_F32>(a, s, P, ml, po) : launch_kv<DT_BF16>(a, s, P, ml, po);
   if (e != hipSuccess || P.S == 1) return e;

@@ -60,12 +60,16 @@ constexpr int MT_VROW = 72;               // bf16 per V^T row in LDS (64 + pad)
 // once.
 constexpr int MT_TASKS = MT_TE / 2 * 8;
 
-template <int KVDT, int CPT>
+template <int KVDT, int CPT, bool SV = false>
 struct MtRegs {
   int4 ent[CPT][2][KVDT == DT_FP8 ? 1 : 2];
   int4 win[CPT][2][2];
   float2 sc[CPT][2];
   int kind[CPT][2];       // 0 entry, 1 window token, -1 nothing
+  // separate values (SV): the value rows of the same items
+  int4 vent[SV ? CPT : 1][2][KVDT == DT_FP8 ? 1 : 2];
+  int4 vwin[SV ? CPT : 1][2][2];
+  float2 vsc[SV ? CPT : 1][2];
 };
 
 // An entry row that the attention takes from elsewhere than the entry cache
@@ -77,9 +81,11 @@ struct FreshEnt {
   const float* sc;
 };
 
-template <int KVDT, int NT, int CPT>
+// SV: the value rows come from A.v / A.v_scale / A.win_v (the layouts of
+// A.kv / A.kv_scale / A.win).
+template <int KVDT, int NT, int CPT, bool SV = false>
 __device__ __forceinline__ void mt_fetch(const AttendArgs& A, int b, int64_t wbase, int nkv, int e_lo, const int* idxl,
-                                         int t0, int p1, MtRegs<KVDT, CPT>& R,
+                                         int t0, int p1, MtRegs<KVDT, CPT, SV>& R,
                                          const FreshEnt& fe = FreshEnt{-1, nullptr, nullptr}) {
   const int tid = threadIdx.x;
 #pragma unroll
@@ -108,11 +114,19 @@ __device__ __forceinline__ void mt_fetch(const AttendArgs& A, int b, int64_t wba
         if (KVDT == DT_FP8) {
           R.ent[c][u][0] = *(const int4*)((const uint8_t*)A.kv + erow * 128 + ch * 16);
           R.sc[c][u] = *(const float2*)(A.kv_scale + erow * 2);
+          if (SV) {
+            R.vent[c][u][0] = *(const int4*)((const uint8_t*)A.v + erow * 128 + ch * 16);
+            R.vsc[c][u] = *(const float2*)(A.v_scale + erow * 2);
+          }
         } else {
           R.ent[c][u][0] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16);
           R.ent[c][u][1] = *(const int4*)((const uint16_t*)A.kv + erow * 128 + ch * 16 + 8);
+          if (SV) {
+            R.vent[c][u][0] = *(const int4*)((const uint16_t*)A.v + erow * 128 + ch * 16);
+            R.vent[c][u][1] = *(const int4*)((const uint16_t*)A.v + erow * 128 + ch * 16 + 8);
+          }
         }
-        if (kind == 0 && j == fe.j) {
+        if (!SV && kind == 0 && j == fe.j) {
           if (KVDT == DT_FP8) {
             R.ent[c][u][0] = *(const int4*)(fe.code + ch * 16);
             R.sc[c][u] = *(const float2*)fe.sc;
@@ -126,6 +140,10 @@ __device__ __forceinline__ void mt_fetch(const AttendArgs& A, int b, int64_t wba
         const int64_t wrow = wbase + (kind == 1 ? p - nkv : 0);
         R.win[c][u][0] = *(const int4*)((const uint16_t*)A.win + wrow * 128 + ch * 16);
         R.win[c][u][1] = *(const int4*)((const uint16_t*)A.win + wrow * 128 + ch * 16 + 8);
+        if (SV) {
+          R.vwin[c][u][0] = *(const int4*)((const uint16_t*)A.win_v + wrow * 128 + ch * 16);
+          R.vwin[c][u][1] = *(const int4*)((const uint16_t*)A.win_v + wrow * 128 + ch * 16 + 8);
+        }
       }
     }
   }
@@ -141,9 +159,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2_from_fp8x2(uint32_t two_codes) {
 // 32k + 16h + 4g + i at column 32k + 8g + 4h + i, so each lane's 8 items of
 // one dim are contiguous).  The permutation keeps item pairs (2m, 2m+1)
 // adjacent, so one 32-bit store writes both items of a pair for one dim.
-template <int KVDT, int NT, int CPT>
-__device__ __forceinline__ void mt_store(const MtRegs<KVDT, CPT>& R, __bf16* Kl, __bf16* Vt, float* sclo, float* schi,
-                                         int* okl) {
+// The bf16 pieces of one staged row: FP8 codes converted exactly (the
+// scales are applied to the products), bf16 rows as they are.
+template <int KVDT>
+__device__ __forceinline__ void mt_row_pieces(const int4 (&ent)[KVDT == DT_FP8 ? 1 : 2], int4& v0, int4& v1) {
+  if (KVDT == DT_FP8) {
+    const int4 q = ent[0];
+    v0.x = (int)pack_bf16x2_from_fp8x2((uint32_t)q.x & 0xFFFFu);
+    v0.y = (int)pack_bf16x2_from_fp8x2((uint32_t)q.x >> 16);
+    v0.z = (int)pack_bf16x2_from_fp8x2((uint32_t)q.y & 0xFFFFu);
+    v0.w = (int)pack_bf16x2_from_fp8x2((uint32_t)q.y >> 16);
+    v1.x = (int)pack_bf16x2_from_fp8x2((uint32_t)q.z & 0xFFFFu);
+    v1.y = (int)pack_bf16x2_from_fp8x2((uint32_t)q.z >> 16);
+    v1.z = (int)pack_bf16x2_from_fp8x2((uint32_t)q.w & 0xFFFFu);
+    v1.w = (int)pack_bf16x2_from_fp8x2((uint32_t)q.w >> 16);
+  } else {
+    v0 = ent[0];
+    v1 = ent[KVDT == DT_FP8 ? 0 : 1];
+  }
+}
+
+// SV: the value rows go to V^T and their scales to vsclo / vschi; otherwise
+// the key rows serve as values too (vsclo / vschi unused).
+template <int KVDT, int NT, int CPT, bool SV = false>
+__device__ __forceinline__ void mt_store(const MtRegs<KVDT, CPT, SV>& R, __bf16* Kl, __bf16* Vt, float* sclo, float* schi,
+                                         int* okl, float* vsclo = nullptr, float* vschi = nullptr) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -156,33 +196,28 @@ __device__ __forceinline__ void mt_store(const MtRegs<KVDT, CPT>& R, __bf16* Kl,
       const int e = 2 * pr + u;
       const int kind = R.kind[c][u];
       int4 v0 = make_int4(0, 0, 0, 0), v1 = make_int4(0, 0, 0, 0);
-      float slo = 1.f, shi = 1.f;
+      int4 w0 = v0, w1 = v0;              // the value row (SV)
+      float slo = 1.f, shi = 1.f, vlo = 1.f, vhi = 1.f;
       if (kind == 0) {
-        if (KVDT == DT_FP8) {
-          const int4 q = R.ent[c][u][0];
-          v0.x = (int)pack_bf16x2_from_fp8x2((uint32_t)q.x & 0xFFFFu);
-          v0.y = (int)pack_bf16x2_from_fp8x2((uint32_t)q.x >> 16);
-          v0.z = (int)pack_bf16x2_from_fp8x2((uint32_t)q.y & 0xFFFFu);
-          v0.w = (int)pack_bf16x2_from_fp8x2((uint32_t)q.y >> 16);
-          v1.x = (int)pack_bf16x2_from_fp8x2((uint32_t)q.z & 0xFFFFu);
-          v1.y = (int)pack_bf16x2_from_fp8x2((uint32_t)q.z >> 16);
-          v1.z = (int)pack_bf16x2_from_fp8x2((uint32_t)q.w & 0xFFFFu);
-          v1.w = (int)pack_bf16x2_from_fp8x2((uint32_t)q.w >> 16);
-          slo = R.sc[c][u].x;
-          shi = R.sc[c][u].y;
-        } else {
-          v0 = R.ent[c][u][0];
-          v1 = R.ent[c][u][KVDT == DT_FP8 ? 0 : 1];
+        mt_row_pieces<KVDT>(R.ent[c][u], v0, v1);
+        if (KVDT == DT_FP8) { slo = R.sc[c][u].x; shi = R.sc[c][u].y; }
+        if (SV) {
+          mt_row_pieces<KVDT>(R.vent[c][u], w0, w1);
+          if (KVDT == DT_FP8) { vlo = R.vsc[c][u].x; vhi = R.vsc[c][u].y; }
         }
       } else if (kind == 1) {
         v0 = R.win[c][u][0];
         v1 = R.win[c][u][1];
+        if (SV) { w0 = R.vwin[c][u][0]; w1 = R.vwin[c][u][1]; }
       }
       *(int4*)&Kl[e * MT_KROW + ch * 16] = v0;
       *(int4*)&Kl[e * MT_KROW + ch * 16 + 8] = v1;
-      v[u][0] = v0;
-      v[u][1] = v1;
-      if (ch == 0) { sclo[e] = slo; schi[e] = shi; okl[e] = kind >= 0; }
+      v[u][0] = SV ? w0 : v0;
+      v[u][1] = SV ? w1 : v1;
+      if (ch == 0) {
+        sclo[e] = slo; schi[e] = shi; okl[e] = kind >= 0;
+        if (SV) { vsclo[e] = vlo; vschi[e] = vhi; }
+      }
     }
     const int e0 = 2 * pr;
     const int ep = (e0 & ~31) | ((e0 & 12) << 1) | ((e0 & 16) >> 2) | (e0 & 3);   // even column of the pair
@@ -208,11 +243,22 @@ struct MtShared {
   int idxl[QB == 1 ? 2048 : 1];
 };
 
+// The same with the value scales of a separate-values call.
+template <int QB>
+struct MtSharedSV {
+  MtShared<QB> m;
+  __align__(16) float vsclo[MT_TE];
+  __align__(16) float vschi[MT_TE];
+};
+
 // Split `split` of query-row group `grp` of one attention call.
-template <int KVDT, int HQ, int QB>
+// SV: separate values (A.v, A.v_scale, A.win_v); vsclo / vschi: LDS for the
+// value scales of a tile (MtSharedSV).
+template <int KVDT, int HQ, int QB, bool SV = false>
 __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int split_items, float* part_ml,
                                                  float* part_o, int split, int grp, MtShared<QB>& sm,
-                                                 const FreshEnt& fe = FreshEnt{-1, nullptr, nullptr}) {
+                                                 const FreshEnt& fe = FreshEnt{-1, nullptr, nullptr},
+                                                 float* vsclo = nullptr, float* vschi = nullptr) {
   // QB query rows of one sequence share each staged tile (dense lists only):
   // the workgroup's list is entries 0 .. max n_elig - 1 followed by the union
   // of the rows' window slices, and every row masks what is not its own.
@@ -283,13 +329,13 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
-  MtRegs<KVDT, CPT> R;
-  if (p0 < p1) mt_fetch<KVDT, NT, CPT>(A, b, wbase, nkv, e_lo, idxl, p0, p1, R, fe);
+  MtRegs<KVDT, CPT, SV> R;
+  if (p0 < p1) mt_fetch<KVDT, NT, CPT, SV>(A, b, wbase, nkv, e_lo, idxl, p0, p1, R, fe);
   for (int t0 = p0; t0 < p1; t0 += MT_TE) {
     __syncthreads();
-    mt_store<KVDT, NT, CPT>(R, Kl, Vt, sclo, schi, okl);
+    mt_store<KVDT, NT, CPT, SV>(R, Kl, Vt, sclo, schi, okl, vsclo, vschi);
     __syncthreads();
-    if (t0 + MT_TE < p1) mt_fetch<KVDT, NT, CPT>(A, b, wbase, nkv, e_lo, idxl, t0 + MT_TE, p1, R, fe);
+    if (t0 + MT_TE < p1) mt_fetch<KVDT, NT, CPT, SV>(A, b, wbase, nkv, e_lo, idxl, t0 + MT_TE, p1, R, fe);
 
     // ---- S^T = K Q^T for 4 subtiles of 16 items: per K-step the four
     // subtiles' fragments are read together and feed four independent
@@ -374,8 +420,8 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
         const int st = 2 * kap + (jj >> 2), i = jj & 3;
         const int e = st * 16 + 4 * g + i;
         if (KVDT == DT_FP8) {
-          plo[jj] = (__bf16)(pv[st][i] * sclo[e]);       // the V scale folds into P
-          phi[jj] = (__bf16)(pv[st][i] * schi[e]);
+          plo[jj] = (__bf16)(pv[st][i] * (SV ? vsclo : sclo)[e]);   // the V scale folds into P
+          phi[jj] = (__bf16)(pv[st][i] * (SV ? vschi : schi)[e]);
         } else {
           plo[jj] = (__bf16)pv[st][i];
           phi[jj] = plo[jj];

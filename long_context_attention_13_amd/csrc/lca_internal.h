@@ -53,7 +53,7 @@ struct AttendArgs {
   void* out; int out_dt; float* lse;
   void* ws; size_t ws_bytes;
   // separate values (NULL: one vector per item is key and value): layouts of
-  // kv / kv_scale / win; such calls run on the fp32 VALU kernel
+  // kv / kv_scale / win; not batched (single calls only)
   const void* v; const float* v_scale; const void* win_v;
 };
 size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W_buf);
