@@ -323,6 +323,55 @@ __device__ __forceinline__ void f32_score_round(const IndexArgs& A, const Rows& 
   key0 = score_key(s);
 }
 
+// The same evaluation with the lane's key row read 32 elements at a time by
+// vector loads, all in flight (each head's dot product is still one float64
+// chain over the elements in order): for callers that do not unroll it.
+__device__ __forceinline__ void f32_score_round_vec(const IndexArgs& A, const Rows& rw, int j0, const float* qrow,
+                                                    const float* wl, uint64_t& key0) {
+  const int lane = threadIdx.x & 63;
+  const int j = j0 + lane;
+  const bool ok = j < rw.n[0];
+  const float4* kr = (const float4*)((const float*)A.ki + ((int64_t)rw.b * A.N_cap + (ok ? j : 0)) * A.d);
+  double s = 0.0;
+  {
+    // steps of (head, 32 elements of the row) in order; the next step's
+    // elements load while these are multiplied
+    const int nc = A.d / 32;
+    const int nst = A.H * nc;
+    float4 cur[8], nxt[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cur[t] = kr[t];
+    double dot = 0.0;
+#pragma unroll 1
+    for (int st = 0; st < nst; ++st) {
+      const int h = st / nc, ci = st - h * nc;
+      const bool more = st + 1 < nst;
+      const int cn = ci + 1 == nc ? 0 : ci + 1;
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) nxt[t] = kr[cn * 8 + t];
+      }
+      const float* q = qrow + h * A.d + ci * 32;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        dot = fma((double)q[4 * t], (double)cur[t].x, dot);
+        dot = fma((double)q[4 * t + 1], (double)cur[t].y, dot);
+        dot = fma((double)q[4 * t + 2], (double)cur[t].z, dot);
+        dot = fma((double)q[4 * t + 3], (double)cur[t].w, dot);
+      }
+      if (ci + 1 == nc) {
+        s = combine_step(s, dot, wl[h]);
+        dot = 0.0;
+      }
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cur[t] = nxt[t];
+      }
+    }
+  }
+  key0 = ok ? score_key(s) : 0ull;
+}
+
 // ------------------------------------------------------------------------
 // Wavefront bitonic sort of one u64 per lane, descending across lanes.
 // ------------------------------------------------------------------------
@@ -699,9 +748,14 @@ struct StreamSrc {
   }
 };
 
-// Exact selection of one row from scratch, re-scoring every eligible entry in
-// each pass (rows with few entries, and rows whose candidates failed the
-// certification).  Kept out of line: it is the rare or the small case.
+__device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_t (&bj)[LB], uint32_t vm, int nu,
+                                          const Thr& th, int ties, bool unsafe, int k, int32_t* out, double* sout,
+                                          SelShared& S);
+
+// Exact selection of one row from scratch (rows with few entries, and rows
+// whose candidates failed the certification): an fp32 row of at most
+// LB * SEL_THREADS entries is scored once into registers; otherwise every
+// pass re-scores the row.
 template <int DT, int HP>
 __device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n, int kk, int32_t* out, double* sout,
                                              SelShared& S, float* tbuf, const float* wl, const float* ql,
@@ -719,6 +773,42 @@ __device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n
     // every eligible entry is selected: only the scores are needed
     for (int i = n + threadIdx.x; i < A.k; i += SEL_THREADS) sout[i] = 0.0;
     src.for_each([&](uint64_t key, int j) { if (j < n) sout[j] = key_score(key); });
+    return;
+  }
+  if (DT == DT_F32 && n <= LB * SEL_THREADS) {
+    // an fp32 row that fits the registers: every eligible entry scored once
+    // (item u*SEL_THREADS + tid = entry j, in the order of the streamed
+    // passes), then the radix select and the emission over the registers
+    // (the MXFP4 scoring state does not leave room for the keys)
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint64_t bk[LB];
+    int32_t bj[LB];
+    uint32_t vm = 0;
+    // the keys go through LDS (the scoring buffers' region, unused by the
+    // fp32 path), so that the scoring loop is not unrolled
+    uint64_t* kl = (uint64_t*)tbuf;
+#pragma unroll 1
+    for (int u = 0; u < LB; ++u) {
+      const int j0 = u * SEL_THREADS + wave * 64;
+      if (j0 >= n) break;                 // uniform over the wavefront
+      uint64_t k0;
+      f32_score_round_vec(A, src.rw, j0, ql, wl, k0);
+      kl[u * SEL_THREADS + threadIdx.x] = k0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int j = u * SEL_THREADS + threadIdx.x;
+      const bool ok = j < n;
+      bk[u] = ok ? kl[j] : 0ull;          // key 0: no entry
+      bj[u] = j;
+      vm |= (uint32_t)ok << u;
+    }
+    const int nu = (n + SEL_THREADS - 1) / SEL_THREADS;
+    if (threadIdx.x == 0) S.bcast[6] = 0;  // emit_regs' "unsafe" flag (find_threshold's barriers order this)
+    RegSrc rs{bk, bj, vm, nu};
+    const Thr th = find_threshold(rs, kk, S);
+    emit_regs(bk, bj, vm, nu, th, -1, false, A.k, out, sout, S);
     return;
   }
   const Thr th = find_threshold(src, kk, S);
