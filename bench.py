@@ -982,6 +982,35 @@ def time_graph(step, reps, setup=None):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
 
 
+def time_graph_steps(steps, reps):
+    """Capture the callables in `steps` back to back in one graph and time
+    reps replays (an event after each); per-step durations in ms (replay
+    time / len(steps)), so the fixed cost of a replay is shared as in a
+    forward graph of many layers."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for f in steps:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in steps:
+            f()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) / len(steps) for i in range(reps)]
+
+
+GRAPH_STEPS = 8                       # steps per graph in the small legs
+
+
 def run_small_csa(reps: int):
     """Small CSA decode in fp32: 1 sequence of 4096 tokens -> 1024 entries, 16
     query heads, indexer 4 x 64, top-64, window 128.  Cache and indexer keys
@@ -1020,12 +1049,14 @@ def run_small_csa(reps: int):
         lca.lightning_index_topk(qi, None, w, key, None, n, k, idx, ws_i)
         lca.sparse_mqa_attend(q, ent, None, idx, win, wb, wlen, sink, c["tau"], out, ws=ws_a)
 
-    ms = time_graph(step, reps)
-    st = stats_us(ms)
+    st = stats_us(time_graph_steps([step] * GRAPH_STEPS, max(reps // GRAPH_STEPS, 25)))
+    st1 = stats_us(time_graph(step, reps))
     return {"workload": "small_csa_decode: CSA decode fp32, 1 query, 4096 tokens -> 1024 entries, 16 heads, "
                         "indexer 4x64, top-64, window 128",
             "us_per_step": st, "decode_tokens_per_s": round(1e6 / st["median"], 1),
-            "schedule": "csa_compress x2 (newest block), lightning_index_topk, sparse_mqa_attend; graph replays",
+            "us_per_step_one_step_per_graph": st1,
+            "schedule": f"csa_compress x2 (newest block), lightning_index_topk, sparse_mqa_attend; one graph of "
+                        f"{GRAPH_STEPS} steps replayed (and one step per graph)",
             "bound": "latency (0.37 MB per step; a roofline fraction is not meaningful at this size)"}
 
 
@@ -1073,15 +1104,20 @@ def run_hca_decode(reps: int):
         lca.hca_compress(x, gate, bias, m, tok, one, row, 1, cache, lca.BF16)
         attend()
 
-    a = stats_us(time_graph(attend, reps))
-    s = stats_us(time_graph(step, reps))
+    nrep = max(reps // GRAPH_STEPS, 25)
+    a = stats_us(time_graph_steps([attend] * GRAPH_STEPS, nrep))
+    s = stats_us(time_graph_steps([step] * GRAPH_STEPS, nrep))
+    a1 = stats_us(time_graph(attend, reps))
+    s1 = stats_us(time_graph(step, reps))
     bs = stats_us(bms)
     step_bytes = B * (nb * D * 2 + W * D * 2 + 2 * Hq * D * 2 + m * D * 2 + m * 4 + D * 2)
     return {"workload": "hca_decode_bf16: 8 sequences x 65536 tokens, m'=128 -> 512 bf16 entries, 64 heads, "
                         "window 128",
             "hca_attend_us": a, "decode_step_us": s, "decode_tokens_per_s": round(B * 1e6 / s["median"], 1),
+            "one_step_per_graph": {"hca_attend_us": a1, "decode_step_us": s1},
             "step_algorithmic_mb": round(step_bytes / 1e6, 3),
-            "schedule": "hca_compress (newest block) + hca_attend; graph replays",
+            "schedule": f"hca_compress (newest block) + hca_attend; one graph of {GRAPH_STEPS} steps replayed (and "
+                        f"one step per graph)",
             "cache_build": {"kernel": "pool_encode_kernel (hca_compress, 4096 blocks of 128 tokens)", "us": bs,
                             "algorithmic_mb": round(build_bytes / 1e6, 2),
                             "gbs": round(build_bytes / (bs["median"] * 1e-6) / 1e9, 1),
@@ -1137,6 +1173,9 @@ def run_csa_fp8(reps: int, copies: int):
         jobs.append((lca.index_job(qi, qi_sc, w, kc, ks, n, k, idx, ws_i),
                      [lca.attend_job(True, q, e, es, idx, win, wb, wlen, sink, tau, out, ws=ws_a)]))
     stream = torch.cuda.current_stream()
+    # one graph holding a step per cache copy (copy c's caches, in order)
+    st = stats_us(time_graph_steps([lambda ij=ij, aj=aj: lca.decode_step([], ij, aj) for ij, aj in jobs],
+                                   max(reps // copies, 25)))
     graphs = []
     for ij, aj in jobs:
         lca.decode_step([], ij, aj)
@@ -1154,7 +1193,7 @@ def run_csa_fp8(reps: int, copies: int):
         graphs[i % copies].replay()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    st = stats_us([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    st1 = stats_us([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
     step_bytes = B * (N * (d_I // 2 + d_I // 32) + H_I * (d_I // 2 + d_I // 32) + H_I * 4 + k * 4
                       + k * (D + 8) + W * D * 2 + 2 * Hq * D * 2)
     gbs = step_bytes / (st["median"] * 1e-6) / 1e9
@@ -1165,7 +1204,9 @@ def run_csa_fp8(reps: int, copies: int):
             "us_per_step": st, "decode_tokens_per_s": round(B * 1e6 / st["median"], 1),
             "algorithmic_mb_per_step": round(step_bytes / 1e6, 2), "hbm_gbs": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "copies": copies,
-            "schedule": "decode_step (indexer + top-512, sparse attention), one graph per cache copy"}
+            "us_per_step_one_step_per_graph": st1,
+            "schedule": "decode_step (indexer + top-512, sparse attention); one graph holding a step per cache "
+                        "copy, replayed (and one graph per copy)"}
 
 
 def cpu_prefill_subset(rows: int):

@@ -184,7 +184,7 @@ lca_status lca_compress_batch(const lca_compress_job* jobs, int32_t njobs, void*
  *   score_out optional [B][Tq][k] double: s_j of each idx_out entry (0 for -1)
  *   ws / ws_bytes: workspace of at least lca_index_topk_ws(...) bytes
  * Supported: 1 <= k <= 2048; MXFP4: H_I <= 16, d_I in {64, 128}; F32:
- * H_I <= 64, d_I in {32, 64, 128}; N_cap < 2^31.
+ * H_I <= 16, d_I in {32, 64, 128}; N_cap < 2^31.
  * Results are deterministic and independent of B and of the other rows.
  */
 lca_status lca_lightning_index_topk(const void* qi, lca_dtype qi_dt, const uint8_t* qi_scale,

@@ -232,7 +232,7 @@ lca_status index_check(const char* name, const void* qi, lca_dtype qi_dt, const 
     REQ(H_I >= 1 && H_I <= 16, LCA_ENOTSUP, "%s: MXFP4 needs 1 <= H_I <= 16 (got %d)", name, H_I);
     REQ(d_I == 64 || d_I == 128, LCA_ENOTSUP, "%s: MXFP4 needs d_I in {64, 128} (got %d)", name, d_I);
   } else if (qi_dt == LCA_F32) {
-    REQ(H_I >= 1 && H_I <= 64, LCA_ENOTSUP, "%s: F32 needs 1 <= H_I <= 64 (got %d)", name, H_I);
+    REQ(H_I >= 1 && H_I <= 16, LCA_ENOTSUP, "%s: F32 needs 1 <= H_I <= 16 (got %d)", name, H_I);
     REQ(d_I == 32 || d_I == 64 || d_I == 128, LCA_ENOTSUP, "%s: F32 needs d_I in {32, 64, 128}", name);
   } else {
     return fail(LCA_ENOTSUP, "%s: qi_dt must be F32 or MXFP4", name);

@@ -48,30 +48,80 @@ __device__ __forceinline__ ListItem list_item(const AttendArgs& A, int b, int r,
   return it;
 }
 
-template <int KVDT>
-__device__ __forceinline__ float kv_elem(const void* kv, const float* kv_scale, int64_t row, int D, int d) {
-  if (KVDT == DT_F32) return ((const float*)kv)[row * D + d];
-  if (KVDT == DT_BF16) return bf16_to_f32(((const uint16_t*)kv)[row * D + d]);
-  const uint8_t c = ((const uint8_t*)kv)[row * D + d];
-  const float2 v = fp8x2_to_f32((uint32_t)c);
-  return v.x * kv_scale[row * (D / 64) + d / 64];
-}
-
-template <int WDT>
-__device__ __forceinline__ float win_elem(const void* win, int64_t row, int D, int d) {
-  if (WDT == DT_F32) return ((const float*)win)[row * D + d];
-  return bf16_to_f32(((const uint16_t*)win)[row * D + d]);
-}
-
 template <int QDT>
 __device__ __forceinline__ float q_elem(const AttendArgs& A, int64_t i) {
   if (QDT == DT_F32) return ((const float*)A.q)[i];
   return bf16_to_f32(((const uint16_t*)A.q)[i]);
 }
 
+// Sixteen consecutive elements d0 .. d0+15 of an item row as fp32 (FP8: the
+// codes times the row's scale for that 64-element half).
+template <int KVDT>
+__device__ __forceinline__ void kv_piece(const void* kv, const float* kv_scale, int64_t row, int d0, float (&v)[16]) {
+  constexpr int D = 128;
+  if (KVDT == DT_F32) {
+    const float4* p = (const float4*)((const float*)kv + row * D + d0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4 x = p[t];
+      v[4 * t] = x.x; v[4 * t + 1] = x.y; v[4 * t + 2] = x.z; v[4 * t + 3] = x.w;
+    }
+  } else if (KVDT == DT_BF16) {
+    const uint4* p = (const uint4*)((const uint16_t*)kv + row * D + d0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint4 x = p[t];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * t + 2 * i] = __uint_as_float(w[i] << 16);
+        v[8 * t + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const uint4 x = *(const uint4*)((const uint8_t*)kv + row * D + d0);
+    const float sc = kv_scale[row * (D / 64) + d0 / 64];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2 lo = fp8x2_to_f32(w[i] & 0xFFFFu), hi = fp8x2_to_f32(w[i] >> 16);
+      v[4 * i] = lo.x * sc; v[4 * i + 1] = lo.y * sc; v[4 * i + 2] = hi.x * sc; v[4 * i + 3] = hi.y * sc;
+    }
+  }
+}
+
+// One thread's piece of a tile: elements 16*part .. +15 of item e (and of its
+// separate value row), fetched into registers.
+struct ValuPiece {
+  float k[16], v[16];
+  int ok;
+};
+
+template <int KVDT, int WDT>
+__device__ __forceinline__ void valu_fetch(const AttendArgs& A, int b, int r, int p, int p1, int nkv, int part,
+                                           ValuPiece& P) {
+  P.ok = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { P.k[i] = 0.f; P.v[i] = 0.f; }
+  if (p >= p1) return;
+  const ListItem it = list_item(A, b, r, p, nkv);
+  if (it.kind == 0) {
+    kv_piece<KVDT>(A.kv, A.kv_scale, it.row, 16 * part, P.k);
+    if (A.v) kv_piece<KVDT>(A.v, A.v_scale, it.row, 16 * part, P.v);
+    P.ok = 1;
+  } else if (it.kind == 1) {
+    kv_piece<WDT>(A.win, nullptr, it.row, 16 * part, P.k);
+    if (A.v) kv_piece<WDT>(A.win_v, nullptr, it.row, 16 * part, P.v);
+    P.ok = 1;
+  }
+}
+
 // ------------------------------------------------------------------------
 // fp32 VALU kernel (any storage types; used for F32 inputs and for separate
-// values: the value tile is staged beside the key tile).
+// values: the value tile is staged beside the key tile).  Each thread stages
+// one 16-element piece of one item per tile, so a tile's loads are all in
+// flight together, and the next tile's pieces are fetched while the current
+// tile is computed.
 // ------------------------------------------------------------------------
 template <int QDT, int KVDT, int WDT, int HQ>
 __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, int S, int split_items, float* part_ml,
@@ -103,30 +153,21 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
   __syncthreads();
 
+  static_assert(ATT_TE * (D / 16) == ATT_THREADS, "one 16-element piece per thread and tile");
+  const int pe_ = tid >> 3, ppart = tid & 7;          // this thread's item in the tile, and piece
+  ValuPiece P;
+  if (p0 < p1) valu_fetch<KVDT, WDT>(A, b, r, p0 + pe_, p1, nkv, ppart, P);
   for (int t0 = p0; t0 < p1; t0 += ATT_TE) {
-    // stage a tile of items as fp32
-    for (int i = tid; i < ATT_TE * D; i += ATT_THREADS) {
-      const int e = i / D, d = i % D;
-      const int p = t0 + e;
-      float v = 0.f, vv = 0.f;
-      int ok = 0;
-      if (p < p1) {
-        const ListItem it = list_item(A, b, r, p, nkv);
-        if (it.kind == 0) {
-          v = kv_elem<KVDT>(A.kv, A.kv_scale, it.row, D, d);
-          if (A.v) vv = kv_elem<KVDT>(A.v, A.v_scale, it.row, D, d);
-          ok = 1;
-        } else if (it.kind == 1) {
-          v = win_elem<WDT>(A.win, it.row, D, d);
-          if (A.v) vv = win_elem<WDT>(A.win_v, it.row, D, d);
-          ok = 1;
-        }
-      }
-      kvs[e][d] = v;
-      if (A.v) vls[e][d] = vv;
-      if (d == 0) valid[e] = ok;
+    // stage the fetched tile as fp32, then fetch the next one
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kvs[pe_][16 * ppart + i] = P.k[i];
+    if (A.v) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vls[pe_][16 * ppart + i] = P.v[i];
     }
+    if (ppart == 0) valid[pe_] = P.ok;
     __syncthreads();
+    if (t0 + ATT_TE < p1) valu_fetch<KVDT, WDT>(A, b, r, t0 + ATT_TE + pe_, p1, nkv, ppart, P);
     // logits
     for (int i = tid; i < HQ * ATT_TE; i += ATT_THREADS) {
       const int hh = i / ATT_TE, e = i % ATT_TE;

@@ -372,6 +372,73 @@ __device__ __forceinline__ void f32_score_round_vec(const IndexArgs& A, const Ro
   key0 = ok ? score_key(s) : 0ull;
 }
 
+// The same evaluation for the 64 entries j0 .. j0+63 of one wavefront with
+// the key rows staged through a wavefront-private LDS tile, 16 elements of
+// every row at a time: four lanes load a row's 64 contiguous bytes, so each
+// load instruction reads 16 whole segments instead of 64 scattered ones (the
+// per-lane row loads above are bound by the address unit when one workgroup
+// scores a whole row).  The tile rows are padded to F32_TS floats, so the
+// per-lane reads that follow hit 64 distinct banks.  Heads are taken four at
+// a time (the rows are staged again for each group); each head keeps its own
+// float64 chain over the elements in order, and the heads are combined in
+// head order once their chains are complete: the same operations in the same
+// order as f32_score_round.  Needs d % 16 == 0.
+constexpr int F32_TS = 17;                 // tile row stride (floats)
+constexpr int F32_TILE = 64 * F32_TS;      // tile floats per wavefront
+__device__ __forceinline__ void f32_score_wave_lds(const IndexArgs& A, int b, int n, int j0, const float* qrow,
+                                                   const float* wl, float* tile, uint64_t& key0) {
+  const int lane = threadIdx.x & 63;
+  const int d = A.d, H = A.H;
+  const float* kb = (const float*)A.ki + (int64_t)b * A.N_cap * d;
+  const int lr = lane >> 2, lf = lane & 3;   // load: row 16*t + lr, float4 lf of the 16 elements
+  const int nc = d / 16;
+  auto load = [&](int c, float4 (&v)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = min(j0 + 16 * t + lr, n - 1);       // rows past n: a valid row, never used
+      v[t] = *(const float4*)(kb + (int64_t)row * d + c * 16 + lf * 4);
+    }
+  };
+  double s = 0.0;
+#pragma unroll 1
+  for (int h0 = 0; h0 < H; h0 += 4) {
+    double dot[4] = {0.0, 0.0, 0.0, 0.0};
+    float4 cur[4], nxt[4];
+    load(0, cur);
+#pragma unroll 1
+    for (int c = 0; c < nc; ++c) {
+      if (c + 1 < nc) load(c + 1, nxt);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float* p = tile + (16 * t + lr) * F32_TS + 4 * lf;
+        p[0] = cur[t].x; p[1] = cur[t].y; p[2] = cur[t].z; p[3] = cur[t].w;
+      }
+      // the LDS operations of one wavefront complete in issue order
+      __builtin_amdgcn_wave_barrier();
+      float kv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kv[e] = tile[lane * F32_TS + e];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        if (h0 + hh < H) {
+          const float* q = qrow + (h0 + hh) * d + c * 16;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) dot[hh] = fma((double)q[e], (double)kv[e], dot[hh]);
+        }
+      }
+      if (c + 1 < nc) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cur[t] = nxt[t];
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh)
+      if (h0 + hh < H) s = combine_step(s, dot[hh], wl[h0 + hh]);
+  }
+  key0 = j0 + lane < n ? score_key(s) : 0ull;
+}
+
 // ------------------------------------------------------------------------
 // Wavefront bitonic sort of one u64 per lane, descending across lanes.
 // ------------------------------------------------------------------------
@@ -422,7 +489,7 @@ struct SelShared {
   uint32_t scan[SEL_WAVES];
   uint64_t red64[2][SEL_WAVES];
   int32_t off[MAXCH + 1];
-  uint32_t bitmap[BITMAP_BITS / 32];
+  __align__(16) uint32_t bitmap[BITMAP_BITS / 32];   // (also fp32 rows' keys: 8-byte aligned)
   uint64_t rkey[64];           // items of the threshold bin, resolved exactly
   int32_t rj[64];
   uint32_t rank[64];
@@ -784,15 +851,21 @@ __device__ __forceinline__ void select_streamed(const IndexArgs& A, int r, int n
     uint64_t bk[LB];
     int32_t bj[LB];
     uint32_t vm = 0;
-    // the keys go through LDS (the scoring buffers' region, unused by the
-    // fp32 path), so that the scoring loop is not unrolled
-    uint64_t* kl = (uint64_t*)tbuf;
+    // the keys go through LDS, so that the scoring loop is not unrolled:
+    // rows of up to 4096 entries keep them in the (here unused) bitmap and
+    // stage their key rows through per-wavefront tiles in the scoring
+    // buffers' region; longer rows keep them in that region and load each
+    // lane's row directly
+    constexpr int KL_BITMAP = BITMAP_BITS / 64;         // keys the bitmap holds
+    const bool tiles = n <= KL_BITMAP && A.d % 16 == 0;
+    uint64_t* kl = tiles ? (uint64_t*)S.bitmap : (uint64_t*)tbuf;
 #pragma unroll 1
     for (int u = 0; u < LB; ++u) {
       const int j0 = u * SEL_THREADS + wave * 64;
       if (j0 >= n) break;                 // uniform over the wavefront
       uint64_t k0;
-      f32_score_round_vec(A, src.rw, j0, ql, wl, k0);
+      if (tiles) f32_score_wave_lds(A, src.rw.b, n, j0, ql, wl, tbuf + wave * F32_TILE, k0);
+      else f32_score_round_vec(A, src.rw, j0, ql, wl, k0);
       kl[u * SEL_THREADS + threadIdx.x] = k0;
     }
     __syncthreads();
@@ -904,6 +977,7 @@ static inline size_t select_smem(int dt, int H, int d) {
   size_t region = 12 * (size_t)CMAX;                                   // candidate keys + indices
   const size_t stream = sizeof(float) * SEL_WAVES * WBUF;              // scoring buffers (aliased)
   if (stream > region) region = stream;
+  static_assert(sizeof(float) * SEL_WAVES * F32_TILE <= 12 * (size_t)CMAX, "fp32 key tiles fit below the weights");
   return sizeof(SelShared) + region + sizeof(float) * 32;
 }
 

@@ -51,8 +51,11 @@ __device__ __forceinline__ void fresh_row(const CompressArgs& k, int b, void* co
   pool_encode_block<DT_BF16, ODT, 128>(a, 0, 0, pe);
 }
 
-// Blocks [0, nscan) are the indexer scan (chunk bid % NCH of row group
-// bid / NCH); the rest are the splits of the dense attention jobs in `bt`.
+// After the compress blocks come the splits of the dense attention jobs in
+// `bt`, then the nscan blocks of the indexer scan (chunk i % NCH of row group
+// i / NCH for scan block i): the splits are dispatched first, so their
+// gathers and partial writes start ahead of the scan's stream instead of
+// trailing it (about 1 us less per step at the 1M layer pair).
 // Three workgroups per CU with 2048-key chunks (the long contexts: 168
 // VGPRs; the LDS union, 44.8 KB, also fits three): a scan that fills two
 // workgroups per CU leaves the third to the attention.  The smaller chunks
@@ -83,6 +86,8 @@ __global__ __launch_bounds__(256, KPL == 32 ? 3 : 2) void step_scan_attend_kerne
     return;
   }
   bid -= fd.ncomp;
+  const int ndense = bt.blk0[bt.njobs];
+  bid = bid < ndense ? bid + nscan : bid - ndense;     // [0, nscan): scan; then the splits
   if (threadIdx.x == 0) zero = 0;
   __syncthreads();
   if (bid < nscan) {

@@ -81,6 +81,8 @@ def test_index_validation(L):
     assert index(L, ki_dt=lca.F32) == 2
     assert index(L, qi_dt=lca.BF16, ki_dt=lca.BF16) == 2
     assert index(L, qi_dt=lca.F32, ki_dt=lca.F32) == 1        # F32 must not pass scales
+    f32 = dict(qi_dt=lca.F32, ki_dt=lca.F32, qi_scale=None, ki_scale=None, d_I=64)
+    assert index(L, H_I=17, **f32) == 2                        # F32: the kernels stage 16 head weights
     assert index(L, ws=None) == 4
     assert index(L, ws_bytes=16) == 4
     assert b"workspace" in L.lca_last_error()
