@@ -96,10 +96,12 @@ const char* lca_last_error(void);
  *   x        [B][x_rows][D]   x_dt in {F32, BF16}
  *   gate     [B][x_rows]      fp32, one logit per raw token
  *   pos_bias [m]              fp32
- *   x_tok0, nblk [B] int32; dst_row0 [B] int64 (device arrays).  Caller
- *            guarantees 0 <= nblk[b] <= nblk_max, x_tok0[b] >= 0,
+ *   x_tok0, nblk [B] int32; dst_row0 [B] int64 (device arrays), meant to
+ *            satisfy 0 <= nblk[b] <= nblk_max, x_tok0[b] >= 0,
  *            x_tok0[b] + nblk[b]*m <= x_rows, 0 <= dst_row0[b],
- *            dst_row0[b] + nblk[b] <= dst_rows.
+ *            dst_row0[b] + nblk[b] <= dst_rows.  Blocks past nblk_max are not
+ *            computed, and a block whose tokens or output row fall outside
+ *            x / dst is skipped (nothing read or written for it).
  *   dst      [B][dst_rows][D] (MXFP4: [B][dst_rows][D/2] bytes)
  *   dst_scale FP8: float [B][dst_rows][D/64]; MXFP4: uint8 [B][dst_rows][D/32];
  *            must be NULL for F32/BF16.
@@ -179,7 +181,7 @@ lca_status lca_compress_batch(const lca_compress_job* jobs, int32_t njobs, void*
  *          [B][Tq][H_I][d_I/32] for MXFP4, NULL otherwise
  *   w      [B][Tq][H_I] fp32 head weights
  *   ki     [B][N_cap][d_I]     ki_dt == qi_dt; ki_scale E8M0 [B][N_cap][d_I/32]
- *   n_elig [B][Tq] int32 (device), caller guarantees 0 <= n_elig <= N_cap
+ *   n_elig [B][Tq] int32 (device); the kernels clamp it to [0, N_cap]
  *   idx_out   [B][Tq][k] int32: the selected j in ascending order, -1 padded
  *   score_out optional [B][Tq][k] double: s_j of each idx_out entry (0 for -1)
  *   ws / ws_bytes: workspace of at least lca_index_topk_ws(...) bytes
@@ -217,8 +219,10 @@ size_t lca_index_topk_ws(int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int64_
  *          [B][N_cap][D/64] for FP8, NULL otherwise
  *   idx    [B][Tq][k] int32 (device); entries < 0 or >= N_cap are skipped
  *   win    [B][W_buf][D]   win_dt in {F32, BF16}; win_begin/win_len [B][Tq]
- *          int32 (device), caller guarantees 0 <= win_begin,
- *          0 <= win_len, win_begin + win_len <= W_buf
+ *          int32 (device), meant to satisfy 0 <= win_begin, 0 <= win_len,
+ *          win_begin + win_len <= W_buf; the kernels clamp the begin to
+ *          [0, W_buf - 1] and the length to [0, W_buf - begin], so no value
+ *          reads outside `win`
  *   sink   [Hq] fp32
  *   out    [B][Tq][Hq][D]  out_dt in {F32, BF16}; lse optional fp32 [B][Tq][Hq]
  * Supported: D = 128; Hq in {16, 32, 64}; 0 <= k <= 2048.  F32 inputs are
@@ -238,7 +242,7 @@ lca_status lca_sparse_mqa_attend(const void* q, lca_dtype q_dt, const void* kv, 
  * eligible entry j < n_elig[r] of sequence b instead of a selected list.
  * [release notes (agentlenshq.com), 重度壓縮注意力 (HCA): the 128x compressed
  * sequence is short, so it is attended densely, plus a sliding window.]
- *   n_elig [B][Tq] int32 (device), caller guarantees 0 <= n_elig <= N_cap.
+ *   n_elig [B][Tq] int32 (device); the kernels clamp it to [0, N_cap].
  * Supported: as lca_sparse_mqa_attend.
  */
 lca_status lca_hca_attend(const void* q, lca_dtype q_dt, const void* kv, lca_dtype kv_dt,

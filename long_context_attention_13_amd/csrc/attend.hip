@@ -28,13 +28,14 @@ size_t attend_ws_bytes(int B, int Tq, int Hq, int D, int64_t n_kv_max, int64_t W
   return align256(sizeof(float) * R * P.S * Hq * 2) + align256(sizeof(float) * R * P.S * Hq * D);
 }
 
-// Item p of row r's list: returns the source pointer class and row, or -1.
+// Item p of row r's list (wb: the row's window begin): returns the source
+// pointer class and row, or -1.
 struct ListItem {
   int kind;      // 0 entry, 1 window token, -1 skip
   int64_t row;   // row in kv ([B][N_cap]) or win ([B][W_buf])
 };
 
-__device__ __forceinline__ ListItem list_item(const AttendArgs& A, int b, int r, int p, int nkv) {
+__device__ __forceinline__ ListItem list_item(const AttendArgs& A, int b, int r, int p, int nkv, int wb) {
   ListItem it;
   if (p < nkv) {
     int64_t j = A.sparse ? (int64_t)A.idx[(int64_t)r * A.k + p] : (int64_t)p;
@@ -43,7 +44,7 @@ __device__ __forceinline__ ListItem list_item(const AttendArgs& A, int b, int r,
     it.row = (int64_t)b * A.N_cap + j;
   } else {
     it.kind = 1;
-    it.row = (int64_t)b * A.W_buf + A.win_begin[r] + (p - nkv);
+    it.row = (int64_t)b * A.W_buf + wb + (p - nkv);
   }
   return it;
 }
@@ -98,13 +99,13 @@ struct ValuPiece {
 };
 
 template <int KVDT, int WDT>
-__device__ __forceinline__ void valu_fetch(const AttendArgs& A, int b, int r, int p, int p1, int nkv, int part,
+__device__ __forceinline__ void valu_fetch(const AttendArgs& A, int b, int r, int p, int p1, int nkv, int wb, int part,
                                            ValuPiece& P) {
   P.ok = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { P.k[i] = 0.f; P.v[i] = 0.f; }
   if (p >= p1) return;
-  const ListItem it = list_item(A, b, r, p, nkv);
+  const ListItem it = list_item(A, b, r, p, nkv, wb);
   if (it.kind == 0) {
     kv_piece<KVDT>(A.kv, A.kv_scale, it.row, 16 * part, P.k);
     if (A.v) kv_piece<KVDT>(A.v, A.v_scale, it.row, 16 * part, P.v);
@@ -132,8 +133,9 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   const int split = blockIdx.x, r = blockIdx.y;
   const int b = r / A.Tq;
   const int tid = threadIdx.x;
-  const int nkv = A.sparse ? A.k : A.n_elig[r];
-  const int L = nkv + A.win_len[r];
+  const int nkv = A.sparse ? A.k : att_nelig(A, r);
+  const int2 win = att_window(A, r);
+  const int L = nkv + win.y;
   const int p0 = split * split_items;
   const int p1 = S == 1 ? L : min(L, p0 + split_items);
   if (S > 1 && p0 >= L) return;             // an empty split: the merge does not read it
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   static_assert(ATT_TE * (D / 16) == ATT_THREADS, "one 16-element piece per thread and tile");
   const int pe_ = tid >> 3, ppart = tid & 7;          // this thread's item in the tile, and piece
   ValuPiece P;
-  if (p0 < p1) valu_fetch<KVDT, WDT>(A, b, r, p0 + pe_, p1, nkv, ppart, P);
+  if (p0 < p1) valu_fetch<KVDT, WDT>(A, b, r, p0 + pe_, p1, nkv, win.x, ppart, P);
   for (int t0 = p0; t0 < p1; t0 += ATT_TE) {
     // stage the fetched tile as fp32, then fetch the next one
 #pragma unroll
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
     }
     if (ppart == 0) valid[pe_] = P.ok;
     __syncthreads();
-    if (t0 + ATT_TE < p1) valu_fetch<KVDT, WDT>(A, b, r, t0 + ATT_TE + pe_, p1, nkv, ppart, P);
+    if (t0 + ATT_TE < p1) valu_fetch<KVDT, WDT>(A, b, r, t0 + ATT_TE + pe_, p1, nkv, win.x, ppart, P);
     // logits
     for (int i = tid; i < HQ * ATT_TE; i += ATT_THREADS) {
       const int hh = i / ATT_TE, e = i % ATT_TE;

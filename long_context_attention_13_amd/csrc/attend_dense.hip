@@ -200,18 +200,19 @@ __global__ __launch_bounds__(DW_NT, 512 / DW_NT) void attend_dense_wide_kernel(A
   const int qrow = wave >> 1, head = (wave & 1) * 32 + n;
   const bool rvalid = t0r + qrow < A.Tq;
   const int r = b * A.Tq + (rvalid ? t0r + qrow : t0r);
-  const int nkv_r = A.n_elig[r];
-  const int wb_r = A.win_begin[r], wl_r = A.win_len[r];
+  const int nkv_r = att_nelig(A, r);
+  const int2 ws_r = att_window(A, r);
+  const int wb_r = ws_r.x, wl_r = ws_r.y;
   // the group's list bounds, the same for every wavefront
   int nkv = 0, wlo = 0x7FFFFFFF, whi = 0;
 #pragma unroll
   for (int q = 0; q < DW_ROWS; ++q) {
     if (t0r + q >= A.Tq) break;
     const int rq = b * A.Tq + t0r + q;
-    nkv = max(nkv, A.n_elig[rq]);
-    const int wb = A.win_begin[rq], wl = A.win_len[rq];
-    wlo = min(wlo, wb);
-    whi = max(whi, wb + wl);
+    nkv = max(nkv, att_nelig(A, rq));
+    const int2 wq = att_window(A, rq);
+    wlo = min(wlo, wq.x);
+    whi = max(whi, wq.x + wq.y);
   }
   if (whi < wlo) whi = wlo;
   const int L = nkv + (whi - wlo);
@@ -359,7 +360,8 @@ __global__ __launch_bounds__(DS_NT) __attribute__((amdgpu_waves_per_eu(2))) void
   const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int head = wave * 32 + n;
-  const int wb_r = A.win_begin[r], wl_r = A.win_len[r];
+  const int2 ws_r = att_window(A, r);
+  const int wb_r = ws_r.x, wl_r = ws_r.y;
   const int L = A.k + wl_r;
   const int64_t wbase = (int64_t)b * A.W_buf + wb_r;
   const int32_t* idr = A.idx + (int64_t)r * A.k;

@@ -34,6 +34,23 @@ inline Plan att_plan(int64_t Tq, int64_t n_kv_max, int64_t W_buf) {
   return Plan{(int)((L + items - 1) / items), (int)items};
 }
 
+// Device-resident sizes are clamped where a kernel reads them, so that no
+// value sends a read outside the buffers the call describes: a row's
+// eligible count to [0, N_cap], its window slice to rows of [0, W_buf) (the
+// begin to a row that exists, as the loads of a tile read the slice's first
+// row even when it is empty).
+// (N_cap and W_buf are below 2^31.)
+__device__ __forceinline__ int att_nelig(const AttendArgs& A, int r) {
+  return min(max(A.n_elig[r], 0), (int)A.N_cap);
+}
+// (begin, length) of row r's window slice
+__device__ __forceinline__ int2 att_window(const AttendArgs& A, int r) {
+  const int W = (int)A.W_buf;
+  const int wb = min(max(A.win_begin[r], 0), max(W - 1, 0));
+  const int wl = min(max(A.win_len[r], 0), W - wb);
+  return make_int2(wb, wl);
+}
+
 __device__ __forceinline__ void store_out(const AttendArgs& A, int64_t i, float v) {
   if (A.out_dt == DT_F32) ((float*)A.out)[i] = v;
   else ((uint16_t*)A.out)[i] = f32_to_bf16(v);
@@ -267,13 +284,14 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
   const int ngrp = (A.Tq + QB - 1) / QB;
   const int b = grp / ngrp;
   const int t0r = (grp % ngrp) * QB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, col = lane & 15;
   const int qrow = wave / (HQ / 16);                // this wave's row within the group
   const bool rvalid = t0r + qrow < A.Tq;
   const int r = b * A.Tq + (rvalid ? t0r + qrow : t0r);
-  const int nkv_r = A.sparse ? A.k : A.n_elig[r];
-  const int wb_r = A.win_begin[r], wl_r = A.win_len[r];
+  const int nkv_r = A.sparse ? A.k : att_nelig(A, r);
+  const int2 ws_r = att_window(A, r);
+  const int wb_r = ws_r.x, wl_r = ws_r.y;
   int nkv = nkv_r, wlo = wb_r, whi = wb_r + wl_r;
   if (QB > 1) {
     // the same for every wave of the group (uniform loop bounds)
@@ -282,10 +300,10 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
     for (int q = 0; q < QB; ++q) {
       if (t0r + q >= A.Tq) break;
       const int rq = b * A.Tq + t0r + q;
-      nkv = max(nkv, A.n_elig[rq]);
-      const int wb = A.win_begin[rq], wl = A.win_len[rq];
-      wlo = min(wlo, wb);
-      whi = max(whi, wb + wl);
+      nkv = max(nkv, att_nelig(A, rq));
+      const int2 wq = att_window(A, rq);
+      wlo = min(wlo, wq.x);
+      whi = max(whi, wq.x + wq.y);
     }
     if (whi < wlo) whi = wlo;
   }
@@ -491,7 +509,7 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
   const int d = threadIdx.x & 127;
   // the row's list length is requested with the partials, which are read for
   // every planned split (all inside the workspace) and masked once it arrives
-  const int L = (A.sparse ? A.k : A.n_elig[r]) + A.win_len[r];
+  const int L = (A.sparse ? A.k : att_nelig(A, r)) + att_window(A, r).y;
   float* wsp = sm.wsp;
   auto& red = sm.red;
   const float sk = A.sink[h] * LOG2E;                       // partial maxima are base-2 logits

@@ -24,6 +24,18 @@ struct PeShared {
 template <int ODT, int D>
 __device__ __forceinline__ void encode_row(const CompressArgs& a, int b, int i, float c);
 
+// Whether block i of sequence b lies inside the buffers the call describes:
+// the tokens it reads (its span less the overlap rows a sequence's first
+// block skips) within [0, x_rows), its output row within [0, dst_rows).  A
+// block outside them (device-resident x_tok0 / dst_row0 out of range) is
+// skipped: nothing is read or written for it.
+__device__ __forceinline__ bool block_in_range(const CompressArgs& a, int b, int i) {
+  const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * a.m;
+  const int64_t row = (int64_t)a.dst_row0[b] + i;
+  const int skip = (a.overlap > 0 && row == 0) ? a.overlap : 0;
+  return tok0 + skip >= 0 && tok0 + a.m + a.overlap <= a.x_rows && row >= 0 && row < a.dst_rows;
+}
+
 // Per-channel gates (gate [B][x_rows][D], bias [m + overlap][D]): one softmax
 // per channel over the block's span.  Thread t handles CPL channels of the
 // tokens of its group, as in pool_encode_block; pass 1 finds each channel's
@@ -35,7 +47,7 @@ __device__ __forceinline__ void pool_encode_block_pc(const CompressArgs& a, int 
   constexpr int NCK = D / CPL;
   constexpr int G = PE_THREADS / NCK;
   static_assert(G * D <= 2048, "group partials fit");
-  if (i >= a.nblk[b]) return;
+  if (i >= a.nblk[b] || !block_in_range(a, b, i)) return;
   const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * a.m;
   const int span = a.m + a.overlap;
   const int skip = (a.overlap > 0 && a.dst_row0[b] + i == 0) ? a.overlap : 0;
@@ -133,7 +145,7 @@ __device__ __forceinline__ void pool_encode_block(const CompressArgs& a, int b, 
   }
   const int nblk = a.nblk[b];
   const int64_t tok0 = (int64_t)a.x_tok0[b] + (int64_t)i * a.m;
-  if (i >= nblk) return;
+  if (i >= nblk || !block_in_range(a, b, i)) return;
   const int tid = threadIdx.x;
   const int ck = tid % NCK, grp = tid / NCK;
   const int m = a.m + a.overlap;                 // tokens of the block's span

@@ -61,7 +61,7 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
 
   // the row length and head weights first (waits for them then do not wait
   // for the larger requests behind), then the per-chunk summaries
-  const int n = A.n_elig[r];
+  const int n = idx_nelig(A, r);
   const float wv = (threadIdx.x < (unsigned)A.H) ? A.w[(int64_t)r * A.H + threadIdx.x] : 0.f;
   constexpr int CPTH = MAXCH / SEL_THREADS;          // chunks per thread
   int cv[CPTH];

@@ -104,8 +104,8 @@ __device__ __forceinline__ void index_chunk_body(const IndexArgs& A, const IdxWs
   // they arrive, in a fixed order: row lengths, head weights, the query
   // operand, then the first round of key tiles (rows up to N_cap exist, and
   // entries past a row's length are discarded by the eligibility test)
-  rw.n[0] = A.n_elig[rw.r[0]];
-  rw.n[1] = A.n_elig[rw.r[1] >= 0 ? rw.r[1] : rw.r[0]];
+  rw.n[0] = idx_nelig(A, rw.r[0]);
+  rw.n[1] = idx_nelig(A, rw.r[1] >= 0 ? rw.r[1] : rw.r[0]);
   const int wq = (threadIdx.x >> 4) & 1, wh = threadIdx.x & 15;
   const int rwq = wq == 0 ? rw.r[0] : rw.r[1];    // (no dynamic indexing: keeps rw in registers)
   const int wrow = (wq < NQ && rwq >= 0) ? rwq : rw.r[0];

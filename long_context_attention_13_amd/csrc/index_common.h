@@ -22,6 +22,12 @@ constexpr int KROW = 20;           // LDS floats per key in the transpose buffer
 constexpr int BITMAP_BITS = 1 << 18;
 
 
+// Row r's eligible count, clamped where a kernel reads it to [0, N_cap], so
+// that no value of the device-resident counts reads past the key cache.
+__device__ __forceinline__ int idx_nelig(const IndexArgs& A, int64_t r) {
+  return min(max(A.n_elig[r], 0), (int)A.N_cap);      // N_cap < 2^31
+}
+
 // ------------------------------------------------------------------------
 // Query state of one wavefront (up to two query rows of one sequence).
 // ------------------------------------------------------------------------

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
   PfQuery<HP> P;
   bool wneg;
   pf_load_query<HP>(A, rv, r, P, wneg);
-  const int nq = rv ? A.n_elig[r] : 0;
+  const int nq = rv ? idx_nelig(A, r) : 0;
   int nmax = nq;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, WAVE));
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
   const int t = blockIdx.x * PF_QROWS + wave * 16 + c;
   const bool rv = t < A.Tq;
   const int64_t r = (int64_t)b * A.Tq + (rv ? t : 0);
-  const int nq = rv ? A.n_elig[r] : 0;
+  const int nq = rv ? idx_nelig(A, r) : 0;
   const float thr = rv ? W.thr[r] : __builtin_inff();
   int nmax = nq;
 #pragma unroll
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(PS_NT) void pf_select_kernel(IndexArgs A, PfWs W, i
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t r = blockIdx.x;
-  const int n = A.n_elig[r];
+  const int n = idx_nelig(A, r);
   const int kk = min(n, A.k);
   int32_t* out = A.idx_out + r * A.k;
   double* sout = A.score_out ? A.score_out + r * A.k : nullptr;
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(SEL_THREADS) void pf_fallback_kernel(IndexArgs A, P
     __syncthreads();
     if (threadIdx.x < 32) wl[threadIdx.x] = (threadIdx.x < (unsigned)A.H) ? A.w[(int64_t)r * A.H + threadIdx.x] : 0.f;
     __syncthreads();
-    const int n = A.n_elig[r];
+    const int n = idx_nelig(A, r);
     const int kk = n < A.k ? n : A.k;
     int32_t* out = A.idx_out + (int64_t)r * A.k;
     double* sout = A.score_out ? A.score_out + (int64_t)r * A.k : nullptr;

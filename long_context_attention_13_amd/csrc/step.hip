@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, KPL == 32 ? 3 : 2) void step_scan_attend_kerne
     const int r = local / S, b = r / aj.Tq;
     const int en = k.nblk[b] > 0 ? (int)k.dst_row0[b] : -1;
     const int p0 = (local % S) * bt.items[j];
-    if (en >= p0 && en < p0 + bt.items[j] && en < aj.n_elig[r]) {   // uniform over the workgroup
+    if (en >= p0 && en < p0 + bt.items[j] && en < att_nelig(aj, r)) {   // uniform over the workgroup
       fresh_row<KVDT>(k, b, fresh, fresh + 128, &zero, sm.pe);
       __syncthreads();
       fe.j = en;
