@@ -342,7 +342,8 @@ lca_status lca_attend_batch(const lca_attend_job* jobs, int32_t njobs, void* str
  *   ajobs    0 <= najobs <= LCA_MAX_ATTEND_JOBS attention jobs (as lca_attend_batch)
  * Each part is validated as its own call.  Dense attention jobs must not
  * read or write memory the indexer job writes (idx_out, score_out, its
- * workspace); sparse jobs may read idx_out.  Host arrays are read during the
+ * workspace); a dense job whose output, lse or workspace overlaps those is
+ * rejected with LCA_EINVAL; sparse jobs may read idx_out.  Host arrays are read during the
  * call only.  When every compress job has nblk_max = 1, overlap = 0, bf16
  * input and width 128, and no compress job writes any byte that the scan or
  * the dense jobs read or write -- except a job that writes exactly the

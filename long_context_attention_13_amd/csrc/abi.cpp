@@ -322,6 +322,36 @@ lca_status attend_batch_check(const char* who, const lca_attend_job* jobs, int32
   return ok();
 }
 
+// The dense attention jobs of a decode step run beside the indexer's scan,
+// so none may write memory that the indexer writes: its output, scores and
+// workspace against each dense job's output, lse and workspace (the bytes the
+// kernels touch: the needed workspace sizes, not the declared ones).
+struct Span {
+  uintptr_t a, n;
+};
+bool spans_overlap(Span x, Span y) { return x.n > 0 && y.n > 0 && x.a < y.a + y.n && y.a < x.a + x.n; }
+
+lca_status step_disjoint_check(const char* name, const lca::IndexArgs& ia, const lca::AttendBatch& ab) {
+  const int64_t R = (int64_t)ia.B * ia.Tq;
+  if (R == 0) return ok();
+  const Span iw[3] = {{(uintptr_t)ia.idx_out, (uintptr_t)(R * ia.k * 4)},
+                      {(uintptr_t)ia.score_out, ia.score_out ? (uintptr_t)(R * ia.k * 8) : 0},
+                      {(uintptr_t)ia.ws, lca::index_ws_bytes(ia.B, ia.Tq, ia.H, ia.d, ia.N_cap, ia.k, ia.dt)}};
+  for (int j = 0; j < ab.njobs; ++j) {
+    const lca::AttendArgs& a = ab.job[j];
+    const int64_t Ra = (int64_t)a.B * a.Tq;
+    if (a.sparse || Ra == 0) continue;
+    const Span aw[3] = {{(uintptr_t)a.out, (uintptr_t)(Ra * a.Hq * a.D * (a.out_dt == lca::DT_F32 ? 4 : 2))},
+                        {(uintptr_t)a.lse, a.lse ? (uintptr_t)(Ra * a.Hq * 4) : 0},
+                        {(uintptr_t)a.ws, lca::attend_ws_bytes(a.B, a.Tq, a.Hq, a.D, a.N_cap, a.W_buf)}};
+    for (const Span& x : aw)
+      for (const Span& y : iw)
+        REQ(!spans_overlap(x, y), LCA_EINVAL,
+            "%s: dense attention job %d writes memory that the index job writes (they run concurrently)", name, j);
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,6 +378,8 @@ lca_status lca_decode_step(const lca_compress_job* cjobs, int32_t ncjobs, const 
   }
   lca::AttendBatch ab;
   st = attend_batch_check(name, ajobs, najobs, 0, &ab);
+  if (st != LCA_OK) return st;
+  st = step_disjoint_check(name, ia, ab);
   if (st != LCA_OK) return st;
   return hip_status(lca::launch_decode_step(nullptr, nullptr, cb, ia, ab, (hipStream_t)stream), name);
 }
@@ -398,6 +430,8 @@ lca_status lca_decode_step_noalloc(const lca_compress_job* cjobs, int32_t ncjobs
   lca::AttendBatch ab;
   st = attend_batch_check(name, A, najobs, 0, &ab);
   if (st != LCA_OK) return st;
+  st = step_disjoint_check(name, ia, ab);
+  if (st != LCA_OK) return st;
   // the current device's scratch (when a workspace is needed at all)
   if (need > 0) {
     void* base = nullptr;
@@ -430,6 +464,8 @@ lca_status lca_decode_step_events(const lca_compress_job* cjobs, int32_t ncjobs,
   }
   lca::AttendBatch ab;
   st = attend_batch_check(name, ajobs, najobs, 0, &ab);
+  if (st != LCA_OK) return st;
+  st = step_disjoint_check(name, ia, ab);
   if (st != LCA_OK) return st;
   lca::LaunchLog lg{(hipEvent_t*)events, LCA_MAX_STEP_LAUNCHES + 1, 0, names};
   st = hip_status(lca::launch_decode_step(nullptr, nullptr, cb, ia, ab, (hipStream_t)stream, &lg), name);
@@ -536,6 +572,8 @@ lca_status lca_decode_loop_step(const lca_append_job* app, int32_t napp, const l
   }
   lca::AttendBatch ab;
   st = attend_batch_check(name, ajobs, najobs, 0, &ab);
+  if (st != LCA_OK) return st;
+  st = step_disjoint_check(name, ia, ab);
   if (st != LCA_OK) return st;
   return hip_status(lca::launch_decode_step(&apb, &mp, cb, ia, ab, (hipStream_t)stream), name);
 }

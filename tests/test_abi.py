@@ -227,6 +227,10 @@ def test_decode_step_validation(L):
     assert decode_step(L, [], index_job(B=0), [attend_job(), attend_job(Hq=32)]) == 2
     assert b"attention job 1" in L.lca_last_error()
     assert decode_step(L, [], index_job(ws=None), []) == 4
+    # a dense job that would write the indexer's output while the scan runs
+    dense = attend_job(sparse=0, idx=None, k=0, n_elig=FAKE, out=FAKE + 4096)
+    assert decode_step(L, [], index_job(idx_out=FAKE + 4096), [dense]) == 1
+    assert b"index job writes" in L.lca_last_error()
 
 
 def test_decode_step_events_validation(L):
