@@ -265,12 +265,15 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
       // at most 8 bits from the highest bit where the row's samples differ
       // (their common leading bits -- most of the exponent -- would put
       // nearly all of them in one bin and serialise the counting)
-      uint32_t vmx = 0, vmn = 0xFFFFu;
-      for (int i = lane; i < Sq; i += 64) {
-        const uint32_t x = v[i];
-        vmx = max(vmx, x);
-        vmn = min(vmn, x);
-      }
+      // Every lane holds at least one sample (Sq >= PF_RANK = 64 lanes), so
+      // the smallest lane maximum vmn has at least PF_RANK samples at or
+      // above it: the PF_RANK-th largest is >= vmn, and samples below vmn
+      // take no part in the counting (they would pile into the lowest bins
+      // and serialise the LDS atomics).
+      static_assert(PF_RANK == WAVE, "one lane maximum per rank");
+      uint32_t vmx = 0;
+      for (int i = lane; i < Sq; i += 64) vmx = max(vmx, (uint32_t)v[i]);
+      uint32_t vmn = vmx;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
         vmx = max(vmx, (uint32_t)__shfl_xor((int)vmx, o, WAVE));
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
         wave_lds_sync();
         for (int i = lane; i < Sq; i += 64) {
           const uint32_t x = v[i];
-          if ((x & pmask) == prefix) atomicAdd(&hw[(x >> shift) & dmask], 1u);
+          if (x >= vmn && (x & pmask) == prefix) atomicAdd(&hw[(x >> shift) & dmask], 1u);
         }
         wave_lds_sync();
         int above;
