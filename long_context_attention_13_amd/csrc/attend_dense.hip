@@ -46,17 +46,31 @@ __device__ __forceinline__ int dw_col(int e) { return (e & ~15) | (e & 3) | ((e 
 // Staging of a tile by NT threads: task (pr, cq) = items 2*pr, 2*pr + 1 of
 // the tile, dims 8*cq .. +7 (32 x 16 tasks); thread t takes pr = t % 32 and
 // cq = t / 32 + (NT / 32) * c.  An item is an entry (kind 0), a window token
-// (1) or nothing (-1); each load reads a valid row.
+// (1) or nothing (-1); each load reads a valid row.  A tile whose items are
+// all entries (`full`, the same for every thread: most tiles of a long list)
+// takes a path without the per-item source selects and masks.
 template <int NT>
 struct DwRegs {
   int4 v[512 / NT][2];
   int kind[2];
+  bool full;
 };
 
 template <int NT>
 __device__ __forceinline__ void dw_fetch(const AttendArgs& A, int b, int64_t wbase, int nkv, int t0, int L,
                                          DwRegs<NT>& R) {
   const int t = threadIdx.x, pr = t & 31, cq0 = t >> 5;
+  R.full = t0 + MT_TE <= nkv && t0 + MT_TE <= A.N_cap;      // (then also <= L)
+  if (R.full) {
+    const uint16_t* row = (const uint16_t*)A.kv + ((int64_t)b * A.N_cap + t0 + 2 * pr) * 128;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int c = 0; c < 512 / NT; ++c) R.v[c][u] = *(const int4*)(row + u * 128 + (cq0 + (NT / 32) * c) * 8);
+      R.kind[u] = 0;
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int p = t0 + 2 * pr + u;
@@ -69,8 +83,8 @@ __device__ __forceinline__ void dw_fetch(const AttendArgs& A, int b, int64_t wba
   }
 }
 
-template <int NT>
-__device__ __forceinline__ void dw_store(const DwRegs<NT>& R, DwShared::Tile& T) {
+template <int NT, bool FULL>
+__device__ __forceinline__ void dw_store_t(const DwRegs<NT>& R, DwShared::Tile& T) {
   const int t = threadIdx.x, pr = t & 31, cq0 = t >> 5;
   uint32_t* vt = (uint32_t*)T.Vt + dw_col(2 * pr) / 2;
 #pragma unroll
@@ -79,7 +93,7 @@ __device__ __forceinline__ void dw_store(const DwRegs<NT>& R, DwShared::Tile& T)
     int4 v[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      v[u] = R.kind[u] >= 0 ? R.v[c][u] : make_int4(0, 0, 0, 0);
+      v[u] = FULL || R.kind[u] >= 0 ? R.v[c][u] : make_int4(0, 0, 0, 0);
       *(int4*)&T.Kl[(2 * pr + u) * DW_KROW + cq * 8] = v[u];
     }
     // V^T: dword (row d, column pair) = dim d of items 2pr (low half) and 2pr + 1
@@ -92,9 +106,15 @@ __device__ __forceinline__ void dw_store(const DwRegs<NT>& R, DwShared::Tile& T)
     }
   }
   if (cq0 == 0) {
-    T.okl[2 * pr] = R.kind[0] >= 0;
-    T.okl[2 * pr + 1] = R.kind[1] >= 0;
+    T.okl[2 * pr] = FULL || R.kind[0] >= 0;
+    T.okl[2 * pr + 1] = FULL || R.kind[1] >= 0;
   }
+}
+
+template <int NT>
+__device__ __forceinline__ void dw_store(const DwRegs<NT>& R, DwShared::Tile& T) {
+  if (R.full) dw_store_t<NT, true>(R, T);          // uniform
+  else dw_store_t<NT, false>(R, T);
 }
 
 __device__ __forceinline__ void dw_store4(const AttendArgs& A, int64_t i, f32x16 acc, int j0, float f) {
@@ -128,7 +148,7 @@ __device__ __forceinline__ void dw_qk(const DwShared::Tile& T, const bf16x8 (&qv
 // online softmax of the tile's logits (masked items -inf) for the lane's
 // head (lanes n and n + 32 share it), then O^T += V^T P^T in steps of 16
 // items.  exp2 is the hardware instruction: a weight below 2^-126 of the
-// row's largest contributes nothing.
+// running reference contributes nothing.
 __device__ __forceinline__ void dw_softmax_pv(const DwShared::Tile& T, f32x16 (&s)[2], float scale2, float& m_run,
                                               float& l_run, f32x16 (&acc)[4]) {
   const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
@@ -138,7 +158,10 @@ __device__ __forceinline__ void dw_softmax_pv(const DwShared::Tile& T, f32x16 (&
 #pragma unroll
     for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[ib][j]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const float m_new = fmaxf(m_run, tmax * scale2);
+  // the reference max moves only when the tile's max exceeds it by more than
+  // 8 (base 2): the weights then stay below 2^8 (exact range in bf16 and
+  // fp32), and the accumulator is rescaled on few tiles
+  const float m_new = (tmax * scale2 > m_run + 8.f) ? tmax * scale2 : m_run;
   const float mb = m_new == -INFINITY ? 0.f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(m_run - mb);
   m_run = m_new;
