@@ -365,6 +365,7 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
   const int64_t r0 = (int64_t)b * A.Tq + blockIdx.x * PF_QROWS + wave * 16;
   char* wlist = (char*)(W.cand + (r0 * PF_NKC + kc) * 4 * PF_LCAP);
   const uint32_t lane_off = (uint32_t)(((c * PF_NKC) * 4 + g) * PF_LCAP) * 8u;
+  uint64_t* const lp = (uint64_t*)(wlist + lane_off);   // this lane's list
   uint32_t cnt = 0;
 
   const int nst = (j1 - j0 + PF_STAGE - 1) / PF_STAGE;
@@ -433,11 +434,10 @@ __global__ __launch_bounds__(256) void pf_score_kernel(IndexArgs A, PfWs W, int 
       float sc[4];
       pf_combine<HP>(acc, P, sc);
       const int jt = sj + tt * 16;
+      const uint32_t jb = (uint32_t)(jt + 4 * g);    // this lane's first key of the tile
       // an overflowing list sends the row to the fallback: clamping the slot is enough
       auto put = [&](int i) {
-        const uint32_t j = (uint32_t)(jt + 4 * g + i);
-        *(uint64_t*)(wlist + lane_off + min(cnt, (uint32_t)PF_LCAP - 1u) * 8u) =
-            ((uint64_t)__float_as_uint(sc[i]) << 32) | j;
+        lp[min(cnt, (uint32_t)PF_LCAP - 1u)] = ((uint64_t)__float_as_uint(sc[i]) << 32) | (jb + (uint32_t)i);
         ++cnt;
       };
       if (jt + 16 <= nlim_min) {
