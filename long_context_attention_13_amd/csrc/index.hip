@@ -109,7 +109,7 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
     }
   }
   for (int i = threadIdx.x; i < 2048; i += SEL_THREADS) S.hist[i] = 0;
-  if (threadIdx.x == 0) { S.bcast[6] = 0; S.bcast[7] = 0; }
+  if (threadIdx.x == 0) S.bcast[6] = 0;
   const int kk = n < A.k ? n : A.k;
   int32_t* out = A.idx_out + (int64_t)r * A.k;
   double* sout = A.score_out ? A.score_out + (int64_t)r * A.k : nullptr;
@@ -135,14 +135,16 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
     // ---------------- candidate path ----------------
     // chunk offsets, the key range [gmin, gmax] of all candidates and the
     // flags (a chunk over its slots: bit 0; a chunk over the speculative
-    // slots: bit 1), in one exchange of per-wavefront partials
+    // slots: bit 1), in one exchange of per-wavefront partials (the flags
+    // as well: a word cleared by one thread could otherwise be set by another
+    // wavefront before the clear)
     static_assert(CPTH == 1, "one chunk per thread");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c0 = threadIdx.x;
     int v = c0 < nch ? cv[0] : 0;
     const bool bad_c = v < 0;
     if (bad_c) v = 0;
-    const uint64_t bal_bad = __ballot(bad_c), bal_over = __ballot(v > spec);
+    const int wfl = (__ballot(bad_c) ? 1 : 0) | (__ballot(v > spec) ? 2 : 0);
     const int incl = wave_incl_scan_dpp(v);
     const uint64_t wmx = wave_max_u64_dpp(v > 0 ? xv[0] : 0ull);
     const uint64_t wmn = wave_min_u64_dpp(v > 0 ? tv[0] : ~0ull);
@@ -150,7 +152,7 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
     if (lane == 0) {
       S.red64[0][wave] = wmx;
       S.red64[1][wave] = wmn;
-      if (bal_bad | bal_over) atomicOr(&S.bcast[7], (bal_bad ? 1 : 0) | (bal_over ? 2 : 0));
+      S.wflag[wave] = (uint32_t)wfl;
     }
     __syncthreads();
     if (wave == 0) {
@@ -159,8 +161,10 @@ __device__ __forceinline__ void index_select_body(const IndexArgs& A, const IdxW
       const int ti = wave_incl_scan_dpp(t);
       const uint64_t gx = wave_max_u64_dpp(lane < SEL_WAVES ? S.red64[0][lane] : 0ull);
       const uint64_t gn = wave_min_u64_dpp(lane < SEL_WAVES ? S.red64[1][lane] : ~0ull);
+      const uint32_t f = lane < SEL_WAVES ? S.wflag[lane] : 0u;
+      const int fl = (__ballot(f & 1u) ? 1 : 0) | (__ballot(f & 2u) ? 2 : 0);
       if (lane < SEL_WAVES) S.woff[lane] = ti - t;
-      if (lane == SEL_WAVES - 1) { S.bcast[4] = ti; S.bcast64[1] = gx; S.bcast64[2] = gn; }
+      if (lane == SEL_WAVES - 1) { S.bcast[4] = ti; S.bcast[7] = fl; S.bcast64[1] = gx; S.bcast64[2] = gn; }
     }
     __syncthreads();
     const int total = S.bcast[4];

@@ -500,6 +500,7 @@ struct SelShared {
   int32_t rj[64];
   uint32_t rank[64];
   uint32_t woff[SEL_WAVES];        // exclusive prefix of per-wavefront counts
+  uint32_t wflag[SEL_WAVES];       // per-wavefront flags of the candidate exchange
   uint32_t ecnt[LB * SEL_WAVES];   // emission: items above the threshold per (pass, wavefront)
   uint32_t epre[LB * SEL_WAVES];   // and their exclusive prefix
   uint32_t ecnt2[LB * SEL_WAVES];  // tied items per (pass, wavefront)
