@@ -122,14 +122,20 @@ __device__ __forceinline__ void valu_fetch(const AttendArgs& A, int b, int r, in
 // values: the value tile is staged beside the key tile).  Each thread stages
 // one 16-element piece of one item per tile, so a tile's loads are all in
 // flight together, and the next tile's pieces are fetched while the current
-// tile is computed.
+// tile is computed.  The TPH = 256 / HQ threads of a head (adjacent lanes)
+// compute its logits (each a few items, four dims per LDS read), run the
+// online softmax with lane shuffles and keep its running max and sum in
+// registers; each then accumulates DPT output dims.
 // ------------------------------------------------------------------------
 template <int QDT, int KVDT, int WDT, int HQ>
 __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, int S, int split_items, float* part_ml,
                                                                    float* part_o) {
   constexpr int D = 128;
-  constexpr int TPH = ATT_THREADS / HQ;      // threads per head
+  constexpr int DP = D + 4;                  // padded LDS row: 16-byte aligned, rows 4 banks apart
+  constexpr int TPH = ATT_THREADS / HQ;      // threads per head (consecutive lanes of one wavefront)
   constexpr int DPT = D / TPH;               // output dims per thread
+  constexpr int IPT = ATT_TE / TPH;          // items per thread and tile for the logits
+  static_assert(TPH <= 64 && IPT * TPH == ATT_TE && DPT % 4 == 0, "thread layout");
   const int split = blockIdx.x, r = blockIdx.y;
   const int b = r / A.Tq;
   const int tid = threadIdx.x;
@@ -140,16 +146,18 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   const int p1 = S == 1 ? L : min(L, p0 + split_items);
   if (S > 1 && p0 >= L) return;             // an empty split: the merge does not read it
 
-  __shared__ float qs[HQ][D];
-  __shared__ float kvs[ATT_TE][D + 1];
-  __shared__ float vls[ATT_TE][D + 1];          // values, when they are separate
+  __shared__ __align__(16) float qs[HQ][DP];
+  __shared__ __align__(16) float kvs[ATT_TE][DP];
+  __shared__ __align__(16) float vls[ATT_TE][DP];   // values, when they are separate
   __shared__ float lg[HQ][ATT_TE + 1];
-  __shared__ float mrun[HQ], lrun[HQ], alpha[HQ];
   __shared__ int valid[ATT_TE];
 
   for (int i = tid; i < HQ * D; i += ATT_THREADS) qs[i / D][i % D] = q_elem<QDT>(A, (int64_t)r * HQ * D + i) * A.scale;
-  if (tid < HQ) { mrun[tid] = -INFINITY; lrun[tid] = 0.f; }
-  const int h = tid / TPH, d0 = (tid % TPH) * DPT;
+  // thread t serves head h = t / TPH: the logits of items j + TPH*i of each
+  // tile (j = t % TPH), and output dims d0 .. d0 + DPT - 1; the head's running
+  // max and sum are held, equal, by all its TPH threads
+  const int h = tid / TPH, j = tid % TPH, d0 = j * DPT;
+  float m_run = -INFINITY, l_run = 0.f;
   float acc[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
@@ -162,44 +170,68 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   for (int t0 = p0; t0 < p1; t0 += ATT_TE) {
     // stage the fetched tile as fp32, then fetch the next one
 #pragma unroll
-    for (int i = 0; i < 16; ++i) kvs[pe_][16 * ppart + i] = P.k[i];
+    for (int i = 0; i < 16; i += 4)
+      *(float4*)&kvs[pe_][16 * ppart + i] = make_float4(P.k[i], P.k[i + 1], P.k[i + 2], P.k[i + 3]);
     if (A.v) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vls[pe_][16 * ppart + i] = P.v[i];
+      for (int i = 0; i < 16; i += 4)
+        *(float4*)&vls[pe_][16 * ppart + i] = make_float4(P.v[i], P.v[i + 1], P.v[i + 2], P.v[i + 3]);
     }
     if (ppart == 0) valid[pe_] = P.ok;
     __syncthreads();
     if (t0 + ATT_TE < p1) valu_fetch<KVDT, WDT>(A, b, r, t0 + ATT_TE + pe_, p1, nkv, win.x, ppart, P);
-    // logits
-    for (int i = tid; i < HQ * ATT_TE; i += ATT_THREADS) {
-      const int hh = i / ATT_TE, e = i % ATT_TE;
-      float s = 0.f;
-      for (int d = 0; d < D; ++d) s = fmaf(qs[hh][d], kvs[e][d], s);
-      lg[hh][e] = valid[e] ? s : -INFINITY;
-    }
-    __syncthreads();
-    // online softmax per head
-    if (tid < HQ) {
-      float mt = mrun[tid];
-      for (int e = 0; e < ATT_TE; ++e) mt = fmaxf(mt, lg[tid][e]);
-      const float a = (mt == -INFINITY) ? 1.f : expf(mrun[tid] - mt);
-      float ls = lrun[tid] * a;
-      for (int e = 0; e < ATT_TE; ++e) {
-        const float pe = (lg[tid][e] == -INFINITY) ? 0.f : expf(lg[tid][e] - mt);
-        lg[tid][e] = pe;
-        ls += pe;
+    // logits of this thread's items: one fma chain per item in dim order,
+    // four dims per LDS read
+    float sv[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) sv[i] = 0.f;
+#pragma unroll 4
+    for (int d = 0; d < D; d += 4) {
+      const float4 q4 = *(const float4*)&qs[h][d];
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const float4 k4 = *(const float4*)&kvs[j + TPH * i][d];
+        sv[i] = fmaf(q4.x, k4.x, sv[i]);
+        sv[i] = fmaf(q4.y, k4.y, sv[i]);
+        sv[i] = fmaf(q4.z, k4.z, sv[i]);
+        sv[i] = fmaf(q4.w, k4.w, sv[i]);
       }
-      mrun[tid] = mt; lrun[tid] = ls; alpha[tid] = a;
     }
+    // online softmax of the head over the tile, across its TPH lanes
+    float mt = m_run;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      if (!valid[j + TPH * i]) sv[i] = -INFINITY;
+      mt = fmaxf(mt, sv[i]);
+    }
+#pragma unroll
+    for (int o = 1; o < TPH; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+    const float a = (mt == -INFINITY) ? 1.f : expf(m_run - mt);
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const float pe = (sv[i] == -INFINITY) ? 0.f : expf(sv[i] - mt);
+      lg[h][j + TPH * i] = pe;
+      ls += pe;
+    }
+#pragma unroll
+    for (int o = 1; o < TPH; o <<= 1) ls += __shfl_xor(ls, o, 64);
+    m_run = mt;
+    l_run = l_run * a + ls;
     __syncthreads();
-    const float a = alpha[h];
 #pragma unroll
     for (int i = 0; i < DPT; ++i) acc[i] *= a;
-    float (*vals)[D + 1] = A.v ? vls : kvs;
+    float (*vals)[DP] = A.v ? vls : kvs;
     for (int e = 0; e < ATT_TE; ++e) {
       const float pe = lg[h][e];
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(pe, vals[e][d0 + i], acc[i]);
+      for (int i = 0; i < DPT; i += 4) {
+        const float4 v4 = *(const float4*)&vals[e][d0 + i];
+        acc[i] = fmaf(pe, v4.x, acc[i]);
+        acc[i + 1] = fmaf(pe, v4.y, acc[i + 1]);
+        acc[i + 2] = fmaf(pe, v4.z, acc[i + 2]);
+        acc[i + 3] = fmaf(pe, v4.w, acc[i + 3]);
+      }
     }
     __syncthreads();
   }
@@ -207,22 +239,22 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_valu_kernel(AttendArgs A, 
   if (S == 1) {
     // final: add the sink and normalise
     const float sk = A.sink[h];
-    const float m = mrun[h];
-    const float M = fmaxf(m, sk);
-    const float em = (m == -INFINITY) ? 0.f : expf(m - M);
-    const float Z = expf(sk - M) + lrun[h] * em;
+    const float M = fmaxf(m_run, sk);
+    const float em = (m_run == -INFINITY) ? 0.f : expf(m_run - M);
+    const float Z = expf(sk - M) + l_run * em;
     const float f = em / Z;
 #pragma unroll
     for (int i = 0; i < DPT; ++i) store_out(A, ((int64_t)r * HQ + h) * D + d0 + i, acc[i] * f);
-    if (A.lse && tid % TPH == 0) A.lse[(int64_t)r * HQ + h] = M + logf(Z);
+    if (A.lse && j == 0) A.lse[(int64_t)r * HQ + h] = M + logf(Z);
   } else {
     const int64_t base = ((int64_t)r * S + split) * HQ + h;
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) part_o[base * D + d0 + i] = acc[i];
-    if (tid % TPH == 0) {
+    for (int i = 0; i < DPT; i += 4)
+      *(float4*)&part_o[base * D + d0 + i] = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+    if (j == 0) {
       // partial maxima in base 2, as the matrix-core kernel writes them
-      part_ml[base * 2] = mrun[h] == -INFINITY ? -INFINITY : mrun[h] * LOG2E;
-      part_ml[base * 2 + 1] = lrun[h];
+      part_ml[base * 2] = m_run == -INFINITY ? -INFINITY : m_run * LOG2E;
+      part_ml[base * 2 + 1] = l_run;
     }
   }
 }
