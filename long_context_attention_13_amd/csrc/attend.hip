@@ -293,10 +293,13 @@ __global__ __launch_bounds__(HQ * 4 * QB, HQ * 4 * QB == 256 ? 2 : 1) void atten
                                        FreshEnt{-1, nullptr, nullptr}, sm.vsclo, sm.vschi);
 }
 
+// BF: partial outputs in bf16 (written by the matrix-core kernels; the fp32
+// kernel writes fp32 ones)
+template <bool BF>
 __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs A, int S, int split_items, const float* part_ml,
                                                            const float* part_o) {
   __shared__ MgShared sm;
-  attend_merge_body(A, S, split_items, part_ml, part_o, blockIdx.x, sm);
+  attend_merge_body<BF>(A, S, split_items, part_ml, part_o, blockIdx.x, sm);
 }
 
 // Several attention calls in one launch: block x of the grid is block
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(128) void attend_merge_batch_kernel(AttendBatch bt)
   __shared__ MgShared sm;
   int j = 0;
   while (j + 1 < bt.njobs && (int)blockIdx.x >= bt.mblk0[j + 1]) ++j;
-  attend_merge_body(bt.job[j], bt.S[j], bt.items[j], bt.ml[j], bt.po[j], (int)blockIdx.x - bt.mblk0[j], sm);
+  attend_merge_body<true>(bt.job[j], bt.S[j], bt.items[j], bt.ml[j], bt.po[j], (int)blockIdx.x - bt.mblk0[j], sm);
 }
 
 // ------------------------------------------------------------------------
@@ -402,7 +405,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (mfma) e = a.kv_dt == DT_FP8 ? launch_mfma<DT_FP8>(a, s, P, ml, po) : launch_mfma<DT_BF16>(a, s, P, ml, po);
   else e = a.q_dt == DT_F32 ? launch_kv<DT_F32>(a, s, P, ml, po) : launch_kv<DT_BF16>(a, s, P, ml, po);
   if (e != hipSuccess || P.S == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, P.S, P.items, ml, po);
+  if (mfma) hipLaunchKernelGGL(attend_merge_kernel<true>, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, P.S, P.items, ml, po);
+  else hipLaunchKernelGGL(attend_merge_kernel<false>, dim3((unsigned)(R * a.Hq)), dim3(128), 0, s, a, P.S, P.items, ml, po);
   return hipGetLastError();
 }
 

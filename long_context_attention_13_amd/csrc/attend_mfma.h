@@ -471,10 +471,18 @@ __device__ __forceinline__ void attend_mfma_body(const AttendArgs& A, int S, int
         store_out(A, ((int64_t)r * HQ + head) * 128 + mt * 16 + 4 * g + i, acc[mt][i] * f);
     if (A.lse && g == 0) A.lse[(int64_t)r * HQ + head] = (M + log2f(Z)) * LN2;
   } else {
+    // partial outputs in bf16 (half the bytes written here and read by the
+    // merge; the rounding is far inside the bf16 / FP8 tolerance), a (row,
+    // head)'s splits side by side ([row][head][split][dim]: the merge reads
+    // them as one contiguous run); maxima and sums in fp32, [row][split][head]
     const int64_t base = ((int64_t)r * S + split) * HQ + head;
+    const int64_t obase = ((int64_t)r * HQ + head) * S + split;
+    uint16_t* pob = (uint16_t*)part_o;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-      *(float4*)&part_o[base * 128 + mt * 16 + 4 * g] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+      *(uint2*)&pob[obase * 128 + mt * 16 + 4 * g] =
+          make_uint2((uint32_t)f32_to_bf16(acc[mt][0]) | ((uint32_t)f32_to_bf16(acc[mt][1]) << 16),
+                     (uint32_t)f32_to_bf16(acc[mt][2]) | ((uint32_t)f32_to_bf16(acc[mt][3]) << 16));
     if (g == 0) { part_ml[base * 2] = m_run; part_ml[base * 2 + 1] = l_run; }
   }
 }
@@ -500,7 +508,11 @@ struct MgShared {
 // Even splits are summed into o0 and odd ones into o1, each in increasing
 // order, whatever MG_PRE and MG_STEP are (both even), so every variant of the
 // body gives the same bits.
-template <int MG_PRE = 64, int MG_STEP = 32>
+// BF: the partial outputs are bf16 in [row][head][split][dim] order (the
+// matrix-core kernels); thread d then loads the dword holding dims d & ~1 and
+// d | 1 (the two lanes of a pair read the same dword) and takes its half.
+// Otherwise fp32 in [row][split][head][dim] order (the fp32 kernel).
+template <bool BF, int MG_PRE = 64, int MG_STEP = 32>
 __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all, int split_items,
                                                   const float* part_ml, const float* part_o, int blk, MgShared& sm,
                                                   bool store = true) {
@@ -516,9 +528,16 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
   const int64_t base0 = (int64_t)r * S_all * A.Hq + h;      // partial (r, s, h) = base0 + s*Hq
   const int64_t ost = (int64_t)A.Hq * A.D;
   const float* po = part_o + base0 * A.D + d;
-  float ov[MG_PRE];
+  const uint32_t* pw =
+      (const uint32_t*)((const uint16_t*)part_o + ((int64_t)r * A.Hq + h) * S_all * A.D) + (d >> 1);
+  const int hs = (d & 1) ? 0 : 16;          // the shift that puts this dim's bf16 in the high half
+  // partial s as loaded (its word; fp32 bits or the bf16 pair), and as a value
+  // (taken only where it is summed, so that every load is issued first)
+  auto raw = [&](int s) -> uint32_t { return BF ? pw[s * (A.D >> 1)] : __float_as_uint(po[s * ost]); };
+  auto val = [&](uint32_t w) -> float { return BF ? __uint_as_float((w << hs) & 0xFFFF0000u) : __uint_as_float(w); };
+  uint32_t ov[MG_PRE];
 #pragma unroll
-  for (int i = 0; i < MG_PRE; ++i) ov[i] = i < S_all ? po[i * ost] : 0.f;
+  for (int i = 0; i < MG_PRE; ++i) ov[i] = i < S_all ? raw(i) : 0u;
   float mv[8], lv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -554,17 +573,17 @@ __device__ __forceinline__ void attend_merge_body(const AttendArgs& A, int S_all
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int i = 0; i < MG_PRE; i += 2) {
-    if (i < S) o0 = fmaf(ov[i], wsp[i], o0);
-    if (i + 1 < S) o1 = fmaf(ov[i + 1], wsp[i + 1], o1);
+    if (i < S) o0 = fmaf(val(ov[i]), wsp[i], o0);
+    if (i + 1 < S) o1 = fmaf(val(ov[i + 1]), wsp[i + 1], o1);
   }
   for (int s0 = MG_PRE; s0 < S; s0 += MG_STEP) {
-    float ot[MG_STEP];
+    uint32_t ot[MG_STEP];
 #pragma unroll
-    for (int i = 0; i < MG_STEP; ++i) ot[i] = s0 + i < S ? po[(s0 + i) * ost] : 0.f;
+    for (int i = 0; i < MG_STEP; ++i) ot[i] = s0 + i < S ? raw(s0 + i) : 0u;
 #pragma unroll
     for (int i = 0; i < MG_STEP; i += 2) {
-      if (s0 + i < S) o0 = fmaf(ot[i], wsp[s0 + i], o0);
-      if (s0 + i + 1 < S) o1 = fmaf(ot[i + 1], wsp[s0 + i + 1], o1);
+      if (s0 + i < S) o0 = fmaf(val(ot[i]), wsp[s0 + i], o0);
+      if (s0 + i + 1 < S) o1 = fmaf(val(ot[i + 1]), wsp[s0 + i + 1], o1);
     }
   }
   const float o = o0 + o1;

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(SEL_THREADS) void index_select_merge_kernel(IndexAr
   int j = 0;
   while (j + 1 < mb.njobs && u >= mb.mblk0[j + 1]) ++j;
   MgShared& sm = ((MgShared*)smem)[g];
-  attend_merge_body<16, 16>(mb.job[j], mb.S[j], mb.items[j], mb.ml[j], mb.po[j], u - mb.mblk0[j], sm, real);
+  attend_merge_body<true, 16, 16>(mb.job[j], mb.S[j], mb.items[j], mb.ml[j], mb.po[j], u - mb.mblk0[j], sm, real);
 }
 
 // ------------------------------------------------------------------------
