@@ -90,6 +90,26 @@ def test_sparse_decode_rows(kv_dt, q_dt, out_dt):
     assert_lse_close(l, rl, rt, "lse")
 
 
+@pytest.mark.parametrize("Hq", [16, 32, 64])
+@pytest.mark.parametrize("k", [40, 700])
+def test_fp32_rows_every_head_count(Hq, k):
+    """The fp32 kernel's per-head lane groups (256 / Hq lanes a head, 32 / (256
+    / Hq) items a lane and tile) on ragged lists: a partial last tile, -1
+    indices inside the list, a short window, an empty window, lists of one
+    split (k = 40 with a 64-token window buffer: 104 items at most) and lists
+    cut into splits (k = 700 with 128)."""
+    B, N_cap = 3, 3000
+    W = 64 if k == 40 else 128
+    g, q, kv, kv_sc, win, sink = make(91 + Hq + k, B, 1, Hq, N_cap, W, lca.F32, lca.F32)
+    sel = np.stack([np.sort(g.choice(N_cap, k, replace=False)) for _ in range(B)]).astype(np.int32)[:, None]
+    sel[1, 0, 3::7] = -1
+    wl = np.array([[W], [5], [0]], np.int32)
+    o, l, ro, rl = run(True, q, lca.F32, kv, lca.F32, None, sel, win, lca.F32, np.zeros((B, 1), np.int32), wl, sink,
+                       1 / math.sqrt(128), lca.F32)
+    assert_rows_close(o, ro, 1e-4, "out")
+    assert_lse_close(l, rl, 1e-4, "lse")
+
+
 @pytest.mark.parametrize("kv_dt,N_cap", [(lca.BF16, 512), (lca.FP8E4M3, 8192), (lca.FP8E4M3, 1000)])
 def test_hca_decode_rows(kv_dt, N_cap):
     B, Hq, W = 3, 64, 128
