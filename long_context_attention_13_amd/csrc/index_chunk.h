@@ -16,7 +16,7 @@ struct IdxWs {
   int32_t* cidx;  // [R][NCH][CAP]
 };
 
-inline IdxWs carve(void* ws, int64_t R, int64_t NCH) {
+__host__ __device__ inline IdxWs carve(void* ws, int64_t R, int64_t NCH) {
   IdxWs w;
   char* p = (char*)ws;
   w.cnt = (int32_t*)p; p += align256(sizeof(int32_t) * R * NCH);

@@ -975,7 +975,7 @@ __device__ __forceinline__ bool emit_regs(const uint64_t (&bk)[LB], const int32_
 
 // The prefill path (index_prefill.hip): many query rows per sequence.
 bool index_prefill_applies(const IndexArgs& a);
-size_t index_prefill_ws_bytes(int B, int Tq);
+size_t index_prefill_ws_bytes(int B, int Tq, int64_t N_cap, int k);
 hipError_t launch_index_prefill(const IndexArgs& a, hipStream_t s);
 
 // Dynamic LDS of a workgroup running the block-wide selection.

@@ -10,9 +10,9 @@
 // contraction so that it runs on the FP4 matrix cores:
 //
 //   sample  each row scores a strided sample of its eligible keys (one key in
-//           sigma) and takes the 64th largest sampled score, rounded down, as
-//           its candidate threshold t: about 64*sigma entries of the row
-//           reach it.  A workgroup samples 16 rows (the MFMA's columns), or
+//           sigma = k/16) and takes the 32nd largest sampled score, rounded
+//           down, as its candidate threshold t: about 32*sigma entries of the
+//           row reach it.  A workgroup samples 16 rows (the MFMA's columns), or
 //           fewer when the rows' samples would not fit its LDS (16 rows up
 //           to about 4200 samples a row, 8 up to 8400, ... 2 up to 33700).
 //   score   a workgroup holds 64 query rows (16 per wavefront, the MFMA's
@@ -34,9 +34,13 @@
 //           set is complete when T(1-eps) >= t(1+eps).
 //   fallback rows failing any check (a candidate list overflowed, too few or
 //           too many candidates, a wide band, a negative head weight, a key
-//           outside the exactness envelope) are queued and selected by
-//           re-scoring every entry exactly, as the decode path does.
+//           outside the exactness envelope) are queued; the first PF_QFAST of
+//           them are selected by the decode path's scan and select over
+//           their key rows (a workgroup per chunk and queued row, then one per
+//           row), any further ones by re-scoring every entry exactly in one
+//           workgroup per row.
 #include "index_common.h"
+#include "index_select.h"
 
 namespace lca {
 
@@ -51,7 +55,8 @@ constexpr int PF_SPAD = 16;                  // padding of a row of samples (16-
 // sampled keys per row at most: a row of them, rounded up to 64 and padded,
 // fits half of PF_SROWS_LDS (two rows a workgroup)
 constexpr int PF_SMAX = (PF_SROWS_LDS / 2 / 2 - PF_SPAD) / 64 * 64;
-constexpr int PF_RANK = 64;           // threshold = PF_RANK-th largest sampled score
+constexpr int PF_RANK = 32;           // threshold = PF_RANK-th largest sampled score
+constexpr int PF_QFAST = 16;          // queued rows the decode scan and select take
 constexpr int PF_CAND = 3840;         // candidates per row the select pass holds
 constexpr int PF_CPL = PF_CAND / 64;  // ... per lane
 constexpr int PF_BAND = 64;           // band entries re-scored exactly
@@ -65,6 +70,7 @@ struct PfWs {
   int32_t* cnt;     // [R][PF_NKC][4] candidates per list (> PF_LCAP: overflow)
   uint64_t* cand;   // [R][PF_NKC][4][PF_LCAP] (fp32 score bits << 32) | j
   int32_t* queue;   // [1 + R] fallback queue: count, rows
+  char* qws;        // [PF_QFAST] decode-scan workspaces of the queued rows (qslot bytes each)
 };
 
 static PfWs pf_carve(void* ws, int64_t R) {
@@ -74,8 +80,26 @@ static PfWs pf_carve(void* ws, int64_t R) {
   w.flags = (int32_t*)p; p += align256(sizeof(int32_t) * R);
   w.cnt = (int32_t*)p; p += align256(sizeof(int32_t) * R * PF_NKC * 4);
   w.cand = (uint64_t*)p; p += align256(sizeof(uint64_t) * R * PF_NKC * 4 * PF_LCAP);
-  w.queue = (int32_t*)p;
+  w.queue = (int32_t*)p; p += align256(sizeof(int32_t) * (R + 1));
+  w.qws = p;
   return w;
+}
+
+// The decode scan of PF_QFAST queued rows: its chunk size (chosen as for a
+// call of PF_QFAST one-row sequences) and the workspace of one row.
+struct PfQPlan {
+  int kpl, NCH;
+  size_t slot;
+};
+static PfQPlan pf_qplan(int64_t N_cap, int k) {
+  IndexArgs v{};
+  v.B = PF_QFAST; v.Tq = 1; v.N_cap = N_cap; v.k = k;
+  PfQPlan q;
+  q.kpl = choose_kpl(v, 1);
+  const int64_t nch = (N_cap + 64 * q.kpl - 1) / (64 * q.kpl);
+  q.NCH = (int)(nch > 0 ? nch : 1);
+  q.slot = align256(carve_bytes(1, q.NCH));
+  return q;
 }
 
 static size_t pf_bytes(int64_t R) {
@@ -83,10 +107,13 @@ static size_t pf_bytes(int64_t R) {
          align256(sizeof(uint64_t) * R * PF_NKC * 4 * PF_LCAP) + align256(sizeof(int32_t) * (R + 1));
 }
 
-// Sample stride: at least k/32 (so about 64*sigma <= 2k candidates per row
-// at sigma = k/32) and enough to keep the sample within PF_SMAX keys.
+// Sample stride: at least k/16 (so about 32*sigma <= 2k candidates per row
+// at sigma = k/16) and enough to keep the sample within PF_SMAX keys.  The
+// threshold misses a row's k-th largest score when 32 of its top-k entries
+// fall in a sample that holds 16 of them on average, about once in 10^4
+// rows; such a row is queued and selected by the decode scan.
 static int pf_sigma(const IndexArgs& a) {
-  int s = a.k / 32;
+  int s = a.k / 16;
   const int64_t need = (a.N_cap + PF_SMAX - 1) / PF_SMAX;
   if (need > s) s = (int)need;
   return s < 1 ? 1 : s;
@@ -103,7 +130,9 @@ bool index_prefill_applies(const IndexArgs& a) {
          a.N_cap >= 64 && a.N_cap <= PF_NMAX && a.N_cap % 4 == 0;
 }
 
-size_t index_prefill_ws_bytes(int B, int Tq) { return pf_bytes((int64_t)B * Tq); }
+size_t index_prefill_ws_bytes(int B, int Tq, int64_t N_cap, int k) {
+  return pf_bytes((int64_t)B * Tq) + PF_QFAST * pf_qplan(N_cap, k).slot;
+}
 
 // ------------------------------------------------------------------------
 // The lane's query operands: row c = lane & 15 of the wave's 16 rows,
@@ -265,12 +294,12 @@ __global__ __launch_bounds__(PF_SWAVES * 64) void pf_sample_kernel(IndexArgs A, 
       // at most 8 bits from the highest bit where the row's samples differ
       // (their common leading bits -- most of the exponent -- would put
       // nearly all of them in one bin and serialise the counting)
-      // Every lane holds at least one sample (Sq >= PF_RANK = 64 lanes), so
-      // the smallest lane maximum vmn has at least PF_RANK samples at or
-      // above it: the PF_RANK-th largest is >= vmn, and samples below vmn
-      // take no part in the counting (they would pile into the lowest bins
-      // and serialise the LDS atomics).
-      static_assert(PF_RANK == WAVE, "one lane maximum per rank");
+      // The smallest lane maximum vmn has at least 64 samples at or above it
+      // when every lane holds one (and is 0 otherwise), so the PF_RANK-th
+      // largest (PF_RANK <= 64) is >= vmn, and samples below vmn take no
+      // part in the counting (they would pile into the lowest bins and
+      // serialise the LDS atomics).
+      static_assert(PF_RANK <= WAVE, "the smallest lane maximum bounds the rank");
       uint32_t vmx = 0;
       for (int i = lane; i < Sq; i += 64) vmx = max(vmx, (uint32_t)v[i]);
       uint32_t vmn = vmx;
@@ -768,7 +797,7 @@ __global__ __launch_bounds__(SEL_THREADS) void pf_fallback_kernel(IndexArgs A, P
   float* wl = (float*)(region + 12 * CMAX);
   const int qn = W.queue[0];
 #pragma unroll 1
-  for (int i = blockIdx.x; i < qn; i += gridDim.x) {
+  for (int i = PF_QFAST + blockIdx.x; i < qn; i += gridDim.x) {
     const int r = W.queue[1 + i];
     __syncthreads();
     if (threadIdx.x < 32) wl[threadIdx.x] = (threadIdx.x < (unsigned)A.H) ? A.w[(int64_t)r * A.H + threadIdx.x] : 0.f;
@@ -779,6 +808,44 @@ __global__ __launch_bounds__(SEL_THREADS) void pf_fallback_kernel(IndexArgs A, P
     double* sout = A.score_out ? A.score_out + (int64_t)r * A.k : nullptr;
     select_streamed<DT_MXFP4, HP>(A, r, n, kk, out, sout, S, tbuf, wl, nullptr, n <= A.k);
   }
+}
+
+// The queued row r as a call of one sequence with one query row (the decode
+// scan and select read the row through it).
+__device__ __forceinline__ IndexArgs pf_row_view(const IndexArgs& A, int64_t r) {
+  IndexArgs v = A;
+  const int64_t b = r / A.Tq;
+  v.B = 1;
+  v.Tq = 1;
+  v.qi = (const uint8_t*)A.qi + r * A.H * (A.d / 2);
+  v.qi_scale = A.qi_scale + r * A.H * (A.d / 32);
+  v.w = A.w + r * A.H;
+  v.n_elig = A.n_elig + r;
+  v.ki = (const uint8_t*)A.ki + b * A.N_cap * (A.d / 2);
+  v.ki_scale = A.ki_scale + b * A.N_cap * (A.d / 32);
+  v.idx_out = A.idx_out + r * A.k;
+  v.score_out = A.score_out ? A.score_out + r * A.k : nullptr;
+  return v;
+}
+
+// Chunk c of queued row g (g < PF_QFAST; slots past the queue exit at once).
+template <int KPL, int HP>
+__global__ __launch_bounds__(256) void pf_qscan_kernel(IndexArgs A, PfWs W, size_t slot, int NCH) {
+  __shared__ ChunkShared<1> sm;
+  const int g = blockIdx.y;
+  if (g >= min(W.queue[0], PF_QFAST)) return;
+  const IndexArgs v = pf_row_view(A, W.queue[1 + g]);
+  index_chunk_body<DT_MXFP4, KPL, HP, 1>(v, carve(W.qws + g * slot, 1, NCH), NCH, 1, blockIdx.x, 0, sm);
+}
+
+// The selection of queued row g over its chunks' candidates.
+template <int HP>
+__global__ __launch_bounds__(SEL_THREADS) void pf_qselect_kernel(IndexArgs A, PfWs W, size_t slot, int NCH, int CH) {
+  extern __shared__ __align__(16) char smem[];
+  const int g = blockIdx.x;
+  if (g >= min(W.queue[0], PF_QFAST)) return;
+  const IndexArgs v = pf_row_view(A, W.queue[1 + g]);
+  index_select_body<DT_MXFP4, HP>(v, carve(W.qws + g * slot, 1, NCH), NCH, CH, 0, smem);
 }
 
 // ------------------------------------------------------------------------
@@ -802,6 +869,22 @@ static hipError_t launch_pf(const IndexArgs& a, hipStream_t s) {
                      dim3(256), (size_t)2 * PF_STAGE_B, s, a, W, KC);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((pf_select_kernel<HP>), dim3((unsigned)R), dim3(PS_NT), sizeof(PfSelShared), s, a, W, KC);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the first PF_QFAST queued rows: decode scan (when the rows are long
+  // enough to use it) and select
+  const PfQPlan q = pf_qplan(a.N_cap, a.k);
+  const int qn = (int)(R < PF_QFAST ? R : PF_QFAST);
+  if (a.N_cap > NDIRECT) {
+    const dim3 qg((unsigned)q.NCH, (unsigned)qn);
+    switch (q.kpl) {
+      case 32: hipLaunchKernelGGL((pf_qscan_kernel<32, HP>), qg, dim3(256), 0, s, a, W, q.slot, q.NCH); break;
+      case 16: hipLaunchKernelGGL((pf_qscan_kernel<16, HP>), qg, dim3(256), 0, s, a, W, q.slot, q.NCH); break;
+      default: hipLaunchKernelGGL((pf_qscan_kernel<4, HP>), qg, dim3(256), 0, s, a, W, q.slot, q.NCH); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((pf_qselect_kernel<HP>), dim3((unsigned)qn), dim3(SEL_THREADS), select_smem(a.dt, a.H, a.d), s, a,
+                     W, q.slot, q.NCH, 64 * q.kpl);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned fg = (unsigned)(R < PF_FALLBACK_GRID ? R : PF_FALLBACK_GRID);
   hipLaunchKernelGGL((pf_fallback_kernel<HP>), dim3(fg), dim3(SEL_THREADS), select_smem(a.dt, a.H, a.d), s, a, W);

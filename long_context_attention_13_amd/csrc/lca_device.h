@@ -11,7 +11,7 @@
 namespace lca {
 
 // byte sizes of carved workspace regions are rounded up to 256
-static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 
 constexpr int WAVE = 64;
